@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the hybrid compressed-attention path on one MI355X.
+
+A step is one pass of the whole path over one batch: for every sequence the
+new token is inserted into the raw-window, c4a-main and c4a-index pools
+(compress_insert x3), the indexer picks the causal top-512 (index_topk) and
+64-head attention runs over top-512 U the 128-token window with the inverse
+RoPE epilogue (hybrid_attn_decode).  Default workload: 16 sequences of 131072
+cached tokens (32768 c4a entries each), queries at p = 131072.
+
+Inputs are resident in HBM before timing; every step reads a different one of
+R cache replicas (R * 538 MB main + 134 MB index) so that the 256 MB
+Infinity Cache cannot serve one step's reads to the next.  Steps are replayed
+from HIP graphs (the launch-amortisation the pages describe for decode).
+
+Prints one JSON line (rank 0, N = 1).  The CPU oracle is timed beside it on a
+bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/s + HBM GB/s, c4a top-k512+SWA128 at 128K ctx, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_c4a_decode_b16_128k.pmc.json")
+SCORE_SOURCE = os.path.join(ROOT, "compressed_sparse_long_amd", "csrc", "index_topk.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workload setup (GPU)
+# ---------------------------------------------------------------------------
+
+class DecodeSetup:
+    """Pools, block table and step inputs of a decode workload, resident on the GPU."""
+
+    def __init__(self, w, replicas: int, device="cuda"):
+        import torch
+
+        import compressed_sparse_long_amd as csl
+        from synth import workloads as W
+
+        self.w, self.csl, self.torch = w, csl, torch
+        self.dev = device
+        T, D, R, DI = w.ctx, w.dim, w.rope_dims, w.idx_dim
+        P = w.num_pages
+        self.bt = W.block_table(w).to(device)
+        ns = w.num_seqs
+        kv = w.kv_dtype
+        self.layers = w.layers
+        base = {}
+        if "c4a" in w.layers:
+            base["main4"] = csl.Pool(4, 2, D, R, w.theta, kv, P, device=device)
+            base["idx"] = csl.Pool(4, 2, DI, 0, w.theta, csl.BF16, P, device=device)
+        if "c128a" in w.layers:
+            base["main128"] = csl.Pool(128, 1, D, R, w.theta, kv, P, device=device)
+        base["raw"] = csl.Pool(1, 1, D, R, w.theta, kv, P, device=device, state=False)
+        zeros = torch.zeros(ns, dtype=torch.int64, device=device)
+        t0 = time.time()
+        for s in range(ns):
+            cu = torch.tensor([0] * (s + 1) + [T] * (ns - s), dtype=torch.int32, device=device)
+            x = W.latent(w, s, 0, T, device=device)
+            csl.compress_insert(base["raw"], self.bt, zeros, cu, x)
+            if "c4a" in w.layers:
+                csl.compress_insert(base["main4"], self.bt, zeros, cu, x, W.logits(w, s, 0, T, 2, device=device),
+                                    W.gain(w, D, device=device))
+                if w.synth_index_keys:
+                    keys = W.index_keys(w, s, 0, T // 4, device=device)
+                    nb = T // 256
+                    rows = base["idx"].rows.view(P, 64, DI * 2)
+                    rows[self.bt[s, :nb].long()] = keys.view(torch.uint8).view(nb, 64, DI * 2)
+                else:
+                    xi = W.latent(w, s, 0, T, dim=DI, tid=W.T_XI, device=device)
+                    csl.compress_insert(base["idx"], self.bt, zeros, cu, xi,
+                                        W.logits(w, s, 0, T, 2, tid=W.T_LOGITS_I, device=device),
+                                        W.gain(w, DI, tid=W.T_GAIN_I, device=device))
+            if "c128a" in w.layers:
+                csl.compress_insert(base["main128"], self.bt, zeros, cu, x,
+                                    W.logits(w, s, 0, T, 1, tid=W.T_LOGITS_128, device=device))
+            del x
+        torch.cuda.synchronize()
+        log(f"cache built in {time.time() - t0:.1f}s")
+        # replicas: own rows, shared compressor state
+        self.reps = [base]
+        for _ in range(replicas - 1):
+            r = {}
+            for k, p in base.items():
+                r[k] = csl.Pool(p.ratio, p.coff, p.dim, p.rope_dims, p.theta, p.dtype, p.num_pages,
+                                rows=p.rows.clone(), state=False, state_x=p.state_x, state_logits=p.state_logits)
+            self.reps.append(r)
+        torch.cuda.synchronize()
+        # step inputs: the new token at position T of every sequence, queries at p = T
+        self.start = torch.full((ns,), T, dtype=torch.int64, device=device)
+        self.cu1 = torch.arange(ns + 1, dtype=torch.int32, device=device)
+        self.x_new = torch.stack([W.latent(w, s, T, 1, device=device)[0] for s in range(ns)])
+        self.lg_new = torch.stack([W.logits(w, s, T, 1, 2, device=device)[0] for s in range(ns)])
+        self.lg128_new = torch.stack([W.logits(w, s, T, 1, 1, tid=W.T_LOGITS_128, device=device)[0]
+                                      for s in range(ns)])
+        self.xi_new = torch.stack([W.latent(w, s, T, 1, dim=DI, tid=W.T_XI, device=device)[0] for s in range(ns)])
+        self.lgi_new = torch.stack([W.logits(w, s, T, 1, 2, tid=W.T_LOGITS_I, device=device)[0] for s in range(ns)])
+        self.gain = W.gain(w, D, device=device)
+        self.gain_i = W.gain(w, DI, tid=W.T_GAIN_I, device=device)
+        qd = W.queries(w, device=device)
+        self.q, self.q_idx, self.w_idx = qd["q"], qd["q_idx"], qd["w_idx"]
+        self.q_seq = w.query_seqs().to(device)
+        self.q_pos = w.query_positions().to(device)
+        nq = w.num_q
+        self.max_pos = T
+        self.topk = torch.empty((nq, w.topk), dtype=torch.int32, device=device)
+        self.ws_idx = torch.empty(max(1, csl.index_topk_workspace(nq, T, w.topk) // 4), dtype=torch.float32,
+                                  device=device)
+        ws4 = csl.hybrid_attn_workspace(nq, w.n_heads, D, 4, w.topk, w.swa, T) if "c4a" in w.layers else 0
+        ws128 = csl.hybrid_attn_workspace(nq, w.n_heads, D, 128, 0, w.swa, T) if "c128a" in w.layers else 0
+        self.ws_attn = torch.empty(max(1, max(ws4, ws128) // 4), dtype=torch.float32, device=device)
+        odt = {0: torch.float32, 1: torch.bfloat16, 2: torch.uint8}[w.out_dtype]
+        self.out = {l: torch.empty((nq, w.n_heads, D), dtype=odt, device=device) for l in w.layers}
+        self.out_scales = {l: (torch.empty((nq, w.n_heads, D // 64), dtype=torch.float32, device=device)
+                               if w.out_dtype == 2 else None) for l in w.layers}
+        self.scale = D ** -0.5
+
+    def step(self, r: int):
+        csl, w, p = self.csl, self.w, self.reps[r]
+        csl.compress_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new)
+        if "c4a" in self.layers:
+            csl.compress_insert(p["main4"], self.bt, self.start, self.cu1, self.x_new, self.lg_new, self.gain)
+            csl.compress_insert(p["idx"], self.bt, self.start, self.cu1, self.xi_new, self.lgi_new, self.gain_i)
+            csl.index_topk(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx, w.topk,
+                           self.topk, None, self.ws_idx)
+            csl.hybrid_attn_decode(p["main4"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q,
+                                   self.topk, w.topk, w.swa, self.scale, w.out_dtype, self.out["c4a"],
+                                   self.out_scales["c4a"], self.ws_attn)
+        if "c128a" in self.layers:
+            csl.compress_insert(p["main128"], self.bt, self.start, self.cu1, self.x_new, self.lg128_new)
+            csl.hybrid_attn_decode(p["main128"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q,
+                                   None, 0, w.swa, self.scale, w.out_dtype, self.out["c128a"],
+                                   self.out_scales["c128a"], self.ws_attn)
+
+    def algorithmic_bytes_per_step(self) -> dict:
+        """Bytes the method must move per step (no intermediate buffers)."""
+        w = self.w
+        nq, D, H = w.num_q, w.dim, w.n_heads
+        rb = self.csl.row_bytes(D, w.kv_dtype)
+        ob = {0: 4 * D, 1: 2 * D, 2: D + 4 * (D // 64)}[w.out_dtype]
+        per_q = {}
+        qio = H * D * 2 + H * ob
+        ins = 2 * D * 2 + rb  # raw insert: x read, state x write (c4a/c128a), raw row write
+        if "c4a" in w.layers:
+            idx = w.ctx // 4 * w.idx_dim * 2 + w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4
+            per_q["index_score"] = idx
+            per_q["c4a"] = idx + (w.topk + w.swa) * rb + qio + ins + w.idx_dim * 2 * 2
+        if "c128a" in w.layers:
+            per_q["c128a"] = (w.ctx // 128 + w.swa) * rb + qio + ins
+        return {k: v * nq for k, v in per_q.items()}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(setup: DecodeSetup, n_seqs: int, seconds: float) -> dict:
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from synth import workloads as W
+
+    w = setup.w
+    assert w.layers == ("c4a",), "the CPU baseline covers the c4a decode workload"
+    T, D, R, DI = w.ctx, w.dim, w.rope_dims, w.idx_dim
+    n = min(n_seqs, w.num_seqs)
+    mb = w.max_blocks
+    bt = np.arange(n * mb, dtype=np.int32).reshape(n, mb)
+    P = n * mb
+    t0 = time.time()
+    main = O.HostPool(4, 2, D, R, w.theta, O.BF16, P)
+    raw = O.HostPool(1, 1, D, R, w.theta, O.BF16, P)
+    idx = O.HostPool(4, 2, DI, 0, w.theta, O.BF16, P)
+
+    def u16(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    xs = np.concatenate([u16(W.latent(w, s, 0, T, device="cuda")) for s in range(n)])
+    lgs = np.concatenate([W.logits(w, s, 0, T, 2, device="cuda").cpu().numpy() for s in range(n)])
+    st = np.zeros(n, np.int64)
+    cu = (np.arange(n + 1) * T).astype(np.int32)
+    assert O.compress_insert(main, bt, st, cu, xs, lgs) == 0
+    assert O.compress_insert(raw, bt, st, cu, xs) == 0
+    del xs, lgs
+    for s in range(n):
+        keys = u16(W.index_keys(w, s, 0, T // 4, device="cuda"))
+        idx.rows[bt[s, :T // 256]] = keys.view(np.uint8).reshape(T // 256, 64, DI * 2)
+    log(f"oracle cache for {n} sequences built in {time.time() - t0:.1f}s")
+    x_new = u16(setup.x_new[:n])
+    lg_new = setup.lg_new[:n].cpu().numpy()
+    xi_new = u16(setup.xi_new[:n])
+    lgi_new = setup.lgi_new[:n].cpu().numpy()
+    q = u16(setup.q[:n])
+    qi = u16(setup.q_idx[:n])
+    wi = setup.w_idx[:n].cpu().numpy()
+    q_seq = np.arange(n, dtype=np.int32)
+    q_pos = np.full(n, T, np.int64)
+    st1 = np.full(n, T, np.int64)
+    cu1 = np.arange(n + 1, dtype=np.int32)
+    reps, t_start = 0, time.perf_counter()
+    while True:
+        O.compress_insert(raw, bt, st1, cu1, x_new)
+        O.compress_insert(main, bt, st1, cu1, x_new, lg_new)
+        O.compress_insert(idx, bt, st1, cu1, xi_new, lgi_new)
+        topk, _, _, _ = O.index_topk(idx, bt, q_seq, q_pos, qi, wi, w.topk)
+        O.hybrid_attn(main, raw, bt, q_seq, q_pos, q, topk=topk, swa_window=w.swa, softmax_scale=setup.scale,
+                      out_dtype=w.out_dtype)
+        reps += 1
+        el = time.perf_counter() - t_start
+        if el >= seconds:
+            break
+    threads = O.num_threads()
+    return {"value": round(n * reps / el, 3), "unit": "queries/s", "cores": min(threads, n), "kind": "oracle",
+            "sample": f"{n} of the {w.num_seqs} sequences (one query each) x {reps} full decode steps "
+                      f"(compress_insert x3, index_topk, hybrid_attn) in {el:.1f}s, fp64, OpenMP over queries "
+                      f"({threads} threads available)"}
+
+
+# ---------------------------------------------------------------------------
+
+def traffic_from_profile(launch_kind: str):
+    """HBM bytes per launch of the index score kernel from committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    sha = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
+    if d.get("source_sha256") != sha or d.get("launch") != launch_kind:
+        return None
+    return float(d["hbm_bytes_per_launch"])
+
+
+def copy_calibration(mb: int, iters: int):
+    import torch
+    n = mb * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "iters": iters}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="c4a", choices=["c4a", "c128a", "1m"])
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying HIP graphs")
+    ap.add_argument("--cpu-seqs", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path is data-parallel per sequence and this build runs on a "
+              "single MI355X; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb, 10)
+        return
+
+    import torch
+
+    import compressed_sparse_long_amd as csl
+    from synth import workloads as W
+
+    w = {"c4a": W.c4a_decode, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
+    R = max(1, args.replicas)
+    setup = DecodeSetup(w, R)
+    log(f"workload {w.name}: {w.num_seqs} x {w.ctx} tokens, {R} replicas")
+
+    for i in range(args.warmup):
+        setup.step(i % R)
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0, "device error flags after warm-up"
+
+    timing_kernel = csl.KERNEL_INDEX_SCORE if "c4a" in w.layers else csl.KERNEL_ATTN
+    graphs = None
+    if not args.no_graph:
+        graphs = []
+        csl.timer_enable(timing_kernel, True)
+        for r in range(R):                         # creates the event pairs outside the capture
+            setup.step(r)
+        torch.cuda.synchronize()
+        csl.timer_read(timing_kernel)
+        for r in range(R):                         # event pairs become nodes of each step graph
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                setup.step(r)
+            graphs.append(g)
+        csl.timer_enable(timing_kernel, False)
+        torch.cuda.synchronize()
+        csl.timer_read(timing_kernel)              # nothing ran yet; resets the counter
+        for r in range(R):
+            graphs[r].replay()
+        torch.cuda.synchronize()
+
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graphs:
+        for i in range(K):
+            graphs[i % R].replay()
+    else:
+        csl.timer_enable(timing_kernel, True)
+        for i in range(K):
+            setup.step(i % R)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not graphs:
+        csl.timer_enable(timing_kernel, False)
+    k_ms, k_n = csl.timer_read(timing_kernel)
+    assert csl.read_device_error() == 0, "device error flags after the timed steps"
+    ms_per_step = (t1 - t0) * 1e3 / K
+    qps = w.num_q / (ms_per_step * 1e-3)
+    alg = setup.algorithmic_bytes_per_step()
+    step_bytes = sum(v for k, v in alg.items() if k != "index_score")
+    kernel_name = "index_score_kernel" if "c4a" in w.layers else "hybrid_attn_kernel"
+    k_avg_ms = k_ms / max(1, k_n)
+    k_bytes = alg["index_score"] if "c4a" in w.layers else alg["c128a"]
+    achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9 if k_n else None
+    roof = {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+            "traffic": traffic_from_profile(w.name) if "c4a" in w.layers else None,
+            "algorithmic_bytes_per_launch": k_bytes, "avg_launch_ms": round(k_avg_ms, 5), "timed_launches": k_n,
+            "timing": "HIP event pair around each launch, recorded inside the step graphs (last replay of each "
+                      "replica's graph)" if graphs else "HIP event pair around each launch of the timed steps"}
+    res = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == 1 else "fp8-kv/bf16-mfma", "data": "synthetic",
+        "hbm_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "context": w.ctx, "layers": list(w.layers),
+                   "topk": w.topk, "swa": w.swa, "heads": w.n_heads, "latent_dim": w.dim, "rope_dims": w.rope_dims,
+                   "indexer": f"{w.idx_heads}x{w.idx_dim}", "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
+                   "out_dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.out_dtype], "replicas": R,
+                   "hip_graphs": bool(graphs), "algorithmic_bytes_per_step": step_bytes},
+        "roofline": roof,
+    }
+    if not args.no_cpu and w.layers == ("c4a",):
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(setup, args.cpu_seqs, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

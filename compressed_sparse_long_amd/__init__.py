@@ -1,0 +1,201 @@
+"""Python binding of libcsl.so, the gfx950 hybrid compressed-attention library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels; torch supplies device memory and the stream.  The functions carry
+the C ABI's names (include/csl.h) without the ``csl_`` prefix.  Importing this
+module fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsl.so")
+
+F32, BF16, FP8 = 0, 1, 2
+BLOCK = 256
+KERNEL_COMPRESS, KERNEL_INDEX_SCORE, KERNEL_TOPK_SELECT, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 0, 1, 2, 3, 4
+DEVERR_UNMAPPED_PAGE, DEVERR_TOPK_ID, DEVERR_POSITION, DEVERR_SEQ = 1, 2, 4, 8
+
+_STATUS = {0: "CSL_OK", -1: "CSL_EINVAL", -2: "CSL_ERANGE", -3: "CSL_EALIGN", -4: "CSL_EWORKSPACE",
+           -5: "CSL_EHIP", -6: "CSL_EUNSUPPORTED"}
+
+
+class CslError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+
+class _Pool(C.Structure):
+    _fields_ = [
+        ("ratio", C.c_int32), ("coff", C.c_int32), ("dim", C.c_int32), ("rope_dims", C.c_int32),
+        ("rope_theta", C.c_double),
+        ("dtype", C.c_int32), ("num_pages", C.c_int32),
+        ("rows", C.c_void_p), ("state_x", C.c_void_p), ("state_logits", C.c_void_p),
+    ]
+
+
+class _Pages(C.Structure):
+    _fields_ = [("block_table", C.c_void_p), ("num_seqs", C.c_int32), ("max_blocks", C.c_int32)]
+
+
+_lib = C.CDLL(LIB_PATH)
+_vp, _i32, _i64, _sz, _f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+_P = C.POINTER(_Pool)
+_G = C.POINTER(_Pages)
+
+
+def _sig(name, res, args):
+    fn = getattr(_lib, name)
+    fn.restype = res
+    fn.argtypes = args
+    return fn
+
+
+_row_bytes = _sig("csl_row_bytes", _sz, [_i32, _i32])
+_compress_insert = _sig("csl_compress_insert", C.c_int, [_P, _G, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp])
+_index_topk_ws = _sig("csl_index_topk_workspace", _sz, [_i32, _i64, _i32])
+_index_topk = _sig("csl_index_topk", C.c_int,
+                   [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
+_attn_ws = _sig("csl_hybrid_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i64])
+_attn_decode = _sig("csl_hybrid_attn_decode", C.c_int,
+                    [_P, _P, _G, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz,
+                     _vp])
+_attn_prefill = _sig("csl_hybrid_attn_prefill", C.c_int,
+                     [_P, _P, _G, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp])
+_last_error = _sig("csl_last_error", C.c_char_p, [])
+_read_dev_err = _sig("csl_read_device_error", C.c_int, [C.POINTER(C.c_uint32)])
+_timer_enable = _sig("csl_timer_enable", C.c_int, [_i32, _i32])
+_timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)])
+
+EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_index_topk_workspace", "csl_index_topk",
+           "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill", "csl_last_error",
+           "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
+
+
+def _check(st: int):
+    if st != 0:
+        raise CslError(st, _last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def row_bytes(dim: int, dtype: int) -> int:
+    return int(_row_bytes(dim, dtype))
+
+
+class Pool:
+    """A paged pool: rows [num_pages][256/ratio][row_bytes] uint8, plus the compressor state
+    (ratio > 1).  Tensors are supplied by the caller or allocated here with torch."""
+
+    def __init__(self, ratio, coff, dim, rope_dims, theta, dtype, num_pages, device="cuda", state=True,
+                 rows=None, state_x=None, state_logits=None):
+        self.ratio, self.coff, self.dim, self.rope_dims = ratio, coff, dim, rope_dims
+        self.theta, self.dtype, self.num_pages = float(theta), dtype, num_pages
+        self.row_bytes = row_bytes(dim, dtype)
+        self.rows_per_page = BLOCK // ratio
+        if rows is None:
+            rows = torch.zeros((num_pages, self.rows_per_page, self.row_bytes), dtype=torch.uint8, device=device)
+        self.rows = rows
+        if ratio > 1 and state and state_x is None:
+            state_x = torch.zeros((num_pages, BLOCK, dim), dtype=torch.bfloat16, device=device)
+            state_logits = torch.zeros((num_pages, BLOCK, coff), dtype=torch.float32, device=device)
+        self.state_x, self.state_logits = state_x, state_logits
+
+    def struct(self) -> _Pool:
+        return _Pool(self.ratio, self.coff, self.dim, self.rope_dims, self.theta, self.dtype, self.num_pages,
+                     _ptr(self.rows), _ptr(self.state_x), _ptr(self.state_logits))
+
+
+def pages(block_table: torch.Tensor) -> _Pages:
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    return _Pages(block_table.data_ptr(), block_table.shape[0], block_table.shape[1])
+
+
+def compress_insert(pool: Pool, block_table, start_pos, cu_new, x, logits=None, gain=None, eps=1e-6, stream=None):
+    ps = pool.struct()
+    pg = pages(block_table)
+    total = int(x.shape[0])
+    _check(_compress_insert(C.byref(ps), C.byref(pg), _ptr(start_pos), _ptr(cu_new), total, _ptr(x), _ptr(logits),
+                            _ptr(gain), float(eps), _stream(stream)))
+
+
+def index_topk_workspace(num_q: int, max_q_pos: int, k: int) -> int:
+    return int(_index_topk_ws(num_q, max_q_pos, k))
+
+
+def index_topk(pool: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k, topk, kth_score=None, ws=None,
+               stream=None):
+    ps = pool.struct()
+    pg = pages(block_table)
+    nq, nh = int(w.shape[0]), int(w.shape[1])
+    _check(_index_topk(C.byref(ps), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos), _ptr(q_idx), _ptr(w),
+                       nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                       _stream(stream)))
+
+
+def hybrid_attn_workspace(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos) -> int:
+    return int(_attn_ws(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos))
+
+
+def hybrid_attn_decode(comp: Pool | None, swa: Pool, block_table, q_seq, q_pos, max_q_pos, q, topk, k, swa_window,
+                       softmax_scale, out_dtype, out, out_scales=None, ws=None, stream=None):
+    cs = comp.struct() if comp is not None else None
+    ss = swa.struct()
+    pg = pages(block_table)
+    nq, nh = int(q.shape[0]), int(q.shape[1])
+    _check(_attn_decode(C.byref(cs) if cs is not None else None, C.byref(ss), C.byref(pg), nq, _ptr(q_seq),
+                        _ptr(q_pos), int(max_q_pos), _ptr(q), nh, _ptr(topk), int(k), int(swa_window),
+                        float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), _ptr(ws),
+                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hybrid_attn_prefill(comp: Pool | None, swa: Pool, block_table, cu_q, q_pos_start, max_q_pos, q, topk, k,
+                        swa_window, softmax_scale, out_dtype, out, out_scales=None, stream=None):
+    cs = comp.struct() if comp is not None else None
+    ss = swa.struct()
+    pg = pages(block_table)
+    nq, nh = int(q.shape[0]), int(q.shape[1])
+    _check(_attn_prefill(C.byref(cs) if cs is not None else None, C.byref(ss), C.byref(pg), _ptr(cu_q),
+                         _ptr(q_pos_start), nq, int(max_q_pos), _ptr(q), nh, _ptr(topk), int(k), int(swa_window),
+                         float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), _stream(stream)))
+
+
+def read_device_error() -> int:
+    v = C.c_uint32(0)
+    _check(_read_dev_err(C.byref(v)))
+    return int(v.value)
+
+
+def timer_enable(kernel_id: int, on: bool = True):
+    _check(_timer_enable(kernel_id, 1 if on else 0))
+
+
+def timer_read(kernel_id: int):
+    ms, n = C.c_double(0), C.c_int64(0)
+    _check(_timer_read(kernel_id, C.byref(ms), C.byref(n)))
+    return float(ms.value), int(n.value)
+
+
+def last_error() -> str:
+    return _last_error().decode()

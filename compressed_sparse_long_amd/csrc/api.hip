@@ -1,0 +1,461 @@
+// Host side of the C ABI (include/csl.h): argument validation, workspace
+// sizing, launch configuration, the sticky device error word and the
+// optional per-kernel event timers.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "csl.h"
+#include "csl_kernels.hpp"
+
+__device__ uint32_t csl_device_error_word;
+
+namespace {
+
+using namespace csl;
+
+thread_local std::string g_err;
+
+csl_status fail(csl_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+csl_status hip_fail(hipError_t e, const char* what) {
+    return fail(CSL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+
+csl_status device_error_ptr(uint32_t** out) {
+    static uint32_t* ptrs[kMaxDevices] = {};
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CSL_EUNSUPPORTED, "device id %d beyond %d", dev, kMaxDevices);
+    hipError_t se = hipSuccess;
+    std::call_once(once[dev], [&] {
+        se = hipGetSymbolAddress(reinterpret_cast<void**>(&ptrs[dev]), HIP_SYMBOL(csl_device_error_word));
+    });
+    if (se != hipSuccess) return hip_fail(se, "hipGetSymbolAddress(error word)");
+    if (!ptrs[dev]) return fail(CSL_EHIP, "error word of device %d is unavailable", dev);
+    *out = ptrs[dev];
+    return CSL_OK;
+}
+
+// ---------------------------------------------------------------- timers
+
+struct Timer {
+    bool on = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+    size_t used = 0;
+};
+constexpr int kNumKernels = 5;
+constexpr size_t kMaxTimed = 65536;
+Timer g_timer[kNumKernels];
+std::mutex g_timer_mu;
+
+template <typename F>
+hipError_t timed(int kid, hipStream_t st, F&& launch) {
+    hipEvent_t b = nullptr, e = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_timer_mu);
+        Timer& t = g_timer[kid];
+        if (t.on && t.used < kMaxTimed) {
+            if (t.used == t.ev.size()) {
+                hipEvent_t x, y;
+                if (hipEventCreate(&x) == hipSuccess && hipEventCreate(&y) == hipSuccess) t.ev.push_back({x, y});
+            }
+            if (t.used < t.ev.size()) {
+                b = t.ev[t.used].first;
+                e = t.ev[t.used].second;
+                ++t.used;
+            }
+        }
+    }
+    if (b) (void)hipEventRecord(b, st);
+    hipError_t r = launch();
+    if (e) (void)hipEventRecord(e, st);
+    return r;
+}
+
+// ---------------------------------------------------------------- validation
+
+size_t row_bytes_of(int dim, int dtype) {
+    if (dim <= 0) return 0;
+    if (dtype == CSL_BF16) return 2 * (size_t)dim;
+    if (dtype == CSL_FP8_E4M3) return (dim % 256 == 0) ? (size_t)dim + dim / 16 : 0;
+    if (dtype == CSL_F32) return 4 * (size_t)dim;
+    return 0;
+}
+
+csl_status check_pages(const csl_pages* pg) {
+    if (!pg || !pg->block_table) return fail(CSL_EINVAL, "pages or block_table is NULL");
+    if (pg->num_seqs <= 0 || pg->max_blocks <= 0)
+        return fail(CSL_EINVAL, "num_seqs (%d) and max_blocks (%d) must be > 0", pg->num_seqs, pg->max_blocks);
+    return CSL_OK;
+}
+
+csl_status check_pool(const csl_pool* P, const char* name) {
+    if (!P) return fail(CSL_EINVAL, "%s pool is NULL", name);
+    if (!P->rows) return fail(CSL_EINVAL, "%s.rows is NULL", name);
+    if (P->ratio != 1 && P->ratio != 4 && P->ratio != 128)
+        return fail(CSL_EINVAL, "%s.ratio = %d, expected 1, 4 or 128", name, P->ratio);
+    if (P->coff < 1 || P->coff > 2 || (P->ratio == 1 && P->coff != 1))
+        return fail(CSL_EINVAL, "%s.coff = %d invalid for ratio %d", name, P->coff, P->ratio);
+    if (P->dim < 8 || P->dim > 512 || P->dim % 8)
+        return fail(CSL_ERANGE, "%s.dim = %d, expected a multiple of 8 in [8, 512]", name, P->dim);
+    if (P->rope_dims < 0 || P->rope_dims > P->dim || P->rope_dims % 4 || P->rope_dims > 128)
+        return fail(CSL_EINVAL, "%s.rope_dims = %d, expected a multiple of 4 in [0, min(dim, 128)]", name,
+                    P->rope_dims);
+    if (P->rope_dims > 0 && !(P->rope_theta > 0.0)) return fail(CSL_EINVAL, "%s.rope_theta must be > 0", name);
+    if (P->dtype != CSL_BF16 && P->dtype != CSL_FP8_E4M3)
+        return fail(CSL_EINVAL, "%s.dtype = %d, expected CSL_BF16 or CSL_FP8_E4M3", name, P->dtype);
+    if (P->dtype == CSL_FP8_E4M3 && P->dim % 256)
+        return fail(CSL_EUNSUPPORTED, "%s: fp8 rows need dim %% 256 == 0 (got %d)", name, P->dim);
+    if (P->num_pages <= 0) return fail(CSL_EINVAL, "%s.num_pages must be > 0", name);
+    if (!aligned16(P->rows)) return fail(CSL_EALIGN, "%s.rows is not 16-byte aligned", name);
+    if (P->ratio > 1) {
+        if (P->state_x && !aligned16(P->state_x)) return fail(CSL_EALIGN, "%s.state_x is not 16-byte aligned", name);
+    }
+    return CSL_OK;
+}
+
+RopeFreqs make_freqs(int rope_dims, double theta) {
+    RopeFreqs rf;
+    for (int j = 0; j < 64; ++j)
+        rf.inv_freq[j] = (j < rope_dims / 2) ? std::pow(theta, -2.0 * j / (double)rope_dims) : 0.0;
+    return rf;
+}
+
+int64_t index_stride(int64_t max_q_pos) {
+    int64_t nv = max_q_pos / 4;
+    if (nv < 1) nv = 1;
+    return (nv + 2047) / 2048 * 2048;
+}
+
+int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
+    int64_t keys = (int64_t)(swa_window < max_q_pos ? swa_window : max_q_pos);
+    if (comp_ratio > 0) keys += k > 0 ? k : max_q_pos / comp_ratio;
+    int64_t tiles = (keys + 31) / 32;
+    int64_t want = (512 + num_q - 1) / (num_q > 0 ? num_q : 1);
+    int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
+    int64_t sp = want < cap ? want : cap;
+    if (sp > 1024) sp = 1024;
+    return (int)(sp > 1 ? sp : 1);
+}
+
+csl_status check_attn_common(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int n_heads,
+                             const int32_t* topk, int k, int swa_window, int out_dtype, const void* out,
+                             const float* out_scales, const uint16_t* q, int64_t max_q_pos) {
+    csl_status st;
+    if ((st = check_pages(pages))) return st;
+    if ((st = check_pool(swa, "swa"))) return st;
+    if (swa->ratio != 1) return fail(CSL_EINVAL, "swa.ratio must be 1 (raw window keys)");
+    if (swa->dim != 128 && swa->dim != 512) return fail(CSL_EUNSUPPORTED, "attention dim %d (supported: 128, 512)", swa->dim);
+    if (comp) {
+        if ((st = check_pool(comp, "comp"))) return st;
+        if (comp->ratio == 1) return fail(CSL_EINVAL, "comp.ratio must be 4 or 128");
+        if (comp->dim != swa->dim || comp->rope_dims != swa->rope_dims || comp->rope_theta != swa->rope_theta)
+            return fail(CSL_EINVAL, "comp and swa pools differ in dim / rope_dims / rope_theta");
+        if (comp->dtype != swa->dtype) return fail(CSL_EUNSUPPORTED, "comp and swa pools must share one dtype");
+    } else if (topk) {
+        return fail(CSL_EINVAL, "topk given without a compressed pool");
+    }
+    if (swa->dtype == CSL_FP8_E4M3 && swa->dim != 512) return fail(CSL_EUNSUPPORTED, "fp8 keys need dim 512");
+    if (n_heads < 1 || n_heads > 64) return fail(CSL_ERANGE, "n_heads = %d, supported 1..64", n_heads);
+    if (topk && (k < 1 || k > 65536)) return fail(CSL_ERANGE, "k = %d out of range", k);
+    if (swa_window < 0) return fail(CSL_EINVAL, "swa_window < 0");
+    if (max_q_pos < 0) return fail(CSL_EINVAL, "max_q_pos < 0");
+    if (max_q_pos >= (int64_t)pages->max_blocks * 256 + 1)
+        return fail(CSL_ERANGE, "max_q_pos %lld beyond the block table (%d blocks)", (long long)max_q_pos,
+                    pages->max_blocks);
+    if (out_dtype != CSL_F32 && out_dtype != CSL_BF16 && out_dtype != CSL_FP8_E4M3)
+        return fail(CSL_EINVAL, "out_dtype = %d", out_dtype);
+    if (!out || !q) return fail(CSL_EINVAL, "q or out is NULL");
+    if (out_dtype == CSL_FP8_E4M3 && !out_scales) return fail(CSL_EINVAL, "fp8 output needs out_scales");
+    if (!aligned16(q) || !aligned16(out)) return fail(CSL_EALIGN, "q and out must be 16-byte aligned");
+    return CSL_OK;
+}
+
+void fill_attn(AttnArgs& a, const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int n_heads,
+               const int32_t* topk, int k, int swa_window, float softmax_scale, int out_dtype, void* out,
+               float* out_scales, const uint16_t* q, int64_t max_q_pos, uint32_t* err) {
+    a.comp_rows = comp ? static_cast<const uint8_t*>(comp->rows) : nullptr;
+    a.swa_rows = static_cast<const uint8_t*>(swa->rows);
+    a.bt = pages->block_table;
+    a.q = q;
+    a.topk = topk;
+    a.out = out;
+    a.out_scales = out_scales;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    a.err = err;
+    a.max_q_pos = max_q_pos;
+    a.n_heads = n_heads;
+    a.dim = swa->dim;
+    a.rope_dims = swa->rope_dims;
+    a.k = topk ? k : 0;
+    a.swa_window = swa_window;
+    a.comp_ratio = comp ? comp->ratio : 1;
+    a.comp_dtype = comp ? comp->dtype : swa->dtype;
+    a.swa_dtype = swa->dtype;
+    a.out_dtype = out_dtype;
+    a.comp_pages = comp ? comp->num_pages : 0;
+    a.swa_pages = swa->num_pages;
+    a.num_seqs = pages->num_seqs;
+    a.max_blocks = pages->max_blocks;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.rf = make_freqs(swa->rope_dims, swa->rope_theta);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csl_row_bytes(int32_t dim, int32_t dtype) { return row_bytes_of(dim, dtype); }
+
+const char* csl_last_error(void) { return g_err.c_str(); }
+
+csl_status csl_read_device_error(uint32_t* flags) {
+    if (!flags) return fail(CSL_EINVAL, "flags is NULL");
+    uint32_t* p = nullptr;
+    csl_status st = device_error_ptr(&p);
+    if (st) return st;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    e = hipMemcpy(flags, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+    uint32_t zero = 0;
+    e = hipMemcpy(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear error word)");
+    return CSL_OK;
+}
+
+csl_status csl_timer_enable(int32_t kid, int32_t on) {
+    if (kid < 0 || kid >= kNumKernels) return fail(CSL_EINVAL, "kernel id %d", kid);
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    g_timer[kid].on = on != 0;
+    return CSL_OK;
+}
+
+csl_status csl_timer_read(int32_t kid, double* total_ms, int64_t* launches) {
+    if (kid < 0 || kid >= kNumKernels || !total_ms || !launches) return fail(CSL_EINVAL, "bad timer read");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    Timer& t = g_timer[kid];
+    double sum = 0.0;
+    for (size_t i = 0; i < t.used; ++i) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, t.ev[i].first, t.ev[i].second);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = (int64_t)t.used;
+    t.used = 0;
+    return CSL_OK;
+}
+
+csl_status csl_compress_insert(const csl_pool* pool, const csl_pages* pages, const int64_t* start_pos,
+                               const int32_t* cu_new, int32_t total_new, const uint16_t* x, const float* logits,
+                               const float* gain, float eps, csl_stream_t stream) {
+    csl_status st;
+    if ((st = check_pool(pool, "pool"))) return st;
+    if ((st = check_pages(pages))) return st;
+    if (total_new < 0) return fail(CSL_EINVAL, "total_new < 0");
+    if (!start_pos || !cu_new) return fail(CSL_EINVAL, "start_pos or cu_new is NULL");
+    if (total_new > 0 && !x) return fail(CSL_EINVAL, "x is NULL");
+    if (x && !aligned16(x)) return fail(CSL_EALIGN, "x is not 16-byte aligned");
+    if (pool->ratio == 1) {
+        if (logits || gain) return fail(CSL_EINVAL, "ratio-1 (raw window) inserts take no logits and no gain");
+    } else {
+        if (!pool->state_x || !pool->state_logits) return fail(CSL_EINVAL, "ratio > 1 needs the compressor state");
+        if (total_new > 0 && !logits) return fail(CSL_EINVAL, "logits is NULL");
+        if (!(eps >= 0.f)) return fail(CSL_EINVAL, "eps must be >= 0");
+    }
+    if (total_new == 0) return CSL_OK;
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    CompressArgs a;
+    a.rows = static_cast<uint8_t*>(pool->rows);
+    a.state_x = static_cast<uint16_t*>(pool->state_x);
+    a.state_logits = pool->state_logits;
+    a.bt = pages->block_table;
+    a.start_pos = start_pos;
+    a.cu_new = cu_new;
+    a.x = x;
+    a.logits = logits;
+    a.gain = gain;
+    a.err = err;
+    a.ratio = pool->ratio;
+    a.coff = pool->coff;
+    a.dim = pool->dim;
+    a.rope_dims = pool->rope_dims;
+    a.dtype = pool->dtype;
+    a.num_pages = pool->num_pages;
+    a.row_bytes = (int)row_bytes_of(pool->dim, pool->dtype);
+    a.num_seqs = pages->num_seqs;
+    a.max_blocks = pages->max_blocks;
+    a.total_new = total_new;
+    a.eps = eps;
+    a.rf = make_freqs(pool->rope_dims, pool->rope_theta);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(CSL_KERNEL_COMPRESS, s, [&] { return launch_compress(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "compress_insert launch");
+    return CSL_OK;
+}
+
+size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k) {
+    (void)k;
+    if (num_q <= 0 || max_q_pos < 0) return 0;
+    return (size_t)num_q * (size_t)index_stride(max_q_pos) * sizeof(float);
+}
+
+csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
+                          const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q_idx, const float* w,
+                          int32_t n_heads, int32_t k, int32_t* topk, float* kth_score, void* ws, size_t ws_bytes,
+                          csl_stream_t stream) {
+    csl_status st;
+    if ((st = check_pool(index_pool, "index"))) return st;
+    if ((st = check_pages(pages))) return st;
+    if (index_pool->ratio != 4) return fail(CSL_EUNSUPPORTED, "the indexer runs on ratio-4 (c4a) pools only");
+    if (index_pool->dtype != CSL_BF16) return fail(CSL_EUNSUPPORTED, "index rows must be bf16");
+    if (index_pool->dim != 32 && index_pool->dim != 64 && index_pool->dim != 128)
+        return fail(CSL_EUNSUPPORTED, "index dim %d (supported: 32, 64, 128)", index_pool->dim);
+    if (n_heads < 1 || n_heads > 16) return fail(CSL_ERANGE, "index n_heads = %d, supported 1..16", n_heads);
+    if (k < 1 || k > 2048) return fail(CSL_ERANGE, "k = %d, supported 1..2048", k);
+    if (num_q < 0 || num_q > 65535) return fail(CSL_ERANGE, "num_q = %d, supported 0..65535", num_q);
+    if (max_q_pos < 0) return fail(CSL_EINVAL, "max_q_pos < 0");
+    if (max_q_pos >= (int64_t)pages->max_blocks * 256 + 1)
+        return fail(CSL_ERANGE, "max_q_pos beyond the block table");
+    if (num_q == 0) return CSL_OK;
+    if (!q_seq || !q_pos || !q_idx || !w || !topk) return fail(CSL_EINVAL, "a required pointer is NULL");
+    if (!aligned16(q_idx)) return fail(CSL_EALIGN, "q_idx is not 16-byte aligned");
+    size_t need = csl_index_topk_workspace(num_q, max_q_pos, k);
+    if (!ws || ws_bytes < need) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned16(ws)) return fail(CSL_EALIGN, "ws is not 16-byte aligned");
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    IndexArgs a;
+    a.rows = static_cast<const uint8_t*>(index_pool->rows);
+    a.bt = pages->block_table;
+    a.q_seq = q_seq;
+    a.q_pos = q_pos;
+    a.q_idx = q_idx;
+    a.w = w;
+    a.scores = static_cast<float*>(ws);
+    a.topk = topk;
+    a.kth = kth_score;
+    a.err = err;
+    a.max_q_pos = max_q_pos;
+    a.stride = index_stride(max_q_pos);
+    a.num_q = num_q;
+    a.n_heads = n_heads;
+    a.dim = index_pool->dim;
+    a.k = k;
+    a.num_pages = index_pool->num_pages;
+    a.num_seqs = pages->num_seqs;
+    a.max_blocks = pages->max_blocks;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, s, [&] { return launch_index_score(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "index_score launch");
+    e = timed(CSL_KERNEL_TOPK_SELECT, s, [&] { return launch_topk_select(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "topk_select launch");
+    return CSL_OK;
+}
+
+size_t csl_hybrid_attn_workspace(int32_t num_q, int32_t n_heads, int32_t dim, int32_t comp_ratio, int32_t k,
+                                 int32_t swa_window, int64_t max_q_pos) {
+    if (num_q <= 0 || n_heads <= 0 || dim <= 0) return 0;
+    int sp = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos);
+    if (sp <= 1) return 0;
+    return (size_t)num_q * sp * n_heads * ((size_t)dim + 2) * sizeof(float);
+}
+
+csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int32_t num_q,
+                                  const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q,
+                                  int32_t n_heads, const int32_t* topk, int32_t k, int32_t swa_window,
+                                  float softmax_scale, int32_t out_dtype, void* out, float* out_scales, void* ws,
+                                  size_t ws_bytes, csl_stream_t stream) {
+    if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
+    if (num_q == 0) return CSL_OK;
+    csl_status st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
+                                      max_q_pos);
+    if (st) return st;
+    if (!q_seq || !q_pos) return fail(CSL_EINVAL, "q_seq or q_pos is NULL");
+    const int cr = comp ? comp->ratio : 0;
+    const int kk = topk ? k : 0;
+    const int sp = decode_splits(num_q, cr, kk, swa_window, max_q_pos);
+    if ((int64_t)num_q * sp > 0x7fffffff) return fail(CSL_ERANGE, "grid too large");
+    size_t need = csl_hybrid_attn_workspace(num_q, n_heads, swa->dim, cr, kk, swa_window, max_q_pos);
+    if (need > 0 && (!ws || ws_bytes < need)) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (need > 0 && !aligned16(ws)) return fail(CSL_EALIGN, "ws is not 16-byte aligned");
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    AttnArgs a;
+    fill_attn(a, comp, swa, pages, n_heads, topk, k, swa_window, softmax_scale, out_dtype, out, out_scales, q,
+              max_q_pos, err);
+    a.q_seq = q_seq;
+    a.q_pos = q_pos;
+    a.cu_q = nullptr;
+    a.q_pos_start = nullptr;
+    a.num_q = num_q;
+    a.n_splits = sp;
+    if (sp > 1) {
+        a.part_o = static_cast<float*>(ws);
+        a.part_ml = a.part_o + (size_t)num_q * sp * n_heads * swa->dim;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&] { return launch_attn(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
+    if (sp > 1) {
+        e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&] { return launch_attn_combine(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
+    }
+    return CSL_OK;
+}
+
+csl_status csl_hybrid_attn_prefill(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages,
+                                   const int32_t* cu_q, const int64_t* q_pos_start, int32_t total_q,
+                                   int64_t max_q_pos, const uint16_t* q, int32_t n_heads, const int32_t* topk,
+                                   int32_t k, int32_t swa_window, float softmax_scale, int32_t out_dtype, void* out,
+                                   float* out_scales, csl_stream_t stream) {
+    if (total_q < 0) return fail(CSL_EINVAL, "total_q < 0");
+    if (total_q == 0) return CSL_OK;
+    csl_status st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
+                                      max_q_pos);
+    if (st) return st;
+    if (!cu_q || !q_pos_start) return fail(CSL_EINVAL, "cu_q or q_pos_start is NULL");
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    AttnArgs a;
+    fill_attn(a, comp, swa, pages, n_heads, topk, k, swa_window, softmax_scale, out_dtype, out, out_scales, q,
+              max_q_pos, err);
+    a.q_seq = nullptr;
+    a.q_pos = nullptr;
+    a.cu_q = cu_q;
+    a.q_pos_start = q_pos_start;
+    a.num_q = total_q;
+    a.n_splits = 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&] { return launch_attn(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
+    return CSL_OK;
+}
+
+}  // extern "C"

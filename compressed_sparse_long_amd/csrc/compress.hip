@@ -1,0 +1,223 @@
+// Step 1 on gfx950: token-axis compressor + RMSNorm + RoPE + paged insert,
+// one fused kernel ([Notes] 融合 1：Compressor + RMSNorm + RoPE + Cache Insert;
+// windows from [Notes] 数学附录精要: C4A / C128A 的精确位置范围), plus the
+// raw-window insert (ratio 1: RoPE at the token, no norm; [Notes] 融合 3).
+//
+// Work mapping.  One 256-thread workgroup per new token for ratio > 1: wave 0
+// appends the token to the compressor state; if the token closes an entry,
+// the four waves split the window's tokens, the weighted partial sums meet in
+// LDS and wave 0 normalises, rotates and stores the row.  For ratio 1 each
+// wave handles one token.  A lane owns 8 consecutive dims (one 16-byte
+// load/store per row), so a wave covers a row of up to 512 dims and RoPE pairs
+// never straddle lanes.  Elementwise and HBM-bound: no MFMA.
+#include "csl_kernels.hpp"
+
+namespace csl {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int num_seqs, int j) {
+    int lo = 0, hi = num_seqs;  // invariant: cu[lo] <= j < cu[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] <= j) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+    u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        v[2 * c] = __uint_as_float(r[c] << 16);
+        v[2 * c + 1] = __uint_as_float(r[c] & 0xffff0000u);
+    }
+}
+
+// Rotate the lane's 8 dims [d0, d0+8) at position `pos` (pairs in the last R dims).
+__device__ __forceinline__ void rope8(float* v, int d0, int dim, int rope_dims, const RopeFreqs& rf, int64_t pos) {
+    int base = dim - rope_dims;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        int d = d0 + 2 * c;
+        if (d >= base) {
+            float cs, sn;
+            rope_cs(pos, rf.inv_freq[(d - base) >> 1], cs, sn);
+            float a = v[2 * c], b = v[2 * c + 1];
+            v[2 * c] = a * cs - b * sn;
+            v[2 * c + 1] = a * sn + b * cs;
+        }
+    }
+}
+
+// Store the lane's 8 values of a row; every lane of the wave must call this
+// (fp8 reduces the group amax across 8 lanes).  `active` = lane owns dims.
+__device__ __forceinline__ void store8(uint8_t* row, int dtype, int dim, int lane, bool active, const float* v) {
+    if (dtype == kBF16) {
+        if (active) {
+            u32x4 o;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
+            *reinterpret_cast<u32x4*>(row + 16 * lane) = o;
+        }
+        return;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[c]));
+    amax = group8_max(active ? amax : 0.f);
+    float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (active) {
+        u32x2 o = {0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c >> 2] |= f32_to_e4m3(v[c] / scale) << (8 * (c & 3));
+        *reinterpret_cast<u32x2*>(row + 8 * lane) = o;
+        if ((lane & 7) == 0) *reinterpret_cast<float*>(row + dim + 4 * (lane >> 3)) = scale;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs a) {
+    __shared__ float s_w[kThreads];
+    __shared__ const uint16_t* s_ptr[kThreads];
+    __shared__ float s_red[4][512];
+    __shared__ float s_tmp[8];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int D = a.dim;
+    const bool active = lane * 8 < D;
+
+    if (a.ratio == 1) {
+        int j = blockIdx.x * 4 + wave;
+        if (j >= a.total_new) return;
+        int s = find_seq(a.cu_new, a.num_seqs, j);
+        int64_t t = a.start_pos[s] + (j - a.cu_new[s]);
+        int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, t);
+        if (pg < 0) {
+            if (lane == 0) raise_error(a.err, (t < 0 || (t >> 8) >= a.max_blocks) ? kErrPos : kErrPage);
+            return;
+        }
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (active) load8(a.x + (int64_t)j * D + 8 * lane, v);
+        rope8(v, 8 * lane, D, a.rope_dims, a.rf, t);
+        uint8_t* row = a.rows + ((int64_t)pg * kBlockPositions + (t & 255)) * a.row_bytes;
+        store8(row, a.dtype, D, lane, active, v);
+        return;
+    }
+
+    const int j = blockIdx.x;
+    const int s = find_seq(a.cu_new, a.num_seqs, j);
+    const int64_t start = a.start_pos[s];
+    const int cbase = a.cu_new[s];
+    const int64_t t = start + (j - cbase);
+    const int r = a.ratio, W = a.coff * a.ratio;
+
+    // 1. append the token to the compressor state
+    if (wave == 0) {
+        int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, t);
+        if (pg < 0) {
+            if (lane == 0) raise_error(a.err, (t < 0 || (t >> 8) >= a.max_blocks) ? kErrPos : kErrPage);
+        } else {
+            int64_t tok = (int64_t)pg * kBlockPositions + (t & 255);
+            if (active)
+                *reinterpret_cast<u32x4*>(a.state_x + tok * D + 8 * lane) =
+                    *reinterpret_cast<const u32x4*>(a.x + (int64_t)j * D + 8 * lane);
+            if (lane < a.coff) a.state_logits[tok * a.coff + lane] = a.logits[(int64_t)j * a.coff + lane];
+        }
+    }
+    if ((t + 1) % r != 0) return;  // uniform across the workgroup
+    const int64_t i = (t + 1) / r - 1;
+
+    // 2. window weights: thread k owns window slot k
+    float lg = -INFINITY;
+    const uint16_t* ptr = nullptr;
+    if (tid < W) {
+        int64_t tk = (int64_t)r * (i + 1) - W + tid;
+        int col = tid / r;
+        if (tk >= start) {
+            int64_t jj = cbase + (tk - start);
+            lg = a.logits[jj * a.coff + col];
+            ptr = a.x + jj * D;
+        } else if (tk >= 0) {
+            int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, tk);
+            if (pg < 0) {
+                raise_error(a.err, kErrPage);
+            } else {
+                int64_t tok = (int64_t)pg * kBlockPositions + (tk & 255);
+                lg = a.state_logits[tok * a.coff + col];
+                ptr = a.state_x + tok * D;
+            }
+        }
+    }
+    float m = wave_max(lg);
+    if (lane == 0) s_tmp[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_tmp[0], s_tmp[1]), fmaxf(s_tmp[2], s_tmp[3]));
+    float e = ptr ? __expf(lg - m) : 0.f;
+    float den = wave_sum(e);
+    __syncthreads();
+    if (lane == 0) s_tmp[4 + wave] = den;
+    s_w[tid] = e;
+    s_ptr[tid] = ptr;
+    __syncthreads();
+    den = s_tmp[4] + s_tmp[5] + s_tmp[6] + s_tmp[7];
+    const float inv_den = den > 0.f ? 1.0f / den : 0.f;
+
+    // 3. weighted sum: wave w takes window slots w, w+4, w+8, ...
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active) {
+#pragma unroll 4
+        for (int k = wave; k < W; k += 4) {
+            const uint16_t* p = s_ptr[k];
+            if (!p) continue;
+            float wk = s_w[k] * inv_den;
+            float v[8];
+            load8(p + 8 * lane, v);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = fmaf(wk, v[c], acc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s_red[wave][8 * lane + c] = acc[c];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+
+    // 4. RMSNorm, RoPE at r*i, store
+    float u[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        int d = 8 * lane + c;
+        u[c] = active ? (s_red[0][d] + s_red[1][d]) + (s_red[2][d] + s_red[3][d]) : 0.f;
+        ss = fmaf(u[c], u[c], ss);
+    }
+    ss = wave_sum(ss);
+    float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float g = (a.gain && active) ? a.gain[8 * lane + c] : 1.0f;
+        u[c] = u[c] * inv * g;
+    }
+    rope8(u, 8 * lane, D, a.rope_dims, a.rf, (int64_t)r * i);
+    int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, (int64_t)r * i);
+    if (pg < 0) {
+        if (lane == 0) raise_error(a.err, kErrPage);
+        return;
+    }
+    const int per_page = kBlockPositions / r;
+    uint8_t* row = a.rows + ((int64_t)pg * per_page + (i % per_page)) * a.row_bytes;
+    store8(row, a.dtype, D, lane, active, u);
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
+    if (a.total_new <= 0) return hipSuccess;
+    int blocks = a.ratio == 1 ? (a.total_new + 3) / 4 : a.total_new;
+    hipLaunchKernelGGL(compress_insert_kernel, dim3(blocks), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace csl

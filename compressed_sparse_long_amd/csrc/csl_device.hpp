@@ -1,0 +1,118 @@
+// Device-side building blocks shared by the gfx950 kernels: storage-format
+// conversions, wavefront reductions, RoPE angles and paged addressing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csl {
+
+constexpr int kBlockPositions = 256;  // native positions per page
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum : uint32_t { kErrPage = 1u, kErrTopk = 2u, kErrPos = 4u, kErrSeq = 8u };
+
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct RopeFreqs {
+    // theta^(-2j/R) for the R/2 rotated pairs, fp64, built on the host.
+    double inv_freq[64];
+};
+
+// ---------------------------------------------------------------- formats
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// OCP e4m3fn code -> fp32 (S.1111.111 is NaN; no infinities).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t mag = c & 0x7fu;
+    float normal = __uint_as_float((mag << 20) + (120u << 23));
+    float sub = (float)(c & 7u) * 0.001953125f;  // m * 2^-9
+    float v = (mag >> 3) == 0 ? sub : normal;
+    v = mag == 0x7fu ? __uint_as_float(0x7fc00000u) : v;
+    return (c & 0x80u) ? -v : v;
+}
+
+// fp32 -> OCP e4m3fn code, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t s = (u >> 24) & 0x80u;
+    float a = fabsf(x);
+    if (a != a) return s | 0x7fu;
+    if (a >= 448.0f) return s | 0x7eu;
+    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+        return s | (uint32_t)rintf(a * 512.0f);  // 8 -> code 0x08 = 2^-6, consistent
+    }
+    uint32_t ua = __float_as_uint(a);
+    uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);  // RNE at the 3rd mantissa bit
+    uint32_t e = (r >> 23) - 120u;
+    uint32_t m = (r >> 20) & 7u;
+    return s | (e << 3) | m;
+}
+
+// ---------------------------------------------------------------- waves
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Reduce across the 8 lanes of an aligned group (lane bits 0..2).
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    return v;
+}
+
+// ---------------------------------------------------------------- RoPE
+
+// cos/sin of pos * inv_freq, the product and its reduction in fp64.
+__device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float& c, float& s) {
+    double phi = (double)pos * inv_freq;
+    double sd, cd;
+    sincos(phi, &sd, &cd);
+    c = (float)cd;
+    s = (float)sd;
+}
+
+// ---------------------------------------------------------------- paging
+
+// Page of native position `t` of sequence `seq`, or -1 (unmapped / beyond the table).
+__device__ __forceinline__ int32_t page_of(const int32_t* __restrict__ bt, int max_blocks, int num_pages, int seq,
+                                           int64_t t) {
+    int64_t b = t >> 8;
+    if (t < 0 || b >= max_blocks) return -1;
+    int32_t pg = bt[(int64_t)seq * max_blocks + b];
+    return (pg < 0 || pg >= num_pages) ? -1 : pg;
+}
+
+__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) { atomicOr(err, bits); }
+
+}  // namespace csl

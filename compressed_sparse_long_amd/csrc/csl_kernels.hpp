@@ -1,0 +1,71 @@
+// Argument blocks and launchers of the gfx950 kernels (host + device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csl_device.hpp"
+
+namespace csl {
+
+struct CompressArgs {
+    uint8_t* rows;
+    uint16_t* state_x;
+    float* state_logits;
+    const int32_t* bt;
+    const int64_t* start_pos;
+    const int32_t* cu_new;
+    const uint16_t* x;
+    const float* logits;
+    const float* gain;
+    uint32_t* err;
+    int ratio, coff, dim, rope_dims, dtype, num_pages, row_bytes, num_seqs, max_blocks, total_new;
+    float eps;
+    RopeFreqs rf;
+};
+
+struct IndexArgs {
+    const uint8_t* rows;  // ratio-4 index pool, bf16 rows
+    const int32_t* bt;
+    const int32_t* q_seq;
+    const int64_t* q_pos;
+    const uint16_t* q_idx;  // [num_q][n_heads][dim]
+    const float* w;         // [num_q][n_heads]
+    float* scores;          // [num_q][stride]
+    int32_t* topk;          // [num_q][k]
+    float* kth;             // [num_q] or null
+    uint32_t* err;
+    int64_t max_q_pos;
+    int64_t stride;  // entries per query row of `scores` (multiple of 256)
+    int num_q, n_heads, dim, k, num_pages, num_seqs, max_blocks;
+};
+
+struct AttnArgs {
+    const uint8_t* comp_rows;  // null = no compressed keys
+    const uint8_t* swa_rows;
+    const int32_t* bt;
+    const int32_t* q_seq;        // decode: [num_q]; null in prefill
+    const int64_t* q_pos;        // decode: [num_q]; null in prefill
+    const int32_t* cu_q;         // prefill: [num_seqs+1]
+    const int64_t* q_pos_start;  // prefill: [num_seqs]
+    const uint16_t* q;
+    const int32_t* topk;  // null = dense over visible entries
+    void* out;
+    float* out_scales;
+    float* part_o;   // [num_q][n_splits][n_heads][dim]
+    float* part_ml;  // [num_q][n_splits][n_heads][2]
+    uint32_t* err;
+    int64_t max_q_pos;
+    int num_q, n_heads, dim, rope_dims, k, swa_window, comp_ratio, comp_dtype, swa_dtype, out_dtype;
+    int comp_pages, swa_pages, num_seqs, max_blocks, n_splits;
+    float scale_log2;  // softmax_scale * log2(e)
+    RopeFreqs rf;
+};
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+hipError_t launch_index_score(const IndexArgs& a, hipStream_t st);
+hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
+
+}  // namespace csl

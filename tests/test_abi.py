@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every symbol include/csl.h declares, and its
+host-side validation rejects bad arguments before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def csl():
+    import compressed_sparse_long_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "csl.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(csl_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(csl):
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = C.CDLL(csl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(csl.EXPORTS) == names
+
+
+def test_row_bytes(csl):
+    assert csl.row_bytes(512, csl.BF16) == 1024
+    assert csl.row_bytes(128, csl.BF16) == 256
+    assert csl.row_bytes(512, csl.FP8) == 544
+    assert csl.row_bytes(128, csl.FP8) == 0      # fp8 rows need dim % 256 == 0
+
+
+def test_workspace_sizes(csl):
+    assert csl.index_topk_workspace(16, 131072, 512) == 16 * 32768 * 4
+    assert csl.index_topk_workspace(1, 100, 64) == 2048 * 4
+    # decode split-KV partials: num_q * splits * heads * (dim + 2) floats
+    ws = csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072)
+    assert ws > 0 and ws % (16 * 64 * 514 * 4) == 0
+    assert csl.hybrid_attn_workspace(1, 64, 512, 0, 0, 0, 10) == 0
+
+
+FAKE = 0x100000  # a 16-byte aligned host address that is never dereferenced
+
+
+def pool(csl, **kw):
+    p = dict(ratio=4, coff=2, dim=512, rope_dims=64, rope_theta=1e4, dtype=csl.BF16, num_pages=8, rows=FAKE,
+             state_x=FAKE, state_logits=FAKE)
+    p.update(kw)
+    return csl._Pool(**p)
+
+
+def pg(csl, **kw):
+    p = dict(block_table=FAKE, num_seqs=1, max_blocks=4)
+    p.update(kw)
+    return csl._Pages(**p)
+
+
+def compress(csl, P, G, x=FAKE, logits=FAKE, gain=None, total=1, eps=1e-6):
+    return csl._compress_insert(C.byref(P), C.byref(G), FAKE, FAKE, total, x, logits, gain, eps, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ratio=3), -1), (dict(coff=3), -1), (dict(dim=520), -2), (dict(rope_dims=6), -1),
+    (dict(dtype=7), -1), (dict(dtype=2, dim=128), -6), (dict(num_pages=0), -1), (dict(rows=FAKE + 8), -3),
+    (dict(rows=None), -1), (dict(state_x=None), -1),
+])
+def test_compress_validation(csl, kw, status):
+    assert compress(csl, pool(csl, **kw), pg(csl)) == status
+    assert csl.last_error() != ""
+
+
+def test_compress_raw_rejects_logits(csl):
+    assert compress(csl, pool(csl, ratio=1, coff=1, state_x=None, state_logits=None), pg(csl)) == -1
+    assert compress(csl, pool(csl), pg(csl, num_seqs=0)) == -1
+    assert compress(csl, pool(csl), pg(csl), x=FAKE + 4) == -3
+    assert compress(csl, pool(csl), pg(csl), total=0) == 0   # nothing to do, nothing launched
+
+
+def index(csl, P, G, k=64, heads=16, nq=4, ws_bytes=1 << 30, max_pos=1000, qidx=FAKE):
+    return csl._index_topk(C.byref(P), C.byref(G), nq, FAKE, FAKE, max_pos, qidx, FAKE, heads, k, FAKE, None, FAKE,
+                           ws_bytes, None)
+
+
+def test_index_validation(csl):
+    ip = pool(csl, dim=128, rope_dims=0)
+    assert index(csl, pool(csl, dim=128, rope_dims=0, ratio=128, coff=1), pg(csl)) == -6
+    assert index(csl, pool(csl, dim=96, rope_dims=0), pg(csl)) == -6
+    assert index(csl, ip, pg(csl), k=0) == -2
+    assert index(csl, ip, pg(csl), k=4096) == -2
+    assert index(csl, ip, pg(csl), heads=17) == -2
+    assert index(csl, ip, pg(csl), ws_bytes=16) == -4
+    assert index(csl, ip, pg(csl), max_pos=4 * 256 + 1) == -2
+    assert index(csl, ip, pg(csl), qidx=FAKE + 2) == -3
+    assert index(csl, ip, pg(csl), nq=0) == 0
+
+
+def attn(csl, comp, swa, G, heads=64, topk=FAKE, k=512, out_dtype=1, scales=None, max_pos=1000, ws_bytes=1 << 30):
+    cp = C.byref(comp) if comp is not None else None
+    return csl._attn_decode(cp, C.byref(swa), C.byref(G), 4, FAKE, FAKE, max_pos, FAKE, heads, topk, k, 128, 0.04,
+                            out_dtype, FAKE, scales, FAKE, ws_bytes, None)
+
+
+def test_attn_validation(csl):
+    comp = pool(csl, state_x=None, state_logits=None)
+    swa = pool(csl, ratio=1, coff=1, state_x=None, state_logits=None)
+    assert attn(csl, comp, pool(csl), pg(csl)) == -1                       # swa must be ratio 1
+    assert attn(csl, pool(csl, dim=256), swa, pg(csl)) == -1               # dims differ
+    assert attn(csl, comp, pool(csl, ratio=1, coff=1, dim=256), pg(csl)) == -6
+    assert attn(csl, pool(csl, dtype=2), swa, pg(csl)) == -6               # mixed dtypes
+    assert attn(csl, comp, swa, pg(csl), heads=65) == -2
+    assert attn(csl, comp, swa, pg(csl), out_dtype=2) == -1                # fp8 output needs scales
+    assert attn(csl, None, swa, pg(csl)) == -1                             # top-k without a compressed pool
+    assert attn(csl, comp, swa, pg(csl), max_pos=5000) == -2
+    assert attn(csl, comp, swa, pg(csl), ws_bytes=0) == -4

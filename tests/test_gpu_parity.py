@@ -1,0 +1,346 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Sizes span several tiles and ragged tails; tolerances are the north-star's:
+rows and outputs rtol 1e-2 / atol 1e-2, fp8 within one e4m3 ULP of the
+oracle's quantisation, top-k sets equal up to swaps within 1e-4 of the k-th
+score.  Every case prints its name before its GPU step.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.gpu_util import (DEV, assert_close, assert_fp8_close, assert_topk_equivalent, dev, dev_bf16, host,
+                            host_u16)
+from tests.util import block_table, gather_rows, rand_u, randn_bf16, randn_f32, scatter_rows
+
+pytestmark = pytest.mark.gpu
+THETA = 10000.0
+
+
+@pytest.fixture(scope="module")
+def csl():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import compressed_sparse_long_amd as m
+    m.read_device_error()  # clear
+    return m
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def gpu_pool(csl, hp: O.HostPool, state=True):
+    """Device pool with the same bytes as a host pool."""
+    p = csl.Pool(hp.ratio, hp.coff, hp.dim, hp.rope_dims, hp.theta, hp.dtype, hp.num_pages,
+                 rows=dev(hp.rows), state=False)
+    if state and hp.state_x is not None:
+        p.state_x = dev(hp.state_x.view(np.int16), torch.bfloat16)
+        p.state_logits = dev(hp.state_logits)
+    return p
+
+
+# ---------------------------------------------------------------------------
+# compress_insert
+# ---------------------------------------------------------------------------
+
+COMPRESS_CASES = [
+    dict(name="c4a_d128_r32_bf16_1seq", ratio=4, coff=2, D=128, R=32, dtype=O.BF16, lens=[1024],
+         chunks=[[1024]]),
+    dict(name="c4a_d512_r64_fp8_2seq_ragged_chunks", ratio=4, coff=2, D=512, R=64, dtype=O.FP8, lens=[700, 413],
+         chunks=[[300, 1, 399], [5, 0, 408]]),
+    dict(name="c128a_d512_r64_bf16_3seq_chunked", ratio=128, coff=1, D=512, R=64, dtype=O.BF16,
+         lens=[1100, 640, 129], chunks=[[127, 500, 473], [640, 0, 0], [1, 127, 1]]),
+    dict(name="c128a_d512_fp8", ratio=128, coff=1, D=512, R=64, dtype=O.FP8, lens=[768], chunks=[[700, 68]]),
+    dict(name="raw_d512_bf16_2seq", ratio=1, coff=1, D=512, R=64, dtype=O.BF16, lens=[300, 77], chunks=[[200, 100],
+                                                                                                         [77, 0]]),
+    dict(name="raw_d512_fp8", ratio=1, coff=1, D=512, R=64, dtype=O.FP8, lens=[260], chunks=[[260]]),
+    dict(name="index_d32_norope", ratio=4, coff=2, D=32, R=0, dtype=O.BF16, lens=[1024], chunks=[[1000, 24]]),
+    dict(name="index_d128_gain", ratio=4, coff=2, D=128, R=0, dtype=O.BF16, lens=[520], chunks=[[3, 517]],
+         gain=True),
+    dict(name="c4a_d512_gain_start_offset", ratio=4, coff=2, D=512, R=64, dtype=O.BF16, lens=[600],
+         chunks=[[0, 600]], gain=True),
+]
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=[c["name"] for c in COMPRESS_CASES])
+def test_compress_insert_parity(csl, orc, case):
+    r, c, D, R, dt = case["ratio"], case["coff"], case["D"], case["R"], case["dtype"]
+    lens, chunks = case["lens"], case["chunks"]
+    ns = len(lens)
+    seed = zlib.crc32(case["name"].encode()) % 1000
+    mb = max(lens) // 256 + 1
+    bt = block_table(seed, ns, mb, extra_pages=2)
+    npages = ns * mb + 2
+    hp = O.HostPool(r, c, D, R, THETA, dt, npages)
+    gp = gpu_pool(csl, hp)
+    gbt = dev(bt)
+    xs = [randn_bf16(seed, 100 + s, (lens[s], D)) for s in range(ns)]
+    ls = [randn_f32(seed, 200 + s, (lens[s], c)).astype(np.float32) for s in range(ns)]
+    gain = rand_u(seed, 300, (D,), 0.5, 1.5).astype(np.float32) if case.get("gain") else None
+    done = [0] * ns
+    for rnd in range(max(len(ch) for ch in chunks)):
+        sizes = [chunks[s][rnd] if rnd < len(chunks[s]) else 0 for s in range(ns)]
+        cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        st = np.array(done, np.int64)
+        x = np.concatenate([xs[s][done[s]:done[s] + sizes[s]] for s in range(ns)])
+        lg = np.concatenate([ls[s][done[s]:done[s] + sizes[s]] for s in range(ns)]) if r > 1 else None
+        assert O.compress_insert(hp, bt, st, cu, x, lg, gain) == 0
+        say(f"compress {case['name']} round {rnd} sizes {sizes}")
+        csl.compress_insert(gp, gbt, dev(st), dev(cu), dev_bf16(x), None if lg is None else dev(lg),
+                            None if gain is None else dev(gain))
+        done = [done[s] + sizes[s] for s in range(ns)]
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0
+    g_rows = host(gp.rows)
+    for s in range(ns):
+        n_ent = lens[s] // r
+        go = gather_rows(g_rows, bt, s, r, 0, n_ent)
+        oo = gather_rows(hp.rows, bt, s, r, 0, n_ent)
+        if dt == O.BF16:
+            assert_close(O.decode_rows(go, D, dt), O.decode_rows(oo, D, dt), what=f"{case['name']} seq {s}")
+        else:
+            assert_fp8_close(orc, go[:, :D], go[:, D:].copy().view(np.float32), oo[:, :D],
+                             oo[:, D:].copy().view(np.float32), what=f"{case['name']} seq {s}")
+    if r > 1:
+        assert np.array_equal(host_u16(gp.state_x), hp.state_x)
+        assert np.array_equal(host(gp.state_logits), hp.state_logits)
+
+
+# ---------------------------------------------------------------------------
+# index_topk
+# ---------------------------------------------------------------------------
+
+INDEX_CASES = [
+    dict(name="h4_d32_k64", H=4, DI=32, k=64, pos=[[0, 3, 4, 7, 255, 256, 257, 259, 260, 1023, 1024]]),
+    dict(name="h16_d128_k512_2seq", H=16, DI=128, k=512, pos=[[2047, 2048, 2051, 9000, 20000], [4, 5000, 6000]]),
+    dict(name="h16_d64_k100", H=16, DI=64, k=100, pos=[[401, 403, 404, 3000, 3003]]),
+    dict(name="h13_d128_k2048", H=13, DI=128, k=2048, pos=[[8191, 8192, 12000, 40000]]),
+]
+
+
+@pytest.mark.parametrize("case", INDEX_CASES, ids=[c["name"] for c in INDEX_CASES])
+def test_index_topk_parity(csl, orc, case):
+    H, DI, k = case["H"], case["DI"], case["k"]
+    seed = zlib.crc32(case["name"].encode()) % 1000
+    ns = len(case["pos"])
+    max_pos = max(max(p) for p in case["pos"])
+    mb = max_pos // 256 + 1
+    bt = block_table(seed, ns, mb, extra_pages=1)
+    hp = O.HostPool(4, 2, DI, 0, THETA, O.BF16, ns * mb + 1, state=False)
+    for s in range(ns):
+        scatter_rows(hp.rows, bt, s, 4, randn_bf16(seed, 10 + s, (64 * mb, DI)).view(np.uint8).reshape(64 * mb, -1))
+    q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
+    q_pos = np.concatenate(case["pos"]).astype(np.int64)
+    nq = len(q_pos)
+    qi = randn_bf16(seed, 20, (nq, H, DI))
+    w = rand_u(seed, 21, (nq, H)).astype(np.float32)
+    o_topk, o_kth, o_sc, f = O.index_topk(hp, bt, q_seq, q_pos, qi, w, k, want_scores=True, max_cand=max_pos // 4)
+    assert f == 0
+    gp = gpu_pool(csl, hp, state=False)
+    topk = torch.full((nq, k), -7, dtype=torch.int32, device=DEV)
+    kth = torch.empty(nq, dtype=torch.float32, device=DEV)
+    ws = torch.empty(csl.index_topk_workspace(nq, max_pos, k) // 4, dtype=torch.float32, device=DEV)
+    say(f"index_topk {case['name']} nq {nq} max_pos {max_pos}")
+    csl.index_topk(gp, dev(bt), dev(q_seq), dev(q_pos), max_pos, dev_bf16(qi), dev(w), k, topk, kth, ws)
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0
+    assert_topk_equivalent(host(topk), o_topk, o_sc, o_kth, what=case["name"])
+    g_kth = host(kth).astype(np.float64)
+    for n in range(nq):
+        if np.isneginf(o_kth[n]):
+            assert np.isneginf(g_kth[n]) or g_kth[n] == np.inf
+        else:
+            assert abs(g_kth[n] - o_kth[n]) <= 1e-4 * max(1.0, abs(o_kth[n])) + 1e-6
+
+
+# ---------------------------------------------------------------------------
+# hybrid attention
+# ---------------------------------------------------------------------------
+
+def fp8_random_rows(seed, tid, n, D):
+    """Synthetic fp8 rows: random finite e4m3fn codes and random positive scales."""
+    codes = (rand_u(seed, tid, (n, D)) * 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] &= 0xFE
+    scales = (rand_u(seed, tid + 1, (n, D // 64), 0.5, 1.5) / 128.0).astype(np.float32)
+    return np.concatenate([codes, scales.view(np.uint8)], axis=1)
+
+
+def make_pools(seed, ns, T, D, R, comp_ratio, dtype, with_comp=True):
+    mb = T // 256 + 2
+    bt = block_table(seed, ns, mb, extra_pages=1)
+    np_ = ns * mb + 1
+    comp = O.HostPool(comp_ratio, 1, D, R, THETA, dtype, np_, state=False) if with_comp else None
+    swa = O.HostPool(1, 1, D, R, THETA, dtype, np_, state=False)
+    for s in range(ns):
+        n_raw = 256 * mb
+        if dtype == O.BF16:
+            raw = randn_bf16(seed, 40 + s, (n_raw, D)).view(np.uint8).reshape(n_raw, -1)
+        else:
+            raw = fp8_random_rows(seed, 40 + 2 * s, n_raw, D)
+        scatter_rows(swa.rows, bt, s, 1, raw)
+        if with_comp:
+            nc = n_raw // comp_ratio
+            if dtype == O.BF16:
+                cr = randn_bf16(seed, 60 + s, (nc, D)).view(np.uint8).reshape(nc, -1)
+            else:
+                cr = fp8_random_rows(seed, 60 + 2 * s, nc, D)
+            scatter_rows(comp.rows, bt, s, comp_ratio, cr)
+    return comp, swa, bt
+
+
+def random_topk(seed, q_pos, ratio, k, invalid=False):
+    rs = np.random.default_rng(seed)
+    out = np.full((len(q_pos), k), -1, np.int32)
+    for n, p in enumerate(q_pos):
+        nv = int(p) // ratio
+        m = min(k, nv) if n % 3 else min(k, nv) // 2
+        pick = np.sort(rs.choice(nv, size=m, replace=False)) if m else np.zeros(0, np.int32)
+        out[n, :m] = pick
+    if invalid:
+        out[0, -1] = int(q_pos[0]) // ratio + 5   # not visible: masked, flagged
+    return out
+
+
+ATTN_CASES = [
+    dict(name="c4a_d128_h8_k64_f32", D=128, R=32, H=8, ratio=4, k=64, dtype=O.BF16, out=O.F32,
+         pos=[[1, 5, 127, 128, 130, 600, 1023, 1024]]),
+    dict(name="c4a_d512_h64_k512_bf16_split", D=512, R=64, H=64, ratio=4, k=512, dtype=O.BF16, out=O.BF16,
+         pos=[[2048, 2049, 4099], [3000, 700]]),
+    dict(name="c128a_d512_h64_dense_bf16", D=512, R=64, H=64, ratio=128, k=0, dtype=O.BF16, out=O.BF16,
+         pos=[[0, 100, 128, 129, 5000, 9000]]),
+    dict(name="c4a_d512_h64_fp8kv_fp8out", D=512, R=64, H=64, ratio=4, k=512, dtype=O.FP8, out=O.FP8,
+         pos=[[3000, 2500], [4096]]),
+    dict(name="c128a_d512_h64_fp8kv_fp8out", D=512, R=64, H=64, ratio=128, k=0, dtype=O.FP8, out=O.FP8,
+         pos=[[9000, 130]]),
+    dict(name="swa_only_d512_h20_f32", D=512, R=64, H=20, ratio=4, k=0, dtype=O.BF16, out=O.F32,
+         pos=[[3, 129, 1000]], no_comp=True),
+    dict(name="c4a_d512_h48_invalid_id_bf16", D=512, R=64, H=48, ratio=4, k=64, dtype=O.BF16, out=O.BF16,
+         pos=[[900, 1200]], invalid=True),
+]
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c["name"] for c in ATTN_CASES])
+def test_hybrid_attn_parity(csl, orc, case, mode):
+    D, R, H, ratio, k, dt, od = case["D"], case["R"], case["H"], case["ratio"], case["k"], case["dtype"], case["out"]
+    seed = zlib.crc32(case["name"].encode()) % 1000
+    pos_lists = case["pos"]
+    if mode == "prefill":  # prefill queries of a sequence are consecutive positions
+        pos_lists = [list(range(p[0], p[0] + len(p))) for p in pos_lists]
+    ns = len(pos_lists)
+    max_pos = max(max(p) for p in pos_lists)
+    comp, swa, bt = make_pools(seed, ns, max_pos, D, R, ratio, dt, with_comp=not case.get("no_comp"))
+    q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(pos_lists)]).astype(np.int32)
+    q_pos = np.concatenate(pos_lists).astype(np.int64)
+    nq = len(q_pos)
+    q = randn_bf16(seed, 80, (nq, H, D))
+    topk = random_topk(seed, q_pos, ratio, k, case.get("invalid", False)) if k else None
+    scale = D ** -0.5
+    o_out, o_sc, o64, f = O.hybrid_attn(comp, swa, bt, q_seq, q_pos, q, topk=topk, k=k, swa_window=128,
+                                        softmax_scale=scale, out_dtype=od)
+    assert f == (1 if case.get("invalid") else 0)
+    gcomp = gpu_pool(csl, comp, state=False) if comp is not None else None
+    gswa = gpu_pool(csl, swa, state=False)
+    odt = {O.F32: torch.float32, O.BF16: torch.bfloat16, O.FP8: torch.uint8}[od]
+    out = torch.empty((nq, H, D), dtype=odt, device=DEV)
+    scales = torch.empty((nq, H, D // 64), dtype=torch.float32, device=DEV) if od == O.FP8 else None
+    gtopk = dev(topk) if topk is not None else None
+    say(f"hybrid_attn {mode} {case['name']} nq {nq}")
+    if mode == "decode":
+        wsb = csl.hybrid_attn_workspace(nq, H, D, ratio if comp is not None else 0, k, 128, max_pos)
+        ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=DEV)
+        csl.hybrid_attn_decode(gcomp, gswa, dev(bt), dev(q_seq), dev(q_pos), max_pos, dev_bf16(q), gtopk, k, 128,
+                               scale, od, out, scales, ws)
+    else:
+        cu = np.concatenate([[0], np.cumsum([len(p) for p in pos_lists])]).astype(np.int32)
+        starts = np.array([p[0] for p in pos_lists], np.int64)
+        csl.hybrid_attn_prefill(gcomp, gswa, dev(bt), dev(cu), dev(starts), max_pos, dev_bf16(q), gtopk, k, 128,
+                                scale, od, out, scales)
+    torch.cuda.synchronize()
+    flags = csl.read_device_error()
+    assert flags == (csl.DEVERR_TOPK_ID if case.get("invalid") else 0)
+    if od == O.F32:
+        assert_close(host(out), o64, what=case["name"])
+    elif od == O.BF16:
+        assert_close(O.bf16_array_to_f64(host_u16(out)), o64, what=case["name"])
+    else:
+        assert_fp8_close(orc, host(out), host(scales), o_out, o_sc, what=case["name"])
+
+
+def test_unmapped_page_is_masked_and_flagged(csl, orc):
+    D, R, H = 512, 64, 16
+    comp, swa, bt = make_pools(7, 1, 1000, D, R, 4, O.BF16)
+    bt = bt.copy()
+    bt[0, 3] = -1          # positions 768..1023: raw tokens 872..999 partly, entries 192..255
+    q_pos = np.array([1000], np.int64)
+    q = randn_bf16(7, 80, (1, H, D))
+    topk = np.array([[1, 50, 200, 240, -1]], np.int32)
+    _, _, o64, f = O.hybrid_attn(comp, swa, bt, [0], q_pos, q, topk=topk, out_dtype=O.F32)
+    assert f > 0
+    out = torch.empty((1, H, D), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(1, csl.hybrid_attn_workspace(1, H, D, 4, 5, 128, 1000) // 4), dtype=torch.float32,
+                     device=DEV)
+    say("unmapped page masked")
+    csl.hybrid_attn_decode(gpu_pool(csl, comp, False), gpu_pool(csl, swa, False), dev(bt), dev(np.zeros(1, np.int32)),
+                           dev(q_pos), 1000, dev_bf16(q), dev(topk), 5, 128, D ** -0.5, O.F32, out, None, ws)
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == csl.DEVERR_UNMAPPED_PAGE
+    assert_close(host(out), o64, what="unmapped")
+
+
+# ---------------------------------------------------------------------------
+# the tiny workload end to end (compress x3 -> index_topk -> decode)
+# ---------------------------------------------------------------------------
+
+def test_tiny_workload_end_to_end(csl, orc):
+    from synth import workloads as W
+    w = W.tiny()
+    T, D, R, H, HI, DI, k = w.total_tokens, w.dim, w.rope_dims, w.n_heads, w.idx_heads, w.idx_dim, w.topk
+    bt = W.block_table(w).numpy()
+    from tests.util import bf16_np
+    x = bf16_np(W.latent(w, 0, 0, T))
+    lg = W.logits(w, 0, 0, T, 2).numpy()
+    xi = bf16_np(W.latent(w, 0, 0, T, dim=DI, tid=W.T_XI))
+    lgi = W.logits(w, 0, 0, T, 2, tid=W.T_LOGITS_I).numpy()
+    qd = W.queries(w)
+    q, qi, wi = bf16_np(qd["q"]), bf16_np(qd["q_idx"]), qd["w_idx"].numpy()
+    q_pos = w.query_positions().numpy()
+    q_seq = w.query_seqs().numpy()
+    nq = len(q_pos)
+    P = w.num_pages
+    o_main = O.HostPool(4, 2, D, R, THETA, O.BF16, P)
+    o_idx = O.HostPool(4, 2, DI, 0, THETA, O.BF16, P)
+    o_raw = O.HostPool(1, 1, D, R, THETA, O.BF16, P)
+    for pool, xx, ll in ((o_main, x, lg), (o_idx, xi, lgi), (o_raw, x, None)):
+        assert O.compress_insert(pool, bt, [0], [0, T], xx, ll) == 0
+    o_topk, o_kth, o_sc, _ = O.index_topk(o_idx, bt, q_seq, q_pos, qi, wi, k, want_scores=True, max_cand=T // 4)
+    o_out, _, o64, _ = O.hybrid_attn(o_main, o_raw, bt, q_seq, q_pos, q, topk=o_topk, swa_window=w.swa,
+                                     out_dtype=O.F32)
+    g_main = csl.Pool(4, 2, D, R, THETA, csl.BF16, P)
+    g_idx = csl.Pool(4, 2, DI, 0, THETA, csl.BF16, P)
+    g_raw = csl.Pool(1, 1, D, R, THETA, csl.BF16, P)
+    gbt, st, cu = dev(bt), dev(np.zeros(1, np.int64)), dev(np.array([0, T], np.int32))
+    say("tiny workload: compress x3")
+    csl.compress_insert(g_main, gbt, st, cu, dev_bf16(x), dev(lg))
+    csl.compress_insert(g_idx, gbt, st, cu, dev_bf16(xi), dev(lgi))
+    csl.compress_insert(g_raw, gbt, st, cu, dev_bf16(x))
+    topk = torch.empty((nq, k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(csl.index_topk_workspace(nq, T, k) // 4, dtype=torch.float32, device=DEV)
+    say("tiny workload: index_topk")
+    csl.index_topk(g_idx, gbt, dev(q_seq), dev(q_pos), T, dev_bf16(qi), dev(wi), k, topk, None, ws)
+    out = torch.empty((nq, H, D), dtype=torch.float32, device=DEV)
+    wsa = torch.empty(max(1, csl.hybrid_attn_workspace(nq, H, D, 4, k, w.swa, T) // 4), dtype=torch.float32,
+                      device=DEV)
+    say("tiny workload: hybrid_attn_decode")
+    csl.hybrid_attn_decode(g_main, g_raw, gbt, dev(q_seq), dev(q_pos), T, dev_bf16(q), topk, k, w.swa, D ** -0.5,
+                           O.F32, out, None, wsa)
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0
+    g_topk = host(topk)
+    assert_topk_equivalent(g_topk, o_topk, o_sc, o_kth, what="tiny")
+    same = [n for n in range(nq) if np.array_equal(g_topk[n], o_topk[n])]
+    assert len(same) >= nq * 3 // 4
+    assert_close(host(out)[same], o64[same], what="tiny attention")
