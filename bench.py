@@ -45,7 +45,7 @@ def log(msg):
 class DecodeSetup:
     """Pools, block table and step inputs of a decode workload, resident on the GPU."""
 
-    def __init__(self, w, replicas: int, device="cuda"):
+    def __init__(self, w, replicas: int, device="cuda", side_stream: bool = False):
         import torch
 
         import compressed_sparse_long_amd as csl
@@ -128,23 +128,42 @@ class DecodeSetup:
         self.out_scales = {l: (torch.empty((nq, w.n_heads, D // 64), dtype=torch.float32, device=device)
                                if w.out_dtype == 2 else None) for l in w.layers}
         self.scale = D ** -0.5
+        self.side = torch.cuda.Stream() if side_stream else None
 
-    def step(self, r: int):
-        csl, w, p = self.csl, self.w, self.reps[r]
+    def inserts(self, p):
+        """compress_insert of the new token into every pool of the layer."""
+        csl = self.csl
         csl.compress_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new)
         if "c4a" in self.layers:
             csl.compress_insert(p["main4"], self.bt, self.start, self.cu1, self.x_new, self.lg_new, self.gain)
             csl.compress_insert(p["idx"], self.bt, self.start, self.cu1, self.xi_new, self.lgi_new, self.gain_i)
+        if "c128a" in self.layers:
+            csl.compress_insert(p["main128"], self.bt, self.start, self.cu1, self.x_new, self.lg128_new)
+
+    def step(self, r: int):
+        """One decode step.  With side streams, the inserts of the new token run
+        beside the indexer and attention (the query at p reads positions < p
+        only), forked from and joined back into the current stream."""
+        csl, w, p, torch = self.csl, self.w, self.reps[r], self.torch
+        if self.side is not None:
+            main = torch.cuda.current_stream()
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                self.inserts(p)
+        else:
+            self.inserts(p)
+        if "c4a" in self.layers:
             csl.index_topk(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx, w.topk,
                            self.topk, None, self.ws_idx)
             csl.hybrid_attn_decode(p["main4"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q,
                                    self.topk, w.topk, w.swa, self.scale, w.out_dtype, self.out["c4a"],
                                    self.out_scales["c4a"], self.ws_attn)
         if "c128a" in self.layers:
-            csl.compress_insert(p["main128"], self.bt, self.start, self.cu1, self.x_new, self.lg128_new)
             csl.hybrid_attn_decode(p["main128"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q,
                                    None, 0, w.swa, self.scale, w.out_dtype, self.out["c128a"],
                                    self.out_scales["c128a"], self.ws_attn)
+        if self.side is not None:
+            torch.cuda.current_stream().wait_stream(self.side)
 
     def algorithmic_bytes_per_step(self) -> dict:
         """Bytes the method must move per step (no intermediate buffers)."""
@@ -265,6 +284,8 @@ def main():
     ap.add_argument("--workload", default="c4a", choices=["c4a", "c128a", "1m"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying HIP graphs")
+    ap.add_argument("--side-stream", action="store_true",
+                    help="run the inserts on a side stream beside the indexer and attention")
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -287,7 +308,7 @@ def main():
 
     w = {"c4a": W.c4a_decode, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)
-    setup = DecodeSetup(w, R)
+    setup = DecodeSetup(w, R, side_stream=args.side_stream)
     log(f"workload {w.name}: {w.num_seqs} x {w.ctx} tokens, {R} replicas")
 
     for i in range(args.warmup):
@@ -311,7 +332,6 @@ def main():
             graphs.append(g)
         csl.timer_enable(timing_kernel, False)
         torch.cuda.synchronize()
-        csl.timer_read(timing_kernel)              # nothing ran yet; resets the counter
         for r in range(R):
             graphs[r].replay()
         torch.cuda.synchronize()
@@ -356,7 +376,8 @@ def main():
                    "topk": w.topk, "swa": w.swa, "heads": w.n_heads, "latent_dim": w.dim, "rope_dims": w.rope_dims,
                    "indexer": f"{w.idx_heads}x{w.idx_dim}", "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
                    "out_dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.out_dtype], "replicas": R,
-                   "hip_graphs": bool(graphs), "algorithmic_bytes_per_step": step_bytes},
+                   "hip_graphs": bool(graphs), "insert_stream": "side" if args.side_stream else "main",
+                   "algorithmic_bytes_per_step": step_bytes},
         "roofline": roof,
     }
     if not args.no_cpu and w.layers == ("c4a",):

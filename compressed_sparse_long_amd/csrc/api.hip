@@ -151,6 +151,8 @@ int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_
     int64_t keys = (int64_t)(swa_window < max_q_pos ? swa_window : max_q_pos);
     if (comp_ratio > 0) keys += k > 0 ? k : max_q_pos / comp_ratio;
     int64_t tiles = (keys + 31) / 32;
+    // enough workgroups to spread over the CUs, but at least 2 tiles (64 keys)
+    // per split: every split writes a heads x dim fp32 partial
     int64_t want = (512 + num_q - 1) / (num_q > 0 ? num_q : 1);
     int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
     int64_t sp = want < cap ? want : cap;

@@ -19,6 +19,16 @@
 // reused as the P^T operand without an LDS round trip: the key order inside
 // the operand is permuted and V^T is read with the same permutation.  The
 // online softmax runs in the exp2 domain with one max/sum per head column.
+//
+// Key addresses (top-k id -> block table -> page row) are resolved once per
+// chunk of 8 tiles, one key per thread, into an LDS table, so a tile load is
+// a single dependent global access.
+//
+// Precision variant (PREC, used for fp8 output, whose one-ULP acceptance near
+// zero needs the pre-quantisation output to fp32-level accuracy): P is carried
+// as P_hi + P_lo (two bf16 MFMAs), and fp8 keys are dequantised to fp32 and
+// stored as two bf16 copies hi + lo, so S = K_hi.q + K_lo.q and
+// O = V_hi.P_hi + V_hi.P_lo + V_lo.P_hi (~2^-16 relative).
 #include "csl_kernels.hpp"
 
 namespace csl {
@@ -27,7 +37,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;  // keys per tile
-constexpr int kVtStride = kTile + 4;
+constexpr int kVtStride = kTile + 8;  // 80-byte rows: a 16-lane phase of 16-byte reads hits 64 distinct banks
 
 template <int D>
 struct Cfg {
@@ -102,13 +112,11 @@ struct Slice {
 };
 
 template <int D, int KV>
-__device__ __forceinline__ void load_slice(Slice<D, KV>& sl, const AttnArgs& a, int n, int s, int64_t tile,
-                                           int64_t L, int64_t Lc, int64_t nv_c, int64_t lo, int kg, int dc) {
+__device__ __forceinline__ void load_slice(Slice<D, KV>& sl, const uint8_t* const* rows, int kg, int dc) {
     constexpr int DPT = Cfg<D>::DPT;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        int64_t j = tile * kTile + 4 * kg + q;
-        const uint8_t* row = j < L ? key_row(a, n, s, j, Lc, nv_c, lo) : nullptr;
+        const uint8_t* row = rows[4 * kg + q];
         sl.valid[q] = row != nullptr;
         if constexpr (KV == kBF16) {
             if constexpr (DPT == 16) {
@@ -143,22 +151,10 @@ __device__ __forceinline__ void load_slice(Slice<D, KV>& sl, const AttnArgs& a, 
     }
 }
 
-template <int D, int KV>
-__device__ __forceinline__ void store_slice(const Slice<D, KV>& sl, uint16_t* Kl, uint16_t* Vt, uint32_t* valid,
-                                            int kg, int dc) {
+template <int D>
+__device__ __forceinline__ void write_kv(const uint32_t (&h)[4][Cfg<D>::DPT], uint16_t* Kl, uint16_t* Vt, int kg,
+                                         int dc) {
     constexpr int DPT = Cfg<D>::DPT, KSTR = Cfg<D>::KSTR;
-    uint32_t h[4][DPT];  // bf16 bits, key q, element e
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if constexpr (KV == kBF16) {
-#pragma unroll
-            for (int e = 0; e < DPT; ++e) h[q][e] = (sl.w[q][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        } else {
-#pragma unroll
-            for (int e = 0; e < DPT; ++e)
-                h[q][e] = f32_to_bf16_bits(e4m3_to_f32((sl.w[q][e >> 2] >> (8 * (e & 3))) & 0xffu) * sl.scale[q]);
-        }
-    }
     // K rows
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -175,24 +171,59 @@ __device__ __forceinline__ void store_slice(const Slice<D, KV>& sl, uint16_t* Kl
             *reinterpret_cast<u32x2*>(dst) = u32x2{h[q][0] | (h[q][1] << 16), h[q][2] | (h[q][3] << 16)};
         }
     }
-    // V^T rows: element e of the 4 keys side by side
+    // V^T rows in the order the P^T operand uses: position 8g + c holds key
+    // 4g + c (c < 4) or 16 + 4g + (c - 4) (c >= 4), so a lane's 8 keys are one
+    // 16-byte read.  This thread's keys 4kg..4kg+3 land at 4 adjacent positions.
+    const int vpos = kg < 4 ? 8 * kg : 8 * (kg - 4) + 4;
 #pragma unroll
     for (int e = 0; e < DPT; ++e) {
         u32x2 v = {h[0][e] | (h[1][e] << 16), h[2][e] | (h[3][e] << 16)};
-        *reinterpret_cast<u32x2*>(Vt + (dc * DPT + e) * kVtStride + 4 * kg) = v;
+        *reinterpret_cast<u32x2*>(Vt + (dc * DPT + e) * kVtStride + vpos) = v;
     }
+}
+
+// Write a thread's slice to LDS: K rows and V^T rows (and, with SPLITKV, the
+// bf16 remainder copies).
+template <int D, int KV, bool SPLITKV>
+__device__ __forceinline__ void store_slice(const Slice<D, KV>& sl, uint16_t* Kl, uint16_t* Vt, uint16_t* Kl_lo,
+                                            uint16_t* Vt_lo, uint32_t* valid, int kg, int dc) {
+    constexpr int DPT = Cfg<D>::DPT;
+    uint32_t h[4][DPT];  // bf16 bits, key q, element e
+    uint32_t lo[4][SPLITKV ? DPT : 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (KV == kBF16) {
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) h[q][e] = (sl.w[q][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        } else {
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) {
+                float v = e4m3_to_f32((sl.w[q][e >> 2] >> (8 * (e & 3))) & 0xffu) * sl.scale[q];
+                h[q][e] = f32_to_bf16_bits(v);
+                if constexpr (SPLITKV) lo[q][e] = f32_to_bf16_bits(v - bf16_bits_to_f32(h[q][e]));
+            }
+        }
+    }
+    write_kv<D>(h, Kl, Vt, kg, dc);
+    if constexpr (SPLITKV) write_kv<D>(lo, Kl_lo, Vt_lo, kg, dc);
     if (dc == 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) valid[4 * kg + q] = sl.valid[q] ? 1u : 0u;
     }
 }
 
-template <int D, int KV>
-__global__ void __launch_bounds__(kThreads) hybrid_attn_kernel(AttnArgs a) {
+template <int D, int KV, bool PREC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, D == 512 ? 1 : 4)))
+hybrid_attn_kernel(AttnArgs a) {
     constexpr int KS = Cfg<D>::KS, MT = Cfg<D>::MT, KSTR = Cfg<D>::KSTR;
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * kVtStride];
+    constexpr bool SPLITKV = PREC && KV == kFP8;
+    constexpr int NC = SPLITKV ? 2 : 1;
+    constexpr int kChunkTiles = kThreads / kTile;  // tiles whose addresses one pass resolves
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[NC][kTile * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[NC][D * kVtStride];
+    __shared__ const uint8_t* s_rows[kThreads];
     __shared__ uint32_t s_valid[kTile];
+    __shared__ float s_rope[2][64];  // cos, sin of -p * theta^(-2j/R) for the R/2 pairs
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -215,6 +246,7 @@ __global__ void __launch_bounds__(kThreads) hybrid_attn_kernel(AttnArgs a) {
 
     const int head = 16 * wave + r16;
     const bool wave_active = 16 * wave < a.n_heads;
+    if (a.n_splits == 1 && tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
 
     // q rows as B operands: lane = head column, 8 dims per k-step
     bf16x8 qb[KS];
@@ -231,68 +263,88 @@ __global__ void __launch_bounds__(kThreads) hybrid_attn_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     Slice<D, KV> sl;
-    if (t_begin < t_end) load_slice<D, KV>(sl, a, n, s, t_begin, L, Lc, nv_c, lo, kg, dc);
-
-    for (int64_t t = t_begin; t < t_end; ++t) {
-        __syncthreads();  // the previous tile's LDS reads are done
-        store_slice<D, KV>(sl, s_k, s_vt, s_valid, kg, dc);
+    for (int64_t cs = t_begin; cs < t_end; cs += kChunkTiles) {
+        const int64_t ce = cs + kChunkTiles < t_end ? cs + kChunkTiles : t_end;
+        __syncthreads();  // the previous chunk's reads of s_rows are done
+        {
+            const int64_t j = cs * kTile + tid;
+            s_rows[tid] = (j < ce * kTile && j < L) ? key_row(a, n, s, j, Lc, nv_c, lo) : nullptr;
+        }
         __syncthreads();
-        if (t + 1 < t_end) load_slice<D, KV>(sl, a, n, s, t + 1, L, Lc, nv_c, lo, kg, dc);
-        if (!wave_active) continue;
+        load_slice<D, KV>(sl, s_rows, kg, dc);
+        for (int64_t t = cs; t < ce; ++t) {
+            __syncthreads();  // the previous tile's LDS reads are done
+            store_slice<D, KV, SPLITKV>(sl, s_k[0], s_vt[0], s_k[NC - 1], s_vt[NC - 1], s_valid, kg, dc);
+            __syncthreads();
+            if (t + 1 < ce) load_slice<D, KV>(sl, s_rows + (t + 1 - cs) * kTile, kg, dc);
+            if (!wave_active) continue;
 
-        // S^T = K . Q^T for the tile's two 16-key m-tiles
-        f32x4 st[2];
+            // S^T = K . Q^T for the tile's two 16-key m-tiles
+            f32x4 st[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t* krow = s_k + (16 * mt + r16) * KSTR + 8 * g;
+            for (int mt = 0; mt < 2; ++mt) {
+                st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
-                st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[mt], 0, 0, 0);
+                for (int c = 0; c < NC; ++c) {
+                    const uint16_t* krow = s_k[c] + (16 * mt + r16) * KSTR + 8 * g;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+                        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[mt], 0, 0, 0);
+                    }
+                }
             }
-        }
-        // online softmax over this head column (keys 16mt + 4g + i)
-        float x[8];
-        float tmax = -INFINITY;
+            // online softmax over this head column (keys 16mt + 4g + i)
+            float x[8];
+            float tmax = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = s_valid[16 * mt + 4 * g + i] ? st[mt][i] * a.scale_log2 : -INFINITY;
-                x[4 * mt + i] = v;
-                tmax = fmaxf(tmax, v);
+                for (int i = 0; i < 4; ++i) {
+                    float v = s_valid[16 * mt + 4 * g + i] ? st[mt][i] * a.scale_log2 : -INFINITY;
+                    x[4 * mt + i] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float m_new = fmaxf(m_run, tmax);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = exp2f(m_run - m_use);
+            float psum = 0.f;
+            uint32_t pw[4], pl[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float p0 = exp2f(x[2 * c] - m_use), p1 = exp2f(x[2 * c + 1] - m_use);
+                psum += p0 + p1;
+                pw[c] = pack_bf16x2(p0, p1);
+                if constexpr (PREC) {
+                    pl[c] = pack_bf16x2(p0 - bf16_bits_to_f32(pw[c] & 0xffffu), p1 - bf16_bits_to_f32(pw[c] >> 16));
+                }
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        float psum = 0.f;
-        uint32_t pw[4];
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float p0 = exp2f(x[2 * c] - m_use), p1 = exp2f(x[2 * c + 1] - m_use);
-            psum += p0 + p1;
-            pw[c] = pack_bf16x2(p0, p1);
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__ballot(alpha != 1.0f)) {
+                for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+            }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+            bf16x8 pbl = pb;
+            if constexpr (PREC) pbl = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+            // O^T += V^T . P^T; operand slot c <-> key 4g+c (c<4), 16+4g+(c-4) (c>=4)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] *= alpha;
-        }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-        // O^T += V^T . P^T; operand slot c <-> key 4g+c (c<4), 16+4g+(c-4) (c>=4)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint16_t* vrow = s_vt + (16 * m + r16) * kVtStride + 4 * g;
-            u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-            u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-            bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[m], 0, 0, 0);
+            for (int m = 0; m < MT; ++m) {
+                const bf16x8 va = *reinterpret_cast<const bf16x8*>(s_vt[0] + (16 * m + r16) * kVtStride + 8 * g);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[m], 0, 0, 0);
+                if constexpr (PREC) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, acc[m], 0, 0, 0);
+                if constexpr (SPLITKV) {
+                    const bf16x8 vb =
+                        *reinterpret_cast<const bf16x8*>(s_vt[NC - 1] + (16 * m + r16) * kVtStride + 8 * g);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb, acc[m], 0, 0, 0);
+                }
+            }
         }
     }
+    __syncthreads();  // every wave passes here: s_rope is visible to the epilogue
     if (!wave_active) return;
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -322,8 +374,8 @@ __global__ void __launch_bounds__(kThreads) hybrid_attn_kernel(AttnArgs a) {
         if (d0 >= rbase) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                float cs, sn;
-                rope_cs(-p, a.rf.inv_freq[(d0 + 2 * c - rbase) >> 1], cs, sn);
+                const int j = (d0 + 2 * c - rbase) >> 1;
+                const float cs = s_rope[0][j], sn = s_rope[1][j];
                 float u = acc[m][2 * c], v = acc[m][2 * c + 1];
                 acc[m][2 * c] = u * cs - v * sn;
                 acc[m][2 * c + 1] = u * sn + v * cs;
@@ -342,25 +394,28 @@ __global__ void __launch_bounds__(kThreads) hybrid_attn_kernel(AttnArgs a) {
             *reinterpret_cast<u32x2*>(o + 16 * m + 4 * g) =
                 u32x2{pack_bf16x2(acc[m][0], acc[m][1]), pack_bf16x2(acc[m][2], acc[m][3])};
     } else {
+        // 64-element groups = 4 consecutive m-tiles x the 4 lanes g of this head
         uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + obase;
+        float gmax[D / 64];
+#pragma unroll
+        for (int G = 0; G < D / 64; ++G) gmax[G] = 0.f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gmax[m >> 2] = fmaxf(gmax[m >> 2], fabsf(acc[m][i]));
 #pragma unroll
         for (int G = 0; G < D / 64; ++G) {
-            float amax = 0.f;
+            float v = fmaxf(gmax[G], __shfl_xor(gmax[G], 16));
+            v = fmaxf(v, __shfl_xor(v, 32));
+            gmax[G] = v > 0.f ? v / 448.0f : 1.0f;  // the group's scale
+            if (g == 0) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + G] = gmax[G];
+        }
 #pragma unroll
-            for (int m = 4 * G; m < 4 * G + 4; ++m)
+        for (int m = 0; m < MT; ++m) {
+            uint32_t code = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[m][i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-#pragma unroll
-            for (int m = 4 * G; m < 4 * G + 4; ++m) {
-                uint32_t code = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) code |= f32_to_e4m3(acc[m][i] / scale) << (8 * i);
-                *reinterpret_cast<uint32_t*>(o + 16 * m + 4 * g) = code;
-            }
-            if (g == 0) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + G] = scale;
+            for (int i = 0; i < 4; ++i) code |= f32_to_e4m3(acc[m][i] / gmax[m >> 2]) << (8 * i);
+            *reinterpret_cast<uint32_t*>(o + 16 * m + 4 * g) = code;
         }
     }
 }
@@ -377,23 +432,25 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
     const int64_t p = qi.ok ? qi.p : 0;
 
     const float* ml = a.part_ml + ((int64_t)n * a.n_splits * a.n_heads + head) * 2;
+    const int64_t mstride = (int64_t)a.n_heads * 2;
     float M = -INFINITY;
-    for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, ml[(int64_t)sp * a.n_heads * 2]);
+    for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, ml[sp * mstride]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float Lsum = 0.f;
+    const float* po = a.part_o + ((int64_t)n * a.n_splits * a.n_heads + head) * D + 8 * (active ? lane : 0);
+    const int64_t pstride = (int64_t)a.n_heads * D;
+#pragma unroll 4
     for (int sp = 0; sp < a.n_splits; ++sp) {
-        const float wsp = exp2f(ml[(int64_t)sp * a.n_heads * 2] - Mu);
-        Lsum += ml[(int64_t)sp * a.n_heads * 2 + 1] * wsp;
-        if (active && wsp > 0.f) {
-            const float* po = a.part_o + (((int64_t)n * a.n_splits + sp) * a.n_heads + head) * D + 8 * lane;
-            f32x4 v0 = *reinterpret_cast<const f32x4*>(po);
-            f32x4 v1 = *reinterpret_cast<const f32x4*>(po + 4);
+        // an empty split stored m = -inf, l = 0 and zeros: its weight is 0
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(po + sp * pstride);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(po + sp * pstride + 4);
+        const float wsp = exp2f(ml[sp * mstride] - Mu);
+        Lsum += ml[sp * mstride + 1] * wsp;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                o[c] = fmaf(wsp, v0[c], o[c]);
-                o[4 + c] = fmaf(wsp, v1[c], o[4 + c]);
-            }
+        for (int c = 0; c < 4; ++c) {
+            o[c] = fmaf(wsp, v0[c], o[c]);
+            o[4 + c] = fmaf(wsp, v1[c], o[4 + c]);
         }
     }
     const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
@@ -441,13 +498,19 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
 
 }  // namespace
 
+template <int D, int KV>
+void launch_prec(const AttnArgs& a, dim3 grid, hipStream_t st) {
+    if (a.out_dtype == kFP8) hipLaunchKernelGGL((hybrid_attn_kernel<D, KV, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((hybrid_attn_kernel<D, KV, false>), grid, dim3(kThreads), 0, st, a);
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     if (a.num_q <= 0) return hipSuccess;
     dim3 grid((unsigned)((int64_t)a.num_q * a.n_splits));
     const int kv = a.comp_rows ? a.comp_dtype : a.swa_dtype;
-    if (a.dim == 512 && kv == kBF16) hipLaunchKernelGGL((hybrid_attn_kernel<512, kBF16>), grid, dim3(kThreads), 0, st, a);
-    else if (a.dim == 512 && kv == kFP8) hipLaunchKernelGGL((hybrid_attn_kernel<512, kFP8>), grid, dim3(kThreads), 0, st, a);
-    else if (a.dim == 128 && kv == kBF16) hipLaunchKernelGGL((hybrid_attn_kernel<128, kBF16>), grid, dim3(kThreads), 0, st, a);
+    if (a.dim == 512 && kv == kBF16) launch_prec<512, kBF16>(a, grid, st);
+    else if (a.dim == 512 && kv == kFP8) launch_prec<512, kFP8>(a, grid, st);
+    else if (a.dim == 128 && kv == kBF16) launch_prec<128, kBF16>(a, grid, st);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -18,14 +18,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Sequence s with cu[s] <= j < cu[s+1]: the wave reads 64 boundaries per step
+// in parallel and counts the ones <= j (cu is non-decreasing).  Wave-uniform.
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int num_seqs, int j) {
-    int lo = 0, hi = num_seqs;  // invariant: cu[lo] <= j < cu[hi]
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (cu[mid] <= j) lo = mid;
-        else hi = mid;
+    const int lane = threadIdx.x & 63;
+    int s = -1;
+    for (int base = 1; base <= num_seqs; base += 64) {
+        const int i = base + lane;
+        const bool le = i <= num_seqs && cu[i] <= j;
+        s += (int)__popcll(__ballot(le));
+        if (!__ballot(i <= num_seqs && !le)) continue;
+        break;
     }
-    return lo;
+    s += 1;
+    return s < num_seqs ? s : num_seqs - 1;
 }
 
 __device__ __forceinline__ void load8(const uint16_t* p, float* v) {

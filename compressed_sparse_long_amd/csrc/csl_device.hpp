@@ -93,13 +93,18 @@ __device__ __forceinline__ float group8_max(float v) {
 
 // ---------------------------------------------------------------- RoPE
 
-// cos/sin of pos * inv_freq, the product and its reduction in fp64.
+// cos/sin of pos * inv_freq.  The angle is formed and reduced to [-pi, pi] in
+// fp64 (two-constant Cody-Waite split of 2*pi: 2*pi rounded to 34 significant
+// bits, so k*C1 is exact for |k| < 2^19, i.e. angles up to ~3.3e6 rad), then
+// the small-argument sincos runs in fp32.  Error ~1e-7 rad at 2^20 positions.
 __device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float& c, float& s) {
-    double phi = (double)pos * inv_freq;
-    double sd, cd;
-    sincos(phi, &sd, &cd);
-    c = (float)cd;
-    s = (float)sd;
+    constexpr double kTwoPiHi = 6.283185307402164;        // 2*pi to 34 bits
+    constexpr double kTwoPiLo = -2.2257726704749154e-10;  // 2*pi - kTwoPiHi
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const double phi = (double)pos * inv_freq;
+    const double k = rint(phi * kInvTwoPi);
+    const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, phi));
+    sincosf((float)r, &s, &c);
 }
 
 // ---------------------------------------------------------------- paging

@@ -140,50 +140,32 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& tota
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
-__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
-    __shared__ uint32_t s_hist[2048];
-    __shared__ uint32_t s_wave[kSelWaves];
-    __shared__ uint32_t s_cnt[2][kSelWaves];
-    __shared__ uint32_t s_prefix, s_rem;
-    __shared__ float s_min[kSelWaves];
+// Keys of a query's scores: in LDS, or read from global memory.
+struct LdsKeys {
+    const uint32_t* k;
+    __device__ __forceinline__ uint32_t operator()(int64_t e) const { return k[e]; }
+};
+struct GlobalKeys {
+    const float* sc;
+    __device__ __forceinline__ uint32_t operator()(int64_t e) const { return score_key(sc[e]); }
+};
 
-    const int n = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int s;
-    int64_t p;
-    int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;  // the score kernel reports bad queries
-    const float* sc = a.scores + (int64_t)n * a.stride;
-    int32_t* out = a.topk + (int64_t)n * a.k;
-    const int k = a.k;
-
-    if (nv <= k) {
-        for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
-        if (a.kth) {
-            float m = INFINITY;
-            for (int64_t e = tid; e < nv; e += kSelThreads) m = fminf(m, sc[e]);
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) m = fminf(m, __shfl_xor(m, o));
-            if (lane == 0) s_min[wave] = m;
-            __syncthreads();
-            if (tid == 0) {
-                float r = INFINITY;
-                for (int w = 0; w < kSelWaves; ++w) r = fminf(r, s_min[w]);
-                a.kth[n] = nv > 0 ? r : -INFINITY;
-            }
-        }
-        return;
-    }
-
-    // radix select of the k-th largest key: rounds of 11, 11 and 10 bits
-    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)k;
+// Exact radix select (11/11/10-bit rounds) of the `want`-th largest key among
+// keys [0, n) of `key_at`; returns the key, and in *rem how many copies of it
+// are taken.  LDS histograms; every thread of the workgroup must call it.
+template <typename Keys>
+__device__ uint32_t radix_select(const Keys& key_at, int64_t n, uint32_t want, uint32_t* rem_out, uint32_t* s_hist,
+                                 uint32_t* s_wave, uint32_t* s_sel) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0, rem = want;
     const int shifts[3] = {21, 10, 0};
     const int widths[3] = {11, 11, 10};
     for (int r = 0; r < 3; ++r) {
         const int sh = shifts[r], nb = 1 << widths[r];
         for (int b = tid; b < 2048; b += kSelThreads) s_hist[b] = 0;
         __syncthreads();
-        for (int64_t e = tid; e < nv; e += kSelThreads) {
-            uint32_t key = score_key(sc[e]);
+        for (int64_t e = tid; e < n; e += kSelThreads) {
+            uint32_t key = key_at(e);
             if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1u);
         }
         __syncthreads();
@@ -195,29 +177,36 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
         uint32_t above = block_excl_scan(c_hi + c_lo, s_wave, tot);
         if (hi >= 0) {
             if (above < rem && rem <= above + c_hi) {
-                s_prefix = prefix | ((uint32_t)hi << sh);
-                s_rem = rem - above;
+                s_sel[0] = prefix | ((uint32_t)hi << sh);
+                s_sel[1] = rem - above;
             } else if (hi - 1 >= 0 && above + c_hi < rem && rem <= above + c_hi + c_lo) {
-                s_prefix = prefix | ((uint32_t)(hi - 1) << sh);
-                s_rem = rem - above - c_hi;
+                s_sel[0] = prefix | ((uint32_t)(hi - 1) << sh);
+                s_sel[1] = rem - above - c_hi;
             }
         }
         __syncthreads();
-        prefix = s_prefix;
-        rem = s_rem;
+        prefix = s_sel[0];
+        rem = s_sel[1];
         pmask |= (uint32_t)(nb - 1) << sh;
         __syncthreads();
     }
-    const uint32_t T = prefix;  // the k-th largest key; `rem` copies of it are taken
+    *rem_out = rem;
+    return prefix;
+}
 
-    // each wave owns ids [w*seg, (w+1)*seg); count keys > T and == T per wave
+// Emit the ids of keys > T, plus the first `rem` ids (by id) of keys == T, in
+// ascending id order.  Wave w owns ids [w*seg, (w+1)*seg).
+template <typename Keys>
+__device__ void emit_ordered(const Keys& key_at, int64_t nv, uint32_t T, uint32_t rem, int k, int32_t* out,
+                             uint32_t (*s_cnt)[kSelWaves]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t seg = ((nv + kSelWaves - 1) / kSelWaves + 63) & ~(int64_t)63;
     const int64_t lo = (int64_t)wave * seg;
     const int64_t hi = lo + seg < nv ? lo + seg : nv;
     uint32_t n_gt = 0, n_eq = 0;
     for (int64_t e = lo + lane; e - lane < hi; e += 64) {
-        uint32_t key = e < hi ? score_key(sc[e]) : 0u;
         bool in = e < hi;
+        uint32_t key = in ? key_at(e) : 0u;
         n_gt += __popcll(__ballot(in && key > T));
         n_eq += __popcll(__ballot(in && key == T));
     }
@@ -233,10 +222,9 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
         out_pos += s_cnt[0][w] + take_eq;
         eq_seen += eq_w;
     }
-    // ordered emission
     for (int64_t e = lo + lane; e - lane < hi; e += 64) {
         bool in = e < hi;
-        uint32_t key = in ? score_key(sc[e]) : 0u;
+        uint32_t key = in ? key_at(e) : 0u;
         bool gt = in && key > T, eq = in && key == T;
         uint64_t eqm = __ballot(eq);
         uint32_t eq_rank = eq_seen + __popcll(eqm & lanemask_lt(lane));
@@ -247,7 +235,224 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
         out_pos += __popcll(selm);
         eq_seen += __popcll(eqm);
     }
-    if (tid == 0 && a.kth) a.kth[n] = key_score(T);
+}
+
+constexpr int kRegKeys = 32;                     // keys per thread held in registers
+constexpr int kRegMax = kRegKeys * kSelThreads;  // 32768 candidates
+constexpr int kCandCap = 4096;                   // boundary-bin candidates kept in LDS
+constexpr int kRankCap = kSelThreads;            // candidates ranked directly
+
+// Exact radix select (11/11/10-bit rounds) over register-resident keys: the
+// `want`-th largest of the valid keys; *rem = copies of it that are taken.
+__device__ uint32_t radix_select_regs(const uint32_t (&key)[32], int nmine, uint32_t want, uint32_t* rem_out,
+                                      uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0, rem = want;
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int r = 0; r < 3; ++r) {
+        const int sh = shifts[r], nb = 1 << widths[r];
+        for (int b = tid; b < 2048; b += kSelThreads) s_hist[b] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (i < nmine && (key[i] & pmask) == prefix) atomicAdd(&s_hist[(key[i] >> sh) & (nb - 1)], 1u);
+        __syncthreads();
+        const int hi = nb - 1 - 2 * tid;
+        uint32_t c_hi = hi >= 0 ? s_hist[hi] : 0u;
+        uint32_t c_lo = hi - 1 >= 0 ? s_hist[hi - 1] : 0u;
+        uint32_t tot;
+        uint32_t above = block_excl_scan(c_hi + c_lo, s_wave, tot);
+        if (hi >= 0) {
+            if (above < rem && rem <= above + c_hi) {
+                s_sel[0] = prefix | ((uint32_t)hi << sh);
+                s_sel[1] = rem - above;
+            } else if (hi - 1 >= 0 && above + c_hi < rem && rem <= above + c_hi + c_lo) {
+                s_sel[0] = prefix | ((uint32_t)(hi - 1) << sh);
+                s_sel[1] = rem - above - c_hi;
+            }
+        }
+        __syncthreads();
+        prefix = s_sel[0];
+        rem = s_sel[1];
+        pmask |= (uint32_t)(nb - 1) << sh;
+        __syncthreads();
+    }
+    *rem_out = rem;
+    return prefix;
+}
+
+// Register-resident select for nv <= 32768.  Thread t holds the 32 keys of ids
+// [32t, 32t+32), so ids stay ordered by thread and every compaction is one
+// block-wide exclusive scan of per-thread counts:
+//  1. a 2048-bin histogram of the keys inside a window of 2^24 key units
+//     below the largest key (two octaves of fp32 score below the maximum;
+//     keys under the window are not counted), scanned from the top: the bin b
+//     that holds the k-th key and `want` = its rank inside b.  Bins of 2^13
+//     key units keep b small.  If fewer than k keys fall in the window, an
+//     exact 3-round radix select over all keys is used instead;
+//  2. b's keys are compacted to LDS and the k-th key T is the candidate with
+//     #(> T) < want <= #(>= T);
+//  3. ids with key > T, then the first `rem` ids with key == T, are written in
+//     ascending order through one scan of packed (count_gt, count_eq).
+__device__ void select_registers(const float* sc, int64_t nv, int k, int32_t* out, float* kth, uint32_t* s_hist,
+                                 uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t e0 = (int64_t)tid * kRegKeys;
+    uint32_t key[kRegKeys];
+    if (e0 + kRegKeys <= nv) {
+        const float4* p4 = reinterpret_cast<const float4*>(sc + e0);
+#pragma unroll
+        for (int i = 0; i < kRegKeys / 4; ++i) {
+            const float4 v = p4[i];
+            key[4 * i] = score_key(v.x);
+            key[4 * i + 1] = score_key(v.y);
+            key[4 * i + 2] = score_key(v.z);
+            key[4 * i + 3] = score_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRegKeys; ++i) key[i] = e0 + i < nv ? score_key(sc[e0 + i]) : 0u;
+    }
+    const int nmine = (int)(nv - e0 < 0 ? 0 : (nv - e0 < kRegKeys ? nv - e0 : kRegKeys));
+
+    // the largest key, and the histogram zeroed under the same barrier
+    uint32_t kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) kmax = i < nmine ? max(kmax, key[i]) : kmax;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    if (lane == 0) s_sel[8 + wave] = kmax;
+    for (int b = tid; b < 2048; b += kSelThreads) s_hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) kmax = max(kmax, s_sel[8 + w]);
+    constexpr uint32_t kWin = (1u << 24) - 1u;
+    const uint32_t lo = kmax > kWin ? kmax - kWin : 0u;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i)
+        if (i < nmine && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
+    __syncthreads();
+    const int hb = 2047 - 2 * tid;  // this thread's two bins, from the top
+    const uint32_t c_hi = s_hist[hb], c_lo = s_hist[hb - 1];
+    uint32_t tot;
+    const uint32_t above = block_excl_scan(c_hi + c_lo, s_wave, tot);
+    if (above < (uint32_t)k && (uint32_t)k <= above + c_hi) {
+        s_sel[0] = hb;
+        s_sel[1] = k - above;
+        s_sel[2] = c_hi;
+    } else if (above + c_hi < (uint32_t)k && (uint32_t)k <= above + c_hi + c_lo) {
+        s_sel[0] = hb - 1;
+        s_sel[1] = k - above - c_hi;
+        s_sel[2] = c_lo;
+    }
+    __syncthreads();
+
+    uint32_t T, rem;
+    if (tot >= (uint32_t)k && s_sel[2] <= (uint32_t)kCandCap) {
+        const uint32_t bsel = s_sel[0], want = s_sel[1], cnt = s_sel[2];
+        auto in_bin = [&](uint32_t kk) { return kk >= lo && ((kk - lo) >> 13) == bsel; };
+        uint32_t mine = 0;
+#pragma unroll
+        for (int i = 0; i < kRegKeys; ++i) mine += (i < nmine && in_bin(key[i])) ? 1u : 0u;
+        uint32_t off = block_excl_scan(mine, s_wave, tot);
+#pragma unroll
+        for (int i = 0; i < kRegKeys; ++i)
+            if (i < nmine && in_bin(key[i])) s_cand[off++] = key[i];
+        __syncthreads();
+        if (cnt <= (uint32_t)kRankCap) {
+            if ((uint32_t)tid < cnt) {
+                const uint32_t kc = s_cand[tid];
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t j = 0; j < cnt; ++j) {
+                    const uint32_t kj = s_cand[j];
+                    gt += kj > kc ? 1u : 0u;
+                    ge += kj >= kc ? 1u : 0u;
+                }
+                if (gt < want && want <= ge) {  // every copy of T writes the same values
+                    s_sel[4] = kc;
+                    s_sel[5] = want - gt;
+                }
+            }
+            __syncthreads();
+            T = s_sel[4];
+            rem = s_sel[5];
+        } else {
+            T = radix_select(LdsKeys{s_cand}, (int64_t)cnt, want, &rem, s_hist, s_wave, s_sel + 4);
+        }
+    } else {
+        T = radix_select_regs(key, nmine, (uint32_t)k, &rem, s_hist, s_wave, s_sel + 4);
+    }
+
+    // 3. ordered emission: one scan of packed (count_gt | count_eq << 16)
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+        ngt += (i < nmine && key[i] > T) ? 1u : 0u;
+        neq += (i < nmine && key[i] == T) ? 1u : 0u;
+    }
+    const uint32_t pre = block_excl_scan(ngt | (neq << 16), s_wave, tot);
+    uint32_t eq_before = pre >> 16;
+    uint32_t pos = (pre & 0xffffu) + (eq_before < rem ? eq_before : rem);
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+        if (i >= nmine) break;
+        bool sel = key[i] > T;
+        if (key[i] == T) {
+            sel = eq_before < rem;
+            ++eq_before;
+        }
+        if (sel) {
+            if (pos < (uint32_t)k) out[pos] = (int32_t)(e0 + i);
+            ++pos;
+        }
+    }
+    if (tid == 0 && kth) *kth = key_score(T);
+}
+
+__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
+    __shared__ uint32_t s_hist[2048];
+    __shared__ uint32_t s_cand[kCandCap];
+    __shared__ uint32_t s_wave[kSelWaves];
+    __shared__ uint32_t s_cnt[2][kSelWaves];
+    __shared__ uint32_t s_sel[8 + kSelWaves];
+    __shared__ float s_min[kSelWaves];
+
+    const int n = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int s;
+    int64_t p;
+    const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;  // the score kernel reports bad queries
+    const float* sc = a.scores + (int64_t)n * a.stride;
+    int32_t* out = a.topk + (int64_t)n * a.k;
+    const int k = a.k;
+    float* kth = a.kth ? a.kth + n : nullptr;
+
+    if (nv <= k) {
+        for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
+        if (kth) {
+            float m = INFINITY;
+            for (int64_t e = tid; e < nv; e += kSelThreads) m = fminf(m, sc[e]);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) m = fminf(m, __shfl_xor(m, o));
+            if (lane == 0) s_min[wave] = m;
+            __syncthreads();
+            if (tid == 0) {
+                float r = INFINITY;
+                for (int w = 0; w < kSelWaves; ++w) r = fminf(r, s_min[w]);
+                *kth = nv > 0 ? r : -INFINITY;
+            }
+        }
+        return;
+    }
+    if (nv <= kRegMax) {
+        select_registers(sc, nv, k, out, kth, s_hist, s_wave, s_sel, s_cand);
+    } else {
+        uint32_t rem;
+        const uint32_t T = radix_select(GlobalKeys{sc}, nv, (uint32_t)k, &rem, s_hist, s_wave, s_sel);
+        emit_ordered(GlobalKeys{sc}, nv, T, rem, k, out, s_cnt);
+        if (tid == 0 && kth) *kth = key_score(T);
+    }
 }
 
 }  // namespace

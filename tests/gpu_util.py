@@ -58,10 +58,11 @@ def assert_fp8_close(orc, codes_g, scales_g, codes_o, scales_o, group=64, what="
     assert_close(scales_g, scales_o, rtol=1e-2, atol=0, what=what + " scales")
     sg = np.repeat(np.asarray(scales_g, np.float64), group, axis=-1).reshape(codes_g.shape)
     so = np.repeat(np.asarray(scales_o, np.float64), group, axis=-1).reshape(codes_o.shape)
-    co = tab[codes_o]
-    vg = tab[codes_g] * sg
+    co, cg = tab[codes_o], tab[codes_g]
+    vg = cg * sg
     vo = co * so
-    lim = e4m3_ulp(co) * so + np.abs(co) * np.abs(sg - so) + 1e-30
+    # vg - vo = (cg - co) * so + cg * (sg - so): one code step plus the scale difference
+    lim = e4m3_ulp(co) * so + np.abs(cg) * np.abs(sg - so) + 1e-30
     bad = np.abs(vg - vo) > lim * (1 + 1e-6)
     if bad.any():
         i = np.argwhere(bad)[0]

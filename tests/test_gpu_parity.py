@@ -118,6 +118,12 @@ INDEX_CASES = [
     dict(name="h16_d128_k512_2seq", H=16, DI=128, k=512, pos=[[2047, 2048, 2051, 9000, 20000], [4, 5000, 6000]]),
     dict(name="h16_d64_k100", H=16, DI=64, k=100, pos=[[401, 403, 404, 3000, 3003]]),
     dict(name="h13_d128_k2048", H=13, DI=128, k=2048, pos=[[8191, 8192, 12000, 40000]]),
+    # every score equal: the k-th score is shared by all candidates, ties go to the lower ids
+    dict(name="h4_d32_k64_all_ties", H=4, DI=32, k=64, pos=[[1000, 1024]], mode="equal"),
+    # a few huge scores far above the rest: fewer than k keys near the maximum
+    dict(name="h16_d128_k512_outliers", H=16, DI=128, k=512, pos=[[20000, 131072]], mode="outlier"),
+    # more than 32768 candidates: the select reads its keys from global memory
+    dict(name="h16_d128_k512_40k_candidates", H=16, DI=128, k=512, pos=[[160000, 150003]]),
 ]
 
 
@@ -131,7 +137,14 @@ def test_index_topk_parity(csl, orc, case):
     bt = block_table(seed, ns, mb, extra_pages=1)
     hp = O.HostPool(4, 2, DI, 0, THETA, O.BF16, ns * mb + 1, state=False)
     for s in range(ns):
-        scatter_rows(hp.rows, bt, s, 4, randn_bf16(seed, 10 + s, (64 * mb, DI)).view(np.uint8).reshape(64 * mb, -1))
+        keys = randn_bf16(seed, 10 + s, (64 * mb, DI))
+        if case.get("mode") == "equal":
+            keys[:] = keys[0]
+        elif case.get("mode") == "outlier":
+            keys = (keys.astype(np.uint32) - (12 << 7)).astype(np.uint16)       # x 2^-12 (exact in bf16)
+            big = np.arange(7, 64 * mb, 997)                                      # ~1 in 1000 keeps its scale
+            keys[big] = randn_bf16(seed, 30 + s, (len(big), DI))
+        scatter_rows(hp.rows, bt, s, 4, keys.view(np.uint8).reshape(64 * mb, -1))
     q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
     q_pos = np.concatenate(case["pos"]).astype(np.int64)
     nq = len(q_pos)
