@@ -43,6 +43,10 @@ class _Pool(C.Structure):
     ]
 
 
+class _InsertJob(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("x", C.c_void_p), ("logits", C.c_void_p), ("gain", C.c_void_p)]
+
+
 class _Pages(C.Structure):
     _fields_ = [("block_table", C.c_void_p), ("num_seqs", C.c_int32), ("max_blocks", C.c_int32)]
 
@@ -62,6 +66,8 @@ def _sig(name, res, args):
 
 _row_bytes = _sig("csl_row_bytes", _sz, [_i32, _i32])
 _compress_insert = _sig("csl_compress_insert", C.c_int, [_P, _G, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp])
+_compress_insert_multi = _sig("csl_compress_insert_multi", C.c_int,
+                              [_i32, C.POINTER(_InsertJob), _G, _vp, _vp, _i32, _f32, _vp])
 _index_topk_ws = _sig("csl_index_topk_workspace", _sz, [_i32, _i64, _i32])
 _index_topk = _sig("csl_index_topk", C.c_int,
                    [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
@@ -76,7 +82,7 @@ _read_dev_err = _sig("csl_read_device_error", C.c_int, [C.POINTER(C.c_uint32)])
 _timer_enable = _sig("csl_timer_enable", C.c_int, [_i32, _i32])
 _timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)])
 
-EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_index_topk_workspace", "csl_index_topk",
+EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_index_topk_workspace", "csl_index_topk",
            "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill", "csl_last_error",
            "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
 
@@ -138,6 +144,17 @@ def compress_insert(pool: Pool, block_table, start_pos, cu_new, x, logits=None, 
     total = int(x.shape[0])
     _check(_compress_insert(C.byref(ps), C.byref(pg), _ptr(start_pos), _ptr(cu_new), total, _ptr(x), _ptr(logits),
                             _ptr(gain), float(eps), _stream(stream)))
+
+
+def compress_insert_multi(jobs, block_table, start_pos, cu_new, eps=1e-6, stream=None):
+    """jobs: list of (pool, x, logits or None, gain or None) sharing one batch of new tokens."""
+    structs = [p.struct() for p, _, _, _ in jobs]
+    arr = (_InsertJob * len(jobs))(*[_InsertJob(C.addressof(structs[i]), _ptr(x), _ptr(lg), _ptr(g))
+                                     for i, (_, x, lg, g) in enumerate(jobs)])
+    pg = pages(block_table)
+    total = int(jobs[0][1].shape[0])
+    _check(_compress_insert_multi(len(jobs), arr, C.byref(pg), _ptr(start_pos), _ptr(cu_new), total, float(eps),
+                                  _stream(stream)))
 
 
 def index_topk_workspace(num_q: int, max_q_pos: int, k: int) -> int:

@@ -147,6 +147,19 @@ int64_t index_stride(int64_t max_q_pos) {
     return (nv + 2047) / 2048 * 2048;
 }
 
+// First-stage candidates per 2048-id chunk for the two-stage top-k: the
+// expected share of the top k in a chunk plus five standard deviations (a
+// chunk holding more only costs the exact fallback), 0 = single-pass select.
+int index_local_k(int64_t max_q_pos, int k) {
+    const int64_t nv = max_q_pos / 4;
+    if (nv <= k) return 0;
+    const double expect = (double)k * 2048.0 / (double)nv;
+    int kl = (int)std::ceil((expect + 5.0 * std::sqrt(expect) + 4.0) / 16.0) * 16;
+    kl = kl < 64 ? 64 : (kl > 1024 ? 1024 : kl);
+    const int64_t nchunks = index_stride(max_q_pos) / 2048;
+    return nchunks * kl <= 8192 ? kl : 0;
+}
+
 int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
     int64_t keys = (int64_t)(swa_window < max_q_pos ? swa_window : max_q_pos);
     if (comp_ratio > 0) keys += k > 0 ? k : max_q_pos / comp_ratio;
@@ -273,59 +286,76 @@ csl_status csl_timer_read(int32_t kid, double* total_ms, int64_t* launches) {
     return CSL_OK;
 }
 
-csl_status csl_compress_insert(const csl_pool* pool, const csl_pages* pages, const int64_t* start_pos,
-                               const int32_t* cu_new, int32_t total_new, const uint16_t* x, const float* logits,
-                               const float* gain, float eps, csl_stream_t stream) {
+csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs, const csl_pages* pages,
+                                     const int64_t* start_pos, const int32_t* cu_new, int32_t total_new, float eps,
+                                     csl_stream_t stream) {
     csl_status st;
-    if ((st = check_pool(pool, "pool"))) return st;
+    if (n_jobs < 1 || n_jobs > kMaxInsertJobs) return fail(CSL_ERANGE, "n_jobs = %d, supported 1..%d", n_jobs, kMaxInsertJobs);
+    if (!jobs) return fail(CSL_EINVAL, "jobs is NULL");
     if ((st = check_pages(pages))) return st;
     if (total_new < 0) return fail(CSL_EINVAL, "total_new < 0");
     if (!start_pos || !cu_new) return fail(CSL_EINVAL, "start_pos or cu_new is NULL");
-    if (total_new > 0 && !x) return fail(CSL_EINVAL, "x is NULL");
-    if (x && !aligned16(x)) return fail(CSL_EALIGN, "x is not 16-byte aligned");
-    if (pool->ratio == 1) {
-        if (logits || gain) return fail(CSL_EINVAL, "ratio-1 (raw window) inserts take no logits and no gain");
-    } else {
-        if (!pool->state_x || !pool->state_logits) return fail(CSL_EINVAL, "ratio > 1 needs the compressor state");
-        if (total_new > 0 && !logits) return fail(CSL_EINVAL, "logits is NULL");
-        if (!(eps >= 0.f)) return fail(CSL_EINVAL, "eps must be >= 0");
+    if (!(eps >= 0.f)) return fail(CSL_EINVAL, "eps must be >= 0");
+    CompressArgs a;
+    for (int i = 0; i < n_jobs; ++i) {
+        const csl_pool* pool = jobs[i].pool;
+        if ((st = check_pool(pool, "pool"))) return st;
+        if (total_new > 0 && !jobs[i].x) return fail(CSL_EINVAL, "job %d: x is NULL", i);
+        if (jobs[i].x && !aligned16(jobs[i].x)) return fail(CSL_EALIGN, "job %d: x is not 16-byte aligned", i);
+        if (pool->ratio == 1) {
+            if (jobs[i].logits || jobs[i].gain)
+                return fail(CSL_EINVAL, "job %d: ratio-1 (raw window) inserts take no logits and no gain", i);
+        } else {
+            if (!pool->state_x || !pool->state_logits)
+                return fail(CSL_EINVAL, "job %d: ratio > 1 needs the compressor state", i);
+            if (total_new > 0 && !jobs[i].logits) return fail(CSL_EINVAL, "job %d: logits is NULL", i);
+        }
+        CompressJob& J = a.job[i];
+        J.rows = static_cast<uint8_t*>(pool->rows);
+        J.state_x = static_cast<uint16_t*>(pool->state_x);
+        J.state_logits = pool->state_logits;
+        J.x = jobs[i].x;
+        J.logits = jobs[i].logits;
+        J.gain = jobs[i].gain;
+        J.ratio = pool->ratio;
+        J.coff = pool->coff;
+        J.dim = pool->dim;
+        J.rope_dims = pool->rope_dims;
+        J.dtype = pool->dtype;
+        J.num_pages = pool->num_pages;
+        J.row_bytes = (int)row_bytes_of(pool->dim, pool->dtype);
+        a.rf[i] = make_freqs(pool->rope_dims, pool->rope_theta);
     }
     if (total_new == 0) return CSL_OK;
     uint32_t* err = nullptr;
     if ((st = device_error_ptr(&err))) return st;
-    CompressArgs a;
-    a.rows = static_cast<uint8_t*>(pool->rows);
-    a.state_x = static_cast<uint16_t*>(pool->state_x);
-    a.state_logits = pool->state_logits;
     a.bt = pages->block_table;
     a.start_pos = start_pos;
     a.cu_new = cu_new;
-    a.x = x;
-    a.logits = logits;
-    a.gain = gain;
     a.err = err;
-    a.ratio = pool->ratio;
-    a.coff = pool->coff;
-    a.dim = pool->dim;
-    a.rope_dims = pool->rope_dims;
-    a.dtype = pool->dtype;
-    a.num_pages = pool->num_pages;
-    a.row_bytes = (int)row_bytes_of(pool->dim, pool->dtype);
+    a.n_jobs = n_jobs;
     a.num_seqs = pages->num_seqs;
     a.max_blocks = pages->max_blocks;
     a.total_new = total_new;
     a.eps = eps;
-    a.rf = make_freqs(pool->rope_dims, pool->rope_theta);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed(CSL_KERNEL_COMPRESS, s, [&] { return launch_compress(a, s); });
     if (e != hipSuccess) return hip_fail(e, "compress_insert launch");
     return CSL_OK;
 }
 
+csl_status csl_compress_insert(const csl_pool* pool, const csl_pages* pages, const int64_t* start_pos,
+                               const int32_t* cu_new, int32_t total_new, const uint16_t* x, const float* logits,
+                               const float* gain, float eps, csl_stream_t stream) {
+    csl_insert_job job = {pool, x, logits, gain};
+    return csl_compress_insert_multi(1, &job, pages, start_pos, cu_new, total_new, eps, stream);
+}
+
 size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k) {
-    (void)k;
-    if (num_q <= 0 || max_q_pos < 0) return 0;
-    return (size_t)num_q * (size_t)index_stride(max_q_pos) * sizeof(float);
+    if (num_q <= 0 || max_q_pos < 0 || k < 1) return 0;
+    const int64_t stride = index_stride(max_q_pos), nchunks = stride / 2048;
+    const int kl = index_local_k(max_q_pos, k);
+    return (size_t)num_q * ((size_t)stride * sizeof(float) + (size_t)nchunks * (kl + 1) * 8);
 }
 
 csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
@@ -366,6 +396,10 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     a.err = err;
     a.max_q_pos = max_q_pos;
     a.stride = index_stride(max_q_pos);
+    a.nchunks = (int)(a.stride / 2048);
+    a.kl = index_local_k(max_q_pos, k);
+    a.cand = reinterpret_cast<uint2*>(a.scores + (size_t)num_q * a.stride);
+    a.c_next = a.cand + (size_t)num_q * a.nchunks * a.kl;
     a.num_q = num_q;
     a.n_heads = n_heads;
     a.dim = index_pool->dim;

@@ -433,25 +433,49 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
 
     const float* ml = a.part_ml + ((int64_t)n * a.n_splits * a.n_heads + head) * 2;
     const int64_t mstride = (int64_t)a.n_heads * 2;
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, ml[sp * mstride]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float Lsum = 0.f;
     const float* po = a.part_o + ((int64_t)n * a.n_splits * a.n_heads + head) * D + 8 * (active ? lane : 0);
     const int64_t pstride = (int64_t)a.n_heads * D;
-#pragma unroll 4
-    for (int sp = 0; sp < a.n_splits; ++sp) {
-        // an empty split stored m = -inf, l = 0 and zeros: its weight is 0
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(po + sp * pstride);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(po + sp * pstride + 4);
-        const float wsp = exp2f(ml[sp * mstride] - Mu);
-        Lsum += ml[sp * mstride + 1] * wsp;
+    // one pass, batches of 16 splits: all loads of a batch are issued before
+    // any use; the running max M rescales what earlier batches accumulated
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float Lsum = 0.f, M = -INFINITY;
+    constexpr int kB = 16;
+    for (int sp0 = 0; sp0 < a.n_splits; sp0 += kB) {
+        f32x4 v0[kB], v1[kB];
+        float msp[kB], lsp[kB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            o[c] = fmaf(wsp, v0[c], o[c]);
-            o[4 + c] = fmaf(wsp, v1[c], o[4 + c]);
+        for (int u = 0; u < kB; ++u) {
+            msp[u] = -INFINITY;
+            lsp[u] = 0.f;
+            v0[u] = v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sp0 + u < a.n_splits) {
+                const int sp = sp0 + u;
+                msp[u] = ml[sp * mstride];
+                lsp[u] = ml[sp * mstride + 1];
+                v0[u] = *reinterpret_cast<const f32x4*>(po + sp * pstride);
+                v1[u] = *reinterpret_cast<const f32x4*>(po + sp * pstride + 4);
+            }
         }
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) Mb = fmaxf(Mb, msp[u]);
+        const float Mu = Mb == -INFINITY ? 0.f : Mb;
+        const float r = exp2f(M - Mu);  // 0 while nothing was accumulated
+        Lsum *= r;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] *= r;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            // an empty split stored m = -inf, l = 0 and zeros: its weight is 0
+            const float wsp = exp2f(msp[u] - Mu);
+            Lsum = fmaf(lsp[u], wsp, Lsum);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o[c] = fmaf(wsp, v0[u][c], o[c]);
+                o[4 + c] = fmaf(wsp, v1[u][c], o[4 + c]);
+            }
+        }
+        M = Mb;
     }
     const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     const int rbase = D - a.rope_dims;

@@ -3,11 +3,14 @@
 // windows from [Notes] 数学附录精要: C4A / C128A 的精确位置范围), plus the
 // raw-window insert (ratio 1: RoPE at the token, no norm; [Notes] 融合 3).
 //
-// Work mapping.  One 256-thread workgroup per new token for ratio > 1: wave 0
-// appends the token to the compressor state; if the token closes an entry,
-// the four waves split the window's tokens, the weighted partial sums meet in
-// LDS and wave 0 normalises, rotates and stores the row.  For ratio 1 each
-// wave handles one token.  A lane owns 8 consecutive dims (one 16-byte
+// Work mapping.  Several pools of a layer (raw window, c4a main, c4a index,
+// c128a main) are filled by one launch: grid.y picks the pool (job), grid.x
+// the new token -- the horizontal fusion of independent per-pool work.  One
+// 256-thread workgroup per (token, pool).  For ratio > 1, wave 0 appends the
+// token to the compressor state; if the token closes an entry, the four waves
+// split the window's tokens, the weighted partial sums meet in LDS and wave 0
+// normalises, rotates and stores the row.  For ratio 1, wave 0 rotates and
+// stores the token's row.  A lane owns 8 consecutive dims (one 16-byte
 // load/store per row), so a wave covers a row of up to 512 dims and RoPE pairs
 // never straddle lanes.  Elementwise and HBM-bound: no MFMA.
 #include "csl_kernels.hpp"
@@ -85,7 +88,9 @@ __device__ __forceinline__ void store8(uint8_t* row, int dtype, int dim, int lan
     }
 }
 
-__global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs a) {
+__global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs args) {
+    const CompressJob& a = args.job[blockIdx.y];
+    const RopeFreqs& rf = args.rf[blockIdx.y];
     __shared__ float s_w[kThreads];
     __shared__ const uint16_t* s_ptr[kThreads];
     __shared__ float s_red[4][512];
@@ -96,35 +101,35 @@ __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs 
     const bool active = lane * 8 < D;
 
     if (a.ratio == 1) {
-        int j = blockIdx.x * 4 + wave;
-        if (j >= a.total_new) return;
-        int s = find_seq(a.cu_new, a.num_seqs, j);
-        int64_t t = a.start_pos[s] + (j - a.cu_new[s]);
-        int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, t);
+        const int j = blockIdx.x;
+        if (wave != 0) return;
+        int s = find_seq(args.cu_new, args.num_seqs, j);
+        int64_t t = args.start_pos[s] + (j - args.cu_new[s]);
+        int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, t);
         if (pg < 0) {
-            if (lane == 0) raise_error(a.err, (t < 0 || (t >> 8) >= a.max_blocks) ? kErrPos : kErrPage);
+            if (lane == 0) raise_error(args.err, (t < 0 || (t >> 8) >= args.max_blocks) ? kErrPos : kErrPage);
             return;
         }
         float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (active) load8(a.x + (int64_t)j * D + 8 * lane, v);
-        rope8(v, 8 * lane, D, a.rope_dims, a.rf, t);
+        rope8(v, 8 * lane, D, a.rope_dims, rf, t);
         uint8_t* row = a.rows + ((int64_t)pg * kBlockPositions + (t & 255)) * a.row_bytes;
         store8(row, a.dtype, D, lane, active, v);
         return;
     }
 
     const int j = blockIdx.x;
-    const int s = find_seq(a.cu_new, a.num_seqs, j);
-    const int64_t start = a.start_pos[s];
-    const int cbase = a.cu_new[s];
+    const int s = find_seq(args.cu_new, args.num_seqs, j);
+    const int64_t start = args.start_pos[s];
+    const int cbase = args.cu_new[s];
     const int64_t t = start + (j - cbase);
     const int r = a.ratio, W = a.coff * a.ratio;
 
     // 1. append the token to the compressor state
     if (wave == 0) {
-        int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, t);
+        int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, t);
         if (pg < 0) {
-            if (lane == 0) raise_error(a.err, (t < 0 || (t >> 8) >= a.max_blocks) ? kErrPos : kErrPage);
+            if (lane == 0) raise_error(args.err, (t < 0 || (t >> 8) >= args.max_blocks) ? kErrPos : kErrPage);
         } else {
             int64_t tok = (int64_t)pg * kBlockPositions + (t & 255);
             if (active)
@@ -147,9 +152,9 @@ __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs 
             lg = a.logits[jj * a.coff + col];
             ptr = a.x + jj * D;
         } else if (tk >= 0) {
-            int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, tk);
+            int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, tk);
             if (pg < 0) {
-                raise_error(a.err, kErrPage);
+                raise_error(args.err, kErrPage);
             } else {
                 int64_t tok = (int64_t)pg * kBlockPositions + (tk & 255);
                 lg = a.state_logits[tok * a.coff + col];
@@ -200,16 +205,16 @@ __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs 
         ss = fmaf(u[c], u[c], ss);
     }
     ss = wave_sum(ss);
-    float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+    float inv = 1.0f / sqrtf(ss / (float)D + args.eps);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         float g = (a.gain && active) ? a.gain[8 * lane + c] : 1.0f;
         u[c] = u[c] * inv * g;
     }
-    rope8(u, 8 * lane, D, a.rope_dims, a.rf, (int64_t)r * i);
-    int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, (int64_t)r * i);
+    rope8(u, 8 * lane, D, a.rope_dims, rf, (int64_t)r * i);
+    int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, (int64_t)r * i);
     if (pg < 0) {
-        if (lane == 0) raise_error(a.err, kErrPage);
+        if (lane == 0) raise_error(args.err, kErrPage);
         return;
     }
     const int per_page = kBlockPositions / r;
@@ -220,9 +225,9 @@ __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs 
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
-    if (a.total_new <= 0) return hipSuccess;
-    int blocks = a.ratio == 1 ? (a.total_new + 3) / 4 : a.total_new;
-    hipLaunchKernelGGL(compress_insert_kernel, dim3(blocks), dim3(kThreads), 0, st, a);
+    if (a.total_new <= 0 || a.n_jobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(compress_insert_kernel, dim3((unsigned)a.total_new, (unsigned)a.n_jobs), dim3(kThreads), 0, st,
+                       a);
     return hipGetLastError();
 }
 

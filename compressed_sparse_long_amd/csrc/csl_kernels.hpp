@@ -8,20 +8,27 @@
 
 namespace csl {
 
-struct CompressArgs {
+struct CompressJob {
     uint8_t* rows;
     uint16_t* state_x;
     float* state_logits;
-    const int32_t* bt;
-    const int64_t* start_pos;
-    const int32_t* cu_new;
     const uint16_t* x;
     const float* logits;
     const float* gain;
+    int ratio, coff, dim, rope_dims, dtype, num_pages, row_bytes;
+};
+
+constexpr int kMaxInsertJobs = 4;
+
+struct CompressArgs {
+    CompressJob job[kMaxInsertJobs];
+    RopeFreqs rf[kMaxInsertJobs];
+    const int32_t* bt;
+    const int64_t* start_pos;
+    const int32_t* cu_new;
     uint32_t* err;
-    int ratio, coff, dim, rope_dims, dtype, num_pages, row_bytes, num_seqs, max_blocks, total_new;
+    int n_jobs, num_seqs, max_blocks, total_new;
     float eps;
-    RopeFreqs rf;
 };
 
 struct IndexArgs {
@@ -34,10 +41,14 @@ struct IndexArgs {
     float* scores;          // [num_q][stride]
     int32_t* topk;          // [num_q][k]
     float* kth;             // [num_q] or null
+    uint2* cand;            // [num_q][nchunks][kl] (key, id) first-stage candidates
+    uint2* c_next;          // [num_q][nchunks] (key, id) of each chunk's (kl+1)-th element
     uint32_t* err;
     int64_t max_q_pos;
-    int64_t stride;  // entries per query row of `scores` (multiple of 256)
+    int64_t stride;  // entries per query row of `scores` (multiple of 2048)
     int num_q, n_heads, dim, k, num_pages, num_seqs, max_blocks;
+    int nchunks;     // stride / 2048
+    int kl;          // first-stage candidates per chunk (0: single-pass select)
 };
 
 struct AttnArgs {

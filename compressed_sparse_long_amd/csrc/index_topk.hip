@@ -112,11 +112,12 @@ __device__ __forceinline__ float key_score(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
-// Exclusive scan of one uint32 per thread over the workgroup; also returns the total.
+// Exclusive scan of one uint32 per thread over an NT-thread workgroup; also returns the total.
+template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
 #pragma unroll
@@ -128,7 +129,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& tota
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         uint32_t c = s_wave[w];
         before += w < wave ? c : 0u;
         tot += c;
@@ -138,22 +139,49 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& tota
     return before + x - v;
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+// Scan of a 2048-bin histogram from the top: the bin holding the `want`-th
+// largest key and the rank of that key inside the bin.  Every thread calls it;
+// the result lands in s_sel[0] (bin), s_sel[1] (rank), s_sel[2] (bin count),
+// and the histogram total is returned.
+template <int NT>
+__device__ uint32_t find_bin(const uint32_t* s_hist, uint32_t want, int nbins, uint32_t* s_wave, uint32_t* s_sel) {
+    constexpr int PER = 2048 / NT;  // bins per thread (2 for 1024 threads, 8 for 256)
+    const int tid = threadIdx.x;
+    const int top = nbins - 1 - PER * tid;  // this thread's bins top, top-1, ..., from the top
+    uint32_t c[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        c[i] = top - i >= 0 ? s_hist[top - i] : 0u;
+        sum += c[i];
+    }
+    uint32_t tot;
+    uint32_t above = block_excl_scan<NT>(sum, s_wave, tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (top - i >= 0 && above < want && want <= above + c[i]) {
+            s_sel[0] = top - i;
+            s_sel[1] = want - above;
+            s_sel[2] = c[i];
+        }
+        above += c[i];
+    }
+    __syncthreads();
+    return tot;
+}
 
-// Keys of a query's scores: in LDS, or read from global memory.
-struct LdsKeys {
-    const uint32_t* k;
-    __device__ __forceinline__ uint32_t operator()(int64_t e) const { return k[e]; }
-};
+// Keys of a query's scores read from global memory.
 struct GlobalKeys {
     const float* sc;
     __device__ __forceinline__ uint32_t operator()(int64_t e) const { return score_key(sc[e]); }
 };
+struct LdsKeys {
+    const uint32_t* k;
+    __device__ __forceinline__ uint32_t operator()(int64_t e) const { return k[e]; }
+};
 
-// Exact radix select (11/11/10-bit rounds) of the `want`-th largest key among
-// keys [0, n) of `key_at`; returns the key, and in *rem how many copies of it
-// are taken.  LDS histograms; every thread of the workgroup must call it.
-template <typename Keys>
+// Exact radix select (11/11/10-bit rounds) of the `want`-th largest among keys
+// [0, n) of `key_at`; *rem = copies of it that are taken.
+template <int NT, typename Keys>
 __device__ uint32_t radix_select(const Keys& key_at, int64_t n, uint32_t want, uint32_t* rem_out, uint32_t* s_hist,
                                  uint32_t* s_wave, uint32_t* s_sel) {
     const int tid = threadIdx.x;
@@ -162,30 +190,15 @@ __device__ uint32_t radix_select(const Keys& key_at, int64_t n, uint32_t want, u
     const int widths[3] = {11, 11, 10};
     for (int r = 0; r < 3; ++r) {
         const int sh = shifts[r], nb = 1 << widths[r];
-        for (int b = tid; b < 2048; b += kSelThreads) s_hist[b] = 0;
+        for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
         __syncthreads();
-        for (int64_t e = tid; e < n; e += kSelThreads) {
+        for (int64_t e = tid; e < n; e += NT) {
             uint32_t key = key_at(e);
             if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1u);
         }
         __syncthreads();
-        // thread t owns the two bins nb-1-2t and nb-2-2t (counted from the top)
-        const int hi = nb - 1 - 2 * tid;
-        uint32_t c_hi = hi >= 0 ? s_hist[hi] : 0u;
-        uint32_t c_lo = hi - 1 >= 0 ? s_hist[hi - 1] : 0u;
-        uint32_t tot;
-        uint32_t above = block_excl_scan(c_hi + c_lo, s_wave, tot);
-        if (hi >= 0) {
-            if (above < rem && rem <= above + c_hi) {
-                s_sel[0] = prefix | ((uint32_t)hi << sh);
-                s_sel[1] = rem - above;
-            } else if (hi - 1 >= 0 && above + c_hi < rem && rem <= above + c_hi + c_lo) {
-                s_sel[0] = prefix | ((uint32_t)(hi - 1) << sh);
-                s_sel[1] = rem - above - c_hi;
-            }
-        }
-        __syncthreads();
-        prefix = s_sel[0];
+        find_bin<NT>(s_hist, rem, nb, s_wave, s_sel);
+        prefix |= s_sel[0] << sh;
         rem = s_sel[1];
         pmask |= (uint32_t)(nb - 1) << sh;
         __syncthreads();
@@ -194,57 +207,9 @@ __device__ uint32_t radix_select(const Keys& key_at, int64_t n, uint32_t want, u
     return prefix;
 }
 
-// Emit the ids of keys > T, plus the first `rem` ids (by id) of keys == T, in
-// ascending id order.  Wave w owns ids [w*seg, (w+1)*seg).
-template <typename Keys>
-__device__ void emit_ordered(const Keys& key_at, int64_t nv, uint32_t T, uint32_t rem, int k, int32_t* out,
-                             uint32_t (*s_cnt)[kSelWaves]) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t seg = ((nv + kSelWaves - 1) / kSelWaves + 63) & ~(int64_t)63;
-    const int64_t lo = (int64_t)wave * seg;
-    const int64_t hi = lo + seg < nv ? lo + seg : nv;
-    uint32_t n_gt = 0, n_eq = 0;
-    for (int64_t e = lo + lane; e - lane < hi; e += 64) {
-        bool in = e < hi;
-        uint32_t key = in ? key_at(e) : 0u;
-        n_gt += __popcll(__ballot(in && key > T));
-        n_eq += __popcll(__ballot(in && key == T));
-    }
-    if (lane == 0) {
-        s_cnt[0][wave] = n_gt;
-        s_cnt[1][wave] = n_eq;
-    }
-    __syncthreads();
-    uint32_t out_pos = 0, eq_seen = 0;
-    for (int w = 0; w < wave; ++w) {
-        uint32_t eq_w = s_cnt[1][w];
-        uint32_t take_eq = eq_seen >= rem ? 0u : (eq_w < rem - eq_seen ? eq_w : rem - eq_seen);
-        out_pos += s_cnt[0][w] + take_eq;
-        eq_seen += eq_w;
-    }
-    for (int64_t e = lo + lane; e - lane < hi; e += 64) {
-        bool in = e < hi;
-        uint32_t key = in ? key_at(e) : 0u;
-        bool gt = in && key > T, eq = in && key == T;
-        uint64_t eqm = __ballot(eq);
-        uint32_t eq_rank = eq_seen + __popcll(eqm & lanemask_lt(lane));
-        bool sel = gt || (eq && eq_rank < rem);
-        uint64_t selm = __ballot(sel);
-        const uint32_t dst = out_pos + __popcll(selm & lanemask_lt(lane));
-        if (sel && dst < (uint32_t)k) out[dst] = (int32_t)e;
-        out_pos += __popcll(selm);
-        eq_seen += __popcll(eqm);
-    }
-}
-
-constexpr int kRegKeys = 32;                     // keys per thread held in registers
-constexpr int kRegMax = kRegKeys * kSelThreads;  // 32768 candidates
-constexpr int kCandCap = 4096;                   // boundary-bin candidates kept in LDS
-constexpr int kRankCap = kSelThreads;            // candidates ranked directly
-
-// Exact radix select (11/11/10-bit rounds) over register-resident keys: the
-// `want`-th largest of the valid keys; *rem = copies of it that are taken.
-__device__ uint32_t radix_select_regs(const uint32_t (&key)[32], int nmine, uint32_t want, uint32_t* rem_out,
+// The same over register-resident keys (slot i of a thread valid iff bit i of vmask).
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t radix_select_regs(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
                                       uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0, pmask = 0, rem = want;
@@ -252,28 +217,14 @@ __device__ uint32_t radix_select_regs(const uint32_t (&key)[32], int nmine, uint
     const int widths[3] = {11, 11, 10};
     for (int r = 0; r < 3; ++r) {
         const int sh = shifts[r], nb = 1 << widths[r];
-        for (int b = tid; b < 2048; b += kSelThreads) s_hist[b] = 0;
+        for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-            if (i < nmine && (key[i] & pmask) == prefix) atomicAdd(&s_hist[(key[i] >> sh) & (nb - 1)], 1u);
+        for (int i = 0; i < KPT; ++i)
+            if (((vmask >> i) & 1u) && (key[i] & pmask) == prefix) atomicAdd(&s_hist[(key[i] >> sh) & (nb - 1)], 1u);
         __syncthreads();
-        const int hi = nb - 1 - 2 * tid;
-        uint32_t c_hi = hi >= 0 ? s_hist[hi] : 0u;
-        uint32_t c_lo = hi - 1 >= 0 ? s_hist[hi - 1] : 0u;
-        uint32_t tot;
-        uint32_t above = block_excl_scan(c_hi + c_lo, s_wave, tot);
-        if (hi >= 0) {
-            if (above < rem && rem <= above + c_hi) {
-                s_sel[0] = prefix | ((uint32_t)hi << sh);
-                s_sel[1] = rem - above;
-            } else if (hi - 1 >= 0 && above + c_hi < rem && rem <= above + c_hi + c_lo) {
-                s_sel[0] = prefix | ((uint32_t)(hi - 1) << sh);
-                s_sel[1] = rem - above - c_hi;
-            }
-        }
-        __syncthreads();
-        prefix = s_sel[0];
+        find_bin<NT>(s_hist, rem, nb, s_wave, s_sel);
+        prefix |= s_sel[0] << sh;
         rem = s_sel[1];
         pmask |= (uint32_t)(nb - 1) << sh;
         __syncthreads();
@@ -282,85 +233,54 @@ __device__ uint32_t radix_select_regs(const uint32_t (&key)[32], int nmine, uint
     return prefix;
 }
 
-// Register-resident select for nv <= 32768.  Thread t holds the 32 keys of ids
-// [32t, 32t+32), so ids stay ordered by thread and every compaction is one
-// block-wide exclusive scan of per-thread counts:
-//  1. a 2048-bin histogram of the keys inside a window of 2^24 key units
-//     below the largest key (two octaves of fp32 score below the maximum;
-//     keys under the window are not counted), scanned from the top: the bin b
-//     that holds the k-th key and `want` = its rank inside b.  Bins of 2^13
-//     key units keep b small.  If fewer than k keys fall in the window, an
-//     exact 3-round radix select over all keys is used instead;
-//  2. b's keys are compacted to LDS and the k-th key T is the candidate with
-//     #(> T) < want <= #(>= T);
-//  3. ids with key > T, then the first `rem` ids with key == T, are written in
-//     ascending order through one scan of packed (count_gt, count_eq).
-__device__ void select_registers(const float* sc, int64_t nv, int k, int32_t* out, float* kth, uint32_t* s_hist,
-                                 uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t e0 = (int64_t)tid * kRegKeys;
-    uint32_t key[kRegKeys];
-    if (e0 + kRegKeys <= nv) {
-        const float4* p4 = reinterpret_cast<const float4*>(sc + e0);
-#pragma unroll
-        for (int i = 0; i < kRegKeys / 4; ++i) {
-            const float4 v = p4[i];
-            key[4 * i] = score_key(v.x);
-            key[4 * i + 1] = score_key(v.y);
-            key[4 * i + 2] = score_key(v.z);
-            key[4 * i + 3] = score_key(v.w);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kRegKeys; ++i) key[i] = e0 + i < nv ? score_key(sc[e0 + i]) : 0u;
-    }
-    const int nmine = (int)(nv - e0 < 0 ? 0 : (nv - e0 < kRegKeys ? nv - e0 : kRegKeys));
+constexpr int kCandCap = 4096;  // boundary-bin keys kept in LDS
 
-    // the largest key, and the histogram zeroed under the same barrier
+// Exact selection over register-resident keys (slot i valid iff bit i of vmask;
+// at least `want` valid keys in the workgroup): returns the `want`-th largest
+// key T and *rem, the number of its copies inside the top `want`.
+//  1. a 2048-bin histogram of the keys inside a window of 2^24 key units below
+//     the largest key (two octaves of fp32 score below the maximum; keys under
+//     the window are not counted, so crowded low bins cost nothing), scanned
+//     from the top: the bin b that holds the want-th key and its rank in b;
+//  2. b's keys (a few: bins are 2^13 key units wide) are compacted to LDS and T
+//     is the one with #(> T) < rank <= #(>= T).
+// If fewer than `want` keys fall in the window, or b is crowded, an exact
+// 3-round radix select over all keys is used instead.
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
+                                 uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t kmax = 0u;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) kmax = i < nmine ? max(kmax, key[i]) : kmax;
+    for (int i = 0; i < KPT; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
     if (lane == 0) s_sel[8 + wave] = kmax;
-    for (int b = tid; b < 2048; b += kSelThreads) s_hist[b] = 0;
+    for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) kmax = max(kmax, s_sel[8 + w]);
+    for (int w = 0; w < NW; ++w) kmax = max(kmax, s_sel[8 + w]);
     constexpr uint32_t kWin = (1u << 24) - 1u;
     const uint32_t lo = kmax > kWin ? kmax - kWin : 0u;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i)
-        if (i < nmine && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
+    for (int i = 0; i < KPT; ++i)
+        if (((vmask >> i) & 1u) && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
     __syncthreads();
-    const int hb = 2047 - 2 * tid;  // this thread's two bins, from the top
-    const uint32_t c_hi = s_hist[hb], c_lo = s_hist[hb - 1];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan(c_hi + c_lo, s_wave, tot);
-    if (above < (uint32_t)k && (uint32_t)k <= above + c_hi) {
-        s_sel[0] = hb;
-        s_sel[1] = k - above;
-        s_sel[2] = c_hi;
-    } else if (above + c_hi < (uint32_t)k && (uint32_t)k <= above + c_hi + c_lo) {
-        s_sel[0] = hb - 1;
-        s_sel[1] = k - above - c_hi;
-        s_sel[2] = c_lo;
-    }
-    __syncthreads();
-
-    uint32_t T, rem;
-    if (tot >= (uint32_t)k && s_sel[2] <= (uint32_t)kCandCap) {
-        const uint32_t bsel = s_sel[0], want = s_sel[1], cnt = s_sel[2];
-        auto in_bin = [&](uint32_t kk) { return kk >= lo && ((kk - lo) >> 13) == bsel; };
+    const uint32_t tot = find_bin<NT>(s_hist, want, 2048, s_wave, s_sel);
+    if (tot >= want && s_sel[2] <= (uint32_t)kCandCap) {
+        const uint32_t bsel = s_sel[0], rank = s_sel[1], cnt = s_sel[2];
         uint32_t mine = 0;
 #pragma unroll
-        for (int i = 0; i < kRegKeys; ++i) mine += (i < nmine && in_bin(key[i])) ? 1u : 0u;
-        uint32_t off = block_excl_scan(mine, s_wave, tot);
+        for (int i = 0; i < KPT; ++i)
+            mine += (((vmask >> i) & 1u) && key[i] >= lo && ((key[i] - lo) >> 13) == bsel) ? 1u : 0u;
+        uint32_t t2;
+        uint32_t off = block_excl_scan<NT>(mine, s_wave, t2);
 #pragma unroll
-        for (int i = 0; i < kRegKeys; ++i)
-            if (i < nmine && in_bin(key[i])) s_cand[off++] = key[i];
+        for (int i = 0; i < KPT; ++i)
+            if (((vmask >> i) & 1u) && key[i] >= lo && ((key[i] - lo) >> 13) == bsel) s_cand[off++] = key[i];
         __syncthreads();
-        if (cnt <= (uint32_t)kRankCap) {
+        if (cnt <= (uint32_t)NT) {
             if ((uint32_t)tid < cnt) {
                 const uint32_t kc = s_cand[tid];
                 uint32_t gt = 0, ge = 0;
@@ -369,90 +289,324 @@ __device__ void select_registers(const float* sc, int64_t nv, int k, int32_t* ou
                     gt += kj > kc ? 1u : 0u;
                     ge += kj >= kc ? 1u : 0u;
                 }
-                if (gt < want && want <= ge) {  // every copy of T writes the same values
+                if (gt < rank && rank <= ge) {  // every copy of T writes the same values
                     s_sel[4] = kc;
-                    s_sel[5] = want - gt;
+                    s_sel[5] = rank - gt;
                 }
             }
             __syncthreads();
-            T = s_sel[4];
-            rem = s_sel[5];
-        } else {
-            T = radix_select(LdsKeys{s_cand}, (int64_t)cnt, want, &rem, s_hist, s_wave, s_sel + 4);
+            *rem_out = s_sel[5];
+            const uint32_t T = s_sel[4];
+            __syncthreads();
+            return T;
         }
-    } else {
-        T = radix_select_regs(key, nmine, (uint32_t)k, &rem, s_hist, s_wave, s_sel + 4);
+        return radix_select<NT>(LdsKeys{s_cand}, (int64_t)cnt, rank, rem_out, s_hist, s_wave, s_sel + 4);
     }
+    return radix_select_regs<NT, KPT>(key, vmask, want, rem_out, s_hist, s_wave, s_sel + 4);
+}
 
-    // 3. ordered emission: one scan of packed (count_gt | count_eq << 16)
+// Emit, in slot order (ids ascending by thread, then slot), the ids of keys > T
+// and of the first `rem` keys == T.  `ids(i)` gives slot i's id.  Writes
+// positions < k only.  Returns (through s_sel[6]) the id of the last taken copy
+// of T (the k-th element).
+template <int NT, int KPT, typename Ids>
+__device__ __forceinline__ void emit_selected(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t T, uint32_t rem, int k,
+                              const Ids& ids, int32_t* out, uint32_t* s_wave, uint32_t* s_sel, bool write) {
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
-        ngt += (i < nmine && key[i] > T) ? 1u : 0u;
-        neq += (i < nmine && key[i] == T) ? 1u : 0u;
+    for (int i = 0; i < KPT; ++i) {
+        const bool v = (vmask >> i) & 1u;
+        ngt += (v && key[i] > T) ? 1u : 0u;
+        neq += (v && key[i] == T) ? 1u : 0u;
     }
-    const uint32_t pre = block_excl_scan(ngt | (neq << 16), s_wave, tot);
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<NT>(ngt | (neq << 16), s_wave, tot);
     uint32_t eq_before = pre >> 16;
     uint32_t pos = (pre & 0xffffu) + (eq_before < rem ? eq_before : rem);
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
-        if (i >= nmine) break;
+    for (int i = 0; i < KPT; ++i) {
+        if (!((vmask >> i) & 1u)) continue;
         bool sel = key[i] > T;
         if (key[i] == T) {
             sel = eq_before < rem;
+            if (eq_before + 1 == rem) s_sel[6] = (uint32_t)ids(i);
             ++eq_before;
         }
         if (sel) {
-            if (pos < (uint32_t)k) out[pos] = (int32_t)(e0 + i);
+            if (write && pos < (uint32_t)k) out[pos] = ids(i);
             ++pos;
         }
     }
+}
+
+// ---------------------------------------------------------------- single-pass select
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kRegKeys = 32;                     // keys per thread held in registers
+constexpr int kRegMax = kRegKeys * kSelThreads;  // 32768 candidates
+
+// Full select for one query by one 1024-thread workgroup: thread t holds the
+// scores of ids [32t, 32t+32) in registers (nv <= 32768), else the keys are
+// read from global memory in radix rounds.  Used when the two-stage select
+// does not apply or its check fails.
+__device__ __forceinline__ void select_full(const float* sc, int64_t nv, int k, int32_t* out, float* kth, uint32_t* s_hist,
+                            uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
+    const int tid = threadIdx.x;
+    if (nv <= kRegMax) {
+        const int64_t e0 = (int64_t)tid * kRegKeys;
+        uint32_t key[kRegKeys];
+        if (e0 + kRegKeys <= nv) {
+            const float4* p4 = reinterpret_cast<const float4*>(sc + e0);
+#pragma unroll
+            for (int i = 0; i < kRegKeys / 4; ++i) {
+                const float4 v = p4[i];
+                key[4 * i] = score_key(v.x);
+                key[4 * i + 1] = score_key(v.y);
+                key[4 * i + 2] = score_key(v.z);
+                key[4 * i + 3] = score_key(v.w);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRegKeys; ++i) key[i] = e0 + i < nv ? score_key(sc[e0 + i]) : 0u;
+        }
+        const int64_t nm = nv - e0 < 0 ? 0 : (nv - e0 < kRegKeys ? nv - e0 : kRegKeys);
+        const uint32_t vmask = nm >= 32 ? 0xffffffffu : ((1u << nm) - 1u);
+        uint32_t rem;
+        const uint32_t T = block_select<kSelThreads, kRegKeys>(key, vmask, (uint32_t)k, &rem, s_hist, s_wave, s_sel,
+                                                               s_cand);
+        emit_selected<kSelThreads, kRegKeys>(key, vmask, T, rem, k, [&](int i) { return (int32_t)(e0 + i); }, out,
+                                             s_wave, s_sel, true);
+        if (tid == 0 && kth) *kth = key_score(T);
+        return;
+    }
+    // long lists: radix rounds and an ordered emission over global memory;
+    // wave w owns ids [w*seg, (w+1)*seg)
+    uint32_t rem;
+    const uint32_t T = radix_select<kSelThreads>(GlobalKeys{sc}, nv, (uint32_t)k, &rem, s_hist, s_wave, s_sel);
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t seg = ((nv + kSelWaves - 1) / kSelWaves + 63) & ~(int64_t)63;
+    const int64_t lo = (int64_t)wave * seg;
+    const int64_t hi = lo + seg < nv ? lo + seg : nv;
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int64_t e = lo + lane; e - lane < hi; e += 64) {
+        const bool in = e < hi;
+        const uint32_t key = in ? score_key(sc[e]) : 0u;
+        n_gt += __popcll(__ballot(in && key > T));
+        n_eq += __popcll(__ballot(in && key == T));
+    }
+    uint32_t* s_cnt = s_cand;  // [2][kSelWaves]
+    if (lane == 0) {
+        s_cnt[wave] = n_gt;
+        s_cnt[kSelWaves + wave] = n_eq;
+    }
+    __syncthreads();
+    uint32_t out_pos = 0, eq_seen = 0;
+    for (int w = 0; w < wave; ++w) {
+        const uint32_t eq_w = s_cnt[kSelWaves + w];
+        const uint32_t take_eq = eq_seen >= rem ? 0u : (eq_w < rem - eq_seen ? eq_w : rem - eq_seen);
+        out_pos += s_cnt[w] + take_eq;
+        eq_seen += eq_w;
+    }
+    for (int64_t e = lo + lane; e - lane < hi; e += 64) {
+        const bool in = e < hi;
+        const uint32_t key = in ? score_key(sc[e]) : 0u;
+        const bool gt = in && key > T, eq = in && key == T;
+        const uint64_t eqm = __ballot(eq);
+        const uint32_t eq_rank = eq_seen + __popcll(eqm & lanemask_lt(lane));
+        const bool sel = gt || (eq && eq_rank < rem);
+        const uint64_t selm = __ballot(sel);
+        const uint32_t dst = out_pos + __popcll(selm & lanemask_lt(lane));
+        if (sel && dst < (uint32_t)k) out[dst] = (int32_t)e;
+        out_pos += __popcll(selm);
+        eq_seen += __popcll(eqm);
+    }
     if (tid == 0 && kth) *kth = key_score(T);
+}
+
+// Fewer visible entries than k: all of them, then -1; kth = the smallest score.
+__device__ void select_all(const float* sc, int64_t nv, int k, int32_t* out, float* kth, float* s_min) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = blockDim.x / 64;
+    for (int j = tid; j < k; j += blockDim.x) out[j] = j < nv ? j : -1;
+    if (!kth) return;
+    float m = INFINITY;
+    for (int64_t e = tid; e < nv; e += blockDim.x) m = fminf(m, sc[e]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fminf(m, __shfl_xor(m, o));
+    if (lane == 0) s_min[wave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        float r = INFINITY;
+        for (int w = 0; w < nw; ++w) r = fminf(r, s_min[w]);
+        *kth = nv > 0 ? r : -INFINITY;
+    }
 }
 
 __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
     __shared__ uint32_t s_hist[2048];
     __shared__ uint32_t s_cand[kCandCap];
     __shared__ uint32_t s_wave[kSelWaves];
-    __shared__ uint32_t s_cnt[2][kSelWaves];
     __shared__ uint32_t s_sel[8 + kSelWaves];
     __shared__ float s_min[kSelWaves];
-
     const int n = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int s;
     int64_t p;
     const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;  // the score kernel reports bad queries
     const float* sc = a.scores + (int64_t)n * a.stride;
     int32_t* out = a.topk + (int64_t)n * a.k;
-    const int k = a.k;
     float* kth = a.kth ? a.kth + n : nullptr;
+    if (nv <= a.k) select_all(sc, nv, a.k, out, kth, s_min);
+    else select_full(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+}
 
-    if (nv <= k) {
-        for (int j = tid; j < k; j += kSelThreads) out[j] = j < nv ? j : -1;
-        if (kth) {
-            float m = INFINITY;
-            for (int64_t e = tid; e < nv; e += kSelThreads) m = fminf(m, sc[e]);
+// ---------------------------------------------------------------- two-stage select
+
+constexpr int kChunk = 2048;        // ids per first-stage workgroup
+constexpr int kLocalThreads = 256;  // 8 ids per thread
+constexpr int kMergeSlots = 8;      // candidates per thread in the second stage (8192 per query)
+
+// Stage 1: one 256-thread workgroup per (query, chunk of 2048 ids): the chunk's
+// first `kl` ids in (score desc, id asc) order -- its local top-kl, written in
+// ascending id order -- and the (kl+1)-th, whose position the merge checks.
+__global__ void __launch_bounds__(kLocalThreads) topk_local_kernel(IndexArgs a) {
+    __shared__ uint32_t s_hist[2048];
+    __shared__ uint32_t s_cand[kCandCap];
+    __shared__ uint32_t s_wave[kLocalThreads / 64];
+    __shared__ uint32_t s_sel[8 + kLocalThreads / 64];
+    const int n = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+    int s;
+    int64_t p;
+    const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
+    const int64_t base = (int64_t)blk * kChunk;
+    if (base >= nv || nv <= a.k) return;  // the merge reads chunks below nv only
+    const float* sc = a.scores + (int64_t)n * a.stride + base;
+    const int64_t nvalid = nv - base < kChunk ? nv - base : kChunk;
+    const int kl = a.kl;
+    uint2* cand = a.cand + ((int64_t)n * a.nchunks + blk) * kl;
+    const int64_t e0 = (int64_t)tid * 8;
+    uint32_t key[8];
+    uint32_t vmask = 0;
+    if (e0 + 8 <= nvalid) {
+        const float4 v0 = reinterpret_cast<const float4*>(sc + e0)[0];
+        const float4 v1 = reinterpret_cast<const float4*>(sc + e0)[1];
+        key[0] = score_key(v0.x); key[1] = score_key(v0.y); key[2] = score_key(v0.z); key[3] = score_key(v0.w);
+        key[4] = score_key(v1.x); key[5] = score_key(v1.y); key[6] = score_key(v1.z); key[7] = score_key(v1.w);
+        vmask = 0xffu;
+    } else {
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) m = fminf(m, __shfl_xor(m, o));
-            if (lane == 0) s_min[wave] = m;
-            __syncthreads();
-            if (tid == 0) {
-                float r = INFINITY;
-                for (int w = 0; w < kSelWaves; ++w) r = fminf(r, s_min[w]);
-                *kth = nv > 0 ? r : -INFINITY;
-            }
+        for (int i = 0; i < 8; ++i) {
+            key[i] = e0 + i < nvalid ? score_key(sc[e0 + i]) : 0u;
+            vmask |= (e0 + i < nvalid ? 1u : 0u) << i;
         }
+    }
+    if (nvalid <= kl) {
+        // every id is a candidate; no (kl+1)-th element
+        uint32_t tot;
+        uint32_t pos = block_excl_scan<kLocalThreads>((uint32_t)__popc(vmask), s_wave, tot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((vmask >> i) & 1u) cand[pos++] = make_uint2(key[i], (uint32_t)(base + e0 + i));
+        for (int j = (int)tot + tid; j < kl; j += kLocalThreads) cand[j] = make_uint2(0u, 0xffffffffu);
+        if (tid == 0) a.c_next[(int64_t)n * a.nchunks + blk] = make_uint2(0u, 0xffffffffu);
         return;
     }
-    if (nv <= kRegMax) {
-        select_registers(sc, nv, k, out, kth, s_hist, s_wave, s_sel, s_cand);
-    } else {
-        uint32_t rem;
-        const uint32_t T = radix_select(GlobalKeys{sc}, nv, (uint32_t)k, &rem, s_hist, s_wave, s_sel);
-        emit_ordered(GlobalKeys{sc}, nv, T, rem, k, out, s_cnt);
-        if (tid == 0 && kth) *kth = key_score(T);
+    uint32_t rem;
+    const uint32_t T = block_select<kLocalThreads, 8>(key, vmask, (uint32_t)kl + 1, &rem, s_hist, s_wave, s_sel, s_cand);
+    // the top kl+1 = keys > T and the first `rem` copies of T; its last copy of T
+    // (id order) is the (kl+1)-th element and is not a candidate
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bool v = (vmask >> i) & 1u;
+        ngt += (v && key[i] > T) ? 1u : 0u;
+        neq += (v && key[i] == T) ? 1u : 0u;
     }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<kLocalThreads>(ngt | (neq << 16), s_wave, tot);
+    uint32_t eq_before = pre >> 16;
+    uint32_t pos = (pre & 0xffffu) + (eq_before < rem - 1 ? eq_before : rem - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (!((vmask >> i) & 1u)) continue;
+        bool sel = key[i] > T;
+        if (key[i] == T) {
+            sel = eq_before + 1 < rem;
+            if (eq_before + 1 == rem) a.c_next[(int64_t)n * a.nchunks + blk] = make_uint2(T, (uint32_t)(base + e0 + i));
+            ++eq_before;
+        }
+        if (sel) {
+            if (pos < (uint32_t)kl) cand[pos] = make_uint2(key[i], (uint32_t)(base + e0 + i));
+            ++pos;
+        }
+    }
+}
+
+// Stage 2: one 1024-thread workgroup per query.  The chunks' candidate lists,
+// concatenated, are in ascending id order; thread t holds slots [8t, 8t+8).
+// The top k of the candidates (score desc, id asc) is exact when every chunk's
+// (kl+1)-th element comes after the k-th selected element in that order: every
+// id outside the candidates then comes after it too.  Otherwise (or when the
+// lists do not fit) the full select runs on the scores.
+__global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
+    __shared__ uint32_t s_hist[2048];
+    __shared__ uint32_t s_cand[kCandCap];
+    __shared__ uint32_t s_wave[kSelWaves];
+    __shared__ uint32_t s_sel[8 + kSelWaves];
+    __shared__ float s_min[kSelWaves];
+    __shared__ uint32_t s_fail;
+    const int n = blockIdx.x, tid = threadIdx.x;
+    int s;
+    int64_t p;
+    const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
+    const float* sc = a.scores + (int64_t)n * a.stride;
+    int32_t* out = a.topk + (int64_t)n * a.k;
+    float* kth = a.kth ? a.kth + n : nullptr;
+    if (nv <= a.k) {
+        select_all(sc, nv, a.k, out, kth, s_min);
+        return;
+    }
+    const int nch = (int)((nv + kChunk - 1) / kChunk);
+    const int64_t nslots = (int64_t)nch * a.kl;
+    // A chunk of L visible ids yields min(L, kl) candidates; with fewer than k
+    // in all, the candidates cannot hold the top k (short rows, few chunks).
+    const int64_t ncand = (nv / kChunk) * a.kl + (int64_t)min<int64_t>(a.kl, nv % kChunk);
+    if (nslots > (int64_t)kMergeSlots * kSelThreads || ncand < a.k) {
+        select_full(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+        return;
+    }
+    const uint2* cand = a.cand + (int64_t)n * a.nchunks * a.kl;
+    uint32_t key[kMergeSlots], id[kMergeSlots], vmask = 0;
+#pragma unroll
+    for (int i = 0; i < kMergeSlots; ++i) {
+        const int64_t f = (int64_t)tid * kMergeSlots + i;
+        uint2 c = make_uint2(0u, 0xffffffffu);
+        if (f < nslots) c = cand[f];
+        key[i] = c.x;
+        id[i] = c.y;
+        vmask |= (c.y != 0xffffffffu ? 1u : 0u) << i;
+    }
+    if (tid == 0) s_fail = 0;
+    uint32_t rem;
+    const uint32_t T = block_select<kSelThreads, kMergeSlots>(key, vmask, (uint32_t)a.k, &rem, s_hist, s_wave, s_sel,
+                                                             s_cand);
+    // the k-th element's id (s_sel[6]) from a counting pass, then the check
+    emit_selected<kSelThreads, kMergeSlots>(key, vmask, T, rem, a.k, [&](int i) { return (int32_t)id[i]; }, out,
+                                            s_wave, s_sel, false);
+    __syncthreads();
+    const uint32_t idk = s_sel[6];
+    for (int c = tid; c < nch; c += kSelThreads) {
+        const uint2 nx = a.c_next[(int64_t)n * a.nchunks + c];
+        if (nx.y != 0xffffffffu && !(nx.x < T || (nx.x == T && nx.y > idk))) s_fail = 1;
+    }
+    __syncthreads();
+    if (s_fail) {
+        select_full(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+        return;
+    }
+    emit_selected<kSelThreads, kMergeSlots>(key, vmask, T, rem, a.k, [&](int i) { return (int32_t)id[i]; }, out,
+                                            s_wave, s_sel, true);
+    if (tid == 0 && kth) *kth = key_score(T);
 }
 
 }  // namespace
@@ -471,7 +625,13 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t st) {
 
 hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st) {
     if (a.num_q <= 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), 0, st, a);
+    if (a.kl > 0) {
+        hipLaunchKernelGGL(topk_local_kernel, dim3((unsigned)a.nchunks, (unsigned)a.num_q), dim3(kLocalThreads), 0, st,
+                           a);
+        hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), 0, st, a);
+    }
     return hipGetLastError();
 }
 

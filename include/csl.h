@@ -120,6 +120,23 @@ csl_status csl_compress_insert(const csl_pool* pool /* host */, const csl_pages*
                                csl_stream_t stream);
 
 /*
+ * Step 1, several pools of a layer in one launch (the horizontal fusion of
+ * independent per-pool inserts): the same batch of new tokens (start_pos,
+ * cu_new, total_new) goes into every job's pool, each with its own x, logits
+ * and gain, with exactly the semantics of csl_compress_insert per job.
+ * 1 <= n_jobs <= 4; jobs (host array) must target different pools.
+ */
+typedef struct {
+    const csl_pool* pool; /* host */
+    const uint16_t* x;    /* [total_new][pool->dim] bf16 */
+    const float* logits;  /* [total_new][pool->coff] fp32; NULL iff pool->ratio == 1 */
+    const float* gain;    /* [pool->dim] fp32 or NULL (unit gain); NULL for ratio 1 */
+} csl_insert_job;
+csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs /* host */,
+                                     const csl_pages* pages /* host */, const int64_t* start_pos,
+                                     const int32_t* cu_new, int32_t total_new, float eps, csl_stream_t stream);
+
+/*
  * Steps 2-3 -- DSA indexer scores and causal top-k ([Summary] DeepSeek V4
  * 注意力架構: DSA keeps only the top-k compressed tokens; [Notes] 压缩参数细节:
  * k = 512 on c4a layers).

@@ -109,6 +109,50 @@ def test_compress_insert_parity(csl, orc, case):
         assert np.array_equal(host(gp.state_logits), hp.state_logits)
 
 
+def test_compress_insert_multi_parity(csl, orc):
+    """Raw window, c4a main (fp8) and c4a index pools filled by one fused launch per
+    chunk, against the oracle's one-pool inserts."""
+    seed, D, DI, R = 17, 512, 128, 64
+    lens, chunks = [600, 333], [[250, 1, 349], [333, 0, 0]]
+    ns = len(lens)
+    mb = max(lens) // 256 + 1
+    bt = block_table(seed, ns, mb, extra_pages=1)
+    P = ns * mb + 1
+    hps = [O.HostPool(1, 1, D, R, THETA, O.BF16, P), O.HostPool(4, 2, D, R, THETA, O.FP8, P),
+           O.HostPool(4, 2, DI, 0, THETA, O.BF16, P)]
+    gps = [gpu_pool(csl, h) for h in hps]
+    xs = [randn_bf16(seed, 100 + s, (lens[s], D)) for s in range(ns)]
+    xis = [randn_bf16(seed, 110 + s, (lens[s], DI)) for s in range(ns)]
+    ls = [randn_f32(seed, 200 + s, (lens[s], 2)).astype(np.float32) for s in range(ns)]
+    lis = [randn_f32(seed, 210 + s, (lens[s], 2)).astype(np.float32) for s in range(ns)]
+    gain = rand_u(seed, 300, (D,), 0.5, 1.5).astype(np.float32)
+    done = [0] * ns
+    for rnd in range(3):
+        sizes = [chunks[s][rnd] for s in range(ns)]
+        cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        st = np.array(done, np.int64)
+        cat = lambda arrs: np.concatenate([arrs[s][done[s]:done[s] + sizes[s]] for s in range(ns)])
+        x, xi, lg, li = cat(xs), cat(xis), cat(ls), cat(lis)
+        assert O.compress_insert(hps[0], bt, st, cu, x) == 0
+        assert O.compress_insert(hps[1], bt, st, cu, x, lg, gain) == 0
+        assert O.compress_insert(hps[2], bt, st, cu, xi, li) == 0
+        say(f"compress_insert_multi round {rnd} sizes {sizes}")
+        csl.compress_insert_multi([(gps[0], dev_bf16(x), None, None), (gps[1], dev_bf16(x), dev(lg), dev(gain)),
+                                   (gps[2], dev_bf16(xi), dev(li), None)], dev(bt), dev(st), dev(cu))
+        done = [done[s] + sizes[s] for s in range(ns)]
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0
+    for (h, g, r, what) in ((hps[0], gps[0], 1, "raw"), (hps[1], gps[1], 4, "main fp8"), (hps[2], gps[2], 4, "index")):
+        for s in range(ns):
+            go = gather_rows(host(g.rows), bt, s, r, 0, lens[s] // r)
+            oo = gather_rows(h.rows, bt, s, r, 0, lens[s] // r)
+            if h.dtype == O.BF16:
+                assert_close(O.decode_rows(go, h.dim, h.dtype), O.decode_rows(oo, h.dim, h.dtype), what=what)
+            else:
+                assert_fp8_close(orc, go[:, :h.dim], go[:, h.dim:].copy().view(np.float32), oo[:, :h.dim],
+                                 oo[:, h.dim:].copy().view(np.float32), what=what)
+
+
 # ---------------------------------------------------------------------------
 # index_topk
 # ---------------------------------------------------------------------------
@@ -124,6 +168,9 @@ INDEX_CASES = [
     dict(name="h16_d128_k512_outliers", H=16, DI=128, k=512, pos=[[20000, 131072]], mode="outlier"),
     # more than 32768 candidates: the select reads its keys from global memory
     dict(name="h16_d128_k512_40k_candidates", H=16, DI=128, k=512, pos=[[160000, 150003]]),
+    # scores rise with the id (with bf16 ties): the top 512 crowd the last chunks, so the
+    # two-stage select's check fails and the exact single-pass select takes over
+    dict(name="h16_d128_k512_ramp", H=16, DI=128, k=512, pos=[[131072, 70001]], mode="ramp"),
 ]
 
 
@@ -140,6 +187,9 @@ def test_index_topk_parity(csl, orc, case):
         keys = randn_bf16(seed, 10 + s, (64 * mb, DI))
         if case.get("mode") == "equal":
             keys[:] = keys[0]
+        elif case.get("mode") == "ramp":
+            ramp = (1.0 + np.arange(64 * mb) / 8192.0).astype(np.float32)
+            keys = (np.repeat(ramp[:, None], DI, 1).view(np.uint32) >> 16).astype(np.uint16)
         elif case.get("mode") == "outlier":
             keys = (keys.astype(np.uint32) - (12 << 7)).astype(np.uint16)       # x 2^-12 (exact in bf16)
             big = np.arange(7, 64 * mb, 997)                                      # ~1 in 1000 keeps its scale
@@ -149,6 +199,8 @@ def test_index_topk_parity(csl, orc, case):
     q_pos = np.concatenate(case["pos"]).astype(np.int64)
     nq = len(q_pos)
     qi = randn_bf16(seed, 20, (nq, H, DI))
+    if case.get("mode") == "ramp":
+        qi = (np.abs(O.bf16_array_to_f64(qi)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     w = rand_u(seed, 21, (nq, H)).astype(np.float32)
     o_topk, o_kth, o_sc, f = O.index_topk(hp, bt, q_seq, q_pos, qi, w, k, want_scores=True, max_cand=max_pos // 4)
     assert f == 0
