@@ -69,7 +69,7 @@ Timer g_timer[kNumKernels];
 std::mutex g_timer_mu;
 
 template <typename F>
-hipError_t timed(int kid, hipStream_t st, F&& launch) {
+hipError_t timed(int kid, F&& launch) {
     hipEvent_t b = nullptr, e = nullptr;
     {
         std::lock_guard<std::mutex> lk(g_timer_mu);
@@ -86,10 +86,10 @@ hipError_t timed(int kid, hipStream_t st, F&& launch) {
             }
         }
     }
-    if (b) (void)hipEventRecord(b, st);
-    hipError_t r = launch();
-    if (e) (void)hipEventRecord(e, st);
-    return r;
+    LaunchEvents ev;
+    ev.start = b;
+    ev.stop = e;
+    return launch(ev);
 }
 
 // ---------------------------------------------------------------- validation
@@ -339,7 +339,7 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs,
     a.total_new = total_new;
     a.eps = eps;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_COMPRESS, s, [&] { return launch_compress(a, s); });
+    hipError_t e = timed(CSL_KERNEL_COMPRESS, [&](const LaunchEvents& ev) { return launch_compress(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "compress_insert launch");
     return CSL_OK;
 }
@@ -355,7 +355,7 @@ size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k) {
     if (num_q <= 0 || max_q_pos < 0 || k < 1) return 0;
     const int64_t stride = index_stride(max_q_pos), nchunks = stride / 2048;
     const int kl = index_local_k(max_q_pos, k);
-    return (size_t)num_q * ((size_t)stride * sizeof(float) + (size_t)nchunks * (kl + 1) * 8);
+    return (size_t)num_q * ((size_t)stride * sizeof(float) + (kl > 0 ? (size_t)nchunks * (kl + 1) * 8 : 0));
 }
 
 csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
@@ -408,9 +408,9 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     a.num_seqs = pages->num_seqs;
     a.max_blocks = pages->max_blocks;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, s, [&] { return launch_index_score(a, s); });
+    hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
-    e = timed(CSL_KERNEL_TOPK_SELECT, s, [&] { return launch_topk_select(a, s); });
+    e = timed(CSL_KERNEL_TOPK_SELECT, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "topk_select launch");
     return CSL_OK;
 }
@@ -457,10 +457,10 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
         a.part_ml = a.part_o + (size_t)num_q * sp * n_heads * swa->dim;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&] { return launch_attn(a, s); });
+    hipError_t e = timed(CSL_KERNEL_ATTN, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
     if (sp > 1) {
-        e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&] { return launch_attn_combine(a, s); });
+        e = timed(CSL_KERNEL_ATTN_COMBINE, [&](const LaunchEvents& ev) { return launch_attn_combine(a, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
     }
     return CSL_OK;
@@ -489,7 +489,7 @@ csl_status csl_hybrid_attn_prefill(const csl_pool* comp, const csl_pool* swa, co
     a.num_q = total_q;
     a.n_splits = 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&] { return launch_attn(a, s); });
+    hipError_t e = timed(CSL_KERNEL_ATTN, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
     return CSL_OK;
 }

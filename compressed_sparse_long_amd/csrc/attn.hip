@@ -523,27 +523,27 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
 }  // namespace
 
 template <int D, int KV>
-void launch_prec(const AttnArgs& a, dim3 grid, hipStream_t st) {
-    if (a.out_dtype == kFP8) hipLaunchKernelGGL((hybrid_attn_kernel<D, KV, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((hybrid_attn_kernel<D, KV, false>), grid, dim3(kThreads), 0, st, a);
+void launch_prec(const AttnArgs& a, dim3 grid, hipStream_t st, const LaunchEvents& ev) {
+    if (a.out_dtype == kFP8) launch_kernel(ev, true, true, hybrid_attn_kernel<D, KV, true>, grid, dim3(kThreads), st, a);
+    else launch_kernel(ev, true, true, hybrid_attn_kernel<D, KV, false>, grid, dim3(kThreads), st, a);
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
     dim3 grid((unsigned)((int64_t)a.num_q * a.n_splits));
     const int kv = a.comp_rows ? a.comp_dtype : a.swa_dtype;
-    if (a.dim == 512 && kv == kBF16) launch_prec<512, kBF16>(a, grid, st);
-    else if (a.dim == 512 && kv == kFP8) launch_prec<512, kFP8>(a, grid, st);
-    else if (a.dim == 128 && kv == kBF16) launch_prec<128, kBF16>(a, grid, st);
+    if (a.dim == 512 && kv == kBF16) launch_prec<512, kBF16>(a, grid, st, ev);
+    else if (a.dim == 512 && kv == kFP8) launch_prec<512, kFP8>(a, grid, st, ev);
+    else if (a.dim == 128 && kv == kBF16) launch_prec<128, kBF16>(a, grid, st, ev);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0 || a.n_splits <= 1) return hipSuccess;
     dim3 grid((unsigned)((int64_t)a.num_q * ((a.n_heads + 3) / 4)));
-    if (a.dim == 512) hipLaunchKernelGGL(attn_combine_kernel<512>, grid, dim3(kThreads), 0, st, a);
-    else if (a.dim == 128) hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(kThreads), 0, st, a);
+    if (a.dim == 512) launch_kernel(ev, true, true, attn_combine_kernel<512>, grid, dim3(kThreads), st, a);
+    else if (a.dim == 128) launch_kernel(ev, true, true, attn_combine_kernel<128>, grid, dim3(kThreads), st, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

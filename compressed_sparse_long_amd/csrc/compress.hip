@@ -224,10 +224,10 @@ __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs 
 
 }  // namespace
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.total_new <= 0 || a.n_jobs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(compress_insert_kernel, dim3((unsigned)a.total_new, (unsigned)a.n_jobs), dim3(kThreads), 0, st,
-                       a);
+    launch_kernel(ev, true, true, compress_insert_kernel, dim3((unsigned)a.total_new, (unsigned)a.n_jobs),
+                  dim3(kThreads), st, a);
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Argument blocks and launchers of the gfx950 kernels (host + device).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,10 +74,26 @@ struct AttnArgs {
     RopeFreqs rf;
 };
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
-hipError_t launch_index_score(const IndexArgs& a, hipStream_t st);
-hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st);
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
-hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
+// Events of a timed launch.  A launcher hands `start` to the first kernel it
+// starts and `stop` to the last; the runtime stamps them with those kernels'
+// own begin and end times (no marker packets in the queue), so the interval
+// is the kernels' run time.  Both null: an untimed launch.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline void launch_kernel(const LaunchEvents& ev, bool first, bool last, F kernel, dim3 grid, dim3 block,
+                          hipStream_t st, Args... args) {
+    hipEvent_t b = first ? ev.start : nullptr, e = last ? ev.stop : nullptr;
+    if (b || e) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, b, e, 0, args...);
+    else hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 
 }  // namespace csl

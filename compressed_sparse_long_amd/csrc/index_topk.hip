@@ -611,26 +611,26 @@ __global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
 
 }  // namespace
 
-hipError_t launch_index_score(const IndexArgs& a, hipStream_t st) {
+hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
     dim3 grid((unsigned)(a.stride / 256), (unsigned)a.num_q);
     switch (a.dim) {
-        case 32: hipLaunchKernelGGL(index_score_kernel<32>, grid, dim3(256), 0, st, a); break;
-        case 64: hipLaunchKernelGGL(index_score_kernel<64>, grid, dim3(256), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(index_score_kernel<128>, grid, dim3(256), 0, st, a); break;
+        case 32: launch_kernel(ev, true, true, index_score_kernel<32>, grid, dim3(256), st, a); break;
+        case 64: launch_kernel(ev, true, true, index_score_kernel<64>, grid, dim3(256), st, a); break;
+        case 128: launch_kernel(ev, true, true, index_score_kernel<128>, grid, dim3(256), st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st) {
+hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
     if (a.kl > 0) {
-        hipLaunchKernelGGL(topk_local_kernel, dim3((unsigned)a.nchunks, (unsigned)a.num_q), dim3(kLocalThreads), 0, st,
-                           a);
-        hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), 0, st, a);
+        launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)a.nchunks, (unsigned)a.num_q),
+                      dim3(kLocalThreads), st, a);
+        launch_kernel(ev, false, true, topk_merge_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), st, a);
     } else {
-        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), 0, st, a);
+        launch_kernel(ev, true, true, topk_select_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), st, a);
     }
     return hipGetLastError();
 }

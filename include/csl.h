@@ -153,6 +153,11 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs 
  * [dim] bf16; w: [num_q][n_heads] fp32; topk: [num_q][k] int32;
  * n_heads <= 16; 1 <= k <= 2048; every q_pos <= max_q_pos (host bound that
  * sizes the grid).
+ * Workspace (device, caller-owned, contents undefined on entry and exit):
+ * one fp32 score row per query (max_q_pos/4 rounded up to 2048 entries) plus,
+ * when the two-stage select is used (more than k visible entries and at most
+ * 8192 first-stage candidates per query), 8-byte (key, id) candidates for
+ * each 2048-entry chunk.  csl_index_topk_workspace() gives the exact size.
  */
 size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k);
 csl_status csl_index_topk(const csl_pool* index_pool /* host */, const csl_pages* pages /* host */,
@@ -207,11 +212,13 @@ const char* csl_last_error(void);
  * *flags (host) and clears it.  For tests and debugging. */
 csl_status csl_read_device_error(uint32_t* flags);
 
-/* Kernel timers: when enabled for a kernel id, the library records a HIP
- * event pair on the launch stream around every launch of that kernel
- * (at most 65536 launches between reads).  csl_timer_read synchronises the
- * device, returns the summed durations (ms) and the launch count, and
- * resets.  Kernel ids: */
+/* Kernel timers: when enabled for a kernel id, every launch of that kernel
+ * (at most 65536 between reads) goes through hipExtLaunchKernel with a HIP
+ * event pair that the runtime stamps with the kernel's own start and end
+ * (for CSL_KERNEL_TOPK_SELECT: from the first of its kernels to the last),
+ * on the launch stream and with no extra queue packets.  csl_timer_read
+ * synchronises the device, returns the summed durations (ms) and the launch
+ * count, and resets.  Kernel ids: */
 #define CSL_KERNEL_COMPRESS 0
 #define CSL_KERNEL_INDEX_SCORE 1
 #define CSL_KERNEL_TOPK_SELECT 2
