@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode queries/s + HBM GB/s, c4a top-k512+SWA128 at 128K ctx, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_c4a_decode_b16_128k.pmc.json")
 SCORE_SOURCE = os.path.join(ROOT, "compressed_sparse_long_amd", "csrc", "index_topk.hip")
 
@@ -143,7 +144,7 @@ class DecodeSetup:
         """One decode step.  With side streams, the inserts of the new token run
         beside the indexer and attention (the query at p reads positions < p
         only), forked from and joined back into the current stream."""
-        csl, w, p, torch = self.csl, self.w, self.reps[r], self.torch
+        p, torch = self.reps[r], self.torch
         if self.side is not None:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)
@@ -151,6 +152,13 @@ class DecodeSetup:
                 self.inserts(p)
         else:
             self.inserts(p)
+        self.attend(r)
+        if self.side is not None:
+            torch.cuda.current_stream().wait_stream(self.side)
+
+    def attend(self, r: int):
+        """The query side of a step: index top-k and attention of every layer."""
+        csl, w, p = self.csl, self.w, self.reps[r]
         if "c4a" in self.layers:
             csl.index_topk(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx, w.topk,
                            self.topk, None, self.ws_idx)
@@ -161,8 +169,6 @@ class DecodeSetup:
             csl.hybrid_attn_decode(p["main128"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q,
                                    None, 0, w.swa, self.scale, w.out_dtype, self.out["c128a"],
                                    self.out_scales["c128a"], self.ws_attn)
-        if self.side is not None:
-            torch.cuda.current_stream().wait_stream(self.side)
 
     def algorithmic_bytes_per_step(self) -> dict:
         """Bytes the method must move per step (no intermediate buffers)."""
@@ -180,6 +186,91 @@ class DecodeSetup:
         if "c128a" in w.layers:
             per_q["c128a"] = (w.ctx // 128 + w.swa) * rb + qio + ins
         return {k: v * nq for k, v in per_q.items()}
+
+
+class PrefillSetup:
+    """A prefill chunk on one sequence: a prefix built by compress_insert
+    (untimed), then the step: the chunk's new tokens into the raw, c4a-main
+    and c4a-index pools (one fused launch), the indexer's causal top-k for one
+    query per new token, and attention over top-k U window for every query."""
+
+    def __init__(self, w, device="cuda"):
+        import torch
+
+        import compressed_sparse_long_amd as csl
+        from synth import workloads as W
+
+        assert w.prefill and w.num_seqs == 1 and w.layers == ("c4a",)
+        self.w, self.csl, self.torch = w, csl, torch
+        T0, n, D, R, DI, P = w.ctx, w.new_tokens, w.dim, w.rope_dims, w.idx_dim, w.num_pages
+        self.bt = W.block_table(w).to(device)
+        kv = w.kv_dtype
+        self.raw = csl.Pool(1, 1, D, R, w.theta, kv, P, device=device, state=False)
+        self.main = csl.Pool(4, 2, D, R, w.theta, kv, P, device=device)
+        self.idx = csl.Pool(4, 2, DI, 0, w.theta, csl.BF16, P, device=device)
+        self.gain = W.gain(w, D, device=device)
+        self.gain_i = W.gain(w, DI, tid=W.T_GAIN_I, device=device)
+        t0 = time.time()
+        zero = torch.zeros(1, dtype=torch.int64, device=device)
+        cu = torch.tensor([0, T0], dtype=torch.int32, device=device)
+        x = W.latent(w, 0, 0, T0, device=device)
+        xi = W.latent(w, 0, 0, T0, dim=DI, tid=W.T_XI, device=device)
+        csl.compress_insert_multi([(self.raw, x, None, None),
+                                   (self.main, x, W.logits(w, 0, 0, T0, 2, device=device), self.gain),
+                                   (self.idx, xi, W.logits(w, 0, 0, T0, 2, tid=W.T_LOGITS_I, device=device),
+                                    self.gain_i)], self.bt, zero, cu)
+        del x, xi
+        torch.cuda.synchronize()
+        log(f"prefix of {T0} tokens built in {time.time() - t0:.1f}s")
+        self.start = torch.full((1,), T0, dtype=torch.int64, device=device)
+        self.cu_new = torch.tensor([0, n], dtype=torch.int32, device=device)
+        self.x_new = W.latent(w, 0, T0, n, device=device)
+        self.lg_new = W.logits(w, 0, T0, n, 2, device=device)
+        self.xi_new = W.latent(w, 0, T0, n, dim=DI, tid=W.T_XI, device=device)
+        self.lgi_new = W.logits(w, 0, T0, n, 2, tid=W.T_LOGITS_I, device=device)
+        qd = W.queries(w, device=device)
+        self.q, self.q_idx, self.w_idx = qd["q"], qd["q_idx"], qd["w_idx"]
+        self.q_seq = w.query_seqs().to(device)
+        self.q_pos = w.query_positions().to(device)
+        self.max_pos = T0 + n - 1
+        nq = w.num_q
+        self.topk = torch.empty((nq, w.topk), dtype=torch.int32, device=device)
+        self.ws_idx = torch.empty(max(1, csl.index_topk_workspace(nq, self.max_pos, w.topk) // 4),
+                                  dtype=torch.float32, device=device)
+        odt = {0: torch.float32, 1: torch.bfloat16, 2: torch.uint8}[w.out_dtype]
+        self.out = torch.empty((nq, w.n_heads, D), dtype=odt, device=device)
+        self.out_scales = (torch.empty((nq, w.n_heads, D // 64), dtype=torch.float32, device=device)
+                           if w.out_dtype == 2 else None)
+        self.scale = D ** -0.5
+
+    def step(self):
+        csl, w = self.csl, self.w
+        csl.compress_insert_multi([(self.raw, self.x_new, None, None),
+                                   (self.main, self.x_new, self.lg_new, self.gain),
+                                   (self.idx, self.xi_new, self.lgi_new, self.gain_i)], self.bt, self.start,
+                                  self.cu_new)
+        self.index()
+        self.attend()
+
+    def index(self):
+        self.csl.index_topk(self.idx, self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx,
+                            self.w.topk, self.topk, None, self.ws_idx)
+
+    def attend(self):
+        csl, w = self.csl, self.w
+        csl.hybrid_attn_prefill(self.main, self.raw, self.bt, self.cu_new, self.start, self.max_pos, self.q,
+                                self.topk, w.topk, w.swa, self.scale, w.out_dtype, self.out, self.out_scales)
+
+    def algorithmic_flops(self) -> dict:
+        """Multiply-adds x 2 the method must do: indexer over every visible entry
+        of every query, attention (QK and PV) over top-k U window keys."""
+        w = self.w
+        pos = w.query_positions()
+        vis = (pos // 4).clamp(min=0)
+        keys = vis.clamp(max=w.topk) + pos.clamp(max=w.swa)
+        idx = int(vis.sum()) * w.idx_heads * w.idx_dim * 2
+        att = int(keys.sum()) * w.n_heads * w.dim * 2 * 2
+        return {"index_score": idx, "attention": att}
 
 
 # ---------------------------------------------------------------------------
@@ -277,12 +368,70 @@ def copy_calibration(mb: int, iters: int):
     print(json.dumps({"kernel": "neg", "read_bytes": n, "write_bytes": n, "iters": iters}))
 
 
+def run_prefill(args):
+    """Prefill chunk: steps launched eagerly (milliseconds each, launch cost is
+    noise) with every library kernel timed by its own start/end stamps."""
+    import torch
+
+    import compressed_sparse_long_amd as csl
+    from synth import workloads as W
+
+    w = W.prefill()
+    setup = PrefillSetup(w)
+    log(f"workload {w.name}: {w.new_tokens} new tokens on a {w.ctx}-token prefix")
+    K, warm = args.steps, args.warmup
+    for _ in range(warm):
+        setup.step()
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0, "device error flags after warm-up"
+    kids = {"compress_insert": csl.KERNEL_COMPRESS, "index_score": csl.KERNEL_INDEX_SCORE,
+            "topk_select": csl.KERNEL_TOPK_SELECT, "attention": csl.KERNEL_ATTN}
+    for k in kids.values():
+        csl.timer_read(k)
+        csl.timer_enable(k, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        setup.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = {}
+    for name, k in kids.items():
+        csl.timer_enable(k, False)
+        ms, n = csl.timer_read(k)
+        kern[name] = {"avg_ms": round(ms / max(1, n), 4), "launches": n}
+    assert csl.read_device_error() == 0, "device error flags after the timed steps"
+    ms_step = (t1 - t0) * 1e3 / K
+    fl = setup.algorithmic_flops()
+    for name in ("index_score", "attention"):
+        kern[name]["algorithmic_tflop"] = round(fl[name] / 1e12, 2)
+        kern[name]["tflops"] = round(fl[name] / (kern[name]["avg_ms"] * 1e-3) / 1e12, 1)
+    dom = max(("index_score", "attention"), key=lambda k: kern[k]["avg_ms"])
+    ach = kern[dom]["tflops"]
+    res = {
+        "metric": "prefill tokens/s (c4a layer: insert + indexer top-512 + attention over top-512 U SWA128)",
+        "value": round(w.new_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": warm, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "algorithmic_tflops": round((fl["index_score"] + fl["attention"]) / (ms_step * 1e-3) / 1e12, 1),
+        "config": {"workload": w.name, "prefix": w.ctx, "new_tokens": w.new_tokens, "topk": w.topk, "swa": w.swa,
+                   "heads": w.n_heads, "latent_dim": w.dim, "indexer": f"{w.idx_heads}x{w.idx_dim}",
+                   "kv_dtype": "bf16", "out_dtype": "fp8", "hip_graphs": False},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "timing": "hipExtLaunchKernel start/stop events stamped by each launch in the timed steps"},
+        "kernels": kern,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c4a", choices=["c4a", "c128a", "1m"])
+    ap.add_argument("--workload", default="c4a", choices=["c4a", "c128a", "1m", "prefill"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=200,
@@ -309,6 +458,9 @@ def main():
     import compressed_sparse_long_amd as csl
     from synth import workloads as W
 
+    if args.workload == "prefill":
+        run_prefill(args)
+        return
     w = {"c4a": W.c4a_decode, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)
     setup = DecodeSetup(w, R, side_stream=args.side_stream)

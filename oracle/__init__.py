@@ -69,6 +69,8 @@ def lib():
         L.csl_oracle_hybrid_attn.argtypes = [C.POINTER(Pool), C.POINTER(Pool), vp, C.c_int, C.c_int, vp, vp,
                                              vp, C.c_int, vp, C.c_int, C.c_int, dbl, C.c_int, vp, vp, vp]
         L.csl_oracle_hybrid_attn.restype = C.c_int
+        L.csl_oracle_compress_rows.argtypes = [C.POINTER(Pool), C.c_int, vp, vp, vp, vp, dbl, vp]
+        L.csl_oracle_compress_rows.restype = None
         L.csl_oracle_num_threads.argtypes = []
         L.csl_oracle_num_threads.restype = C.c_int
         _lib = L
@@ -140,6 +142,23 @@ def compress_insert(pool: HostPool, bt, start_pos, cu_new, x, logits=None, gain=
     s = pool.struct()
     return lib().csl_oracle_compress_insert(C.byref(s), _p(bt), len(st), bt.shape[1], _p(st), _p(cu), _p(x),
                                             _p(lg), _p(g), float(eps))
+
+
+def compress_rows(ratio, coff, dim, rope_dims, theta, dtype, ids, x_win, logits_win=None, gain=None, eps=1e-6):
+    """Stored rows of entries `ids` computed one by one from their windows:
+    x_win [n][coff*ratio][dim] bf16 (tokens r(i+1)-W .. r(i+1)-1; rows at
+    negative positions are ignored), logits_win [n][coff*ratio][coff] fp32
+    (None for ratio 1).  Returns [n][row_bytes] uint8."""
+    ids = np.ascontiguousarray(ids, np.int64)
+    n = ids.shape[0]
+    W = coff * ratio
+    x_win = np.ascontiguousarray(x_win, np.uint16).reshape(n, W, dim)
+    lg = None if logits_win is None else np.ascontiguousarray(logits_win, np.float32).reshape(n, W, coff)
+    g = None if gain is None else np.ascontiguousarray(gain, np.float32)
+    out = np.zeros((n, row_bytes(dim, dtype)), np.uint8)
+    desc = Pool(ratio, coff, dim, rope_dims, float(theta), dtype, 0, None, None, None)
+    lib().csl_oracle_compress_rows(C.byref(desc), n, _p(ids), _p(x_win), _p(lg), _p(g), float(eps), _p(out))
+    return out
 
 
 def index_topk(pool: HostPool, bt, q_seq, q_pos, q_idx, w, k, want_scores=False, max_cand=None):

@@ -260,25 +260,16 @@ static uint8_t* entry_row(const csl_oracle_pool* P, const int32_t* bt, int max_b
  * (R4).  u = sum_k w_k x_k; y = u / sqrt(mean(u^2) + eps) * gain (R6);
  * then RoPE at position r*i; then the store.  The entry exists once its last
  * token has arrived.  Returns the number of unmapped pages met. */
-static int compress_entry(const csl_oracle_pool* P, const int32_t* bt, int max_blocks, int s,
-                          int64_t i, const float* gain, double eps, double* y)
+/* The entry from its window: xr[k] = token r(i+1)-W+k (NULL = masked: a
+ * negative position or an unmapped page), lg[k] = that token's logit in
+ * column floor(k/r). */
+static void entry_from_window(const csl_oracle_pool* P, int64_t i, const uint16_t* const* xr, const double* lg,
+                              const float* gain, double eps, double* y)
 {
-    int r = P->ratio, W = P->coff * P->ratio, D = P->dim;
-    double* lg = (double*)malloc(sizeof(double) * W);
-    const uint16_t** xr = (const uint16_t**)malloc(sizeof(void*) * W);
-    int faults = 0;
+    int W = P->coff * P->ratio, D = P->dim;
     double mx = -INFINITY;
-    for (int k = 0; k < W; k++) {
-        int64_t t = (int64_t)r * (i + 1) - W + k;
-        xr[k] = NULL;
-        if (t < 0) continue;                       /* before the sequence: masked */
-        int64_t pg = page_of(bt, max_blocks, s, t, P->num_pages);
-        if (pg < 0) { faults++; continue; }
-        size_t tok = (size_t)pg * O_BLOCK + (size_t)(t % O_BLOCK);
-        xr[k] = P->state_x + tok * (size_t)D;
-        lg[k] = P->state_logits[tok * (size_t)P->coff + (size_t)(k / r)];
-        if (lg[k] > mx) mx = lg[k];
-    }
+    for (int k = 0; k < W; k++)
+        if (xr[k] && lg[k] > mx) mx = lg[k];
     double den = 0.0;
     for (int k = 0; k < W; k++)
         if (xr[k]) den += exp(lg[k] - mx);
@@ -293,10 +284,70 @@ static int compress_entry(const csl_oracle_pool* P, const int32_t* bt, int max_b
     ms /= D;
     double inv = 1.0 / sqrt(ms + eps);
     for (int d = 0; d < D; d++) y[d] = y[d] * inv * (gain ? (double)gain[d] : 1.0);
-    rope(y, D, P->rope_dims, P->rope_theta, (double)((int64_t)r * i));
+    rope(y, D, P->rope_dims, P->rope_theta, (double)((int64_t)P->ratio * i));
+}
+
+/* Entry i of sequence s, its window read from the compressor state.
+ * Returns the number of unmapped pages met. */
+static int compress_entry(const csl_oracle_pool* P, const int32_t* bt, int max_blocks, int s,
+                          int64_t i, const float* gain, double eps, double* y)
+{
+    int r = P->ratio, W = P->coff * P->ratio, D = P->dim;
+    double* lg = (double*)malloc(sizeof(double) * W);
+    const uint16_t** xr = (const uint16_t**)malloc(sizeof(void*) * W);
+    int faults = 0;
+    for (int k = 0; k < W; k++) {
+        int64_t t = (int64_t)r * (i + 1) - W + k;
+        xr[k] = NULL;
+        lg[k] = 0.0;
+        if (t < 0) continue;                       /* before the sequence: masked */
+        int64_t pg = page_of(bt, max_blocks, s, t, P->num_pages);
+        if (pg < 0) { faults++; continue; }
+        size_t tok = (size_t)pg * O_BLOCK + (size_t)(t % O_BLOCK);
+        xr[k] = P->state_x + tok * (size_t)D;
+        lg[k] = P->state_logits[tok * (size_t)P->coff + (size_t)(k / r)];
+    }
+    entry_from_window(P, i, xr, lg, gain, eps, y);
     free(lg);
     free(xr);
     return faults;
+}
+
+/* Rows one by one from explicit windows, with no pool state: for each n,
+ * entry ids[n] of a pool shaped like P from x_win[n] = its W = coff*ratio
+ * window tokens r(i+1)-W .. r(i+1)-1 ([W][dim] bf16; rows at negative
+ * positions are ignored) and logits_win[n] = those tokens' logits
+ * ([W][coff] fp32; NULL for ratio 1).  Ratio 1: row = RoPE(x_i, i), no norm.
+ * out[n] receives the stored row (P->dtype).  The same arithmetic as
+ * csl_oracle_compress_insert, for checking sampled entries of a large cache. */
+void csl_oracle_compress_rows(const csl_oracle_pool* P, int n, const int64_t* ids, const uint16_t* x_win,
+                              const float* logits_win, const float* gain, double eps, uint8_t* out)
+{
+    int r = P->ratio, W = P->coff * P->ratio, D = P->dim;
+    size_t rb = csl_oracle_row_bytes(D, P->dtype);
+#pragma omp parallel for schedule(dynamic)
+    for (int m = 0; m < n; m++) {
+        double* y = (double*)malloc(sizeof(double) * D);
+        const uint16_t* xw = x_win + (size_t)m * W * D;
+        int64_t i = ids[m];
+        if (r == 1) {
+            for (int d = 0; d < D; d++) y[d] = bf16_to_f64(xw[d]);
+            rope(y, D, P->rope_dims, P->rope_theta, (double)i);
+        } else {
+            double* lg = (double*)malloc(sizeof(double) * W);
+            const uint16_t** xr = (const uint16_t**)malloc(sizeof(void*) * W);
+            for (int k = 0; k < W; k++) {
+                int64_t t = (int64_t)r * (i + 1) - W + k;
+                xr[k] = t < 0 ? NULL : xw + (size_t)k * D;
+                lg[k] = t < 0 ? 0.0 : (double)logits_win[((size_t)m * W + k) * P->coff + (size_t)(k / r)];
+            }
+            entry_from_window(P, i, xr, lg, gain, eps, y);
+            free(lg);
+            free(xr);
+        }
+        store_row(out + (size_t)m * rb, y, D, P->dtype);
+        free(y);
+    }
 }
 
 /* compress_insert over a batch of chunks: sequence s receives tokens

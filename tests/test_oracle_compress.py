@@ -187,3 +187,34 @@ def test_unmapped_page_counts_fault(orc, seq):
     pool = orc.HostPool(4, 2, 64, 0, THETA, orc.BF16, 4)
     f = orc.compress_insert(pool, bt, [0], [0, 1024], x, np.zeros((1024, 2), np.float32))
     assert f > 0
+
+
+@pytest.mark.parametrize("ratio,coff,dtype", [(4, 2, "FP8"), (128, 1, "BF16"), (1, 1, "FP8")])
+def test_rows_one_by_one_equal_streaming_insert(orc, seq, ratio, coff, dtype):
+    """Entries computed from explicit windows (no state, used to check sampled
+    entries of large caches) are byte-identical to the streaming insert."""
+    x, _ = seq
+    x = np.concatenate([x, randn_bf16(7, 9, (1024, 192))], axis=1)   # D = 256 for fp8 rows
+    D = x.shape[1]
+    dt = getattr(orc, dtype)
+    lg = None if ratio == 1 else randn_f32(7, 5, (1024, coff)).astype(np.float32)
+    gain = None if ratio == 1 else np.random.default_rng(3).uniform(0.5, 1.5, D).astype(np.float32)
+    T = 1024
+    mb = T // 256
+    bt = block_table(5, 1, mb)
+    pool = orc.HostPool(ratio, coff, D, 32, THETA, dt, mb)
+    assert orc.compress_insert(pool, bt, [0], [0, T], x, lg, gain) == 0
+    rows = gather_rows(pool.rows, bt, 0, ratio, 0, T // ratio)
+    W = coff * ratio
+    ids = np.array(sorted(set([0, 1, 2, T // ratio - 1] + list(np.random.default_rng(ratio).integers(0, T // ratio, 12)))))
+    xw = np.zeros((len(ids), W, D), np.uint16)
+    lw = None if lg is None else np.zeros((len(ids), W, coff), np.float32)
+    for m, i in enumerate(ids):
+        for k in range(W):
+            t = ratio * (i + 1) - W + k
+            if t >= 0:
+                xw[m, k] = x[t]
+                if lw is not None:
+                    lw[m, k] = lg[t]
+    got = orc.compress_rows(ratio, coff, D, 32, THETA, dt, ids, xw, lw, gain)
+    assert np.array_equal(got, rows[ids])
