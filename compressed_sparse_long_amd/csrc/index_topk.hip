@@ -24,6 +24,10 @@ namespace csl {
 
 namespace {
 
+// 64-entry units per wave in the score kernel (the score row stride is a
+// multiple of 2048 = 8 waves' worth of units, so every launch divides evenly).
+constexpr int kScoreUnits = 4;
+
 __device__ __forceinline__ bool query_ok(const IndexArgs& a, int n, int& s, int64_t& p) {
     s = a.q_seq[n];
     p = a.q_pos[n];
@@ -35,9 +39,14 @@ __device__ __forceinline__ int64_t visible(const IndexArgs& a, int64_t p) {
     return nv < a.stride ? nv : a.stride;
 }
 
-template <int DI>
+template <int DI, int U>
 __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
-    constexpr int KS = DI / 32;
+    constexpr int KS = DI / 32;          // MFMA k-steps per row
+    constexpr int RB = DI * 2;           // index row bytes
+    constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
+    constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
+    __shared__ __attribute__((aligned(16))) uint8_t s_unit[4][64 * LROW];
     const int n = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -48,58 +57,84 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
         return;
     }
     const int64_t nv = visible(a, p);
-    const int64_t e0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
-    if (e0 >= nv) return;
-    float* out = a.scores + (int64_t)n * a.stride + e0;
-    const int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, s, e0 * 4);
-    if (pg < 0) {
-        if (lane == 0) raise_error(a.err, kErrPage);
-        if (e0 + lane < nv) out[lane] = -INFINITY;
-        return;
-    }
-    const uint8_t* base = a.rows + (int64_t)pg * 64 * (DI * 2);
+    // the wave's U consecutive 64-entry units; unit u is block u of the sequence
+    const int64_t u0 = ((int64_t)blockIdx.x * 4 + wave) * U;
+    if (u0 * 64 >= nv) return;
+    int32_t mypg = 0;  // lane j < U: page of unit u0 + j (-1 unmapped)
+    if (lane < U && (u0 + lane) * 64 < nv) mypg = page_of(a.bt, a.max_blocks, a.num_pages, s, (u0 + lane) * 256);
 
-    // B operands: the wave's 64 entries as 4 tiles of 16, issued first
-    bf16x8 kb[4][KS];
+    // A unit (64 rows) streams in with contiguous 1 KiB loads (lane l takes
+    // chunk l % CPR of row l / CPR), non-temporal since every row is read once
+    // per step; it then passes through the wave's own LDS slice to reach the
+    // MFMA operand layout, whose direct loads (16 rows x 64 B per instruction)
+    // stream measurably slower.  The next unit is in flight meanwhile.  An
+    // unmapped or invisible unit reads page 0 (always allocated); its scores
+    // are not used.
+    u32x4 ld[NLD];
+    auto issue = [&](int j) {
+        const int32_t pg = __shfl(mypg, j);
+        const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * 64 * RB);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kb[t][ks] = *reinterpret_cast<const bf16x8*>(base + (16 * t + r16) * (DI * 2) + (32 * ks + 8 * g) * 2);
+        for (int q = 0; q < NLD; ++q) ld[q] = __builtin_nontemporal_load(base + q * 64 + lane);
+    };
+    issue(0);
 
-    // A operands: the query's heads (rows beyond n_heads are zero)
+    // A operands: the query's heads (rows beyond n_heads are zero); head weights
     bf16x8 qa[KS];
     const bool hv = r16 < a.n_heads;
+    const uint16_t* qrow = a.q_idx + ((int64_t)n * a.n_heads + (hv ? r16 : 0)) * DI;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (hv) v = *reinterpret_cast<const u32x4*>(a.q_idx + ((int64_t)n * a.n_heads + r16) * DI + 32 * ks + 8 * g);
+        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+        if (!hv) v = u32x4{0u, 0u, 0u, 0u};
         qa[ks] = __builtin_bit_cast(bf16x8, v);
     }
     float wv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int h = 4 * g + i;
-        wv[i] = h < a.n_heads ? a.w[(int64_t)n * a.n_heads + h] : 0.f;
+        const int h = 4 * g + i;
+        const float x = a.w[(int64_t)n * a.n_heads + (h < a.n_heads ? h : 0)];
+        wv[i] = h < a.n_heads ? x : 0.f;
     }
 
-    float sc[4];
+    uint8_t* su = s_unit[wave];
+    constexpr int RPL = 64 / CPR;  // rows per 1 KiB load
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < U; ++j) {
+        // this unit into LDS (in-order LDS ops of one wave: the reads of the
+        // previous unit have been issued before these writes)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb[t][ks], acc, 0, 0, 0);
-        // acc[i] = <q_head(4g+i), key(16t + r16)>
-        float v = 0.f;
+        for (int q = 0; q < NLD; ++q)
+            *reinterpret_cast<u32x4*>(su + (q * RPL + lane / CPR) * LROW + (lane % CPR) * 16) = ld[q];
+        if (j + 1 < U) issue(j + 1);
+        float sc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[i], 0.f), v);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        sc[t] = v;
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kb = *reinterpret_cast<const bf16x8*>(su + (16 * t + r16) * LROW + (4 * ks + g) * 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc, 0, 0, 0);
+            }
+            // acc[i] = <q_head(4g+i), key(16t + r16)>
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[i], 0.f), v);
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            sc[t] = v;
+        }
+        const int64_t e0 = (u0 + j) * 64;
+        if (e0 >= nv) break;
+        const int32_t pg = __shfl(mypg, j);
+        // lane l stores entry e0 + l, i.e. tile g, column r16
+        float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+        if (pg < 0) {
+            if (lane == 0) raise_error(a.err, kErrPage);
+            mine = -INFINITY;
+        }
+        if (e0 + lane < nv) a.scores[(int64_t)n * a.stride + e0 + lane] = mine;
     }
-    // lane l stores entry e0 + l, i.e. tile g, column r16
-    float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
-    if (e0 + lane < nv) out[lane] = mine;
 }
 
 // Order-preserving 32-bit key of an fp32 score (+0 and -0 share one key).
@@ -613,11 +648,12 @@ __global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
 
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
-    dim3 grid((unsigned)(a.stride / 256), (unsigned)a.num_q);
+    constexpr int U = kScoreUnits;
+    dim3 grid((unsigned)(a.stride / (256 * U)), (unsigned)a.num_q);
     switch (a.dim) {
-        case 32: launch_kernel(ev, true, true, index_score_kernel<32>, grid, dim3(256), st, a); break;
-        case 64: launch_kernel(ev, true, true, index_score_kernel<64>, grid, dim3(256), st, a); break;
-        case 128: launch_kernel(ev, true, true, index_score_kernel<128>, grid, dim3(256), st, a); break;
+        case 32: launch_kernel(ev, true, true, index_score_kernel<32, U>, grid, dim3(256), st, a); break;
+        case 64: launch_kernel(ev, true, true, index_score_kernel<64, U>, grid, dim3(256), st, a); break;
+        case 128: launch_kernel(ev, true, true, index_score_kernel<128, U>, grid, dim3(256), st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
