@@ -147,16 +147,19 @@ int64_t index_stride(int64_t max_q_pos) {
     return (nv + 2047) / 2048 * 2048;
 }
 
-// First-stage candidates per 2048-id chunk for the two-stage top-k: the
-// expected share of the top k in a chunk plus five standard deviations (a
-// chunk holding more only costs the exact fallback), 0 = single-pass select.
+// First-stage candidates per 1024-id chunk for the two-stage top-k (the score
+// kernel's workgroup selects them): the expected share of the top k in a chunk
+// plus five standard deviations (a chunk holding more only costs the exact
+// fallback), at most 8192 per query; 0 = single-pass select.
+constexpr int kIndexChunk = 1024;
+
 int index_local_k(int64_t max_q_pos, int k) {
     const int64_t nv = max_q_pos / 4;
     if (nv <= k) return 0;
-    const double expect = (double)k * 2048.0 / (double)nv;
-    int kl = (int)std::ceil((expect + 5.0 * std::sqrt(expect) + 4.0) / 16.0) * 16;
-    kl = kl < 64 ? 64 : (kl > 1024 ? 1024 : kl);
-    const int64_t nchunks = index_stride(max_q_pos) / 2048;
+    const double expect = (double)k * kIndexChunk / (double)nv;
+    int kl = (int)std::ceil((expect + 5.0 * std::sqrt(expect) + 4.0) / 8.0) * 8;
+    kl = kl < 32 ? 32 : (kl > kIndexChunk ? kIndexChunk : kl);
+    const int64_t nchunks = index_stride(max_q_pos) / kIndexChunk;
     return nchunks * kl <= 8192 ? kl : 0;
 }
 
@@ -353,7 +356,7 @@ csl_status csl_compress_insert(const csl_pool* pool, const csl_pages* pages, con
 
 size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k) {
     if (num_q <= 0 || max_q_pos < 0 || k < 1) return 0;
-    const int64_t stride = index_stride(max_q_pos), nchunks = stride / 2048;
+    const int64_t stride = index_stride(max_q_pos), nchunks = stride / kIndexChunk;
     const int kl = index_local_k(max_q_pos, k);
     return (size_t)num_q * ((size_t)stride * sizeof(float) + (kl > 0 ? (size_t)nchunks * (kl + 1) * 8 : 0));
 }
@@ -396,8 +399,9 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     a.err = err;
     a.max_q_pos = max_q_pos;
     a.stride = index_stride(max_q_pos);
-    a.nchunks = (int)(a.stride / 2048);
+    a.nchunks = (int)(a.stride / kIndexChunk);
     a.kl = index_local_k(max_q_pos, k);
+    a.tiled = index_use_tiled(num_q) ? 1 : 0;
     a.cand = reinterpret_cast<uint2*>(a.scores + (size_t)num_q * a.stride);
     a.c_next = a.cand + (size_t)num_q * a.nchunks * a.kl;
     a.num_q = num_q;

@@ -48,8 +48,9 @@ struct IndexArgs {
     int64_t max_q_pos;
     int64_t stride;  // entries per query row of `scores` (multiple of 2048)
     int num_q, n_heads, dim, k, num_pages, num_seqs, max_blocks;
-    int nchunks;     // stride / 2048
+    int nchunks;     // stride / 1024 (first-stage chunks)
     int kl;          // first-stage candidates per chunk (0: single-pass select)
+    int tiled;       // query-blocked score kernel (many queries) instead of one query per row
 };
 
 struct AttnArgs {
@@ -93,6 +94,7 @@ inline void launch_kernel(const LaunchEvents& ev, bool first, bool last, F kerne
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+bool index_use_tiled(int num_q);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 

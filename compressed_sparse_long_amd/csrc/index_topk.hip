@@ -39,104 +39,6 @@ __device__ __forceinline__ int64_t visible(const IndexArgs& a, int64_t p) {
     return nv < a.stride ? nv : a.stride;
 }
 
-template <int DI, int U>
-__global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
-    constexpr int KS = DI / 32;          // MFMA k-steps per row
-    constexpr int RB = DI * 2;           // index row bytes
-    constexpr int CPR = RB / 16;         // 16-byte chunks per row
-    constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
-    constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
-    __shared__ __attribute__((aligned(16))) uint8_t s_unit[4][64 * LROW];
-    const int n = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, g = lane >> 4;
-    int s;
-    int64_t p;
-    if (!query_ok(a, n, s, p)) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) raise_error(a.err, (s < 0 || s >= a.num_seqs) ? kErrSeq : kErrPos);
-        return;
-    }
-    const int64_t nv = visible(a, p);
-    // the wave's U consecutive 64-entry units; unit u is block u of the sequence
-    const int64_t u0 = ((int64_t)blockIdx.x * 4 + wave) * U;
-    if (u0 * 64 >= nv) return;
-    int32_t mypg = 0;  // lane j < U: page of unit u0 + j (-1 unmapped)
-    if (lane < U && (u0 + lane) * 64 < nv) mypg = page_of(a.bt, a.max_blocks, a.num_pages, s, (u0 + lane) * 256);
-
-    // A unit (64 rows) streams in with contiguous 1 KiB loads (lane l takes
-    // chunk l % CPR of row l / CPR), non-temporal since every row is read once
-    // per step; it then passes through the wave's own LDS slice to reach the
-    // MFMA operand layout, whose direct loads (16 rows x 64 B per instruction)
-    // stream measurably slower.  The next unit is in flight meanwhile.  An
-    // unmapped or invisible unit reads page 0 (always allocated); its scores
-    // are not used.
-    u32x4 ld[NLD];
-    auto issue = [&](int j) {
-        const int32_t pg = __shfl(mypg, j);
-        const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * 64 * RB);
-#pragma unroll
-        for (int q = 0; q < NLD; ++q) ld[q] = __builtin_nontemporal_load(base + q * 64 + lane);
-    };
-    issue(0);
-
-    // A operands: the query's heads (rows beyond n_heads are zero); head weights
-    bf16x8 qa[KS];
-    const bool hv = r16 < a.n_heads;
-    const uint16_t* qrow = a.q_idx + ((int64_t)n * a.n_heads + (hv ? r16 : 0)) * DI;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
-        if (!hv) v = u32x4{0u, 0u, 0u, 0u};
-        qa[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-    float wv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        const float x = a.w[(int64_t)n * a.n_heads + (h < a.n_heads ? h : 0)];
-        wv[i] = h < a.n_heads ? x : 0.f;
-    }
-
-    uint8_t* su = s_unit[wave];
-    constexpr int RPL = 64 / CPR;  // rows per 1 KiB load
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-        // this unit into LDS (in-order LDS ops of one wave: the reads of the
-        // previous unit have been issued before these writes)
-#pragma unroll
-        for (int q = 0; q < NLD; ++q)
-            *reinterpret_cast<u32x4*>(su + (q * RPL + lane / CPR) * LROW + (lane % CPR) * 16) = ld[q];
-        if (j + 1 < U) issue(j + 1);
-        float sc[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 kb = *reinterpret_cast<const bf16x8*>(su + (16 * t + r16) * LROW + (4 * ks + g) * 16);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc, 0, 0, 0);
-            }
-            // acc[i] = <q_head(4g+i), key(16t + r16)>
-            float v = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[i], 0.f), v);
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            sc[t] = v;
-        }
-        const int64_t e0 = (u0 + j) * 64;
-        if (e0 >= nv) break;
-        const int32_t pg = __shfl(mypg, j);
-        // lane l stores entry e0 + l, i.e. tile g, column r16
-        float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
-        if (pg < 0) {
-            if (lane == 0) raise_error(a.err, kErrPage);
-            mine = -INFINITY;
-        }
-        if (e0 + lane < nv) a.scores[(int64_t)n * a.stride + e0 + lane] = mine;
-    }
-}
-
 // Order-preserving 32-bit key of an fp32 score (+0 and -0 share one key).
 __device__ __forceinline__ uint32_t score_key(float f) {
     uint32_t u = __float_as_uint(f + 0.0f);
@@ -281,7 +183,7 @@ constexpr int kCandCap = 4096;  // boundary-bin keys kept in LDS
 //     is the one with #(> T) < rank <= #(>= T).
 // If fewer than `want` keys fall in the window, or b is crowded, an exact
 // 3-round radix select over all keys is used instead.
-template <int NT, int KPT>
+template <int NT, int KPT, int CAP = kCandCap>
 __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
                                  uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
     constexpr int NW = NT / 64;
@@ -303,7 +205,7 @@ __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uin
         if (((vmask >> i) & 1u) && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
     __syncthreads();
     const uint32_t tot = find_bin<NT>(s_hist, want, 2048, s_wave, s_sel);
-    if (tot >= want && s_sel[2] <= (uint32_t)kCandCap) {
+    if (tot >= want && s_sel[2] <= (uint32_t)CAP) {
         const uint32_t bsel = s_sel[0], rank = s_sel[1], cnt = s_sel[2];
         uint32_t mine = 0;
 #pragma unroll
@@ -379,16 +281,16 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&key)[KPT], uint32
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kRegKeys = 32;                     // keys per thread held in registers
-constexpr int kRegMax = kRegKeys * kSelThreads;  // 32768 candidates
 
-// Full select for one query by one 1024-thread workgroup: thread t holds the
-// scores of ids [32t, 32t+32) in registers (nv <= 32768), else the keys are
+// Full select for one query by one NT-thread workgroup: thread t holds the
+// scores of ids [32t, 32t+32) in registers (nv <= 32*NT), else the keys are
 // read from global memory in radix rounds.  Used when the two-stage select
 // does not apply or its check fails.
+template <int NT>
 __device__ __forceinline__ void select_full(const float* sc, int64_t nv, int k, int32_t* out, float* kth, uint32_t* s_hist,
                             uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
     const int tid = threadIdx.x;
-    if (nv <= kRegMax) {
+    if (nv <= (int64_t)kRegKeys * NT) {
         const int64_t e0 = (int64_t)tid * kRegKeys;
         uint32_t key[kRegKeys];
         if (e0 + kRegKeys <= nv) {
@@ -408,9 +310,9 @@ __device__ __forceinline__ void select_full(const float* sc, int64_t nv, int k, 
         const int64_t nm = nv - e0 < 0 ? 0 : (nv - e0 < kRegKeys ? nv - e0 : kRegKeys);
         const uint32_t vmask = nm >= 32 ? 0xffffffffu : ((1u << nm) - 1u);
         uint32_t rem;
-        const uint32_t T = block_select<kSelThreads, kRegKeys>(key, vmask, (uint32_t)k, &rem, s_hist, s_wave, s_sel,
+        const uint32_t T = block_select<NT, kRegKeys>(key, vmask, (uint32_t)k, &rem, s_hist, s_wave, s_sel,
                                                                s_cand);
-        emit_selected<kSelThreads, kRegKeys>(key, vmask, T, rem, k, [&](int i) { return (int32_t)(e0 + i); }, out,
+        emit_selected<NT, kRegKeys>(key, vmask, T, rem, k, [&](int i) { return (int32_t)(e0 + i); }, out,
                                              s_wave, s_sel, true);
         if (tid == 0 && kth) *kth = key_score(T);
         return;
@@ -418,9 +320,10 @@ __device__ __forceinline__ void select_full(const float* sc, int64_t nv, int k, 
     // long lists: radix rounds and an ordered emission over global memory;
     // wave w owns ids [w*seg, (w+1)*seg)
     uint32_t rem;
-    const uint32_t T = radix_select<kSelThreads>(GlobalKeys{sc}, nv, (uint32_t)k, &rem, s_hist, s_wave, s_sel);
+    const uint32_t T = radix_select<NT>(GlobalKeys{sc}, nv, (uint32_t)k, &rem, s_hist, s_wave, s_sel);
     const int lane = tid & 63, wave = tid >> 6;
-    const int64_t seg = ((nv + kSelWaves - 1) / kSelWaves + 63) & ~(int64_t)63;
+    constexpr int NW = NT / 64;
+    const int64_t seg = ((nv + NW - 1) / NW + 63) & ~(int64_t)63;
     const int64_t lo = (int64_t)wave * seg;
     const int64_t hi = lo + seg < nv ? lo + seg : nv;
     uint32_t n_gt = 0, n_eq = 0;
@@ -430,15 +333,15 @@ __device__ __forceinline__ void select_full(const float* sc, int64_t nv, int k, 
         n_gt += __popcll(__ballot(in && key > T));
         n_eq += __popcll(__ballot(in && key == T));
     }
-    uint32_t* s_cnt = s_cand;  // [2][kSelWaves]
+    uint32_t* s_cnt = s_cand;  // [2][NW]
     if (lane == 0) {
         s_cnt[wave] = n_gt;
-        s_cnt[kSelWaves + wave] = n_eq;
+        s_cnt[NW + wave] = n_eq;
     }
     __syncthreads();
     uint32_t out_pos = 0, eq_seen = 0;
     for (int w = 0; w < wave; ++w) {
-        const uint32_t eq_w = s_cnt[kSelWaves + w];
+        const uint32_t eq_w = s_cnt[NW + w];
         const uint32_t take_eq = eq_seen >= rem ? 0u : (eq_w < rem - eq_seen ? eq_w : rem - eq_seen);
         out_pos += s_cnt[w] + take_eq;
         eq_seen += eq_w;
@@ -492,82 +395,82 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
     int32_t* out = a.topk + (int64_t)n * a.k;
     float* kth = a.kth ? a.kth + n : nullptr;
     if (nv <= a.k) select_all(sc, nv, a.k, out, kth, s_min);
-    else select_full(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+    else select_full<kSelThreads>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
 }
 
 // ---------------------------------------------------------------- two-stage select
 
-constexpr int kChunk = 2048;        // ids per first-stage workgroup
-constexpr int kLocalThreads = 256;  // 8 ids per thread
-constexpr int kMergeSlots = 8;      // candidates per thread in the second stage (8192 per query)
+// ---------------------------------------------------------------- scores (+ first stage)
 
-// Stage 1: one 256-thread workgroup per (query, chunk of 2048 ids): the chunk's
-// first `kl` ids in (score desc, id asc) order -- its local top-kl, written in
-// ascending id order -- and the (kl+1)-th, whose position the merge checks.
-__global__ void __launch_bounds__(kLocalThreads) topk_local_kernel(IndexArgs a) {
-    __shared__ uint32_t s_hist[2048];
-    __shared__ uint32_t s_cand[kCandCap];
-    __shared__ uint32_t s_wave[kLocalThreads / 64];
-    __shared__ uint32_t s_sel[8 + kLocalThreads / 64];
-    const int n = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
-    int s;
-    int64_t p;
-    const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
-    const int64_t base = (int64_t)blk * kChunk;
-    if (base >= nv || nv <= a.k) return;  // the merge reads chunks below nv only
-    const float* sc = a.scores + (int64_t)n * a.stride + base;
-    const int64_t nvalid = nv - base < kChunk ? nv - base : kChunk;
+// index_score_kernel<DI, U, LOCAL> -- the HBM stream of the decode step.  A
+// workgroup (4 waves) scores 4*U*64 consecutive entries of one query; a wave
+// streams U consecutive 64-entry units (one paged block each).  A unit comes
+// in with contiguous 1 KiB loads (lane l takes chunk l % CPR of row l / CPR),
+// non-temporal since every row is read once per step, then passes through
+// the wave's own LDS slice to reach the MFMA operand layout, whose direct
+// loads (16 rows x 64 B per instruction) stream measurably slower.  The next
+// unit is in flight meanwhile.  qI[16 heads x d] . K^T[d x 16 entries] is one
+// v_mfma_f32_16x16x32_bf16 per 32 dims; ReLU, the head weight and the head
+// sum are fused on the accumulators (4 heads in-lane, 2 cross-lane steps).
+// An unmapped or invisible unit reads page 0 (always allocated) and its
+// scores are not used; an unmapped unit scores -inf and is flagged.
+//
+// With LOCAL (U = 4: a workgroup = one 1024-entry chunk), the workgroup then
+// reuses its LDS for the first stage of the top-k: the chunk's first kl ids in
+// (score desc, id asc) order -- written in ascending id order -- and the
+// (kl+1)-th, whose position the merge checks.
+constexpr int kChunk = 1024;        // ids per first-stage chunk (one workgroup of the score kernel)
+constexpr int kMergeSlots = 8;      // candidates per merge thread
+
+// First stage of the two-stage top-k over one 1024-id chunk of query n, by a
+// 256-thread workgroup whose thread t holds the keys of ids base + 4t .. 4t+3
+// (ids at or past base + nvalid are invalid): the chunk's first kl ids in
+// (score desc, id asc) order, written in ascending id order, and the
+// (kl+1)-th, whose position the merge checks (none if nvalid <= kl).
+__device__ __forceinline__ void chunk_first_stage(const IndexArgs& a, int n, int blk, const uint32_t (&key)[4], int64_t base,
+                                                  int64_t nvalid, uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel,
+                                                  uint32_t* s_cand) {
+    const int tid = threadIdx.x;
     const int kl = a.kl;
     uint2* cand = a.cand + ((int64_t)n * a.nchunks + blk) * kl;
-    const int64_t e0 = (int64_t)tid * 8;
-    uint32_t key[8];
+    uint2* cnext = a.c_next + (int64_t)n * a.nchunks + blk;
+    const int e0 = tid * 4;
     uint32_t vmask = 0;
-    if (e0 + 8 <= nvalid) {
-        const float4 v0 = reinterpret_cast<const float4*>(sc + e0)[0];
-        const float4 v1 = reinterpret_cast<const float4*>(sc + e0)[1];
-        key[0] = score_key(v0.x); key[1] = score_key(v0.y); key[2] = score_key(v0.z); key[3] = score_key(v0.w);
-        key[4] = score_key(v1.x); key[5] = score_key(v1.y); key[6] = score_key(v1.z); key[7] = score_key(v1.w);
-        vmask = 0xffu;
-    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            key[i] = e0 + i < nvalid ? score_key(sc[e0 + i]) : 0u;
-            vmask |= (e0 + i < nvalid ? 1u : 0u) << i;
-        }
-    }
+    for (int i = 0; i < 4; ++i) vmask |= (e0 + i < nvalid ? 1u : 0u) << i;
     if (nvalid <= kl) {
         // every id is a candidate; no (kl+1)-th element
         uint32_t tot;
-        uint32_t pos = block_excl_scan<kLocalThreads>((uint32_t)__popc(vmask), s_wave, tot);
+        uint32_t pos = block_excl_scan<256>((uint32_t)__popc(vmask), s_wave, tot);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
             if ((vmask >> i) & 1u) cand[pos++] = make_uint2(key[i], (uint32_t)(base + e0 + i));
-        for (int j = (int)tot + tid; j < kl; j += kLocalThreads) cand[j] = make_uint2(0u, 0xffffffffu);
-        if (tid == 0) a.c_next[(int64_t)n * a.nchunks + blk] = make_uint2(0u, 0xffffffffu);
+        for (int j = (int)tot + tid; j < kl; j += 256) cand[j] = make_uint2(0u, 0xffffffffu);
+        if (tid == 0) *cnext = make_uint2(0u, 0xffffffffu);
         return;
     }
     uint32_t rem;
-    const uint32_t T = block_select<kLocalThreads, 8>(key, vmask, (uint32_t)kl + 1, &rem, s_hist, s_wave, s_sel, s_cand);
-    // the top kl+1 = keys > T and the first `rem` copies of T; its last copy of T
-    // (id order) is the (kl+1)-th element and is not a candidate
+    const uint32_t T = block_select<256, 4, kChunk>(key, vmask, (uint32_t)kl + 1, &rem, s_hist, s_wave, s_sel, s_cand);
+    // the top kl+1 = keys > T and the first `rem` copies of T; its last copy
+    // of T (id order) is the (kl+1)-th element and is not a candidate
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const bool v = (vmask >> i) & 1u;
         ngt += (v && key[i] > T) ? 1u : 0u;
         neq += (v && key[i] == T) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t pre = block_excl_scan<kLocalThreads>(ngt | (neq << 16), s_wave, tot);
+    const uint32_t pre = block_excl_scan<256>(ngt | (neq << 16), s_wave, tot);
     uint32_t eq_before = pre >> 16;
     uint32_t pos = (pre & 0xffffu) + (eq_before < rem - 1 ? eq_before : rem - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         if (!((vmask >> i) & 1u)) continue;
         bool sel = key[i] > T;
         if (key[i] == T) {
             sel = eq_before + 1 < rem;
-            if (eq_before + 1 == rem) a.c_next[(int64_t)n * a.nchunks + blk] = make_uint2(T, (uint32_t)(base + e0 + i));
+            if (eq_before + 1 == rem) *cnext = make_uint2(T, (uint32_t)(base + e0 + i));
             ++eq_before;
         }
         if (sel) {
@@ -577,18 +480,315 @@ __global__ void __launch_bounds__(kLocalThreads) topk_local_kernel(IndexArgs a) 
     }
 }
 
-// Stage 2: one 1024-thread workgroup per query.  The chunks' candidate lists,
-// concatenated, are in ascending id order; thread t holds slots [8t, 8t+8).
-// The top k of the candidates (score desc, id asc) is exact when every chunk's
-// (kl+1)-th element comes after the k-th selected element in that order: every
-// id outside the candidates then comes after it too.  Otherwise (or when the
-// lists do not fit) the full select runs on the scores.
-__global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
+// Stand-alone first stage (after the query-blocked score kernel): one
+// 256-thread workgroup per (query, chunk), keys read from the score row.
+__global__ void __launch_bounds__(256) topk_local_kernel(IndexArgs a) {
+    __shared__ uint32_t s_hist[2048];
+    __shared__ uint32_t s_cand[kChunk];
+    __shared__ uint32_t s_wave[4];
+    __shared__ uint32_t s_sel[12];
+    const int n = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+    int s;
+    int64_t p;
+    const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
+    const int64_t base = (int64_t)blk * kChunk;
+    if (base >= nv || nv <= a.k) return;  // uniform; the merge reads chunks below nv only
+    const int64_t nvalid = nv - base < kChunk ? nv - base : kChunk;
+    const float* sc = a.scores + (int64_t)n * a.stride + base;
+    uint32_t key[4];
+    if (tid * 4 + 4 <= nvalid) {
+        const float4 v = reinterpret_cast<const float4*>(sc)[tid];
+        key[0] = score_key(v.x);
+        key[1] = score_key(v.y);
+        key[2] = score_key(v.z);
+        key[3] = score_key(v.w);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) key[i] = tid * 4 + i < nvalid ? score_key(sc[tid * 4 + i]) : 0u;
+    }
+    chunk_first_stage(a, n, blk, key, base, nvalid, s_hist, s_wave, s_sel, s_cand);
+}
+
+template <int DI, int U, bool LOCAL>
+__global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
+    constexpr int KS = DI / 32;          // MFMA k-steps per row
+    constexpr int RB = DI * 2;           // index row bytes
+    constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
+    constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
+    constexpr int kUnitBytes = 4 * 64 * LROW;
+    constexpr int kSelBytes = (kChunk + 2048 + kChunk + 16) * 4;
+    static_assert(!LOCAL || 4 * U * 64 == kChunk, "a first-stage chunk is one workgroup");
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[kUnitBytes > kSelBytes ? kUnitBytes : kSelBytes];
+    const int n = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    int s;
+    int64_t p;
+    if (!query_ok(a, n, s, p)) {
+        if (blockIdx.x == 0 && tid == 0) raise_error(a.err, (s < 0 || s >= a.num_seqs) ? kErrSeq : kErrPos);
+        return;
+    }
+    const int64_t nv = visible(a, p);
+    const int64_t wg0 = (int64_t)blockIdx.x * 4 * U * 64;  // first entry of the workgroup
+    if (wg0 >= nv) return;                                   // uniform over the workgroup
+    // the wave's U consecutive 64-entry units; unit u is block u of the sequence
+    const int64_t u0 = ((int64_t)blockIdx.x * 4 + wave) * U;
+    float mine_u[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) mine_u[j] = -INFINITY;
+    if (u0 * 64 < nv) {
+        int32_t mypg = 0;  // lane j < U: page of unit u0 + j (-1 unmapped)
+        if (lane < U && (u0 + lane) * 64 < nv) mypg = page_of(a.bt, a.max_blocks, a.num_pages, s, (u0 + lane) * 256);
+        u32x4 ld[NLD];
+        auto issue = [&](int j) {
+            const int32_t pg = __shfl(mypg, j);
+            const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * 64 * RB);
+#pragma unroll
+            for (int q = 0; q < NLD; ++q) ld[q] = __builtin_nontemporal_load(base + q * 64 + lane);
+        };
+        issue(0);
+
+        // A operands: the query's heads (rows beyond n_heads are zero); head weights
+        bf16x8 qa[KS];
+        const bool hv = r16 < a.n_heads;
+        const uint16_t* qrow = a.q_idx + ((int64_t)n * a.n_heads + (hv ? r16 : 0)) * DI;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+            if (!hv) v = u32x4{0u, 0u, 0u, 0u};
+            qa[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+        float wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * g + i;
+            const float x = a.w[(int64_t)n * a.n_heads + (h < a.n_heads ? h : 0)];
+            wv[i] = h < a.n_heads ? x : 0.f;
+        }
+
+        uint8_t* su = s_mem + wave * 64 * LROW;
+        constexpr int RPL = 64 / CPR;  // rows per 1 KiB load
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            // this unit into LDS (in-order LDS ops of one wave: the reads of the
+            // previous unit have been issued before these writes)
+#pragma unroll
+            for (int q = 0; q < NLD; ++q)
+                *reinterpret_cast<u32x4*>(su + (q * RPL + lane / CPR) * LROW + (lane % CPR) * 16) = ld[q];
+            if (j + 1 < U) issue(j + 1);
+            float sc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(su + (16 * t + r16) * LROW + (4 * ks + g) * 16);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc, 0, 0, 0);
+                }
+                // acc[i] = <q_head(4g+i), key(16t + r16)>
+                float v = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[i], 0.f), v);
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                sc[t] = v;
+            }
+            const int64_t e0 = (u0 + j) * 64;
+            if (e0 >= nv) break;
+            const int32_t pg = __shfl(mypg, j);
+            // lane l stores entry e0 + l, i.e. tile g, column r16
+            float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+            if (pg < 0) {
+                if (lane == 0) raise_error(a.err, kErrPage);
+                mine = -INFINITY;
+            }
+            mine_u[j] = mine;
+            if (e0 + lane < nv) a.scores[(int64_t)n * a.stride + e0 + lane] = mine;
+        }
+    }
+    if constexpr (LOCAL) {
+        if (nv <= a.k) return;  // uniform: the merge takes every visible id
+        // ---- first stage of the top-k over this chunk
+        __syncthreads();  // every wave is done with its unit slice
+        uint32_t* s_keys = reinterpret_cast<uint32_t*>(s_mem);  // [kChunk], entry order
+        uint32_t* s_hist = s_keys + kChunk;                     // [2048]
+        uint32_t* s_cand = s_hist + 2048;                       // [kChunk]
+        uint32_t* s_wave = s_cand + kChunk;                     // [4]
+        uint32_t* s_sel = s_wave + 4;                           // [12]
+#pragma unroll
+        for (int j = 0; j < U; ++j) s_keys[(wave * U + j) * 64 + lane] = score_key(mine_u[j]);
+        __syncthreads();
+        const int64_t nvalid = nv - wg0 < kChunk ? nv - wg0 : kChunk;
+        const uint4 kv = reinterpret_cast<const uint4*>(s_keys)[tid];
+        const uint32_t key[4] = {kv.x, kv.y, kv.z, kv.w};
+        chunk_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_wave, s_sel, s_cand);
+    }
+}
+// index_score_tiled_kernel<DI> -- scores for many queries (prefill chunks).
+// A workgroup takes a block of 16 queries and one 1024-entry chunk.  The
+// chunk's pages of the queries' sequence stream once through double-buffered
+// LDS (contiguous 16-byte loads by all 256 threads); each wave contracts its 4
+// queries' heads (A operands, registers) against every staged page (B = 16
+// entries per MFMA, from LDS), so one page load feeds 16 queries x 16 heads.
+// The ReLU / head-weight / head-sum epilogue is the decode kernel's.  Queries
+// of another sequence inside the block are taken in further passes over the
+// chunk, one per sequence.
+constexpr int kTiledQ = 16;           // queries per workgroup
+constexpr int kTiledMinQueries = 64;  // calls with at least this many queries use the tiled kernel
+
+template <int DI>
+__global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
+    constexpr int KS = DI / 32, RB = DI * 2, CPR = RB / 16, LROW = RB + 16;
+    constexpr int UNIT = 64 * RB;         // bytes of a 64-entry page
+    constexpr int LPT = UNIT / 16 / 256;  // 16-byte loads per thread per page
+    static_assert(LPT >= 1 && UNIT == LPT * 16 * 256, "a page is a whole number of workgroup loads");
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][64 * LROW];
+    __shared__ int32_t s_qs[kTiledQ];
+    __shared__ int64_t s_qnv[kTiledQ];
+    __shared__ int32_t s_pg[kChunk / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int blk = blockIdx.x;
+    const int64_t c0 = (int64_t)blk * kChunk;
+    const int q0 = blockIdx.y * kTiledQ;
+    if (tid < kTiledQ) {
+        const int n = q0 + tid;
+        int s = -1;
+        int64_t p = 0, nv = 0;
+        if (n < a.num_q) {
+            if (query_ok(a, n, s, p)) {
+                nv = visible(a, p);
+            } else {
+                if (blk == 0) raise_error(a.err, (s < 0 || s >= a.num_seqs) ? kErrSeq : kErrPos);
+                s = -1;
+            }
+        }
+        s_qs[tid] = s;
+        s_qnv[tid] = nv;
+    }
+    __syncthreads();
+
+    // the wave's 4 queries: A operands (rows beyond n_heads are zero) and head weights
+    bf16x8 qa[4][KS];
+    float wv[4][4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+        const int n = q0 + 4 * wave + qq;
+        const bool qv = n < a.num_q && s_qs[4 * wave + qq] >= 0;
+        const int nn = qv ? n : 0;
+        const bool hv = qv && r16 < a.n_heads;
+        const uint16_t* qrow = a.q_idx + ((int64_t)nn * a.n_heads + (r16 < a.n_heads ? r16 : 0)) * DI;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+            if (!hv) v = u32x4{0u, 0u, 0u, 0u};
+            qa[qq][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * g + i;
+            const float x = a.w[(int64_t)nn * a.n_heads + (h < a.n_heads ? h : 0)];
+            wv[qq][i] = (qv && h < a.n_heads) ? x : 0.f;
+        }
+    }
+
+    uint32_t done = 0;  // queries handled (the same in every thread)
+    for (;;) {
+        // the next sequence: the first query not handled whose visible range reaches this chunk
+        int sg = -1;
+        int64_t nvmax = 0;
+        uint32_t gmask = 0;
+        for (int i = 0; i < kTiledQ; ++i) {
+            if ((done >> i) & 1u) continue;
+            const int si = s_qs[i];
+            const int64_t nvi = s_qnv[i];
+            if (si < 0 || nvi <= c0) {
+                done |= 1u << i;
+                continue;
+            }
+            if (sg < 0) sg = si;
+            if (si == sg) {
+                gmask |= 1u << i;
+                nvmax = nvi > nvmax ? nvi : nvmax;
+            }
+        }
+        if (sg < 0) break;
+        done |= gmask;
+        const int64_t ce = c0 + kChunk < nvmax ? c0 + kChunk : nvmax;
+        const int npages = (int)((ce - c0 + 63) / 64);
+        __syncthreads();  // the previous pass's reads of s_pg and s_k are done
+        if (tid < npages) s_pg[tid] = page_of(a.bt, a.max_blocks, a.num_pages, sg, (c0 + 64 * tid) * 4);
+        __syncthreads();
+        u32x4 st[LPT];
+        auto load_page = [&](int j) {
+            const int32_t pg = s_pg[j];
+            const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT);
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) st[q] = __builtin_nontemporal_load(base + q * 256 + tid);
+        };
+        auto store_page = [&](int b) {
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) {
+                const int c = q * 256 + tid;  // 16-byte chunk of the page
+                *reinterpret_cast<u32x4*>(s_k[b] + (c / CPR) * LROW + (c % CPR) * 16) = st[q];
+            }
+        };
+        load_page(0);
+        store_page(0);
+        __syncthreads();
+        for (int j = 0; j < npages; ++j) {
+            if (j + 1 < npages) load_page(j + 1);
+            const uint8_t* sk = s_k[j & 1];
+            const int64_t e0 = c0 + 64 * j;
+            const int32_t pg = s_pg[j];
+            if (pg < 0 && lane == 0 && ((gmask >> (4 * wave)) & 0xfu)) raise_error(a.err, kErrPage);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                bf16x8 kb[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kb[ks] = *reinterpret_cast<const bf16x8*>(sk + (16 * t + r16) * LROW + (4 * ks + g) * 16);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int qi = 4 * wave + qq;
+                    if (!((gmask >> qi) & 1u)) continue;  // uniform over the wave
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qq][ks], kb[ks], acc, 0, 0, 0);
+                    float v = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v = fmaf(wv[qq][i], fmaxf(acc[i], 0.f), v);
+                    v += __shfl_xor(v, 16);
+                    v += __shfl_xor(v, 32);
+                    // every lane group holds the tile's 16 sums; group t stores them
+                    const int64_t e = e0 + 16 * t + r16;
+                    if (g == t && e < s_qnv[qi])
+                        a.scores[(int64_t)(q0 + qi) * a.stride + e] = pg < 0 ? -INFINITY : v;
+                }
+            }
+            if (j + 1 < npages) store_page((j + 1) & 1);
+            __syncthreads();
+        }
+    }
+}
+
+// Stage 2: one NT-thread workgroup per query (8*NT candidate slots).  The
+// chunks' candidate lists, concatenated, are in ascending id order; thread t
+// holds slots [8t, 8t+8).  The top k of the candidates (score desc, id asc)
+// is exact when every chunk's (kl+1)-th element comes after the k-th selected
+// element in that order: every id outside the candidates then comes after it
+// too.  Otherwise, or when the candidates cannot hold k ids (short rows), the
+// full select runs on the score row and overwrites the output.
+template <int NT>
+__global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
+    constexpr int NW = NT / 64;
     __shared__ uint32_t s_hist[2048];
     __shared__ uint32_t s_cand[kCandCap];
-    __shared__ uint32_t s_wave[kSelWaves];
-    __shared__ uint32_t s_sel[8 + kSelWaves];
-    __shared__ float s_min[kSelWaves];
+    __shared__ uint32_t s_wave[NW];
+    __shared__ uint32_t s_sel[8 + NW];
+    __shared__ float s_min[NW];
     __shared__ uint32_t s_fail;
     const int n = blockIdx.x, tid = threadIdx.x;
     int s;
@@ -603,13 +803,15 @@ __global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
     }
     const int nch = (int)((nv + kChunk - 1) / kChunk);
     const int64_t nslots = (int64_t)nch * a.kl;
-    // A chunk of L visible ids yields min(L, kl) candidates; with fewer than k
-    // in all, the candidates cannot hold the top k (short rows, few chunks).
+    // a chunk of L visible ids yields min(L, kl) candidates
     const int64_t ncand = (nv / kChunk) * a.kl + (int64_t)min<int64_t>(a.kl, nv % kChunk);
-    if (nslots > (int64_t)kMergeSlots * kSelThreads || ncand < a.k) {
-        select_full(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+    if (nslots > (int64_t)kMergeSlots * NT || ncand < a.k) {
+        select_full<NT>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
         return;
     }
+    // the chunks' (kl+1)-th elements, fetched beside the candidates
+    const uint2* cnext = a.c_next + (int64_t)n * a.nchunks;
+    const uint2 nx = tid < nch ? cnext[tid] : make_uint2(0u, 0xffffffffu);
     const uint2* cand = a.cand + (int64_t)n * a.nchunks * a.kl;
     uint32_t key[kMergeSlots], id[kMergeSlots], vmask = 0;
 #pragma unroll
@@ -623,24 +825,24 @@ __global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
     }
     if (tid == 0) s_fail = 0;
     uint32_t rem;
-    const uint32_t T = block_select<kSelThreads, kMergeSlots>(key, vmask, (uint32_t)a.k, &rem, s_hist, s_wave, s_sel,
-                                                             s_cand);
-    // the k-th element's id (s_sel[6]) from a counting pass, then the check
-    emit_selected<kSelThreads, kMergeSlots>(key, vmask, T, rem, a.k, [&](int i) { return (int32_t)id[i]; }, out,
-                                            s_wave, s_sel, false);
+    const uint32_t T = block_select<NT, kMergeSlots>(key, vmask, (uint32_t)a.k, &rem, s_hist, s_wave, s_sel, s_cand);
+    // emit, and learn the k-th element's id (s_sel[6]) for the check; a failed
+    // check rewrites every output position
+    emit_selected<NT, kMergeSlots>(key, vmask, T, rem, a.k, [&](int i) { return (int32_t)id[i]; }, out, s_wave, s_sel,
+                                   true);
     __syncthreads();
     const uint32_t idk = s_sel[6];
-    for (int c = tid; c < nch; c += kSelThreads) {
-        const uint2 nx = a.c_next[(int64_t)n * a.nchunks + c];
-        if (nx.y != 0xffffffffu && !(nx.x < T || (nx.x == T && nx.y > idk))) s_fail = 1;
+    bool bad = nx.y != 0xffffffffu && !(nx.x < T || (nx.x == T && nx.y > idk));
+    for (int c = tid + NT; c < nch; c += NT) {
+        const uint2 x = cnext[c];
+        bad |= x.y != 0xffffffffu && !(x.x < T || (x.x == T && x.y > idk));
     }
+    if (bad) s_fail = 1;
     __syncthreads();
     if (s_fail) {
-        select_full(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+        select_full<NT>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
         return;
     }
-    emit_selected<kSelThreads, kMergeSlots>(key, vmask, T, rem, a.k, [&](int i) { return (int32_t)id[i]; }, out,
-                                            s_wave, s_sel, true);
     if (tid == 0 && kth) *kth = key_score(T);
 }
 
@@ -648,27 +850,57 @@ __global__ void __launch_bounds__(kSelThreads) topk_merge_kernel(IndexArgs a) {
 
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
+    if (a.tiled) {
+        dim3 grid((unsigned)(a.stride / kChunk), (unsigned)((a.num_q + kTiledQ - 1) / kTiledQ));
+        switch (a.dim) {
+            case 32: launch_kernel(ev, true, true, index_score_tiled_kernel<32>, grid, dim3(256), st, a); break;
+            case 64: launch_kernel(ev, true, true, index_score_tiled_kernel<64>, grid, dim3(256), st, a); break;
+            case 128: launch_kernel(ev, true, true, index_score_tiled_kernel<128>, grid, dim3(256), st, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     constexpr int U = kScoreUnits;
     dim3 grid((unsigned)(a.stride / (256 * U)), (unsigned)a.num_q);
+    const bool local = a.kl > 0;
     switch (a.dim) {
-        case 32: launch_kernel(ev, true, true, index_score_kernel<32, U>, grid, dim3(256), st, a); break;
-        case 64: launch_kernel(ev, true, true, index_score_kernel<64, U>, grid, dim3(256), st, a); break;
-        case 128: launch_kernel(ev, true, true, index_score_kernel<128, U>, grid, dim3(256), st, a); break;
+        case 32:
+            if (local) launch_kernel(ev, true, true, index_score_kernel<32, U, true>, grid, dim3(256), st, a);
+            else launch_kernel(ev, true, true, index_score_kernel<32, U, false>, grid, dim3(256), st, a);
+            break;
+        case 64:
+            if (local) launch_kernel(ev, true, true, index_score_kernel<64, U, true>, grid, dim3(256), st, a);
+            else launch_kernel(ev, true, true, index_score_kernel<64, U, false>, grid, dim3(256), st, a);
+            break;
+        case 128:
+            if (local) launch_kernel(ev, true, true, index_score_kernel<128, U, true>, grid, dim3(256), st, a);
+            else launch_kernel(ev, true, true, index_score_kernel<128, U, false>, grid, dim3(256), st, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+// With a first stage (kl > 0): the decode score kernel has already written each
+// chunk's candidates (the tiled one has not: the stand-alone first stage runs),
+// then the merge; otherwise one full select per query.
 hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
     if (a.kl > 0) {
-        launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)a.nchunks, (unsigned)a.num_q),
-                      dim3(kLocalThreads), st, a);
-        launch_kernel(ev, false, true, topk_merge_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), st, a);
+        if (a.tiled)
+            launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)a.nchunks, (unsigned)a.num_q), dim3(256), st,
+                          a);
+        if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256)
+            launch_kernel(ev, !a.tiled, true, topk_merge_kernel<256>, dim3((unsigned)a.num_q), dim3(256), st, a);
+        else
+            launch_kernel(ev, !a.tiled, true, topk_merge_kernel<kSelThreads>, dim3((unsigned)a.num_q),
+                          dim3(kSelThreads), st, a);
     } else {
         launch_kernel(ev, true, true, topk_select_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), st, a);
     }
     return hipGetLastError();
 }
+
+bool index_use_tiled(int num_q) { return num_q >= kTiledMinQueries; }
 
 }  // namespace csl

@@ -157,7 +157,7 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs 
  * one fp32 score row per query (max_q_pos/4 rounded up to 2048 entries) plus,
  * when the two-stage select is used (more than k visible entries and at most
  * 8192 first-stage candidates per query), 8-byte (key, id) candidates for
- * each 2048-entry chunk.  csl_index_topk_workspace() gives the exact size.
+ * each 1024-entry chunk.  csl_index_topk_workspace() gives the exact size.
  */
 size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k);
 csl_status csl_index_topk(const csl_pool* index_pool /* host */, const csl_pages* pages /* host */,

@@ -38,9 +38,9 @@ def test_row_bytes(csl):
 
 
 def test_workspace_sizes(csl):
-    # score rows of 32768 fp32, plus 16 chunks x (80 + 1) (key, id) candidates:
-    # 80 = 512*2048/32768 = 32 expected per chunk + 5 sqrt(32) + 4, rounded up to 16
-    assert csl.index_topk_workspace(16, 131072, 512) == 16 * (32768 * 4 + 16 * 81 * 8)
+    # score rows of 32768 fp32, plus 32 chunks x (40 + 1) (key, id) candidates:
+    # 40 = 512*1024/32768 = 16 expected per chunk + 5 sqrt(16) + 4, rounded up to 8
+    assert csl.index_topk_workspace(16, 131072, 512) == 16 * (32768 * 4 + 32 * 41 * 8)
     assert csl.index_topk_workspace(1, 100, 64) == 2048 * 4      # 25 entries <= k: one pass
     # decode split-KV partials: num_q * splits * heads * (dim + 2) floats
     ws = csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072)

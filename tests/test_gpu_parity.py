@@ -171,6 +171,15 @@ INDEX_CASES = [
     # scores rise with the id (with bf16 ties): the top 512 crowd the last chunks, so the
     # two-stage select's check fails and the exact single-pass select takes over
     dict(name="h16_d128_k512_ramp", H=16, DI=128, k=512, pos=[[131072, 70001]], mode="ramp"),
+    # 64+ queries: the query-blocked score kernel.  A prefill-like run of 100
+    # consecutive positions (6 full 16-query blocks and a ragged one)
+    dict(name="tiled_h16_d128_k512_prefill", H=16, DI=128, k=512, pos=[list(range(9000, 9100))]),
+    # three sequences, queries shuffled so every 16-query block mixes sequences,
+    # positions from 0 (nothing visible) past k entries, chunk-ragged
+    dict(name="tiled_h4_d32_k64_mixed", H=4, DI=32, k=64,
+         pos=[[0, 3, 4, 5, 255, 256, 300] + list(range(4096, 4121)), list(range(1020, 1050)),
+              [260 + 37 * i for i in range(20)]], shuffle=True),
+    dict(name="tiled_h16_d64_k100_ties", H=16, DI=64, k=100, pos=[list(range(6000, 6070))], mode="equal"),
 ]
 
 
@@ -197,6 +206,9 @@ def test_index_topk_parity(csl, orc, case):
         scatter_rows(hp.rows, bt, s, 4, keys.view(np.uint8).reshape(64 * mb, -1))
     q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
     q_pos = np.concatenate(case["pos"]).astype(np.int64)
+    if case.get("shuffle"):
+        perm = np.random.default_rng(seed).permutation(len(q_pos))
+        q_seq, q_pos = q_seq[perm], q_pos[perm]
     nq = len(q_pos)
     qi = randn_bf16(seed, 20, (nq, H, DI))
     if case.get("mode") == "ramp":
