@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <cfloat>
 #include <stdint.h>
 
 namespace csl {
@@ -12,6 +13,7 @@ constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -68,6 +70,20 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 }
 
 // ---------------------------------------------------------------- waves
+
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] with the gfx950 lane-swap VALU ops
+// (no LDS crossbar): permlane16_swap(v, v) returns, in every lane, the
+// lower-row and the upper-row value of the lane's row pair (rows of 16 lanes);
+// permlane32_swap(v, v) the same for the two 32-lane halves.  Every lane adds
+// the same two operands in the same order, so all lanes hold identical sums.
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {

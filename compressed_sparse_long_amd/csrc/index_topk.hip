@@ -590,8 +590,8 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
                 float v = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[i], 0.f), v);
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
+                v = sum_xor16(v);
+                v = sum_xor32(v);
                 sc[t] = v;
             }
             const int64_t e0 = (u0 + j) * 64;
@@ -625,30 +625,37 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
         chunk_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_wave, s_sel, s_cand);
     }
 }
-// index_score_tiled_kernel<DI> -- scores for many queries (prefill chunks).
-// A workgroup takes a block of 16 queries and one 1024-entry chunk.  The
+// index_score_tiled_kernel<DI, QW> -- scores for many queries (prefill chunks).
+// A workgroup takes a block of 4*QW queries and one 1024-entry chunk.  The
 // chunk's pages of the queries' sequence stream once through double-buffered
-// LDS (contiguous 16-byte loads by all 256 threads); each wave contracts its 4
-// queries' heads (A operands, registers) against every staged page (B = 16
-// entries per MFMA, from LDS), so one page load feeds 16 queries x 16 heads.
-// The ReLU / head-weight / head-sum epilogue is the decode kernel's.  Queries
-// of another sequence inside the block are taken in further passes over the
-// chunk, one per sequence.
-constexpr int kTiledQ = 16;           // queries per workgroup
+// LDS (contiguous 16-byte loads by all 256 threads; pages are reused by every
+// query block, so the loads are cached).  Each wave contracts its QW queries,
+// two at a time, against every staged page with v_mfma_f32_32x32x16_bf16:
+// A = 32 rows = 2 queries x 16 heads (registers), B = 32 entries (LDS), so one
+// LDS read of an operand feeds QW/2 MFMAs and one page load 4*QW queries.  In
+// the 32x32 accumulator a lane holds 8 heads of each of the two queries for
+// its entry column: ReLU, head weight and the in-lane sum, then one 32-lane
+// swap completes the head sum.  Score rows stream out (non-temporal stores).
+// Queries of another sequence inside the block are taken in further passes
+// over the chunk, one per sequence.
+constexpr int kTiledQW = 4;           // queries per wave (4 waves per workgroup; even)
 constexpr int kTiledMinQueries = 64;  // calls with at least this many queries use the tiled kernel
 
-template <int DI>
+template <int DI, int QW>
 __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
-    constexpr int KS = DI / 32, RB = DI * 2, CPR = RB / 16, LROW = RB + 16;
+    constexpr int kTiledQ = 4 * QW;       // queries per workgroup
+    constexpr int PP = QW / 2;            // query pairs per wave
+    constexpr int KS = DI / 16, RB = DI * 2, CPR = RB / 16, LROW = RB + 16;
     constexpr int UNIT = 64 * RB;         // bytes of a 64-entry page
     constexpr int LPT = UNIT / 16 / 256;  // 16-byte loads per thread per page
+    static_assert(QW % 2 == 0, "queries go to the MFMA in pairs");
     static_assert(LPT >= 1 && UNIT == LPT * 16 * 256, "a page is a whole number of workgroup loads");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2][64 * LROW];
     __shared__ int32_t s_qs[kTiledQ];
     __shared__ int64_t s_qnv[kTiledQ];
     __shared__ int32_t s_pg[kChunk / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r16 = lane & 15, g = lane >> 4;
+    const int r32 = lane & 31, h2 = lane >> 5;
     const int blk = blockIdx.x;
     const int64_t c0 = (int64_t)blk * kChunk;
     const int q0 = blockIdx.y * kTiledQ;
@@ -669,29 +676,43 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
     }
     __syncthreads();
 
-    // the wave's 4 queries: A operands (rows beyond n_heads are zero) and head weights
-    bf16x8 qa[4][KS];
-    float wv[4][4];
+    // A operands of the wave's query pairs: row r32 = query 2pp + r32/16, head
+    // r32 % 16 (rows beyond n_heads or of invalid queries are zero); dims
+    // 16 ks + 8 h2 .. +7.  Head weights of the lane's accumulator rows: value
+    // 4j + i of the 32x32 accumulator is row 8j + 4 h2 + i.
+    bf16x8 qa[PP][KS];
+    float wv[PP][16];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-        const int n = q0 + 4 * wave + qq;
-        const bool qv = n < a.num_q && s_qs[4 * wave + qq] >= 0;
+    for (int pp = 0; pp < PP; ++pp) {
+        const int qi = QW * wave + 2 * pp + (r32 >> 4);
+        const int n = q0 + qi;
+        const bool qv = n < a.num_q && s_qs[qi] >= 0;
         const int nn = qv ? n : 0;
-        const bool hv = qv && r16 < a.n_heads;
-        const uint16_t* qrow = a.q_idx + ((int64_t)nn * a.n_heads + (r16 < a.n_heads ? r16 : 0)) * DI;
+        const int hd = r32 & 15;
+        const bool hv = qv && hd < a.n_heads;
+        const uint16_t* qrow = a.q_idx + ((int64_t)nn * a.n_heads + (hd < a.n_heads ? hd : 0)) * DI;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h2);
             if (!hv) v = u32x4{0u, 0u, 0u, 0u};
-            qa[qq][ks] = __builtin_bit_cast(bf16x8, v);
+            qa[pp][ks] = __builtin_bit_cast(bf16x8, v);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * g + i;
-            const float x = a.w[(int64_t)nn * a.n_heads + (h < a.n_heads ? h : 0)];
-            wv[qq][i] = (qv && h < a.n_heads) ? x : 0.f;
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 8 * j + 4 * h2 + i;  // query 2pp + row/16, head row % 16
+                const int qj = QW * wave + 2 * pp + (row >> 4);
+                const int nj = q0 + qj;
+                const int h = row & 15;
+                const bool ok = nj < a.num_q && s_qs[qj] >= 0 && h < a.n_heads;
+                const float x = a.w[(int64_t)(ok ? nj : 0) * a.n_heads + (ok ? h : 0)];
+                wv[pp][4 * j + i] = ok ? x : 0.f;
+            }
     }
+    int64_t nvl[PP];  // visible entries of the query this lane stores, per pair
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) nvl[pp] = s_qnv[QW * wave + 2 * pp + h2];
 
     uint32_t done = 0;  // queries handled (the same in every thread)
     for (;;) {
@@ -725,7 +746,7 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
             const int32_t pg = s_pg[j];
             const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT);
 #pragma unroll
-            for (int q = 0; q < LPT; ++q) st[q] = __builtin_nontemporal_load(base + q * 256 + tid);
+            for (int q = 0; q < LPT; ++q) st[q] = base[q * 256 + tid];
         };
         auto store_page = [&](int b) {
 #pragma unroll
@@ -742,31 +763,45 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
             const uint8_t* sk = s_k[j & 1];
             const int64_t e0 = c0 + 64 * j;
             const int32_t pg = s_pg[j];
-            if (pg < 0 && lane == 0 && ((gmask >> (4 * wave)) & 0xfu)) raise_error(a.err, kErrPage);
+            if (pg < 0 && lane == 0 && ((gmask >> (QW * wave)) & ((1u << QW) - 1u))) raise_error(a.err, kErrPage);
+            float mine[PP][2];  // the lane's score: query 2pp + h2, entry e0 + 32 t + r32
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                bf16x8 kb[KS];
+            for (int t = 0; t < 2; ++t) {
+                f32x16 acc[PP];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kb[ks] = *reinterpret_cast<const bf16x8*>(sk + (16 * t + r16) * LROW + (4 * ks + g) * 16);
+                for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int qi = 4 * wave + qq;
-                    if (!((gmask >> qi) & 1u)) continue;  // uniform over the wave
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int c = 0; c < 16; ++c) acc[pp][c] = 0.f;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qq][ks], kb[ks], acc, 0, 0, 0);
-                    float v = 0.f;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 kb =
+                        *reinterpret_cast<const bf16x8*>(sk + (32 * t + r32) * LROW + (16 * ks + 8 * h2) * 2);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v = fmaf(wv[qq][i], fmaxf(acc[i], 0.f), v);
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    // every lane group holds the tile's 16 sums; group t stores them
-                    const int64_t e = e0 + 16 * t + r16;
-                    if (g == t && e < s_qnv[qi])
-                        a.scores[(int64_t)(q0 + qi) * a.stride + e] = pg < 0 ? -INFINITY : v;
+                    for (int pp = 0; pp < PP; ++pp)
+                        acc[pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[pp][ks], kb, acc[pp], 0, 0, 0);
                 }
+#pragma unroll
+                for (int pp = 0; pp < PP; ++pp) {
+                    float va = 0.f, vb = 0.f;  // the pair's first and second query
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        va = fmaf(wv[pp][c], __builtin_amdgcn_fmed3f(acc[pp][c], 0.f, FLT_MAX), va);
+                        vb = fmaf(wv[pp][8 + c], __builtin_amdgcn_fmed3f(acc[pp][8 + c], 0.f, FLT_MAX), vb);
+                    }
+                    va = sum_xor32(va);
+                    vb = sum_xor32(vb);
+                    mine[pp][t] = h2 == 0 ? va : vb;
+                }
+            }
+#pragma unroll
+            for (int pp = 0; pp < PP; ++pp) {
+                const int qi = QW * wave + 2 * pp + h2;
+                const bool store = (gmask >> qi) & 1u;
+                float* row = a.scores + (int64_t)(q0 + qi) * a.stride + e0 + r32;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (store && e0 + 32 * t + r32 < nvl[pp])
+                        __builtin_nontemporal_store(pg < 0 ? -INFINITY : mine[pp][t], row + 32 * t);
             }
             if (j + 1 < npages) store_page((j + 1) & 1);
             __syncthreads();
@@ -851,11 +886,12 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0) return hipSuccess;
     if (a.tiled) {
-        dim3 grid((unsigned)(a.stride / kChunk), (unsigned)((a.num_q + kTiledQ - 1) / kTiledQ));
+        constexpr int QW = kTiledQW;
+        dim3 grid((unsigned)(a.stride / kChunk), (unsigned)((a.num_q + 4 * QW - 1) / (4 * QW)));
         switch (a.dim) {
-            case 32: launch_kernel(ev, true, true, index_score_tiled_kernel<32>, grid, dim3(256), st, a); break;
-            case 64: launch_kernel(ev, true, true, index_score_tiled_kernel<64>, grid, dim3(256), st, a); break;
-            case 128: launch_kernel(ev, true, true, index_score_tiled_kernel<128>, grid, dim3(256), st, a); break;
+            case 32: launch_kernel(ev, true, true, index_score_tiled_kernel<32, QW>, grid, dim3(256), st, a); break;
+            case 64: launch_kernel(ev, true, true, index_score_tiled_kernel<64, QW>, grid, dim3(256), st, a); break;
+            case 128: launch_kernel(ev, true, true, index_score_tiled_kernel<128, QW>, grid, dim3(256), st, a); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
