@@ -520,6 +520,424 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------- 512-dim bf16 keys, 32x32 tiles
+
+// hybrid_attn_mqa512_kernel -- the path for bf16 keys of 512 dims (every
+// layer of the decode and prefill workloads).  One 256-thread workgroup per
+// (query, split); wave w owns heads 32 (w & 1) .. +31 and output dims
+// 256 (w >> 1) .. +255.  Per tile of 32 gathered key rows:
+//   * the rows are staged in LDS in their stored (row-major) layout by direct
+//     global->LDS loads (each wave copies 8 rows, one 1 KiB row per
+//     instruction) into a ring of 4 tiles: up to three tiles are in flight
+//     while one is computed, with no registers held for them;
+//   * S^T[32 keys x 32 heads] = K . Q^T on v_mfma_f32_32x32x16_bf16: A = key
+//     rows from LDS, B = the wave's q rows over its 256 dims (registers); the
+//     two halves of a head group are summed through LDS;
+//   * online softmax per head column in the exp2 domain (v_exp_f32: weights
+//     below 2^-126 of the reference flush to 0) with a lazy reference
+//     max: the accumulator is rescaled only when the max grows past the
+//     reference by more than 8 (so P <= 2^8), which makes rescales rare;
+//   * software pipelined: the S MFMAs of the next tile are issued before the
+//     softmax of the current one, so the matrix unit and the vector ALU
+//     overlap within the wave (one wave per SIMD);
+//   * O^T[256 dims x 32 heads] += V^T . P^T: B = P straight from the S
+//     accumulator (a lane holds 16 keys of its head; they are assigned to the
+//     two k-steps' slots), A = V^T read from the row-major tile with the
+//     transposing LDS read ds_read_b64_tr_b16 (in each 16-lane group, output
+//     lane 4b+e receives element e of the 8-byte reads of lanes b, b+4, b+8,
+//     b+12: four lanes pointing at four key rows give a lane four keys of one
+//     dim), so no transposed copy of the tile is written.
+// With PREC (fp8 output) P is carried as P_hi + P_lo.  The epilogue and the
+// split partials match hybrid_attn_kernel's.
+constexpr int kT2 = 32;          // keys per tile
+constexpr int kRow2 = 1040;      // LDS stride of a staged row (1024 B + 16: spreads the S-operand reads)
+constexpr int kMaxKeys2 = 1024;  // key addresses resolved per pass
+constexpr int kRing2 = 4;        // staged tiles: one computed, up to three in flight
+
+// Source of masked key rows (zeros: a masked key then contributes 0 * 0).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_kv_row[1024];
+
+// One 1 KiB row from global memory straight into LDS: lane l's 16 bytes land
+// at lds + 16 l (M0 holds the LDS address).  Issued as inline assembly so the
+// compiler does not order later LDS reads behind it; the caller waits with an
+// explicit vmcnt before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_dma_row(uint32_t lds, const uint8_t* src) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)p);
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v*)(const_cast<uint8_t*>(p)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <bool PREC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+hybrid_attn_mqa512_kernel(AttnArgs a) {
+    constexpr int D = 512;
+    __shared__ __attribute__((aligned(16))) uint8_t s_kt[kRing2][kT2 * kRow2];
+    __shared__ __attribute__((aligned(16))) float s_sx[4][64 * 16];  // S^T partials, one per wave
+    __shared__ const uint8_t* s_rows[kMaxKeys2];
+    __shared__ uint32_t s_vbits[kMaxKeys2 / 32];
+    __shared__ float s_rope[2][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, h2 = lane >> 5;
+    const int hg = wave & 1, dh = wave >> 1;
+    const int n = blockIdx.x % a.num_q;
+    const int sp = blockIdx.x / a.num_q;
+
+    QueryInfo qi = query_info(a, n);
+    if (!qi.ok && sp == 0 && tid == 0) raise_error(a.err, (qi.s < 0 || qi.s >= a.num_seqs) ? kErrSeq : kErrPos);
+    const int s = qi.s;
+    const int64_t p = qi.ok ? qi.p : 0;
+    const int64_t nv_c = (qi.ok && a.comp_rows) ? p / a.comp_ratio : 0;
+    const int64_t Lc = a.comp_rows ? (a.topk ? (int64_t)a.k : nv_c) : 0;
+    const int64_t lo = p - a.swa_window > 0 ? p - a.swa_window : 0;
+    const int64_t L = qi.ok ? Lc + (p - lo) : 0;
+    const int64_t n_tiles = (L + kT2 - 1) / kT2;
+    const int64_t tps = (n_tiles + a.n_splits - 1) / a.n_splits;
+    const int64_t t_begin = sp * tps;
+    const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
+    const int64_t k_end = t_end * kT2 < L ? t_end * kT2 : L;
+    if (a.n_splits == 1 && tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
+
+    const int head = 32 * hg + r32;
+    const bool hv = head < a.n_heads;
+    // q as the B operand of S^T over the wave's 256 dims: column = head, k-step ks =
+    // dims 256 dh + 16 ks + 8 h2 .. +7
+    bf16x8 qb[16];
+    {
+        const uint16_t* qrow = a.q + ((int64_t)n * a.n_heads + (hv ? head : 0)) * D + 256 * dh + 8 * h2;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+            if (!hv) v = u32x4{0u, 0u, 0u, 0u};
+            qb[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    // O^T tiles m = 0..7: value 4j + i = dim 256 dh + 32 m + 8 j + 4 h2 + i of this head
+    f32x16 oacc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) oacc[m][c] = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    // transposed-read addresses: within 16-lane group G = lane / 16 (dims
+    // 16 (G & 1) .. +15 of a 32-dim tile, key half h2 = G / 2), lane 4c + b
+    // points at the key of slot c of its group (key 16 h2 + 4c + 2kk, + 1 for
+    // the second read), dims +4b .. +4b+3
+    const int ig = lane & 15, G = lane >> 4;
+    const int tr_row = 16 * (G >> 1) + 4 * (ig >> 2);
+    const int tr_col = (256 * dh + 16 * (G & 1) + 4 * (ig & 3)) * 2;  // bytes, + 64 m
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue_tile = [&](int tl) {
+        const uint8_t* buf = s_kt[tl % kRing2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * wave_u + i;
+            const uint8_t* row = s_rows[tl * kT2 + r];
+            lds_dma_row(lds_addr(buf + r * kRow2), (row ? row : g_zero_kv_row) + 16 * lane);
+        }
+    };
+    // the wave's half of S^T for a staged tile (its 256 dims): A = key rows (LDS), B = q
+    // accumulator row r = 8j + 4h + i holds key sigma(r) = 16h + 4i + j of the tile:
+    // then the four keys a transposed read gathers (i = 0..3) sit 4 rows apart,
+    // whose 32-byte windows fall in disjoint LDS banks
+    const int s_row = 16 * ((r32 >> 2) & 1) + 4 * (r32 & 3) + (r32 >> 3);
+    auto s_loads = [&](const uint8_t* kt, bf16x8 (&ka)[16]) {
+        const uint8_t* krow = kt + s_row * kRow2 + 512 * dh + 16 * h2;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+    };
+    auto s_mfma = [&](const bf16x8 (&ka)[16]) {
+        // two independent accumulation chains (even / odd k-steps)
+        f32x16 s0, s1;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s0[c] = s1[c] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 16; ks += 2) {
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks + 1], qb[ks + 1], s1, 0, 0, 0);
+        }
+        return s0 + s1;
+    };
+    // the two halves of a head group meet in LDS (the lanes of waves w and w ^ 2
+    // hold the same (head, key) positions)
+    // (layout [wave][quad][lane][4]: a quad's 16-byte accesses of 16 lanes hit distinct banks)
+    float* sx_mine = s_sx[wave] + 4 * lane;
+    const float* sx_other = s_sx[wave ^ 2] + 4 * lane;
+    auto put_half = [&](const f32x16& h) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 4)
+            *reinterpret_cast<f32x4*>(sx_mine + 64 * c) = f32x4{h[c], h[c + 1], h[c + 2], h[c + 3]};
+    };
+    auto add_other = [&](f32x16& h) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 4) {
+            const f32x4 o = *reinterpret_cast<const f32x4*>(sx_other + 64 * c);
+            h[c] += o[0];
+            h[c + 1] += o[1];
+            h[c + 2] += o[2];
+            h[c + 3] += o[3];
+        }
+    };
+    // softmax update for a tile whose S^T is in sacc (branch-free): P operands of
+    // the two k-steps, and the factor of the accumulator rescale if the lane's
+    // reference moved (alpha = 0 at the first move, which meets a zero accumulator)
+    struct Soft {
+        bf16x8 pb[2], plo[2];
+        float alpha;
+        bool rescale;
+    };
+    auto softmax = [&](uint32_t vb, const f32x16& sacc) {
+        Soft o;
+        // value 4j + i is accumulator row 8j + 4h2 + i = key 16 h2 + 4i + j of this head column
+        float x[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * h2 + 4 * i + j;
+                const float v = ((vb >> key) & 1u) ? sacc[4 * j + i] * a.scale_log2 : -INFINITY;
+                x[4 * j + i] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+        // lazy reference: moves only when the max passes it by more than 8
+        const bool move = tmax > m_ref + 8.0f;
+        const float alpha = __builtin_amdgcn_exp2f(move ? m_ref - tmax : 0.f);
+        o.alpha = alpha;
+        o.rescale = move && m_ref != -INFINITY;
+        l_run *= alpha;
+        m_ref = move ? tmax : m_ref;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float psum = 0.f;
+        uint32_t pw[8], pl[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float p0 = __builtin_amdgcn_exp2f(x[2 * c] - m_use), p1 = __builtin_amdgcn_exp2f(x[2 * c + 1] - m_use);
+            psum += p0 + p1;
+            pw[c] = pack_bf16x2(p0, p1);
+            if constexpr (PREC)
+                pl[c] = pack_bf16x2(p0 - bf16_bits_to_f32(pw[c] & 0xffffu), p1 - bf16_bits_to_f32(pw[c] >> 16));
+        }
+        l_run += psum;
+        // k-step kk takes values j = 2kk (slots 8 h2 + 0..3) and j = 2kk+1 (slots 8 h2 + 4..7):
+        // slot 8 h2 + 4u + i is key 16 h2 + 4i + 2kk + u
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            o.pb[kk] = __builtin_bit_cast(bf16x8, u32x4{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
+            o.plo[kk] = o.pb[kk];
+            if constexpr (PREC)
+                o.plo[kk] = __builtin_bit_cast(bf16x8, u32x4{pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]});
+        }
+        return o;
+    };
+    // O^T += V^T . P^T for a staged tile (A = V^T by transposed LDS reads)
+    auto pv = [&](const Soft& sm, const uint8_t* kt) {
+        if (__ballot(sm.rescale)) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) oacc[m] *= sm.alpha;
+        }
+        bf16x8 va[8][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const uint8_t* base = kt + (tr_row + 2 * kk) * kRow2 + tr_col + 64 * m;
+                const u32x2 v0 = lds_read_tr16(base);
+                const u32x2 v1 = lds_read_tr16(base + kRow2);
+                va[m][kk] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+            }
+        // consecutive MFMAs go to different accumulators (no back-to-back dependences)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m][kk], sm.pb[kk], oacc[m], 0, 0, 0);
+            if constexpr (PREC) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m][kk], sm.plo[kk], oacc[m], 0, 0, 0);
+            }
+        }
+        // transposed reads run 4 MFMAs ahead: 8 reads, then (MFMA, 2 reads) x 12, then the rest
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PREC ? 2 : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PREC ? 8 : 4, 0);
+    };
+    // S of the next tile overlapped with the softmax of the current one: the 16
+    // operand reads first, then each MFMA followed by a share of the softmax's
+    // vector instructions
+    auto s_next_softmax = [&](const uint8_t* kt_next, uint32_t vb, const f32x16& sacc, f32x16& s_out) {
+        bf16x8 ka[16];
+        s_loads(kt_next, ka);
+        const Soft sm = softmax(vb, sacc);
+        s_out = s_mfma(ka);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        return sm;
+    };
+
+    for (int64_t kb = t_begin * kT2; kb < k_end; kb += kMaxKeys2) {
+        const int64_t ke = kb + kMaxKeys2 < k_end ? kb + kMaxKeys2 : k_end;
+        const int ntl = (int)((ke - kb + kT2 - 1) / kT2);
+        __syncthreads();  // the previous pass is done with s_rows and the tiles
+        for (int base = 0; base < ntl * kT2; base += kThreads) {
+            const int i = base + tid;
+            const uint8_t* r = (kb + i < ke) ? key_row(a, n, s, kb + i, Lc, nv_c, lo) : nullptr;
+            if (i < ntl * kT2) s_rows[i] = r;
+            const uint64_t bits = __ballot(r != nullptr);
+            const int t0 = (base + 64 * wave) / kT2;
+            if (lane == 0 && t0 < ntl) s_vbits[t0] = (uint32_t)bits;
+            if (lane == 0 && t0 + 1 < ntl) s_vbits[t0 + 1] = (uint32_t)(bits >> 32);
+        }
+        __syncthreads();
+        for (int t = 0; t < 3 && t < ntl; ++t) issue_tile(t);
+        // tile 0 (at most tiles 1 and 2 pending), then S of tile 0
+        if (ntl >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (ntl == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        f32x16 s_cur;
+        {
+            bf16x8 ka[16];
+            s_loads(s_kt[0], ka);
+            s_cur = s_mfma(ka);
+        }
+        put_half(s_cur);
+        __syncthreads();
+        add_other(s_cur);
+        // iteration t: the S MFMAs of tile t+1 interleaved with the softmax of
+        // tile t; then O += V^T P^T for tile t; the S halves of tile t+1 meet
+        // after the PV.  Ring: tile t (PV), t+1 (S), t+2 and t+3 in flight.
+        for (int t = 0; t + 1 < ntl; ++t) {
+            if (t + 2 < ntl) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // tile t+1 complete; every wave is past tile t-1 (buffer t+3) and its S exchange
+            if (t + 3 < ntl) issue_tile(t + 3);
+            f32x16 s_next;
+            const Soft sm = s_next_softmax(s_kt[(t + 1) % kRing2], s_vbits[t], s_cur, s_next);
+            pv(sm, s_kt[t % kRing2]);
+            put_half(s_next);
+            __syncthreads();
+            add_other(s_next);
+            s_cur = s_next;
+        }
+        pv(softmax(s_vbits[ntl - 1], s_cur), s_kt[(ntl - 1) % kRing2]);
+    }
+
+    const float l_tot = sum_xor32(l_run);
+    if (!hv) return;
+
+    if (a.n_splits > 1) {
+        // unnormalised partial relative to m_ref: dims 256 dh + 32 m + 8 j + 4 h2 .. +3 of this head
+        float* po = a.part_o + (((int64_t)n * a.n_splits + sp) * a.n_heads + head) * D + 256 * dh + 4 * h2;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(po + 32 * m + 8 * j) =
+                    f32x4{oacc[m][4 * j], oacc[m][4 * j + 1], oacc[m][4 * j + 2], oacc[m][4 * j + 3]};
+        if (h2 == 0 && dh == 0) {
+            float* ml = a.part_ml + (((int64_t)n * a.n_splits + sp) * a.n_heads + head) * 2;
+            ml[0] = m_ref;
+            ml[1] = l_tot;
+        }
+        return;
+    }
+
+    // epilogue: normalise, RoPE^-1 at p (pairs are adjacent values i = 0,1 / 2,3), store
+    const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const int rbase = D - a.rope_dims;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        oacc[m] *= inv_l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = 256 * dh + 32 * m + 8 * j + 4 * h2;
+            if (d0 >= rbase) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int pj = (d0 + 2 * c - rbase) >> 1;
+                    const float cs = s_rope[0][pj], sn = s_rope[1][pj];
+                    const float u = oacc[m][4 * j + 2 * c], v = oacc[m][4 * j + 2 * c + 1];
+                    oacc[m][4 * j + 2 * c] = u * cs - v * sn;
+                    oacc[m][4 * j + 2 * c + 1] = u * sn + v * cs;
+                }
+            }
+        }
+    }
+    const int64_t obase = ((int64_t)n * a.n_heads + head) * D + 256 * dh + 4 * h2;
+    if (a.out_dtype == kF32) {
+        float* o = reinterpret_cast<float*>(a.out) + obase;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(o + 32 * m + 8 * j) =
+                    f32x4{oacc[m][4 * j], oacc[m][4 * j + 1], oacc[m][4 * j + 2], oacc[m][4 * j + 3]};
+    } else if (a.out_dtype == kBF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + obase;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2*>(o + 32 * m + 8 * j) =
+                    u32x2{pack_bf16x2(oacc[m][4 * j], oacc[m][4 * j + 1]),
+                          pack_bf16x2(oacc[m][4 * j + 2], oacc[m][4 * j + 3])};
+    } else {
+        // 64-dim groups: tiles m = 2G, 2G+1 of the wave's 256 dims, halves h2 = 0, 1
+        uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + obase;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            float amax = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(oacc[2 * g4 + mm][c]));
+            {
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+                amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+            }
+            const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+            if (h2 == 0) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + 4 * dh + g4] = scale;
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                const int m = 2 * g4 + mm;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t code = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) code |= f32_to_e4m3(oacc[m][4 * j + i] / scale) << (8 * i);
+                    *reinterpret_cast<uint32_t*>(o + 32 * m + 8 * j) = code;
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 template <int D, int KV>
@@ -532,6 +950,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev
     if (a.num_q <= 0) return hipSuccess;
     dim3 grid((unsigned)((int64_t)a.num_q * a.n_splits));
     const int kv = a.comp_rows ? a.comp_dtype : a.swa_dtype;
+    if (a.dim == 512 && kv == kBF16) {
+        if (a.out_dtype == kFP8) launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<true>, grid, dim3(kThreads), st, a);
+        else launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<false>, grid, dim3(kThreads), st, a);
+        return hipGetLastError();
+    }
     if (a.dim == 512 && kv == kBF16) launch_prec<512, kBF16>(a, grid, st, ev);
     else if (a.dim == 512 && kv == kFP8) launch_prec<512, kFP8>(a, grid, st, ev);
     else if (a.dim == 128 && kv == kBF16) launch_prec<128, kBF16>(a, grid, st, ev);

@@ -30,17 +30,15 @@ struct RopeFreqs {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round-to-nearest-even fp32 -> bf16 bits.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Round-to-nearest-even fp32 -> bf16 on the conversion unit (v_cvt_pk_bf16_f32,
+// two values per instruction); `lo` lands in bits 0..15.
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_cvt{lo, hi}, bf16x2_cvt));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // OCP e4m3fn code -> fp32 (S.1111.111 is NaN; no infinities).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
