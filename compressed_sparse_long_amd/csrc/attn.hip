@@ -609,6 +609,9 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     const int64_t k_end = t_end * kT2 < L ? t_end * kT2 : L;
     if (a.n_splits == 1 && tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
 
+    // An AGPR operand in inline assembly makes the compiler select the MFMAs'
+    // accumulator-register form, so the output accumulator stays in AGPRs.
+    asm volatile("; accumulators in AGPRs" ::"a"(0.f));
     const int head = 32 * hg + r32;
     const bool hv = head < a.n_heads;
     // q as the B operand of S^T over the wave's 256 dims: column = head, k-step ks =

@@ -296,6 +296,9 @@ ATTN_CASES = [
          pos=[[3, 129, 1000]], no_comp=True),
     dict(name="c4a_d512_h48_invalid_id_bf16", D=512, R=64, H=48, ratio=4, k=64, dtype=O.BF16, out=O.BF16,
          pos=[[900, 1200]], invalid=True),
+    # more keys than one pass of resolved addresses holds (1171 entries + 128 raw in one prefill split)
+    dict(name="c128a_d512_h64_dense_bf16_long", D=512, R=64, H=64, ratio=128, k=0, dtype=O.BF16, out=O.FP8,
+         pos=[[150000, 140001]]),
 ]
 
 
