@@ -83,6 +83,38 @@ __device__ __forceinline__ float sum_xor32(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Prefix scans over the 64 lanes (lane 0 first) on DPP moves, no LDS: shifts
+// by 1, 2, 4, 8 lanes inside each 16-lane row, then the last lane of rows 0
+// and 2 into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31).  A lane whose source lies outside its row, or whose row is
+// masked off, combines with 0 (the identity of both scans here).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t x) {
+    x += dpp_u32<0x111>(x);
+    x += dpp_u32<0x112>(x);
+    x += dpp_u32<0x114>(x);
+    x += dpp_u32<0x118>(x);
+    x += dpp_u32<0x142, 0xa>(x);
+    x += dpp_u32<0x143, 0xc>(x);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_scan_max(uint32_t x) {
+    x = max(x, dpp_u32<0x111>(x));
+    x = max(x, dpp_u32<0x112>(x));
+    x = max(x, dpp_u32<0x114>(x));
+    x = max(x, dpp_u32<0x118>(x));
+    x = max(x, dpp_u32<0x142, 0xa>(x));
+    x = max(x, dpp_u32<0x143, 0xc>(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) { return lane_value(wave_scan_max(x), 63); }
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -56,12 +56,7 @@ template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_scan_add(v);
     if (lane == 63) s_wave[wave] = x;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -191,8 +186,7 @@ __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uin
     uint32_t kmax = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    kmax = wave_max_u32(kmax);
     if (lane == 0) s_sel[8 + wave] = kmax;
     for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
     __syncthreads();
@@ -422,50 +416,205 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
 constexpr int kChunk = 1024;        // ids per first-stage chunk (one workgroup of the score kernel)
 constexpr int kMergeSlots = 8;      // candidates per merge thread
 
-// First stage of the two-stage top-k over one 1024-id chunk of query n, by a
-// 256-thread workgroup whose thread t holds the keys of ids base + 4t .. 4t+3
-// (ids at or past base + nvalid are invalid): the chunk's first kl ids in
-// (score desc, id asc) order, written in ascending id order, and the
-// (kl+1)-th, whose position the merge checks (none if nvalid <= kl).
-__device__ __forceinline__ void chunk_first_stage(const IndexArgs& a, int n, int blk, const uint32_t (&key)[4], int64_t base,
-                                                  int64_t nvalid, uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel,
-                                                  uint32_t* s_cand) {
-    const int tid = threadIdx.x;
+// ---- single-wave selection: no workgroup barriers.  A wave's LDS operations
+// execute in issue order, so after this point a lane reads what any lane of the
+// wave wrote before it; the fence keeps the compiler from moving them across.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// An NB-bin histogram in LDS scanned from the top by one wave: the bin that
+// holds the rank-th largest counted key, the rank inside that bin and its
+// count (valid if total >= rank).  Lane l sums bins NB-1-PER*l downwards; the
+// hit lane's PER bins are then spread over lanes for a second scan.
+struct BinPick {
+    uint32_t bin, rank, cnt, total;
+};
+template <int NB>
+__device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t rank) {
+    constexpr int PER = NB >= 64 ? NB / 64 : 1;
+    const int lane = threadIdx.x & 63;
+    const int top = NB - 1 - PER * lane;
+    uint32_t sum = 0;
+    if constexpr (PER >= 4) {
+#pragma unroll
+        for (int v = 0; v < PER / 4; ++v) {
+            const u32x4 h = *reinterpret_cast<const u32x4*>(hist + top + 1 - PER + 4 * v);
+            sum += h[0] + h[1] + h[2] + h[3];
+        }
+    } else {
+        static_assert(PER == 1, "bins per lane: 1 or a multiple of 4");
+        sum = top >= 0 ? hist[top] : 0u;
+    }
+    const uint32_t incl = wave_scan_add(sum);
+    BinPick r = {0u, 0u, 0u, lane_value(incl, 63)};
+    if (r.total < rank) return r;
+    const uint32_t above = incl - sum;
+    const int L = __builtin_ctzll(__ballot(above < rank && rank <= incl));
+    const uint32_t above_l = lane_value(above, L);
+    if constexpr (PER == 1) {
+        r.bin = (uint32_t)(NB - 1 - L);
+        r.rank = rank - above_l;
+        r.cnt = lane_value(sum, L);
+    } else {
+        const int top_l = NB - 1 - PER * L;
+        const uint32_t c = lane < PER ? hist[top_l - lane] : 0u;
+        const uint32_t in2 = wave_scan_add(c) + above_l;
+        const int J = __builtin_ctzll(__ballot(lane < PER && in2 - c < rank && rank <= in2));
+        r.bin = (uint32_t)(top_l - J);
+        r.cnt = lane_value(c, J);
+        r.rank = rank - (lane_value(in2, J) - r.cnt);
+    }
+    return r;
+}
+
+// The want-th largest of a wave's keys (16 per lane, slot i valid iff bit i of
+// vmask), by one wave.  Radix rounds over rel = key - lo, counting only keys
+// >= lo: with WINDOW, lo = max - (2^24 - 1) (two octaves of fp32 score below
+// the maximum; digits at bits 13..23, 2..12, 0..1), else lo = 0 (bits 21..31,
+// 10..20, 0..9).  Each round histograms its digit in `hist` (2048 words of
+// LDS; with `built` the caller has already histogrammed round 0 there) and
+// finds the bin of the rank; once that bin holds at most 64 keys they are
+// compacted to `cbuf` (64 words) and ranked pairwise.  Returns false (uniform)
+// if fewer than `want` keys are >= lo; else T and *rem, the number of copies
+// of T inside the top `want`.
+template <bool WINDOW>
+__device__ __forceinline__ bool wave_select(const uint32_t (&key)[16], uint32_t vmask, uint32_t want, uint32_t lo,
+                                            bool built, uint32_t* hist, uint32_t* cbuf, uint32_t& T, uint32_t& rem) {
+    const int lane = threadIdx.x & 63;
+    uint32_t rel[16], in = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        rel[i] = key[i] - lo;
+        in |= (((vmask >> i) & 1u) && key[i] >= lo ? 1u : 0u) << i;
+    }
+    uint32_t prefix = 0, pmask = 0, rank = want;
+    auto matches = [&](int i) { return ((in >> i) & 1u) && (rel[i] & pmask) == prefix; };
+    auto build = [&](int sh, int nb) {
+        for (int b = 4 * lane; b < nb; b += 256) *reinterpret_cast<u32x4*>(hist + b) = u32x4{0u, 0u, 0u, 0u};
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (matches(i)) atomicAdd(&hist[(rel[i] >> sh) & (uint32_t)(nb - 1)], 1u);
+        wave_lds_sync();
+    };
+    auto take = [&](const BinPick& b, int sh, int nb) {
+        prefix |= b.bin << sh;
+        pmask |= (uint32_t)(nb - 1) << sh;
+        rank = b.rank;
+    };
+    // the bin's keys (at most 64) ranked pairwise
+    auto finish = [&](uint32_t cn) {
+        const uint32_t mine = [&] {
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m += matches(i) ? 1u : 0u;
+            return m;
+        }();
+        uint32_t off = wave_scan_add(mine) - mine;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (matches(i)) {
+                if (off < 64u) cbuf[off] = rel[i];
+                ++off;
+            }
+        wave_lds_sync();
+        uint32_t kc = 0, gt = 0, ge = 0;
+        if ((uint32_t)lane < cn) {
+            kc = cbuf[lane];
+            for (uint32_t j = 0; j < cn; ++j) {
+                const uint32_t kj = cbuf[j];
+                gt += kj > kc ? 1u : 0u;
+                ge += kj >= kc ? 1u : 0u;
+            }
+        }
+        const int L = __builtin_ctzll(__ballot((uint32_t)lane < cn && gt < rank && rank <= ge));
+        T = lane_value(kc, L) + lo;
+        rem = rank - lane_value(gt, L);
+        wave_lds_sync();
+    };
+    constexpr int kSh0 = WINDOW ? 13 : 21, kSh1 = WINDOW ? 2 : 10;
+    if (!built) build(kSh0, 2048);
+    BinPick b = wave_find_bin<2048>(hist, rank);
+    if (b.total < rank) return false;
+    take(b, kSh0, 2048);
+    if (b.cnt <= 64u) {
+        finish(b.cnt);
+        return true;
+    }
+    build(kSh1, 2048);
+    b = wave_find_bin<2048>(hist, rank);
+    take(b, kSh1, 2048);
+    if (b.cnt <= 64u) {
+        finish(b.cnt);
+        return true;
+    }
+    constexpr int kNb2 = WINDOW ? 4 : 1024;
+    build(0, kNb2);
+    b = wave_find_bin<kNb2>(hist, rank);
+    take(b, 0, kNb2);
+    T = prefix + lo;
+    rem = rank;
+    wave_lds_sync();
+    return true;
+}
+
+// First stage of the two-stage top-k over one 1024-id chunk of query n, by one
+// wave whose lane l holds the keys of ids base + 16 l .. +15 (ids at or past
+// base + nvalid are invalid): the chunk's first kl ids in (score desc, id asc)
+// order, written in ascending id order, and the (kl+1)-th, whose position the
+// merge checks (none if nvalid <= kl).  hist / cbuf: LDS of 2048 and 64 words
+// that only this wave uses from here on.  With `built`, hist already holds the
+// window histogram of the chunk for lo = `lo_built` (see wave_select).
+__device__ __forceinline__ void wave_first_stage(const IndexArgs& a, int n, int blk, const uint32_t (&key)[16],
+                                                 int64_t base, int nvalid, uint32_t* hist, uint32_t* cbuf,
+                                                 bool built = false, uint32_t lo_built = 0u) {
+    const int lane = threadIdx.x & 63;
     const int kl = a.kl;
     uint2* cand = a.cand + ((int64_t)n * a.nchunks + blk) * kl;
     uint2* cnext = a.c_next + (int64_t)n * a.nchunks + blk;
-    const int e0 = tid * 4;
-    uint32_t vmask = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vmask |= (e0 + i < nvalid ? 1u : 0u) << i;
+    const int e0 = 16 * lane;
+    const uint32_t vmask = e0 >= nvalid ? 0u : (nvalid - e0 >= 16 ? 0xffffu : (1u << (nvalid - e0)) - 1u);
     if (nvalid <= kl) {
         // every id is a candidate; no (kl+1)-th element
-        uint32_t tot;
-        uint32_t pos = block_excl_scan<256>((uint32_t)__popc(vmask), s_wave, tot);
+        const uint32_t cntv = (uint32_t)__popc(vmask);
+        uint32_t pos = wave_scan_add(cntv) - cntv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 16; ++i)
             if ((vmask >> i) & 1u) cand[pos++] = make_uint2(key[i], (uint32_t)(base + e0 + i));
-        for (int j = (int)tot + tid; j < kl; j += 256) cand[j] = make_uint2(0u, 0xffffffffu);
-        if (tid == 0) *cnext = make_uint2(0u, 0xffffffffu);
+        for (int j = nvalid + lane; j < kl; j += 64) cand[j] = make_uint2(0u, 0xffffffffu);
+        if (lane == 0) *cnext = make_uint2(0u, 0xffffffffu);
         return;
     }
-    uint32_t rem;
-    const uint32_t T = block_select<256, 4, kChunk>(key, vmask, (uint32_t)kl + 1, &rem, s_hist, s_wave, s_sel, s_cand);
+    const uint32_t want = (uint32_t)kl + 1;
+    uint32_t lo = lo_built;
+    if (!built) {
+        uint32_t kmax = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
+        kmax = wave_max_u32(kmax);
+        constexpr uint32_t kWin = (1u << 24) - 1u;
+        lo = kmax > kWin ? kmax - kWin : 0u;
+    }
+    uint32_t T = 0, rem = 0;
+    if (!wave_select<true>(key, vmask, want, lo, built, hist, cbuf, T, rem))
+        wave_select<false>(key, vmask, want, 0u, false, hist, cbuf, T, rem);
     // the top kl+1 = keys > T and the first `rem` copies of T; its last copy
     // of T (id order) is the (kl+1)-th element and is not a candidate
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
         const bool v = (vmask >> i) & 1u;
         ngt += (v && key[i] > T) ? 1u : 0u;
         neq += (v && key[i] == T) ? 1u : 0u;
     }
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan<256>(ngt | (neq << 16), s_wave, tot);
+    const uint32_t packed = ngt | (neq << 16);
+    const uint32_t pre = wave_scan_add(packed) - packed;
     uint32_t eq_before = pre >> 16;
     uint32_t pos = (pre & 0xffffu) + (eq_before < rem - 1 ? eq_before : rem - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
         if (!((vmask >> i) & 1u)) continue;
         bool sel = key[i] > T;
         if (key[i] == T) {
@@ -480,33 +629,36 @@ __device__ __forceinline__ void chunk_first_stage(const IndexArgs& a, int n, int
     }
 }
 
-// Stand-alone first stage (after the query-blocked score kernel): one
-// 256-thread workgroup per (query, chunk), keys read from the score row.
+// Stand-alone first stage (after the query-blocked score kernel): each wave
+// takes one (query, chunk), keys read from the score row; no barriers.
 __global__ void __launch_bounds__(256) topk_local_kernel(IndexArgs a) {
-    __shared__ uint32_t s_hist[2048];
-    __shared__ uint32_t s_cand[kChunk];
-    __shared__ uint32_t s_wave[4];
-    __shared__ uint32_t s_sel[12];
-    const int n = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[4][2048];
+    __shared__ uint32_t s_cbuf[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = blockIdx.y, blk = blockIdx.x * 4 + wave;
+    if (blk >= a.nchunks) return;
     int s;
     int64_t p;
     const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
     const int64_t base = (int64_t)blk * kChunk;
-    if (base >= nv || nv <= a.k) return;  // uniform; the merge reads chunks below nv only
-    const int64_t nvalid = nv - base < kChunk ? nv - base : kChunk;
-    const float* sc = a.scores + (int64_t)n * a.stride + base;
-    uint32_t key[4];
-    if (tid * 4 + 4 <= nvalid) {
-        const float4 v = reinterpret_cast<const float4*>(sc)[tid];
-        key[0] = score_key(v.x);
-        key[1] = score_key(v.y);
-        key[2] = score_key(v.z);
-        key[3] = score_key(v.w);
+    if (base >= nv || nv <= a.k) return;  // uniform over the wave; the merge reads chunks below nv only
+    const int nvalid = (int)(nv - base < kChunk ? nv - base : kChunk);
+    const float* sc = a.scores + (int64_t)n * a.stride + base + 16 * lane;
+    uint32_t key[16];
+    if (16 * lane + 16 <= nvalid) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float4 x = reinterpret_cast<const float4*>(sc)[v];
+            key[4 * v] = score_key(x.x);
+            key[4 * v + 1] = score_key(x.y);
+            key[4 * v + 2] = score_key(x.z);
+            key[4 * v + 3] = score_key(x.w);
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) key[i] = tid * 4 + i < nvalid ? score_key(sc[tid * 4 + i]) : 0u;
+        for (int i = 0; i < 16; ++i) key[i] = 16 * lane + i < nvalid ? score_key(sc[i]) : 0u;
     }
-    chunk_first_stage(a, n, blk, key, base, nvalid, s_hist, s_wave, s_sel, s_cand);
+    wave_first_stage(a, n, blk, key, base, nvalid, s_hist[wave], s_cbuf[wave]);
 }
 
 template <int DI, int U, bool LOCAL>
@@ -517,7 +669,7 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
     constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
     constexpr int kUnitBytes = 4 * 64 * LROW;
-    constexpr int kSelBytes = (kChunk + 2048 + kChunk + 16) * 4;
+    constexpr int kSelBytes = (kChunk + 2048 + 64 + 4) * 4;
     static_assert(!LOCAL || 4 * U * 64 == kChunk, "a first-stage chunk is one workgroup");
     __shared__ __attribute__((aligned(16))) uint8_t s_mem[kUnitBytes > kSelBytes ? kUnitBytes : kSelBytes];
     const int n = blockIdx.y;
@@ -609,20 +761,45 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     }
     if constexpr (LOCAL) {
         if (nv <= a.k) return;  // uniform: the merge takes every visible id
-        // ---- first stage of the top-k over this chunk
-        __syncthreads();  // every wave is done with its unit slice
+        // ---- first stage of the top-k over this chunk: the four waves
+        // histogram the window below the chunk's largest key, wave 0 finishes
+        const int nvalid = (int)(nv - wg0 < kChunk ? nv - wg0 : kChunk);
+        uint32_t kw[U], kmax = 0u;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            kw[j] = score_key(mine_u[j]);
+            if ((wave * U + j) * 64 + lane < nvalid) kmax = max(kmax, kw[j]);
+        }
+        kmax = wave_max_u32(kmax);
         uint32_t* s_keys = reinterpret_cast<uint32_t*>(s_mem);  // [kChunk], entry order
         uint32_t* s_hist = s_keys + kChunk;                     // [2048]
-        uint32_t* s_cand = s_hist + 2048;                       // [kChunk]
-        uint32_t* s_wave = s_cand + kChunk;                     // [4]
-        uint32_t* s_sel = s_wave + 4;                           // [12]
+        uint32_t* s_cbuf = s_hist + 2048;                       // [64]
+        uint32_t* s_wmax = s_cbuf + 64;                         // [4]
+        __syncthreads();  // every wave is done with its unit slice
 #pragma unroll
-        for (int j = 0; j < U; ++j) s_keys[(wave * U + j) * 64 + lane] = score_key(mine_u[j]);
+        for (int j = 0; j < U; ++j) s_keys[(wave * U + j) * 64 + lane] = kw[j];
+        reinterpret_cast<u32x4*>(s_hist)[tid] = u32x4{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4*>(s_hist)[256 + tid] = u32x4{0u, 0u, 0u, 0u};
+        if (lane == 0) s_wmax[wave] = kmax;
         __syncthreads();
-        const int64_t nvalid = nv - wg0 < kChunk ? nv - wg0 : kChunk;
-        const uint4 kv = reinterpret_cast<const uint4*>(s_keys)[tid];
-        const uint32_t key[4] = {kv.x, kv.y, kv.z, kv.w};
-        chunk_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_wave, s_sel, s_cand);
+        kmax = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
+        constexpr uint32_t kWin = (1u << 24) - 1u;
+        const uint32_t lo = kmax > kWin ? kmax - kWin : 0u;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            if ((wave * U + j) * 64 + lane < nvalid && kw[j] >= lo) atomicAdd(&s_hist[(kw[j] - lo) >> 13], 1u);
+        __syncthreads();
+        if (wave != 0) return;
+        uint32_t key[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint4 kv = reinterpret_cast<const uint4*>(s_keys)[4 * lane + v];
+            key[4 * v] = kv.x;
+            key[4 * v + 1] = kv.y;
+            key[4 * v + 2] = kv.z;
+            key[4 * v + 3] = kv.w;
+        }
+        wave_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_cbuf, true, lo);
     }
 }
 // index_score_tiled_kernel<DI, QW> -- scores for many queries (prefill chunks).
@@ -924,8 +1101,8 @@ hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEv
     if (a.num_q <= 0) return hipSuccess;
     if (a.kl > 0) {
         if (a.tiled)
-            launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)a.nchunks, (unsigned)a.num_q), dim3(256), st,
-                          a);
+            launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)((a.nchunks + 3) / 4), (unsigned)a.num_q),
+                          dim3(256), st, a);
         if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256)
             launch_kernel(ev, !a.tiled, true, topk_merge_kernel<256>, dim3((unsigned)a.num_q), dim3(256), st, a);
         else
