@@ -469,19 +469,67 @@ __device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t 
     return r;
 }
 
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The rank-th largest of cn <= 64 keys in LDS, by one wave (lane j ranks key j
+// against all): T, and *rem = its copies among the top `rank`.
+__device__ __forceinline__ void pairwise_rank(const uint32_t* cbuf, uint32_t cn, uint32_t rank, uint32_t& T,
+                                              uint32_t& rem) {
+    const int lane = threadIdx.x & 63;
+    uint32_t kc = 0, gt = 0, ge = 0;
+    if ((uint32_t)lane < cn) {
+        kc = cbuf[lane];
+        for (uint32_t j = 0; j < cn; ++j) {
+            const uint32_t kj = cbuf[j];
+            gt += kj > kc ? 1u : 0u;
+            ge += kj >= kc ? 1u : 0u;
+        }
+    }
+    const int L = __builtin_ctzll(__ballot((uint32_t)lane < cn && gt < rank && rank <= ge));
+    T = lane_value(kc, L);
+    rem = rank - lane_value(gt, L);
+}
+
+// Emit of a first-stage chunk for slots of 64 consecutive ids (slot i of lane
+// l is id base + 64 (slot0 + i) + l), given T, rem, and the counts of keys > T
+// and == T among the chunk's ids before the first slot: candidates are the
+// keys > T and the first rem - 1 copies of T in id order, each at its rank in
+// id order among the candidates; the rem-th copy of T is the (kl+1)-th element.
+template <int NS>
+__device__ __forceinline__ void emit_first_stage(const uint32_t (&key)[NS], uint32_t vmask, int64_t base, int slot0,
+                                                 uint32_t T, uint32_t rem, uint32_t gt_before, uint32_t eq_before,
+                                                 int kl, uint2* cand, uint2* cnext) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const bool v = (vmask >> i) & 1u;
+        const bool gt = v && key[i] > T, eq = v && key[i] == T;
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        const uint32_t e = eq_before + lanes_below(me);
+        const uint32_t pos = gt_before + lanes_below(mg) + (e < rem - 1 ? e : rem - 1);
+        const uint32_t id = (uint32_t)(base + 64 * (slot0 + i) + lane);
+        if ((gt || (eq && e + 1 < rem)) && pos < (uint32_t)kl) cand[pos] = make_uint2(key[i], id);
+        if (eq && e + 1 == rem) *cnext = make_uint2(T, id);
+        gt_before += (uint32_t)__popcll(mg);
+        eq_before += (uint32_t)__popcll(me);
+    }
+}
+
 // The want-th largest of a wave's keys (16 per lane, slot i valid iff bit i of
 // vmask), by one wave.  Radix rounds over rel = key - lo, counting only keys
 // >= lo: with WINDOW, lo = max - (2^24 - 1) (two octaves of fp32 score below
 // the maximum; digits at bits 13..23, 2..12, 0..1), else lo = 0 (bits 21..31,
 // 10..20, 0..9).  Each round histograms its digit in `hist` (2048 words of
-// LDS; with `built` the caller has already histogrammed round 0 there) and
-// finds the bin of the rank; once that bin holds at most 64 keys they are
+// LDS) and finds the bin of the rank; once that bin holds at most 64 keys they are
 // compacted to `cbuf` (64 words) and ranked pairwise.  Returns false (uniform)
 // if fewer than `want` keys are >= lo; else T and *rem, the number of copies
 // of T inside the top `want`.
 template <bool WINDOW>
 __device__ __forceinline__ bool wave_select(const uint32_t (&key)[16], uint32_t vmask, uint32_t want, uint32_t lo,
-                                            bool built, uint32_t* hist, uint32_t* cbuf, uint32_t& T, uint32_t& rem) {
+                                            uint32_t* hist, uint32_t* cbuf, uint32_t& T, uint32_t& rem) {
     const int lane = threadIdx.x & 63;
     uint32_t rel[16], in = 0;
 #pragma unroll
@@ -506,12 +554,9 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[16], uint32_t 
     };
     // the bin's keys (at most 64) ranked pairwise
     auto finish = [&](uint32_t cn) {
-        const uint32_t mine = [&] {
-            uint32_t m = 0;
+        uint32_t mine = 0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m += matches(i) ? 1u : 0u;
-            return m;
-        }();
+        for (int i = 0; i < 16; ++i) mine += matches(i) ? 1u : 0u;
         uint32_t off = wave_scan_add(mine) - mine;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -520,22 +565,12 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[16], uint32_t 
                 ++off;
             }
         wave_lds_sync();
-        uint32_t kc = 0, gt = 0, ge = 0;
-        if ((uint32_t)lane < cn) {
-            kc = cbuf[lane];
-            for (uint32_t j = 0; j < cn; ++j) {
-                const uint32_t kj = cbuf[j];
-                gt += kj > kc ? 1u : 0u;
-                ge += kj >= kc ? 1u : 0u;
-            }
-        }
-        const int L = __builtin_ctzll(__ballot((uint32_t)lane < cn && gt < rank && rank <= ge));
-        T = lane_value(kc, L) + lo;
-        rem = rank - lane_value(gt, L);
+        pairwise_rank(cbuf, cn, rank, T, rem);
+        T += lo;
         wave_lds_sync();
     };
     constexpr int kSh0 = WINDOW ? 13 : 21, kSh1 = WINDOW ? 2 : 10;
-    if (!built) build(kSh0, 2048);
+    build(kSh0, 2048);
     BinPick b = wave_find_bin<2048>(hist, rank);
     if (b.total < rank) return false;
     take(b, kSh0, 2048);
@@ -565,11 +600,9 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[16], uint32_t 
 // base + nvalid are invalid): the chunk's first kl ids in (score desc, id asc)
 // order, written in ascending id order, and the (kl+1)-th, whose position the
 // merge checks (none if nvalid <= kl).  hist / cbuf: LDS of 2048 and 64 words
-// that only this wave uses from here on.  With `built`, hist already holds the
-// window histogram of the chunk for lo = `lo_built` (see wave_select).
+// that only this wave uses.
 __device__ __forceinline__ void wave_first_stage(const IndexArgs& a, int n, int blk, const uint32_t (&key)[16],
-                                                 int64_t base, int nvalid, uint32_t* hist, uint32_t* cbuf,
-                                                 bool built = false, uint32_t lo_built = 0u) {
+                                                 int64_t base, int nvalid, uint32_t* hist, uint32_t* cbuf) {
     const int lane = threadIdx.x & 63;
     const int kl = a.kl;
     uint2* cand = a.cand + ((int64_t)n * a.nchunks + blk) * kl;
@@ -588,18 +621,14 @@ __device__ __forceinline__ void wave_first_stage(const IndexArgs& a, int n, int 
         return;
     }
     const uint32_t want = (uint32_t)kl + 1;
-    uint32_t lo = lo_built;
-    if (!built) {
-        uint32_t kmax = 0u;
+    uint32_t kmax = 0u;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
-        kmax = wave_max_u32(kmax);
-        constexpr uint32_t kWin = (1u << 24) - 1u;
-        lo = kmax > kWin ? kmax - kWin : 0u;
-    }
+    for (int i = 0; i < 16; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
+    kmax = wave_max_u32(kmax);
+    constexpr uint32_t kWin = (1u << 24) - 1u;
     uint32_t T = 0, rem = 0;
-    if (!wave_select<true>(key, vmask, want, lo, built, hist, cbuf, T, rem))
-        wave_select<false>(key, vmask, want, 0u, false, hist, cbuf, T, rem);
+    if (!wave_select<true>(key, vmask, want, kmax > kWin ? kmax - kWin : 0u, hist, cbuf, T, rem))
+        wave_select<false>(key, vmask, want, 0u, hist, cbuf, T, rem);
     // the top kl+1 = keys > T and the first `rem` copies of T; its last copy
     // of T (id order) is the (kl+1)-th element and is not a candidate
     uint32_t ngt = 0, neq = 0;
@@ -669,7 +698,7 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
     constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
     constexpr int kUnitBytes = 4 * 64 * LROW;
-    constexpr int kSelBytes = (kChunk + 2048 + 64 + 4) * 4;
+    constexpr int kSelBytes = (kChunk + 2048 + 64 + 8) * 4;
     static_assert(!LOCAL || 4 * U * 64 == kChunk, "a first-stage chunk is one workgroup");
     __shared__ __attribute__((aligned(16))) uint8_t s_mem[kUnitBytes > kSelBytes ? kUnitBytes : kSelBytes];
     const int n = blockIdx.y;
@@ -761,45 +790,93 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     }
     if constexpr (LOCAL) {
         if (nv <= a.k) return;  // uniform: the merge takes every visible id
-        // ---- first stage of the top-k over this chunk: the four waves
-        // histogram the window below the chunk's largest key, wave 0 finishes
+        // ---- first stage of the top-k over this chunk (ids wg0 + 64 (wave U + j) + lane):
+        // the four waves histogram the window below the chunk's largest key
+        // (as wave_select's first round), find the bin of the (kl+1)-th key,
+        // gather that bin's keys, rank them pairwise (every wave alike), and
+        // each emits its own ids
+        const int kl = a.kl;
         const int nvalid = (int)(nv - wg0 < kChunk ? nv - wg0 : kChunk);
-        uint32_t kw[U], kmax = 0u;
+        uint2* cand = a.cand + ((int64_t)n * a.nchunks + blockIdx.x) * kl;
+        uint2* cnext = a.c_next + (int64_t)n * a.nchunks + blockIdx.x;
+        uint32_t kw[U], vmask = 0, kmax = 0u;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             kw[j] = score_key(mine_u[j]);
-            if ((wave * U + j) * 64 + lane < nvalid) kmax = max(kmax, kw[j]);
+            const bool v = (wave * U + j) * 64 + lane < nvalid;
+            vmask |= (v ? 1u : 0u) << j;
+            if (v) kmax = max(kmax, kw[j]);
         }
         kmax = wave_max_u32(kmax);
-        uint32_t* s_keys = reinterpret_cast<uint32_t*>(s_mem);  // [kChunk], entry order
+        uint32_t* s_keys = reinterpret_cast<uint32_t*>(s_mem);  // [kChunk], id order
         uint32_t* s_hist = s_keys + kChunk;                     // [2048]
         uint32_t* s_cbuf = s_hist + 2048;                       // [64]
-        uint32_t* s_wmax = s_cbuf + 64;                         // [4]
+        uint32_t* s_w = s_cbuf + 64;                            // [4] wave maxima, then counts; [4] gather count
         __syncthreads();  // every wave is done with its unit slice
+        if (nvalid <= kl) {
+            // every id is a candidate; no (kl+1)-th element
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int e = (wave * U + j) * 64 + lane;
+                if (e < nvalid) cand[e] = make_uint2(kw[j], (uint32_t)(wg0 + e));
+            }
+            for (int j = nvalid + tid; j < kl; j += 256) cand[j] = make_uint2(0u, 0xffffffffu);
+            if (tid == 0) *cnext = make_uint2(0u, 0xffffffffu);
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) s_keys[(wave * U + j) * 64 + lane] = kw[j];
         reinterpret_cast<u32x4*>(s_hist)[tid] = u32x4{0u, 0u, 0u, 0u};
         reinterpret_cast<u32x4*>(s_hist)[256 + tid] = u32x4{0u, 0u, 0u, 0u};
-        if (lane == 0) s_wmax[wave] = kmax;
+        if (lane == 0) s_w[wave] = kmax;
+        if (tid == 0) s_w[4] = 0u;
         __syncthreads();
-        kmax = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
+        kmax = max(max(s_w[0], s_w[1]), max(s_w[2], s_w[3]));
         constexpr uint32_t kWin = (1u << 24) - 1u;
         const uint32_t lo = kmax > kWin ? kmax - kWin : 0u;
 #pragma unroll
         for (int j = 0; j < U; ++j)
-            if ((wave * U + j) * 64 + lane < nvalid && kw[j] >= lo) atomicAdd(&s_hist[(kw[j] - lo) >> 13], 1u);
+            if (((vmask >> j) & 1u) && kw[j] >= lo) atomicAdd(&s_hist[(kw[j] - lo) >> 13], 1u);
         __syncthreads();
-        if (wave != 0) return;
-        uint32_t key[16];
+        const uint32_t want = (uint32_t)kl + 1;
+        const BinPick b = wave_find_bin<2048>(s_hist, want);
+        uint32_t T, rem;
+        if (b.total < want || b.cnt > 64u) {
+            // the window holds fewer than kl+1 keys or a crowded bin: wave 0
+            // runs the single-wave selection over the chunk (after every
+            // wave has read the histogram it reuses)
+            __syncthreads();
+            if (wave != 0) return;
+            uint32_t key[16];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const uint4 kv = reinterpret_cast<const uint4*>(s_keys)[4 * lane + v];
-            key[4 * v] = kv.x;
-            key[4 * v + 1] = kv.y;
-            key[4 * v + 2] = kv.z;
-            key[4 * v + 3] = kv.w;
+            for (int v = 0; v < 4; ++v) {
+                const uint4 kv = reinterpret_cast<const uint4*>(s_keys)[4 * lane + v];
+                key[4 * v] = kv.x;
+                key[4 * v + 1] = kv.y;
+                key[4 * v + 2] = kv.z;
+                key[4 * v + 3] = kv.w;
+            }
+            wave_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_cbuf);
+            return;
         }
-        wave_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_cbuf, true, lo);
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            if (((vmask >> j) & 1u) && kw[j] >= lo && ((kw[j] - lo) >> 13) == b.bin)
+                s_cbuf[atomicAdd(&s_w[4], 1u) & 63u] = kw[j];
+        __syncthreads();
+        pairwise_rank(s_cbuf, b.cnt, b.rank, T, rem);
+        uint32_t ngt = 0, neq = 0;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const bool v = (vmask >> j) & 1u;
+            ngt += (uint32_t)__popcll(__ballot(v && kw[j] > T));
+            neq += (uint32_t)__popcll(__ballot(v && kw[j] == T));
+        }
+        if (lane == 0) s_w[wave] = ngt | (neq << 16);  // the maxima there were read before the histogram
+        __syncthreads();
+        uint32_t before = 0;
+        for (int w = 0; w < wave; ++w) before += s_w[w];
+        emit_first_stage<U>(kw, vmask, wg0, wave * U, T, rem, before & 0xffffu, before >> 16, kl, cand, cnext);
     }
 }
 // index_score_tiled_kernel<DI, QW> -- scores for many queries (prefill chunks).
