@@ -178,8 +178,10 @@ int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_
 
 csl_status check_attn_common(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int n_heads,
                              const int32_t* topk, int k, int swa_window, int out_dtype, const void* out,
-                             const float* out_scales, const uint16_t* q, int64_t max_q_pos) {
+                             const float* out_scales, const uint16_t* q, int64_t max_q_pos, float softmax_scale) {
     csl_status st;
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(CSL_EINVAL, "softmax_scale must be finite and > 0");
     if ((st = check_pages(pages))) return st;
     if ((st = check_pool(swa, "swa"))) return st;
     if (swa->ratio != 1) return fail(CSL_EINVAL, "swa.ratio must be 1 (raw window keys)");
@@ -435,7 +437,7 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
     if (num_q == 0) return CSL_OK;
     csl_status st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
-                                      max_q_pos);
+                                      max_q_pos, softmax_scale);
     if (st) return st;
     if (!q_seq || !q_pos) return fail(CSL_EINVAL, "q_seq or q_pos is NULL");
     const int cr = comp ? comp->ratio : 0;
@@ -478,7 +480,7 @@ csl_status csl_hybrid_attn_prefill(const csl_pool* comp, const csl_pool* swa, co
     if (total_q < 0) return fail(CSL_EINVAL, "total_q < 0");
     if (total_q == 0) return CSL_OK;
     csl_status st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
-                                      max_q_pos);
+                                      max_q_pos, softmax_scale);
     if (st) return st;
     if (!cu_q || !q_pos_start) return fail(CSL_EINVAL, "cu_q or q_pos_start is NULL");
     uint32_t* err = nullptr;

@@ -578,6 +578,26 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// acc *= f for an accumulator tile held in AGPRs, in place.  Written as one
+// assembly block over the 16 registers (read, multiply, write back through
+// one VGPR) so that the compiler keeps no VGPR copy of the accumulator alive
+// for this rarely taken path; the trailing wait states cover an MFMA that
+// reads the tile next.
+__device__ __forceinline__ void scale_agpr16(f32x16& acc, float f) {
+    float e0 = acc[0], e1 = acc[1], e2 = acc[2], e3 = acc[3], e4 = acc[4], e5 = acc[5], e6 = acc[6], e7 = acc[7];
+    float e8 = acc[8], e9 = acc[9], e10 = acc[10], e11 = acc[11], e12 = acc[12], e13 = acc[13], e14 = acc[14],
+          e15 = acc[15];
+    float t;
+#define CSL_RS(i) "v_accvgpr_read_b32 %16, %" #i "\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %" #i ", %16\n\t"
+    asm volatile(CSL_RS(0) CSL_RS(1) CSL_RS(2) CSL_RS(3) CSL_RS(4) CSL_RS(5) CSL_RS(6) CSL_RS(7) CSL_RS(8) CSL_RS(9)
+                     CSL_RS(10) CSL_RS(11) CSL_RS(12) CSL_RS(13) CSL_RS(14) CSL_RS(15) "s_nop 7"
+                 : "+a"(e0), "+a"(e1), "+a"(e2), "+a"(e3), "+a"(e4), "+a"(e5), "+a"(e6), "+a"(e7), "+a"(e8), "+a"(e9),
+                   "+a"(e10), "+a"(e11), "+a"(e12), "+a"(e13), "+a"(e14), "+a"(e15), "=&v"(t)
+                 : "v"(f));
+#undef CSL_RS
+    acc = f32x16{e0, e1, e2, e3, e4, e5, e6, e7, e8, e9, e10, e11, e12, e13, e14, e15};
+}
+
 template <bool PREC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 hybrid_attn_mqa512_kernel(AttnArgs a) {
@@ -663,16 +683,13 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         for (int ks = 0; ks < 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
     };
     auto s_mfma = [&](const bf16x8 (&ka)[16]) {
-        // two independent accumulation chains (even / odd k-steps)
-        f32x16 s0, s1;
+        // one accumulation chain (dependent 32x32x16 MFMAs issue back to back)
+        f32x16 s0;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) s0[c] = s1[c] = 0.f;
+        for (int c = 0; c < 16; ++c) s0[c] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 16; ks += 2) {
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks + 1], qb[ks + 1], s1, 0, 0, 0);
-        }
-        return s0 + s1;
+        for (int ks = 0; ks < 16; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s0, 0, 0, 0);
+        return s0;
     };
     // the two halves of a head group meet in LDS (the lanes of waves w and w ^ 2
     // hold the same (head, key) positions)
@@ -704,22 +721,27 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     };
     auto softmax = [&](uint32_t vb, const f32x16& sacc) {
         Soft o;
-        // value 4j + i is accumulator row 8j + 4h2 + i = key 16 h2 + 4i + j of this head column
+        // value 4j + i is accumulator row 8j + 4h2 + i = key 16 h2 + 4i + j of this head column;
+        // raw scores here, the (positive) logit scale enters the max and the exponent
         float x[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[c] = sacc[c];
+        if (__builtin_amdgcn_readfirstlane(vb) != 0xffffffffu) {
+            // a masked key in this tile (ragged end, unused top-k slot)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((vb >> (16 * h2 + 4 * i + j)) & 1u)) x[4 * j + i] = -INFINITY;
+        }
         float tmax = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = 16 * h2 + 4 * i + j;
-                const float v = ((vb >> key) & 1u) ? sacc[4 * j + i] * a.scale_log2 : -INFINITY;
-                x[4 * j + i] = v;
-                tmax = fmaxf(tmax, v);
-            }
+        for (int c = 0; c < 16; ++c) tmax = fmaxf(tmax, x[c]);
         {
             const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
             tmax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
         }
+        tmax *= a.scale_log2;
         // lazy reference: moves only when the max passes it by more than 8
         const bool move = tmax > m_ref + 8.0f;
         const float alpha = __builtin_amdgcn_exp2f(move ? m_ref - tmax : 0.f);
@@ -732,7 +754,8 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         uint32_t pw[8], pl[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float p0 = __builtin_amdgcn_exp2f(x[2 * c] - m_use), p1 = __builtin_amdgcn_exp2f(x[2 * c + 1] - m_use);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * c], a.scale_log2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * c + 1], a.scale_log2, -m_use));
             psum += p0 + p1;
             pw[c] = pack_bf16x2(p0, p1);
             if constexpr (PREC)
@@ -754,7 +777,7 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     auto pv = [&](const Soft& sm, const uint8_t* kt) {
         if (__ballot(sm.rescale)) {
 #pragma unroll
-            for (int m = 0; m < 8; ++m) oacc[m] *= sm.alpha;
+            for (int m = 0; m < 8; ++m) scale_agpr16(oacc[m], sm.alpha);
         }
         bf16x8 va[8][2];
 #pragma unroll

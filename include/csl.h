@@ -182,8 +182,9 @@ csl_status csl_index_topk(const csl_pool* index_pool /* host */, const csl_pages
  *   CSL_FP8_E4M3: out [num_q][n_heads][dim] e4m3fn codes and out_scales
  *   [num_q][n_heads][dim/64] fp32, scale = amax/448 per 64 elements.
  * An empty key set gives 0.  q: [num_q][n_heads][dim] bf16, already normed
- * and rotated at p.  Limits: dim in {128, 512}, n_heads <= 64, rope_dims and
- * rope_theta taken from `swa` (comp must match).
+ * and rotated at p.  Limits: dim in {128, 512}, n_heads <= 64, softmax_scale
+ * finite and > 0 (else CSL_EINVAL), rope_dims and rope_theta taken from `swa`
+ * (comp must match).
  *
  * decode:  queries listed one by one (q_seq, q_pos: [num_q]); long key sets
  *          are split across workgroups and merged (needs ws).

@@ -103,9 +103,10 @@ def test_index_validation(csl):
     assert index(csl, ip, pg(csl), nq=0) == 0
 
 
-def attn(csl, comp, swa, G, heads=64, topk=FAKE, k=512, out_dtype=1, scales=None, max_pos=1000, ws_bytes=1 << 30):
+def attn(csl, comp, swa, G, heads=64, topk=FAKE, k=512, out_dtype=1, scales=None, max_pos=1000, ws_bytes=1 << 30,
+         scale=0.04):
     cp = C.byref(comp) if comp is not None else None
-    return csl._attn_decode(cp, C.byref(swa), C.byref(G), 4, FAKE, FAKE, max_pos, FAKE, heads, topk, k, 128, 0.04,
+    return csl._attn_decode(cp, C.byref(swa), C.byref(G), 4, FAKE, FAKE, max_pos, FAKE, heads, topk, k, 128, scale,
                             out_dtype, FAKE, scales, FAKE, ws_bytes, None)
 
 
@@ -121,3 +122,5 @@ def test_attn_validation(csl):
     assert attn(csl, None, swa, pg(csl)) == -1                             # top-k without a compressed pool
     assert attn(csl, comp, swa, pg(csl), max_pos=5000) == -2
     assert attn(csl, comp, swa, pg(csl), ws_bytes=0) == -4
+    for bad in (0.0, -0.04, float("inf"), float("nan")):                   # the logit scale must be > 0
+        assert attn(csl, comp, swa, pg(csl), scale=bad) == -1
