@@ -102,6 +102,48 @@ __device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, int n, int 
     return a.swa_rows + ((int64_t)pg * kBlockPositions + (t & 255)) * row_bytes(a.swa_dtype, D);
 }
 
+// key_row for the keys kb + u*NT + tid (u < NU) of one thread at once: every
+// top-k id is loaded before any page-table entry, so the dependent global
+// loads of the NU keys overlap instead of running one key after another.
+template <int NU, int NT>
+__device__ __forceinline__ void key_rows(const AttnArgs& a, int n, int s, int64_t kb, int64_t ke, int64_t Lc,
+                                         int64_t nv_c, int64_t lo, const uint8_t* (&row)[NU]) {
+    const int tid = threadIdx.x;
+    int64_t id[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int64_t j = kb + u * NT + tid;
+        id[u] = (j < ke && j < Lc) ? (a.topk ? (int64_t)a.topk[(int64_t)n * a.k + j] : j) : -1;
+    }
+    int64_t t[NU];
+    int32_t pg[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int64_t j = kb + u * NT + tid;
+        const bool comp = j < Lc;
+        if (comp && id[u] >= nv_c) {
+            raise_error(a.err, kErrTopk);
+            id[u] = -1;
+        }
+        t[u] = j >= ke ? -1 : comp ? (id[u] >= 0 ? id[u] * a.comp_ratio : -1) : lo + (j - Lc);
+        pg[u] = t[u] >= 0 ? page_of(a.bt, a.max_blocks, comp ? a.comp_pages : a.swa_pages, s, t[u]) : -1;
+    }
+    const int D = a.dim;
+    const int per = kBlockPositions / (a.comp_ratio > 0 ? a.comp_ratio : 1);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int64_t j = kb + u * NT + tid;
+        row[u] = nullptr;
+        if (t[u] < 0) continue;
+        if (pg[u] < 0) {
+            raise_error(a.err, kErrPage);
+            continue;
+        }
+        row[u] = j < Lc ? a.comp_rows + ((int64_t)pg[u] * per + (id[u] % per)) * row_bytes(a.comp_dtype, D)
+                        : a.swa_rows + ((int64_t)pg[u] * kBlockPositions + (t[u] & 255)) * row_bytes(a.swa_dtype, D);
+    }
+}
+
 // A thread's slice of 4 key rows: bf16 words, or fp8 codes + the group scale.
 template <int D, int KV>
 struct Slice {
@@ -412,10 +454,9 @@ hybrid_attn_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            uint32_t code = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) code |= f32_to_e4m3(acc[m][i] / gmax[m >> 2]) << (8 * i);
-            *reinterpret_cast<uint32_t*>(o + 16 * m + 4 * g) = code;
+            const float r = 1.0f / gmax[m >> 2];
+            *reinterpret_cast<uint32_t*>(o + 16 * m + 4 * g) =
+                e4m3_pack4(acc[m][0] * r, acc[m][1] * r, acc[m][2] * r, acc[m][3] * r);
         }
     }
 }
@@ -511,9 +552,9 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
         amax = group8_max(active ? amax : 0.f);
         const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
         if (active) {
-            u32x2 w = {0u, 0u};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) w[c >> 2] |= f32_to_e4m3(o[c] / scale) << (8 * (c & 3));
+            const float r = 1.0f / scale;
+            const u32x2 w = {e4m3_pack4(o[0] * r, o[1] * r, o[2] * r, o[3] * r),
+                             e4m3_pack4(o[4] * r, o[5] * r, o[6] * r, o[7] * r)};
             *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.out) + obase) = w;
             if ((lane & 7) == 0) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + (lane >> 3)] = scale;
         }
@@ -663,14 +704,15 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     const int tr_col = (256 * dh + 16 * (G & 1) + 4 * (ig & 3)) * 2;  // bytes, + 64 m
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // (all 8 row addresses are read before the first copy is issued: the
+    // copies' memory clobber would otherwise order each read behind them)
     auto issue_tile = [&](int tl) {
         const uint8_t* buf = s_kt[tl % kRing2];
+        const uint8_t* row[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * wave_u + i;
-            const uint8_t* row = s_rows[tl * kT2 + r];
-            lds_dma_row(lds_addr(buf + r * kRow2), (row ? row : g_zero_kv_row) + 16 * lane);
-        }
+        for (int i = 0; i < 8; ++i) row[i] = s_rows[tl * kT2 + 8 * wave_u + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma_row(lds_addr(buf + (8 * wave_u + i) * kRow2), row[i] + 16 * lane);
     };
     // the wave's half of S^T for a staged tile (its 256 dims): A = key rows (LDS), B = q
     // accumulator row r = 8j + 4h + i holds key sigma(r) = 16h + 4i + j of the tile:
@@ -830,14 +872,20 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         const int64_t ke = kb + kMaxKeys2 < k_end ? kb + kMaxKeys2 : k_end;
         const int ntl = (int)((ke - kb + kT2 - 1) / kT2);
         __syncthreads();  // the previous pass is done with s_rows and the tiles
-        for (int base = 0; base < ntl * kT2; base += kThreads) {
-            const int i = base + tid;
-            const uint8_t* r = (kb + i < ke) ? key_row(a, n, s, kb + i, Lc, nv_c, lo) : nullptr;
-            if (i < ntl * kT2) s_rows[i] = r;
-            const uint64_t bits = __ballot(r != nullptr);
-            const int t0 = (base + 64 * wave) / kT2;
-            if (lane == 0 && t0 < ntl) s_vbits[t0] = (uint32_t)bits;
-            if (lane == 0 && t0 + 1 < ntl) s_vbits[t0 + 1] = (uint32_t)(bits >> 32);
+        {
+            constexpr int kPer = kMaxKeys2 / kThreads;
+            const uint8_t* rr[kPer];
+            key_rows<kPer, kThreads>(a, n, s, kb, ke, Lc, nv_c, lo, rr);
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int i = u * kThreads + tid;
+                if (u * kThreads >= ntl * kT2) break;  // uniform
+                if (i < ntl * kT2) s_rows[i] = rr[u] ? rr[u] : g_zero_kv_row;  // a masked key copies the zero row
+                const uint64_t bits = __ballot(rr[u] != nullptr);
+                const int t0 = (u * kThreads + 64 * wave) / kT2;
+                if (lane == 0 && t0 < ntl) s_vbits[t0] = (uint32_t)bits;
+                if (lane == 0 && t0 + 1 < ntl) s_vbits[t0 + 1] = (uint32_t)(bits >> 32);
+            }
         }
         __syncthreads();
         for (int t = 0; t < 3 && t < ntl; ++t) issue_tile(t);
@@ -948,21 +996,20 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
                 amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
             }
             const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+            const float r = 1.0f / scale;
             if (h2 == 0) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + 4 * dh + g4] = scale;
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
                 const int m = 2 * g4 + mm;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t code = 0;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) code |= f32_to_e4m3(oacc[m][4 * j + i] / scale) << (8 * i);
-                    *reinterpret_cast<uint32_t*>(o + 32 * m + 8 * j) = code;
-                }
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint32_t*>(o + 32 * m + 8 * j) =
+                        e4m3_pack4(oacc[m][4 * j] * r, oacc[m][4 * j + 1] * r, oacc[m][4 * j + 2] * r, oacc[m][4 * j + 3] * r);
             }
         }
     }
 }
+
 
 }  // namespace
 

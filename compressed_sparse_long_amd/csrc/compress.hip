@@ -80,9 +80,9 @@ __device__ __forceinline__ void store8(uint8_t* row, int dtype, int dim, int lan
     amax = group8_max(active ? amax : 0.f);
     float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     if (active) {
-        u32x2 o = {0u, 0u};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c >> 2] |= f32_to_e4m3(v[c] / scale) << (8 * (c & 3));
+        const float r = 1.0f / scale;
+        const u32x2 o = {e4m3_pack4(v[0] * r, v[1] * r, v[2] * r, v[3] * r),
+                         e4m3_pack4(v[4] * r, v[5] * r, v[6] * r, v[7] * r)};
         *reinterpret_cast<u32x2*>(row + 8 * lane) = o;
         if ((lane & 7) == 0) *reinterpret_cast<float*>(row + dim + 4 * (lane >> 3)) = scale;
     }

@@ -50,22 +50,30 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
     return (c & 0x80u) ? -v : v;
 }
 
-// fp32 -> OCP e4m3fn code, round to nearest even, saturating at +-448.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-    uint32_t u = __float_as_uint(x);
-    uint32_t s = (u >> 24) & 0x80u;
-    float a = fabsf(x);
-    if (a != a) return s | 0x7fu;
-    if (a >= 448.0f) return s | 0x7eu;
-    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
-        return s | (uint32_t)rintf(a * 512.0f);  // 8 -> code 0x08 = 2^-6, consistent
-    }
-    uint32_t ua = __float_as_uint(a);
-    uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);  // RNE at the 3rd mantissa bit
-    uint32_t e = (r >> 23) - 120u;
-    uint32_t m = (r >> 20) & 7u;
-    return s | (e << 3) | m;
+// fp32 -> OCP e4m3fn codes, round to nearest even, saturating at +-448, NaN
+// -> 0x7f with the sign.  The packed hardware conversion v_cvt_pk_fp8_f32
+// rounds the same way (checked against the bitwise definition -- sign,
+// exponent and mantissa rounding with subnormals at multiples of 2^-9 -- on
+// every finite input below 464 in magnitude); clamping to +-448 first gives
+// the saturation, and NaN is passed through by hand.
+__device__ __forceinline__ float e4m3_clamp(float x) { return x != x ? x : fminf(fmaxf(x, -448.0f), 448.0f); }
+__device__ __forceinline__ uint32_t e4m3_nan_fix(float x, uint32_t code, int byte) {
+    return x != x ? (code & ~(0xffu << (8 * byte))) | (((__float_as_uint(x) >> 24) & 0x80u | 0x7fu) << (8 * byte)) : code;
 }
+// codes of a, b, c, d in bytes 0..3
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    uint32_t code = (uint32_t)w;
+    if (__builtin_expect((a != a) | (b != b) | (c != c) | (d != d), 0)) {
+        code = e4m3_nan_fix(a, code, 0);
+        code = e4m3_nan_fix(b, code, 1);
+        code = e4m3_nan_fix(c, code, 2);
+        code = e4m3_nan_fix(d, code, 3);
+    }
+    return code;
+}
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) { return e4m3_pack4(x, 0.f, 0.f, 0.f) & 0xffu; }
 
 // ---------------------------------------------------------------- waves
 
