@@ -163,10 +163,15 @@ int index_local_k(int64_t max_q_pos, int k) {
     return nchunks * kl <= 8192 ? kl : 0;
 }
 
-int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
+// 32-key tiles of the longest key list any query at or below max_q_pos can have.
+int64_t decode_tiles(int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
     int64_t keys = (int64_t)(swa_window < max_q_pos ? swa_window : max_q_pos);
     if (comp_ratio > 0) keys += k > 0 ? k : max_q_pos / comp_ratio;
-    int64_t tiles = (keys + 31) / 32;
+    return (keys + 31) / 32;
+}
+
+int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
+    const int64_t tiles = decode_tiles(comp_ratio, k, swa_window, max_q_pos);
     // enough workgroups to spread over the CUs, but at least 2 tiles (64 keys)
     // per split: every split writes a heads x dim fp32 partial
     int64_t want = (512 + num_q - 1) / (num_q > 0 ? num_q : 1);
@@ -458,6 +463,7 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     a.q_pos_start = nullptr;
     a.num_q = num_q;
     a.n_splits = sp;
+    a.tiles_per_split = (decode_tiles(cr, kk, swa_window, max_q_pos) + sp - 1) / sp;
     if (sp > 1) {
         a.part_o = static_cast<float*>(ws);
         a.part_ml = a.part_o + (size_t)num_q * sp * n_heads * swa->dim;
@@ -494,6 +500,7 @@ csl_status csl_hybrid_attn_prefill(const csl_pool* comp, const csl_pool* swa, co
     a.q_pos_start = q_pos_start;
     a.num_q = total_q;
     a.n_splits = 1;
+    a.tiles_per_split = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed(CSL_KERNEL_ATTN, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");

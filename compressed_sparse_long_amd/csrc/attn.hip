@@ -105,15 +105,19 @@ __device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, int n, int 
 // key_row for the keys kb + u*NT + tid (u < NU) of one thread at once: every
 // top-k id is loaded before any page-table entry, so the dependent global
 // loads of the NU keys overlap instead of running one key after another.
+// With use_pre, `pre` holds the ids of these keys loaded earlier (top-k
+// entries for j < k, else j).
 template <int NU, int NT>
 __device__ __forceinline__ void key_rows(const AttnArgs& a, int n, int s, int64_t kb, int64_t ke, int64_t Lc,
-                                         int64_t nv_c, int64_t lo, const uint8_t* (&row)[NU]) {
+                                         int64_t nv_c, int64_t lo, const uint8_t* (&row)[NU], bool use_pre,
+                                         const int64_t (&pre)[NU]) {
     const int tid = threadIdx.x;
     int64_t id[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
         const int64_t j = kb + u * NT + tid;
-        id[u] = (j < ke && j < Lc) ? (a.topk ? (int64_t)a.topk[(int64_t)n * a.k + j] : j) : -1;
+        const bool in = j < ke && j < Lc;
+        id[u] = !in ? -1 : use_pre ? pre[u] : a.topk ? (int64_t)a.topk[(int64_t)n * a.k + j] : j;
     }
     int64_t t[NU];
     int32_t pg[NU];
@@ -655,6 +659,31 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     const int n = blockIdx.x % a.num_q;
     const int sp = blockIdx.x / a.num_q;
 
+    // Loads that do not depend on the query's position go first, so their
+    // latencies overlap with the position lookup: the q rows and the top-k ids
+    // of the first key pass (a split's key range is fixed by the host-side
+    // tiles-per-split bound, not by the position).
+    const int head = 32 * hg + r32;
+    const bool hv = head < a.n_heads;
+    // q as the B operand of S^T over the wave's 256 dims: column = head, k-step ks =
+    // dims 256 dh + 16 ks + 8 h2 .. +7
+    // (a missing head reads zeros from the zero row: 512 bf16, the same span)
+    bf16x8 qb[16];
+    {
+        const uint16_t* qrow = (hv ? a.q + ((int64_t)n * a.n_heads + head) * D
+                                   : reinterpret_cast<const uint16_t*>(g_zero_kv_row)) + 256 * dh + 8 * h2;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+    }
+    const int64_t t_begin = a.n_splits > 1 ? (int64_t)sp * a.tiles_per_split : 0;
+    constexpr int kPer = kMaxKeys2 / kThreads;
+    int64_t pre_id[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t j = t_begin * kT2 + u * kThreads + tid;
+        pre_id[u] = (a.topk && a.comp_rows && j < a.k) ? (int64_t)a.topk[(int64_t)n * a.k + j] : j;
+    }
+
     QueryInfo qi = query_info(a, n);
     if (!qi.ok && sp == 0 && tid == 0) raise_error(a.err, (qi.s < 0 || qi.s >= a.num_seqs) ? kErrSeq : kErrPos);
     const int s = qi.s;
@@ -664,29 +693,14 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     const int64_t lo = p - a.swa_window > 0 ? p - a.swa_window : 0;
     const int64_t L = qi.ok ? Lc + (p - lo) : 0;
     const int64_t n_tiles = (L + kT2 - 1) / kT2;
-    const int64_t tps = (n_tiles + a.n_splits - 1) / a.n_splits;
-    const int64_t t_begin = sp * tps;
-    const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
+    const int64_t t_end = a.n_splits > 1 ? (t_begin + a.tiles_per_split < n_tiles ? t_begin + a.tiles_per_split : n_tiles)
+                                         : n_tiles;
     const int64_t k_end = t_end * kT2 < L ? t_end * kT2 : L;
     if (a.n_splits == 1 && tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
 
     // An AGPR operand in inline assembly makes the compiler select the MFMAs'
     // accumulator-register form, so the output accumulator stays in AGPRs.
     asm volatile("; accumulators in AGPRs" ::"a"(0.f));
-    const int head = 32 * hg + r32;
-    const bool hv = head < a.n_heads;
-    // q as the B operand of S^T over the wave's 256 dims: column = head, k-step ks =
-    // dims 256 dh + 16 ks + 8 h2 .. +7
-    bf16x8 qb[16];
-    {
-        const uint16_t* qrow = a.q + ((int64_t)n * a.n_heads + (hv ? head : 0)) * D + 256 * dh + 8 * h2;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-            if (!hv) v = u32x4{0u, 0u, 0u, 0u};
-            qb[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
     // O^T tiles m = 0..7: value 4j + i = dim 256 dh + 32 m + 8 j + 4 h2 + i of this head
     f32x16 oacc[8];
 #pragma unroll
@@ -871,11 +885,11 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     for (int64_t kb = t_begin * kT2; kb < k_end; kb += kMaxKeys2) {
         const int64_t ke = kb + kMaxKeys2 < k_end ? kb + kMaxKeys2 : k_end;
         const int ntl = (int)((ke - kb + kT2 - 1) / kT2);
-        __syncthreads();  // the previous pass is done with s_rows and the tiles
+        const bool first = kb == t_begin * kT2;
+        if (!first) __syncthreads();  // the previous pass is done with s_rows and the tiles
         {
-            constexpr int kPer = kMaxKeys2 / kThreads;
             const uint8_t* rr[kPer];
-            key_rows<kPer, kThreads>(a, n, s, kb, ke, Lc, nv_c, lo, rr);
+            key_rows<kPer, kThreads>(a, n, s, kb, ke, Lc, nv_c, lo, rr, first, pre_id);
 #pragma unroll
             for (int u = 0; u < kPer; ++u) {
                 const int i = u * kThreads + tid;
@@ -923,9 +937,8 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     }
 
     const float l_tot = sum_xor32(l_run);
-    if (!hv) return;
-
     if (a.n_splits > 1) {
+        if (!hv) return;
         // unnormalised partial relative to m_ref: dims 256 dh + 32 m + 8 j + 4 h2 .. +3 of this head
         float* po = a.part_o + (((int64_t)n * a.n_splits + sp) * a.n_heads + head) * D + 256 * dh + 4 * h2;
 #pragma unroll
@@ -942,12 +955,19 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         return;
     }
 
-    // epilogue: normalise, RoPE^-1 at p (pairs are adjacent values i = 0,1 / 2,3), store
+    // epilogue.  The accumulator is read once: RoPE^-1 at p on the raw values of
+    // the rotated dims (pairs are adjacent values i = 0,1 / 2,3; the rotation
+    // commutes with the 1/l scaling), then 1/l and the conversion.  For fp8 the
+    // 1/l cancels inside each 64-dim group: code = e4m3(v * 448 / amax(v)),
+    // scale = amax(v) / l / 448.  The converted rows are staged in the (now
+    // idle) tile ring in output order, padded against bank conflicts, and the
+    // query's output leaves with contiguous 16-byte stores.
     const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int rbase = D - a.rope_dims;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        oacc[m] *= inv_l;
+    const int esz = a.out_dtype == kF32 ? 4 : a.out_dtype == kBF16 ? 2 : 1;
+    const int rstride = D * esz + 16;
+    uint8_t* stage = &s_kt[0][0];
+    auto rope_tile = [&](f32x16& v, int m) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int d0 = 256 * dh + 32 * m + 8 * j + 4 * h2;
@@ -956,57 +976,68 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
                 for (int c = 0; c < 2; ++c) {
                     const int pj = (d0 + 2 * c - rbase) >> 1;
                     const float cs = s_rope[0][pj], sn = s_rope[1][pj];
-                    const float u = oacc[m][4 * j + 2 * c], v = oacc[m][4 * j + 2 * c + 1];
-                    oacc[m][4 * j + 2 * c] = u * cs - v * sn;
-                    oacc[m][4 * j + 2 * c + 1] = u * sn + v * cs;
+                    const float u = v[4 * j + 2 * c], w = v[4 * j + 2 * c + 1];
+                    v[4 * j + 2 * c] = u * cs - w * sn;
+                    v[4 * j + 2 * c + 1] = u * sn + w * cs;
                 }
             }
         }
-    }
-    const int64_t obase = ((int64_t)n * a.n_heads + head) * D + 256 * dh + 4 * h2;
-    if (a.out_dtype == kF32) {
-        float* o = reinterpret_cast<float*>(a.out) + obase;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<f32x4*>(o + 32 * m + 8 * j) =
-                    f32x4{oacc[m][4 * j], oacc[m][4 * j + 1], oacc[m][4 * j + 2], oacc[m][4 * j + 3]};
-    } else if (a.out_dtype == kBF16) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + obase;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<u32x2*>(o + 32 * m + 8 * j) =
-                    u32x2{pack_bf16x2(oacc[m][4 * j], oacc[m][4 * j + 1]),
-                          pack_bf16x2(oacc[m][4 * j + 2], oacc[m][4 * j + 3])};
-    } else {
-        // 64-dim groups: tiles m = 2G, 2G+1 of the wave's 256 dims, halves h2 = 0, 1
-        uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + obase;
+    };
+    __syncthreads();  // every wave is done with the ring
+    uint8_t* srow = stage + head * rstride;
+    if (a.out_dtype == kFP8) {
+        // 64-dim groups: tiles m = 2 g4, 2 g4 + 1 of the wave's 256 dims, halves h2 = 0, 1
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+            f32x16 v0 = oacc[2 * g4], v1 = oacc[2 * g4 + 1];
+            rope_tile(v0, 2 * g4);
+            rope_tile(v1, 2 * g4 + 1);
             float amax = 0.f;
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-                for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(oacc[2 * g4 + mm][c]));
+            for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fmaxf(fabsf(v0[c]), fabsf(v1[c])));
             {
                 const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
                 amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
             }
-            const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-            const float r = 1.0f / scale;
-            if (h2 == 0) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + 4 * dh + g4] = scale;
+            const float gmax = amax * inv_l;
+            const float scale = gmax > 0.f ? gmax / 448.0f : 1.0f;
+            const float r = gmax > 0.f ? 448.0f / amax : 0.f;
+            if (h2 == 0 && hv) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + 4 * dh + g4] = scale;
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
+                const f32x16& v = mm ? v1 : v0;
                 const int m = 2 * g4 + mm;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint32_t*>(o + 32 * m + 8 * j) =
-                        e4m3_pack4(oacc[m][4 * j] * r, oacc[m][4 * j + 1] * r, oacc[m][4 * j + 2] * r, oacc[m][4 * j + 3] * r);
+                    *reinterpret_cast<uint32_t*>(srow + 256 * dh + 32 * m + 8 * j + 4 * h2) =
+                        e4m3_pack4(v[4 * j] * r, v[4 * j + 1] * r, v[4 * j + 2] * r, v[4 * j + 3] * r);
             }
         }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            f32x16 v = oacc[m];
+            rope_tile(v, m);
+            v *= inv_l;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 256 * dh + 32 * m + 8 * j + 4 * h2;
+                if (a.out_dtype == kF32)
+                    *reinterpret_cast<f32x4*>(srow + 4 * d0) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+                else
+                    *reinterpret_cast<u32x2*>(srow + 2 * d0) =
+                        u32x2{pack_bf16x2(v[4 * j], v[4 * j + 1]), pack_bf16x2(v[4 * j + 2], v[4 * j + 3])};
+            }
+        }
+    }
+    __syncthreads();
+    // the query's n_heads rows (contiguous in the output) in 16-byte chunks
+    const int rchunks = D * esz / 16;
+    const int nchunks = a.n_heads * rchunks;
+    uint8_t* out = reinterpret_cast<uint8_t*>(a.out) + (int64_t)n * a.n_heads * D * esz;
+    for (int c = tid; c < nchunks; c += kThreads) {
+        const int h = c / rchunks, off = (c - h * rchunks) * 16;
+        *reinterpret_cast<u32x4*>(out + (int64_t)c * 16) = *reinterpret_cast<const u32x4*>(stage + h * rstride + off);
     }
 }
 

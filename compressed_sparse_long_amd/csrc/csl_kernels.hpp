@@ -71,6 +71,7 @@ struct AttnArgs {
     int64_t max_q_pos;
     int num_q, n_heads, dim, rope_dims, k, swa_window, comp_ratio, comp_dtype, swa_dtype, out_dtype;
     int comp_pages, swa_pages, num_seqs, max_blocks, n_splits;
+    int64_t tiles_per_split;  // n_splits > 1: 32-key tiles of each split (from the longest possible key list)
     float scale_log2;  // softmax_scale * log2(e)
     RopeFreqs rf;
 };
