@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csl_oracle.c")
 LIB = os.path.join(HERE, "libcsl_oracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, FP4 = 0, 1, 2, 3
 BLOCK = 256
 
 
@@ -59,6 +59,12 @@ def lib():
         L.csl_oracle_e4m3_to_f64.restype = dbl
         L.csl_oracle_f64_to_e4m3.argtypes = [dbl]
         L.csl_oracle_f64_to_e4m3.restype = C.c_uint8
+        L.csl_oracle_e2m1_to_f64.argtypes = [C.c_int]
+        L.csl_oracle_e2m1_to_f64.restype = dbl
+        L.csl_oracle_f64_to_e2m1.argtypes = [dbl]
+        L.csl_oracle_f64_to_e2m1.restype = C.c_int
+        L.csl_oracle_mxfp4_block.argtypes = [vp, vp, vp]
+        L.csl_oracle_mxfp4_block.restype = None
         L.csl_oracle_rope.argtypes = [vp, C.c_int, C.c_int, dbl, i64]
         L.csl_oracle_rope.restype = None
         L.csl_oracle_compress_insert.argtypes = [C.POINTER(Pool), vp, C.c_int, C.c_int, vp, vp, vp, vp, vp, dbl]
@@ -102,6 +108,24 @@ def e4m3_to_f64(c: int) -> float:
 
 def f64_to_e4m3(v: float) -> int:
     return int(lib().csl_oracle_f64_to_e4m3(v))
+
+
+def e2m1_to_f64(c: int) -> float:
+    return float(lib().csl_oracle_e2m1_to_f64(c))
+
+
+def f64_to_e2m1(v: float) -> int:
+    return int(lib().csl_oracle_f64_to_e2m1(v))
+
+
+def mxfp4_block(y: np.ndarray) -> tuple:
+    """One 32-element MXFP4 block of y: (16 code bytes, E8M0 scale code)."""
+    yy = np.ascontiguousarray(y, dtype=np.float64)
+    assert yy.shape == (32,)
+    codes = np.zeros(16, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    lib().csl_oracle_mxfp4_block(yy.ctypes.data, codes.ctypes.data, sc.ctypes.data)
+    return codes, int(sc[0])
 
 
 def rope(v: np.ndarray, rope_dims: int, theta: float, pos: int) -> np.ndarray:
@@ -215,7 +239,7 @@ def num_threads() -> int:
 
 
 def decode_rows(rows: np.ndarray, dim: int, dtype: int) -> np.ndarray:
-    """fp64 values of stored rows [..., row_bytes] (bf16 or fp8+scales), via the oracle's own decoders."""
+    """fp64 values of stored rows [..., row_bytes] (bf16, fp8+scales or fp4+E8M0), via the oracle's own decoders."""
     shp = rows.shape[:-1]
     r = rows.reshape(-1, rows.shape[-1])
     out = np.empty((r.shape[0], dim), np.float64)
@@ -225,6 +249,13 @@ def decode_rows(rows: np.ndarray, dim: int, dtype: int) -> np.ndarray:
         table = np.array([e4m3_to_f64(c) for c in range(256)], np.float64)
         sc = r[:, dim:dim + 4 * (dim // 64)].copy().view(np.float32).astype(np.float64)
         out[:] = table[r[:, :dim]] * np.repeat(sc, 64, axis=1)
+    elif dtype == FP4:
+        table = np.array([e2m1_to_f64(c) for c in range(16)], np.float64)
+        codes = np.empty((r.shape[0], dim), np.uint8)
+        codes[:, 0::2] = r[:, :dim // 2] & 15
+        codes[:, 1::2] = r[:, :dim // 2] >> 4
+        sc = np.ldexp(1.0, r[:, dim // 2:dim // 2 + dim // 32].astype(np.int64) - 127)
+        out[:] = table[codes] * np.repeat(sc, 32, axis=1)
     else:
         out[:] = r.view(np.float32)[:, :dim]
     return out.reshape(*shp, dim)

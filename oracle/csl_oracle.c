@@ -42,6 +42,11 @@
  *       them and -1 padding; ids are emitted in ascending order.
  *   R17 fp8 = OCP e4m3fn, round-to-nearest-even, saturating at 448; one fp32
  *       scale = amax/448 per 64 elements (1 when amax = 0).
+ *   R20 fp4 index rows = OCP MX "MXFP4": blocks of 32 elements share one
+ *       E8M0 scale 2^(floor(log2 amax) - 2); elements are E2M1, rounded to
+ *       nearest even, saturating at 6; an all-zero block has scale code 0.
+ *       The rounding decisions are taken on the fp32 value (the kernel's
+ *       precision).
  * Pinned by tests/test_oracle_*.py; numeric values of the full path beyond
  * those pins are "parity unpinned": the pages print no worked example.
  */
@@ -53,7 +58,7 @@
 #include <omp.h>
 #endif
 
-enum { O_F32 = 0, O_BF16 = 1, O_FP8 = 2 };
+enum { O_F32 = 0, O_BF16 = 1, O_FP8 = 2, O_FP4 = 3 };
 #define O_BLOCK 256 /* native positions per logical block, [Notes] 解决方案一：统一逻辑块大小 */
 
 /* ------------------------------------------------------------------ */
@@ -121,12 +126,64 @@ static uint8_t f64_to_e4m3(double v)
     return s | (uint8_t)(((ex + 7) << 3) | mant);
 }
 
+/* OCP 4-bit float E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit;
+ * exponent 0 is subnormal (0 or 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static double e2m1_to_f64(int c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* The E2M1 code nearest to v: searched over the eight magnitudes, ties to the
+ * even code (mantissa bit 0), anything at or past 6 saturating to 6. */
+static int f64_to_e2m1(double v)
+{
+    int s = signbit(v) ? 8 : 0;
+    double r = fabs(v), bd = r;
+    int best = 0;
+    for (int c = 1; c < 8; c++) {
+        double d = fabs(r - e2m1_to_f64(c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return s | best;
+}
+
+/* One 32-element MXFP4 block: 16 code bytes (element 2i in the low nibble of
+ * byte i) and the E8M0 scale code (value 2^(code - 127)). */
+static void mxfp4_block(const double* y, uint8_t* codes, uint8_t* scale)
+{
+    float v[32];
+    double amax = 0.0;
+    for (int i = 0; i < 32; i++) {
+        v[i] = (float)y[i];
+        if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+    }
+    memset(codes, 0, 16);
+    if (amax == 0.0) {
+        *scale = 0;
+        return;
+    }
+    int e;
+    frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+    int sh = (e - 1) - 2;
+    if (sh < -127) sh = -127;
+    if (sh > 127) sh = 127;
+    *scale = (uint8_t)(sh + 127);
+    for (int i = 0; i < 32; i++) codes[i / 2] |= (uint8_t)(f64_to_e2m1(ldexp((double)v[i], -sh)) << (4 * (i & 1)));
+}
+
 /* Bytes of one stored row: bf16 = 2 per element; fp8 = one code per
- * element followed by one fp32 scale per 64 elements; f32 = 4 per element. */
+ * element followed by one fp32 scale per 64 elements; fp4 = a nibble per
+ * element followed by one E8M0 byte per 32 elements; f32 = 4 per element. */
 int64_t csl_oracle_row_bytes(int dim, int dtype)
 {
     if (dtype == O_BF16) return 2 * (int64_t)dim;
     if (dtype == O_FP8) return (int64_t)dim + 4 * (int64_t)(dim / 64);
+    if (dtype == O_FP4) return (int64_t)dim / 2 + (int64_t)(dim / 32);
     return 4 * (int64_t)dim;
 }
 
@@ -153,6 +210,8 @@ static void store_row(uint8_t* dst, const double* y, int dim, int dtype)
             float sc = fp8_group(y + 64 * g, dst + 64 * g);
             memcpy(&scales[g], &sc, 4);
         }
+    } else if (dtype == O_FP4) {
+        for (int b = 0; b < dim / 32; b++) mxfp4_block(y + 32 * b, dst + 16 * b, dst + dim / 2 + b);
     } else {
         float* d = (float*)dst;
         for (int i = 0; i < dim; i++) d[i] = (float)y[i];
@@ -170,6 +229,9 @@ static void load_row(const uint8_t* src, double* y, int dim, int dtype)
             memcpy(&sc, src + dim + 4 * g, 4);
             for (int i = 0; i < 64; i++) y[64 * g + i] = e4m3_to_f64(src[64 * g + i]) * (double)sc;
         }
+    } else if (dtype == O_FP4) {
+        for (int i = 0; i < dim; i++)
+            y[i] = ldexp(e2m1_to_f64((src[i / 2] >> (4 * (i & 1))) & 15), (int)src[dim / 2 + i / 32] - 127);
     } else {
         const float* s = (const float*)src;
         for (int i = 0; i < dim; i++) y[i] = s[i];
@@ -180,6 +242,9 @@ double csl_oracle_bf16_to_f64(uint16_t h) { return bf16_to_f64(h); }
 uint16_t csl_oracle_f64_to_bf16(double v) { return f64_to_bf16(v); }
 double csl_oracle_e4m3_to_f64(uint8_t c) { return e4m3_to_f64(c); }
 uint8_t csl_oracle_f64_to_e4m3(double v) { return f64_to_e4m3(v); }
+double csl_oracle_e2m1_to_f64(int c) { return e2m1_to_f64(c); }
+int csl_oracle_f64_to_e2m1(double v) { return f64_to_e2m1(v); }
+void csl_oracle_mxfp4_block(const double* y, uint8_t* codes, uint8_t* scale) { mxfp4_block(y, codes, scale); }
 
 /* ------------------------------------------------------------------ */
 /* RoPE                                                                */
