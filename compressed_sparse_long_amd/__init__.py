@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsl.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, FP4 = 0, 1, 2, 3
 BLOCK = 256
 KERNEL_COMPRESS, KERNEL_INDEX_SCORE, KERNEL_TOPK_SELECT, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 0, 1, 2, 3, 4
 DEVERR_UNMAPPED_PAGE, DEVERR_TOPK_ID, DEVERR_POSITION, DEVERR_SEQ = 1, 2, 4, 8

@@ -98,6 +98,7 @@ size_t row_bytes_of(int dim, int dtype) {
     if (dim <= 0) return 0;
     if (dtype == CSL_BF16) return 2 * (size_t)dim;
     if (dtype == CSL_FP8_E4M3) return (dim % 256 == 0) ? (size_t)dim + dim / 16 : 0;
+    if (dtype == CSL_MXFP4) return (dim % 32 == 0) ? (size_t)dim / 2 + dim / 32 : 0;
     if (dtype == CSL_F32) return 4 * (size_t)dim;
     return 0;
 }
@@ -122,10 +123,12 @@ csl_status check_pool(const csl_pool* P, const char* name) {
         return fail(CSL_EINVAL, "%s.rope_dims = %d, expected a multiple of 4 in [0, min(dim, 128)]", name,
                     P->rope_dims);
     if (P->rope_dims > 0 && !(P->rope_theta > 0.0)) return fail(CSL_EINVAL, "%s.rope_theta must be > 0", name);
-    if (P->dtype != CSL_BF16 && P->dtype != CSL_FP8_E4M3)
-        return fail(CSL_EINVAL, "%s.dtype = %d, expected CSL_BF16 or CSL_FP8_E4M3", name, P->dtype);
+    if (P->dtype != CSL_BF16 && P->dtype != CSL_FP8_E4M3 && P->dtype != CSL_MXFP4)
+        return fail(CSL_EINVAL, "%s.dtype = %d, expected CSL_BF16, CSL_FP8_E4M3 or CSL_MXFP4", name, P->dtype);
     if (P->dtype == CSL_FP8_E4M3 && P->dim % 256)
         return fail(CSL_EUNSUPPORTED, "%s: fp8 rows need dim %% 256 == 0 (got %d)", name, P->dim);
+    if (P->dtype == CSL_MXFP4 && P->dim != 128)
+        return fail(CSL_EUNSUPPORTED, "%s: fp4 rows need dim 128 (got %d)", name, P->dim);
     if (P->num_pages <= 0) return fail(CSL_EINVAL, "%s.num_pages must be > 0", name);
     if (!aligned16(P->rows)) return fail(CSL_EALIGN, "%s.rows is not 16-byte aligned", name);
     if (P->ratio > 1) {
@@ -201,6 +204,7 @@ csl_status check_attn_common(const csl_pool* comp, const csl_pool* swa, const cs
         return fail(CSL_EINVAL, "topk given without a compressed pool");
     }
     if (swa->dtype == CSL_FP8_E4M3 && swa->dim != 512) return fail(CSL_EUNSUPPORTED, "fp8 keys need dim 512");
+    if (swa->dtype == CSL_MXFP4) return fail(CSL_EUNSUPPORTED, "fp4 rows are for index pools; attention keys are bf16 or fp8");
     if (n_heads < 1 || n_heads > 64) return fail(CSL_ERANGE, "n_heads = %d, supported 1..64", n_heads);
     if (topk && (k < 1 || k > 65536)) return fail(CSL_ERANGE, "k = %d out of range", k);
     if (swa_window < 0) return fail(CSL_EINVAL, "swa_window < 0");
@@ -376,7 +380,8 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     if ((st = check_pool(index_pool, "index"))) return st;
     if ((st = check_pages(pages))) return st;
     if (index_pool->ratio != 4) return fail(CSL_EUNSUPPORTED, "the indexer runs on ratio-4 (c4a) pools only");
-    if (index_pool->dtype != CSL_BF16) return fail(CSL_EUNSUPPORTED, "index rows must be bf16");
+    if (index_pool->dtype != CSL_BF16 && index_pool->dtype != CSL_MXFP4)
+        return fail(CSL_EUNSUPPORTED, "index rows must be bf16 or fp4");
     if (index_pool->dim != 32 && index_pool->dim != 64 && index_pool->dim != 128)
         return fail(CSL_EUNSUPPORTED, "index dim %d (supported: 32, 64, 128)", index_pool->dim);
     if (n_heads < 1 || n_heads > 16) return fail(CSL_ERANGE, "index n_heads = %d, supported 1..16", n_heads);
@@ -409,6 +414,7 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     a.nchunks = (int)(a.stride / kIndexChunk);
     a.kl = index_local_k(max_q_pos, k);
     a.tiled = index_use_tiled(num_q) ? 1 : 0;
+    a.fp4 = index_pool->dtype == CSL_MXFP4 ? 1 : 0;
     a.cand = reinterpret_cast<uint2*>(a.scores + (size_t)num_q * a.stride);
     a.c_next = a.cand + (size_t)num_q * a.nchunks * a.kl;
     a.num_q = num_q;

@@ -63,7 +63,7 @@ __device__ __forceinline__ void rope8(float* v, int d0, int dim, int rope_dims, 
 }
 
 // Store the lane's 8 values of a row; every lane of the wave must call this
-// (fp8 reduces the group amax across 8 lanes).  `active` = lane owns dims.
+// (fp8 reduces the group amax across 8 lanes, fp4 the block max across 4).  `active` = lane owns dims.
 __device__ __forceinline__ void store8(uint8_t* row, int dtype, int dim, int lane, bool active, const float* v) {
     if (dtype == kBF16) {
         if (active) {
@@ -71,6 +71,36 @@ __device__ __forceinline__ void store8(uint8_t* row, int dtype, int dim, int lan
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
             *reinterpret_cast<u32x4*>(row + 16 * lane) = o;
+        }
+        return;
+    }
+    if (dtype == kFP4) {
+        // MXFP4: the 32-element block is 4 lanes.  Scale 2^(floor(log2 amax) - 2)
+        // as an E8M0 byte; each element scaled by a power of two (exact) and
+        // rounded to E2M1 by counting the midpoints it passes (a tie sits at
+        // the even code: strict at 0.25, 1.25, 2.5, 5; inclusive at 0.75,
+        // 1.75, 3.5), saturating at 6.
+        float bmax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bmax = fmaxf(bmax, fabsf(v[c]));
+        bmax = active ? bmax : 0.f;
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
+        int sh = bmax > 0.f ? __builtin_amdgcn_frexp_expf(bmax) - 3 : -127;
+        sh = sh < -127 ? -127 : (sh > 127 ? 127 : sh);
+        if (active) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float q = __builtin_amdgcn_ldexpf(v[c], -sh);
+                const float r = fabsf(q);
+                const uint32_t code = (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) +
+                                      (uint32_t)(r >= 1.75f) + (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) +
+                                      (uint32_t)(r > 5.0f);
+                word |= (code | ((__float_as_uint(q) >> 28) & 8u)) << (4 * c);
+            }
+            *reinterpret_cast<uint32_t*>(row + 4 * lane) = word;
+            if ((lane & 3) == 0) row[dim / 2 + (lane >> 2)] = (uint8_t)(sh + 127);
         }
         return;
     }

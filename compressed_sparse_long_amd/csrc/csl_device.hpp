@@ -19,7 +19,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum : uint32_t { kErrPage = 1u, kErrTopk = 2u, kErrPos = 4u, kErrSeq = 8u };
 
-enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP4 = 3 };
 
 struct RopeFreqs {
     // theta^(-2j/R) for the R/2 rotated pairs, fp64, built on the host.
@@ -74,6 +74,29 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return code;
 }
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) { return e4m3_pack4(x, 0.f, 0.f, 0.f) & 0xffu; }
+
+// MXFP4 block -> bf16: 32 E2M1 codes (16 bytes, element 2i in the low nibble
+// of byte i) times the E8M0 scale 2^(e8 - 127), as 16 words of bf16 pairs.
+// v_cvt_scalef32_pk_bf16_fp4 converts the two codes of one byte and
+// multiplies by the fp32 scale; every product is exact in bf16 (checked
+// against the format's definition for all bytes, scale codes 0 to 254).
+__device__ __forceinline__ void mxfp4_to_bf16(const u32x4& codes, uint32_t e8, uint32_t (&out)[16]) {
+    const float sc = e8 ? __uint_as_float(e8 << 23) : __uint_as_float(0x00400000u);  // 2^-127 at code 0
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        out[4 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[w], sc, 0));
+        out[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[w], sc, 1));
+        out[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[w], sc, 2));
+        out[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[w], sc, 3));
+    }
+}
+
+// A 16-byte load from a 4-byte aligned address (fp4 rows are 68 bytes).
+__device__ __forceinline__ u32x4 load16_a4(const uint8_t* p) {
+    u32x4 v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 16);
+    return v;
+}
 
 // ---------------------------------------------------------------- waves
 

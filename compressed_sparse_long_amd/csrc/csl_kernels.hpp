@@ -33,7 +33,7 @@ struct CompressArgs {
 };
 
 struct IndexArgs {
-    const uint8_t* rows;  // ratio-4 index pool, bf16 rows
+    const uint8_t* rows;  // ratio-4 index pool: bf16 rows, or MXFP4 rows (fp4 = 1, dim 128: 68 bytes)
     const int32_t* bt;
     const int32_t* q_seq;
     const int64_t* q_pos;
@@ -51,6 +51,7 @@ struct IndexArgs {
     int nchunks;     // stride / 1024 (first-stage chunks)
     int kl;          // first-stage candidates per chunk (0: single-pass select)
     int tiled;       // query-blocked score kernel (many queries) instead of one query per row
+    int fp4;         // index rows are MXFP4
 };
 
 struct AttnArgs {

@@ -690,10 +690,12 @@ __global__ void __launch_bounds__(256) topk_local_kernel(IndexArgs a) {
     wave_first_stage(a, n, blk, key, base, nvalid, s_hist[wave], s_cbuf[wave]);
 }
 
-template <int DI, int U, bool LOCAL>
+template <int DI, int U, bool LOCAL, bool FP4 = false>
 __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     constexpr int KS = DI / 32;          // MFMA k-steps per row
-    constexpr int RB = DI * 2;           // index row bytes
+    constexpr int RB = DI * 2;           // bf16 row bytes (the LDS layout)
+    constexpr int RBG = FP4 ? DI / 2 + DI / 32 : RB;  // stored row bytes
+    static_assert(!FP4 || DI == 128, "fp4 index rows are 128 wide");
     constexpr int CPR = RB / 16;         // 16-byte chunks per row
     constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
     constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
@@ -721,12 +723,21 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     if (u0 * 64 < nv) {
         int32_t mypg = 0;  // lane j < U: page of unit u0 + j (-1 unmapped)
         if (lane < U && (u0 + lane) * 64 < nv) mypg = page_of(a.bt, a.max_blocks, a.num_pages, s, (u0 + lane) * 256);
-        u32x4 ld[NLD];
+        // bf16: contiguous 1 KiB loads; fp4: lane l takes row l (64 code bytes, 4 scale bytes)
+        u32x4 ld[FP4 ? 4 : NLD];
+        uint32_t lds4 = 0;
         auto issue = [&](int j) {
             const int32_t pg = __shfl(mypg, j);
-            const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * 64 * RB);
+            if constexpr (FP4) {
+                const uint8_t* r = a.rows + (int64_t)(pg < 0 ? 0 : pg) * 64 * RBG + lane * RBG;
 #pragma unroll
-            for (int q = 0; q < NLD; ++q) ld[q] = __builtin_nontemporal_load(base + q * 64 + lane);
+                for (int q = 0; q < 4; ++q) ld[q] = load16_a4(r + 16 * q);
+                lds4 = *reinterpret_cast<const uint32_t*>(r + 64);
+            } else {
+                const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * 64 * RB);
+#pragma unroll
+                for (int q = 0; q < NLD; ++q) ld[q] = __builtin_nontemporal_load(base + q * 64 + lane);
+            }
         };
         issue(0);
 
@@ -754,9 +765,21 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
         for (int j = 0; j < U; ++j) {
             // this unit into LDS (in-order LDS ops of one wave: the reads of the
             // previous unit have been issued before these writes)
+            if constexpr (FP4) {
 #pragma unroll
-            for (int q = 0; q < NLD; ++q)
-                *reinterpret_cast<u32x4*>(su + (q * RPL + lane / CPR) * LROW + (lane % CPR) * 16) = ld[q];
+                for (int b = 0; b < 4; ++b) {
+                    uint32_t w[16];
+                    mxfp4_to_bf16(ld[b], (lds4 >> (8 * b)) & 255u, w);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<u32x4*>(su + lane * LROW + 64 * b + 16 * i) =
+                            u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < NLD; ++q)
+                    *reinterpret_cast<u32x4*>(su + (q * RPL + lane / CPR) * LROW + (lane % CPR) * 16) = ld[q];
+            }
             if (j + 1 < U) issue(j + 1);
             float sc[4];
 #pragma unroll
@@ -895,15 +918,17 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
 constexpr int kTiledQW = 4;           // queries per wave (4 waves per workgroup; even)
 constexpr int kTiledMinQueries = 64;  // calls with at least this many queries use the tiled kernel
 
-template <int DI, int QW>
+template <int DI, int QW, bool FP4 = false>
 __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
     constexpr int kTiledQ = 4 * QW;       // queries per workgroup
     constexpr int PP = QW / 2;            // query pairs per wave
     constexpr int KS = DI / 16, RB = DI * 2, CPR = RB / 16, LROW = RB + 16;
-    constexpr int UNIT = 64 * RB;         // bytes of a 64-entry page
-    constexpr int LPT = UNIT / 16 / 256;  // 16-byte loads per thread per page
+    constexpr int RBG = FP4 ? DI / 2 + DI / 32 : RB;  // stored row bytes
+    constexpr int UNIT = 64 * RBG;        // bytes of a 64-entry page
+    constexpr int LPT = FP4 ? 1 : UNIT / 16 / 256;  // 16-byte loads per thread per page
     static_assert(QW % 2 == 0, "queries go to the MFMA in pairs");
-    static_assert(LPT >= 1 && UNIT == LPT * 16 * 256, "a page is a whole number of workgroup loads");
+    static_assert(FP4 || (LPT >= 1 && UNIT == LPT * 16 * 256), "a page is a whole number of workgroup loads");
+    static_assert(!FP4 || DI == 128, "fp4 index rows are 128 wide: thread = (row, 32-element block)");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2][64 * LROW];
     __shared__ int32_t s_qs[kTiledQ];
     __shared__ int64_t s_qnv[kTiledQ];
@@ -996,17 +1021,34 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
         if (tid < npages) s_pg[tid] = page_of(a.bt, a.max_blocks, a.num_pages, sg, (c0 + 64 * tid) * 4);
         __syncthreads();
         u32x4 st[LPT];
+        uint32_t st_e8 = 0;  // fp4: the scale byte of the thread's block
         auto load_page = [&](int j) {
             const int32_t pg = s_pg[j];
-            const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT);
+            if constexpr (FP4) {
+                // thread = (row tid / 4, 32-element block tid % 4)
+                const uint8_t* r = a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT + (tid >> 2) * RBG;
+                st[0] = load16_a4(r + 16 * (tid & 3));
+                st_e8 = r[DI / 2 + (tid & 3)];
+            } else {
+                const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT);
 #pragma unroll
-            for (int q = 0; q < LPT; ++q) st[q] = base[q * 256 + tid];
+                for (int q = 0; q < LPT; ++q) st[q] = base[q * 256 + tid];
+            }
         };
         auto store_page = [&](int b) {
+            if constexpr (FP4) {
+                uint32_t w[16];
+                mxfp4_to_bf16(st[0], st_e8, w);
+                uint8_t* dst = s_k[b] + (tid >> 2) * LROW + 64 * (tid & 3);
 #pragma unroll
-            for (int q = 0; q < LPT; ++q) {
-                const int c = q * 256 + tid;  // 16-byte chunk of the page
-                *reinterpret_cast<u32x4*>(s_k[b] + (c / CPR) * LROW + (c % CPR) * 16) = st[q];
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4*>(dst + 16 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            } else {
+#pragma unroll
+                for (int q = 0; q < LPT; ++q) {
+                    const int c = q * 256 + tid;  // 16-byte chunk of the page
+                    *reinterpret_cast<u32x4*>(s_k[b] + (c / CPR) * LROW + (c % CPR) * 16) = st[q];
+                }
             }
         };
         load_page(0);
@@ -1142,6 +1184,11 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEv
     if (a.tiled) {
         constexpr int QW = kTiledQW;
         dim3 grid((unsigned)(a.stride / kChunk), (unsigned)((a.num_q + 4 * QW - 1) / (4 * QW)));
+        if (a.fp4) {
+            if (a.dim != 128) return hipErrorInvalidValue;
+            launch_kernel(ev, true, true, index_score_tiled_kernel<128, QW, true>, grid, dim3(256), st, a);
+            return hipGetLastError();
+        }
         switch (a.dim) {
             case 32: launch_kernel(ev, true, true, index_score_tiled_kernel<32, QW>, grid, dim3(256), st, a); break;
             case 64: launch_kernel(ev, true, true, index_score_tiled_kernel<64, QW>, grid, dim3(256), st, a); break;
@@ -1153,6 +1200,12 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEv
     constexpr int U = kScoreUnits;
     dim3 grid((unsigned)(a.stride / (256 * U)), (unsigned)a.num_q);
     const bool local = a.kl > 0;
+    if (a.fp4) {
+        if (a.dim != 128) return hipErrorInvalidValue;
+        if (local) launch_kernel(ev, true, true, index_score_kernel<128, U, true, true>, grid, dim3(256), st, a);
+        else launch_kernel(ev, true, true, index_score_kernel<128, U, false, true>, grid, dim3(256), st, a);
+        return hipGetLastError();
+    }
     switch (a.dim) {
         case 32:
             if (local) launch_kernel(ev, true, true, index_score_kernel<32, U, true>, grid, dim3(256), st, a);

@@ -62,7 +62,14 @@ typedef enum {
     CSL_EUNSUPPORTED = -6  /* a valid combination this build does not implement */
 } csl_status;
 
-typedef enum { CSL_F32 = 0, CSL_BF16 = 1, CSL_FP8_E4M3 = 2 } csl_dtype;
+/* Row formats.  CSL_FP8_E4M3 rows: dim e4m3fn codes, then dim/64 fp32 scales
+ * (amax/448 per 64 elements).  CSL_MXFP4 rows (index pools, dim 128): dim/2
+ * bytes of E2M1 codes (element 2i in the low nibble of byte i), then dim/32
+ * E8M0 bytes, the scale 2^(e-127) of each 32-element block -- the OCP MX
+ * "MXFP4" format, our reading of the fp4 indexer cache ([Summary] 將索引器
+ * 快取使用 fp4; [Notes] FP4 Indexer).  The block scale is
+ * 2^(floor(log2 amax) - 2); elements round to nearest even and saturate at 6. */
+typedef enum { CSL_F32 = 0, CSL_BF16 = 1, CSL_FP8_E4M3 = 2, CSL_MXFP4 = 3 } csl_dtype;
 
 /* Device error bits (csl_read_device_error). */
 #define CSL_DEVERR_UNMAPPED_PAGE 0x1u /* a needed page is -1 or >= num_pages: row skipped */
@@ -76,7 +83,7 @@ typedef struct {
     int32_t dim;        /* row width D (512 for the shared latent, 128 for index keys) */
     int32_t rope_dims;  /* rotated tail R of each row (even, <= dim, <= 128; 0 = none) */
     double rope_theta;  /* RoPE base (10000) */
-    int32_t dtype;      /* CSL_BF16 or CSL_FP8_E4M3 */
+    int32_t dtype;      /* CSL_BF16, CSL_FP8_E4M3, or CSL_MXFP4 (index pools only) */
     int32_t num_pages;
     void* rows;          /* [num_pages][256/ratio][row_bytes] */
     void* state_x;       /* [num_pages][256][dim] bf16; required iff ratio > 1 */
@@ -149,7 +156,8 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs 
  * id first) in ascending order, padded with -1 when fewer than k are
  * visible; kth_score[n] (nullable) the score of the weakest selected id
  * (-inf if none).
- * index_pool: ratio 4, dim 32/64/128, bf16 rows.  q_idx: [num_q][n_heads]
+ * index_pool: ratio 4, dim 32/64/128, bf16 rows, or dim 128 CSL_MXFP4 rows
+ * (scored as their bf16 values: every E2M1 value times 2^k is exact in bf16).  q_idx: [num_q][n_heads]
  * [dim] bf16; w: [num_q][n_heads] fp32; topk: [num_q][k] int32;
  * n_heads <= 16; 1 <= k <= 2048; every q_pos <= max_q_pos (host bound that
  * sizes the grid).

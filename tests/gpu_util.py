@@ -71,6 +71,26 @@ def assert_fp8_close(orc, codes_g, scales_g, codes_o, scales_o, group=64, what="
                              f"(code {codes_o[tuple(i)]})")
 
 
+def assert_fp4_close(orc, rows_g, rows_o, dim, what="fp4"):
+    """MXFP4 rows: the rounding decisions sit on fp32 values that differ from the
+    oracle's fp64 ones in the last bits, so an element code, or at a power-of-two
+    edge of a block's maximum its scale, may differ.  At least 99.5% of the
+    elements must decode to the oracle's value, and every element must lie within
+    one step at the top of the grid (2 X, X the larger of the two block scales)."""
+    vg = orc.decode_rows(rows_g, dim, orc.FP4)
+    vo = orc.decode_rows(rows_o, dim, orc.FP4)
+    eg = rows_g[..., dim // 2:dim // 2 + dim // 32].astype(np.int64)
+    eo = rows_o[..., dim // 2:dim // 2 + dim // 32].astype(np.int64)
+    X = np.repeat(np.ldexp(1.0, np.maximum(eg, eo) - 127), 32, axis=-1)
+    bad = np.abs(vg - vo) > 2 * X
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements beyond one grid step; first at "
+                             f"{tuple(i)}: got {vg[tuple(i)]}, want {vo[tuple(i)]}")
+    same = float(np.mean(vg == vo))
+    assert same >= 0.995, f"{what}: only {same:.4f} of the elements match the oracle's code"
+
+
 def assert_topk_equivalent(got: np.ndarray, want: np.ndarray, scores: np.ndarray, kth: np.ndarray, what="topk"):
     """Same id sets, except swaps among ids whose oracle scores lie within
     1e-4 * max(1, |kth|) of the oracle's k-th score; ascending order, -1 padding."""

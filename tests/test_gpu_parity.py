@@ -12,9 +12,10 @@ import pytest
 import torch
 
 import oracle as O
-from tests.gpu_util import (DEV, assert_close, assert_fp8_close, assert_topk_equivalent, dev, dev_bf16, host,
-                            host_u16)
-from tests.util import block_table, gather_rows, rand_u, randn_bf16, randn_f32, scatter_rows
+from tests.gpu_util import (DEV, assert_close, assert_fp4_close, assert_fp8_close, assert_topk_equivalent, dev,
+                            dev_bf16, host, host_u16)
+from tests.util import (bf16_to_f64, block_table, fp4_rows, gather_rows, rand_u, randn_bf16, randn_f32,
+                        scatter_rows)
 
 pytestmark = pytest.mark.gpu
 THETA = 10000.0
@@ -62,6 +63,9 @@ COMPRESS_CASES = [
          gain=True),
     dict(name="c4a_d512_gain_start_offset", ratio=4, coff=2, D=512, R=64, dtype=O.BF16, lens=[600],
          chunks=[[0, 600]], gain=True),
+    # fp4 (MXFP4) index rows, ragged chunks over two sequences
+    dict(name="index_d128_fp4", ratio=4, coff=2, D=128, R=0, dtype=O.FP4, lens=[1100, 300],
+         chunks=[[600, 1, 499], [300]], gain=True),
 ]
 
 
@@ -101,6 +105,8 @@ def test_compress_insert_parity(csl, orc, case):
         oo = gather_rows(hp.rows, bt, s, r, 0, n_ent)
         if dt == O.BF16:
             assert_close(O.decode_rows(go, D, dt), O.decode_rows(oo, D, dt), what=f"{case['name']} seq {s}")
+        elif dt == O.FP4:
+            assert_fp4_close(O, go, oo, D, what=f"{case['name']} seq {s}")
         else:
             assert_fp8_close(orc, go[:, :D], go[:, D:].copy().view(np.float32), oo[:, :D],
                              oo[:, D:].copy().view(np.float32), what=f"{case['name']} seq {s}")
@@ -180,6 +186,11 @@ INDEX_CASES = [
          pos=[[0, 3, 4, 5, 255, 256, 300] + list(range(4096, 4121)), list(range(1020, 1050)),
               [260 + 37 * i for i in range(20)]], shuffle=True),
     dict(name="tiled_h16_d64_k100_ties", H=16, DI=64, k=100, pos=[list(range(6000, 6070))], mode="equal"),
+    # fp4 (MXFP4) index rows: one query per score row, and query-blocked
+    dict(name="fp4_h16_d128_k512_2seq", H=16, DI=128, k=512, pos=[[2047, 2048, 2051, 9000, 20000], [4, 5000, 6000]],
+         fp4=True),
+    dict(name="fp4_h16_d128_k512_outliers", H=16, DI=128, k=512, pos=[[20000, 131072]], mode="outlier", fp4=True),
+    dict(name="tiled_fp4_h16_d128_k512_prefill", H=16, DI=128, k=512, pos=[list(range(9000, 9100))], fp4=True),
 ]
 
 
@@ -191,7 +202,8 @@ def test_index_topk_parity(csl, orc, case):
     max_pos = max(max(p) for p in case["pos"])
     mb = max_pos // 256 + 1
     bt = block_table(seed, ns, mb, extra_pages=1)
-    hp = O.HostPool(4, 2, DI, 0, THETA, O.BF16, ns * mb + 1, state=False)
+    fp4 = bool(case.get("fp4"))
+    hp = O.HostPool(4, 2, DI, 0, THETA, O.FP4 if fp4 else O.BF16, ns * mb + 1, state=False)
     for s in range(ns):
         keys = randn_bf16(seed, 10 + s, (64 * mb, DI))
         if case.get("mode") == "equal":
@@ -203,7 +215,8 @@ def test_index_topk_parity(csl, orc, case):
             keys = (keys.astype(np.uint32) - (12 << 7)).astype(np.uint16)       # x 2^-12 (exact in bf16)
             big = np.arange(7, 64 * mb, 997)                                      # ~1 in 1000 keeps its scale
             keys[big] = randn_bf16(seed, 30 + s, (len(big), DI))
-        scatter_rows(hp.rows, bt, s, 4, keys.view(np.uint8).reshape(64 * mb, -1))
+        rows = fp4_rows(O, bf16_to_f64(keys)) if fp4 else keys.view(np.uint8).reshape(64 * mb, -1)
+        scatter_rows(hp.rows, bt, s, 4, rows)
     q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
     q_pos = np.concatenate(case["pos"]).astype(np.int64)
     if case.get("shuffle"):

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from tests.test_oracle_compress import run
-from tests.util import randn_bf16, randn_f32
+from tests.util import fp4_rows, randn_bf16, randn_f32
 
 # E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is
 # subnormal (0 or 0.5); no infinities or NaN.
@@ -130,18 +130,6 @@ def test_fp4_compressor_rows(orc):
         blk = y32[:, 32 * b:32 * b + 32]
         X = 2.0 ** (np.floor(np.log2(np.abs(blk).max(axis=1))) - 2)
         assert np.all(np.abs(deq[:, 32 * b:32 * b + 32] - blk) <= _err_bound(blk, X[:, None]))
-
-
-def fp4_rows(orc, vals):
-    """MXFP4 rows [n][row_bytes] of vals [n][d], block by block."""
-    n, d = vals.shape
-    rows = np.zeros((n, orc.row_bytes(d, orc.FP4)), np.uint8)
-    for i in range(n):
-        for b in range(d // 32):
-            codes, sc = orc.mxfp4_block(vals[i, 32 * b:32 * b + 32])
-            rows[i, 16 * b:16 * b + 16] = codes
-            rows[i, d // 2 + b] = sc
-    return rows
 
 
 def test_fp4_index_pool_scores_as_its_values(orc):

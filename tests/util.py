@@ -59,3 +59,15 @@ def gather_rows(pool_rows: np.ndarray, bt: np.ndarray, s: int, ratio: int, i0: i
         pg, r = page_row(bt, s, i0 + j, ratio)
         out[j] = pool_rows[pg, r]
     return out
+
+
+def fp4_rows(orc, vals: np.ndarray) -> np.ndarray:
+    """MXFP4 rows [n][row_bytes] of vals [n][d] (float), quantised block by block by the oracle."""
+    n, d = vals.shape
+    rows = np.zeros((n, orc.row_bytes(d, orc.FP4)), np.uint8)
+    for i in range(n):
+        for b in range(d // 32):
+            codes, sc = orc.mxfp4_block(vals[i, 32 * b:32 * b + 32])
+            rows[i, 16 * b:16 * b + 16] = codes
+            rows[i, d // 2 + b] = sc
+    return rows
