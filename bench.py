@@ -63,7 +63,7 @@ class DecodeSetup:
         base = {}
         if "c4a" in w.layers:
             base["main4"] = csl.Pool(4, 2, D, R, w.theta, kv, P, device=device)
-            base["idx"] = csl.Pool(4, 2, DI, 0, w.theta, csl.BF16, P, device=device)
+            base["idx"] = csl.Pool(4, 2, DI, 0, w.theta, w.idx_dtype, P, device=device)
         if "c128a" in w.layers:
             base["main128"] = csl.Pool(128, 1, D, R, w.theta, kv, P, device=device)
         base["raw"] = csl.Pool(1, 1, D, R, w.theta, kv, P, device=device, state=False)
@@ -180,9 +180,10 @@ class DecodeSetup:
         qio = H * D * 2 + H * ob
         ins = 2 * D * 2 + rb  # raw insert: x read, state x write (c4a/c128a), raw row write
         if "c4a" in w.layers:
-            idx = w.ctx // 4 * w.idx_dim * 2 + w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4
+            irb = self.csl.row_bytes(w.idx_dim, w.idx_dtype)
+            idx = w.ctx // 4 * irb + w.idx_heads * w.idx_dim * 2 + w.idx_heads * 4
             per_q["index_score"] = idx
-            per_q["c4a"] = idx + (w.topk + w.swa) * rb + qio + ins + w.idx_dim * 2 * 2
+            per_q["c4a"] = idx + (w.topk + w.swa) * rb + qio + ins + w.idx_dim * 2 + irb
         if "c128a" in w.layers:
             per_q["c128a"] = (w.ctx // 128 + w.swa) * rb + qio + ins
         return {k: v * nq for k, v in per_q.items()}
@@ -294,7 +295,7 @@ def cpu_baseline(setup: DecodeSetup, n_seqs: int, seconds: float) -> dict:
     t0 = time.time()
     main = O.HostPool(4, 2, D, R, w.theta, O.BF16, P)
     raw = O.HostPool(1, 1, D, R, w.theta, O.BF16, P)
-    idx = O.HostPool(4, 2, DI, 0, w.theta, O.BF16, P)
+    idx = O.HostPool(4, 2, DI, 0, w.theta, O.FP4 if w.idx_dtype == 3 else O.BF16, P)
 
     def u16(t):
         return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
@@ -306,9 +307,16 @@ def cpu_baseline(setup: DecodeSetup, n_seqs: int, seconds: float) -> dict:
     assert O.compress_insert(main, bt, st, cu, xs, lgs) == 0
     assert O.compress_insert(raw, bt, st, cu, xs) == 0
     del xs, lgs
-    for s in range(n):
-        keys = u16(W.index_keys(w, s, 0, T // 4, device="cuda"))
-        idx.rows[bt[s, :T // 256]] = keys.view(np.uint8).reshape(T // 256, 64, DI * 2)
+    if w.synth_index_keys:
+        for s in range(n):
+            keys = u16(W.index_keys(w, s, 0, T // 4, device="cuda"))
+            idx.rows[bt[s, :T // 256]] = keys.view(np.uint8).reshape(T // 256, 64, DI * 2)
+    else:
+        xis = np.concatenate([u16(W.latent(w, s, 0, T, dim=DI, tid=W.T_XI, device="cuda")) for s in range(n)])
+        lis = np.concatenate([W.logits(w, s, 0, T, 2, tid=W.T_LOGITS_I, device="cuda").cpu().numpy()
+                              for s in range(n)])
+        assert O.compress_insert(idx, bt, st, cu, xis, lis) == 0
+        del xis, lis
     log(f"oracle cache for {n} sequences built in {time.time() - t0:.1f}s")
     x_new = u16(setup.x_new[:n])
     lg_new = setup.lg_new[:n].cpu().numpy()
@@ -431,7 +439,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c4a", choices=["c4a", "c128a", "1m", "prefill"])
+    ap.add_argument("--workload", default="c4a", choices=["c4a", "c4a_fp4", "c128a", "1m", "prefill"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=200,
@@ -461,7 +469,7 @@ def main():
     if args.workload == "prefill":
         run_prefill(args)
         return
-    w = {"c4a": W.c4a_decode, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
+    w = {"c4a": W.c4a_decode, "c4a_fp4": W.c4a_decode_fp4, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)
     setup = DecodeSetup(w, R, side_stream=args.side_stream)
     log(f"workload {w.name}: {w.num_seqs} x {w.ctx} tokens, {R} replicas")
@@ -535,7 +543,8 @@ def main():
         "hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "context": w.ctx, "layers": list(w.layers),
                    "topk": w.topk, "swa": w.swa, "heads": w.n_heads, "latent_dim": w.dim, "rope_dims": w.rope_dims,
-                   "indexer": f"{w.idx_heads}x{w.idx_dim}", "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
+                   "indexer": f"{w.idx_heads}x{w.idx_dim}", "index_dtype": {1: "bf16", 3: "fp4"}[w.idx_dtype],
+                   "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
                    "out_dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.out_dtype], "replicas": R,
                    "hip_graphs": bool(graphs), "steps_per_graph": per_graph, "insert_stream": "side" if args.side_stream else "main",
                    "algorithmic_bytes_per_step": step_bytes},

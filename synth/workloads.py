@@ -47,6 +47,7 @@ class Workload:
     topk: int = 512
     swa: int = 128
     kv_dtype: int = 1        # 1 = bf16 rows, 2 = fp8 rows (64-element groups + fp32 scales)
+    idx_dtype: int = 1       # index rows: 1 = bf16, 3 = fp4 (MXFP4: E2M1 codes + E8M0 per 32)
     out_dtype: int = 1       # 0 = f32, 1 = bf16, 2 = fp8
     layers: tuple = ("c4a",)  # "c4a" and/or "c128a"
     synth_index_keys: bool = True   # index cache drawn directly (bf16) instead of compressed
@@ -101,6 +102,12 @@ def c128a_decode() -> Workload:
 
 def c4a_decode() -> Workload:
     return Workload("c4a_decode_b16_128k_top512_swa128", seed=2, num_seqs=16, ctx=131072, new_tokens=1)
+
+
+def c4a_decode_fp4() -> Workload:
+    """The c4a decode step with the index cache in fp4 (built by the compressor)."""
+    return Workload("c4a_decode_b16_128k_top512_swa128_fp4idx", seed=2, num_seqs=16, ctx=131072, new_tokens=1,
+                    idx_dtype=3, synth_index_keys=False)
 
 
 def long_1m() -> Workload:
