@@ -24,7 +24,7 @@ import torch
 
 import oracle as O
 from synth import workloads as W
-from tests.gpu_util import DEV, assert_close, assert_fp8_close, assert_topk_equivalent, host, host_u16
+from tests.gpu_util import DEV, assert_close, assert_fp4_close, assert_fp8_close, assert_topk_equivalent, host, host_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -119,9 +119,29 @@ def decode_query_check(csl, w, st, s, layer, theta=10000.0):
     q = host_u16(st.q[s:s + 1])
     if layer == "c4a":
         nv = p // 4
-        keys = host_u16(W.index_keys(w, s, 0, nv, device=DEV))
-        idx_pool = O.HostPool(4, 2, DI, 0, theta, O.BF16, mb, state=False)
-        idx_pool.rows.reshape(-1, DI * 2)[:nv] = keys.view(np.uint8).reshape(nv, DI * 2)
+        if w.synth_index_keys:
+            keys = host_u16(W.index_keys(w, s, 0, nv, device=DEV))
+            idx_pool = O.HostPool(4, 2, DI, 0, theta, O.BF16, mb, state=False)
+            idx_pool.rows.reshape(-1, DI * 2)[:nv] = keys.view(np.uint8).reshape(nv, DI * 2)
+        else:
+            # index rows written by the compressor (fp4 here): every visible entry against
+            # the oracle's compressor over the same latents; the top-k is then checked on
+            # the GPU's own rows, so both sides score the same bytes
+            idt = O.FP4 if w.idx_dtype == 3 else O.BF16
+            xi = host_u16(W.latent(w, s, 0, T + 1, dim=DI, tid=W.T_XI, device=DEV))
+            lgi = host(W.logits(w, s, 0, T + 1, 2, tid=W.T_LOGITS_I, device=DEV))
+            o_idx = O.HostPool(4, 2, DI, 0, theta, idt, mb)
+            gi = W.gain(w, DI, tid=W.T_GAIN_I, device=DEV)
+            assert O.compress_insert(o_idx, bt_o, [0], [0, T + 1], xi, lgi, None if gi is None else host(gi)) == 0
+            ents = np.arange(nv)
+            g_rows = gpu_rows(rep["idx"], bt_row, ents)
+            o_rows = o_idx.rows.reshape(-1, o_idx.row_bytes)[:nv]
+            if idt == O.FP4:
+                assert_fp4_close(O, g_rows, o_rows, DI, what=f"c4a seq {s}: fp4 index rows")
+            else:
+                check_rows(g_rows, o_rows, DI, idt, f"c4a seq {s}: index rows")
+            idx_pool = O.HostPool(4, 2, DI, 0, theta, idt, mb, state=False)
+            idx_pool.rows.reshape(-1, idx_pool.row_bytes)[:nv] = g_rows
         o_topk, o_kth, o_sc, _ = O.index_topk(idx_pool, bt_o, [0], [p], host_u16(st.q_idx[s:s + 1]),
                                               host(st.w_idx[s:s + 1]), w.topk, want_scores=True, max_cand=nv)
         g_topk = host(st.topk[s:s + 1])
@@ -189,6 +209,18 @@ def test_c4a_decode_full_size(csl):
         say(f"{w.name}: oracle check of sequence {s}")
         same += decode_query_check(csl, w, st, s, "c4a")
     assert same >= 2, "top-k sets differ by allowed ties on most sampled queries"
+    del st
+    torch.cuda.empty_cache()
+
+
+def test_c4a_fp4_index_decode_full_size(csl):
+    w = W.c4a_decode_fp4()
+    st = run_decode(csl, w)
+    same = 0
+    for s in (0, 15):
+        say(f"{w.name}: oracle check of sequence {s}")
+        same += decode_query_check(csl, w, st, s, "c4a")
+    assert same >= 1, "top-k sets differ by allowed ties on every sampled query"
     del st
     torch.cuda.empty_cache()
 
