@@ -75,6 +75,9 @@ def lib():
         L.csl_oracle_hybrid_attn.argtypes = [C.POINTER(Pool), C.POINTER(Pool), vp, C.c_int, C.c_int, vp, vp,
                                              vp, C.c_int, vp, C.c_int, C.c_int, dbl, C.c_int, vp, vp, vp]
         L.csl_oracle_hybrid_attn.restype = C.c_int
+        L.csl_oracle_q_norm_rope_insert.argtypes = [C.POINTER(Pool), vp, C.c_int, C.c_int, vp, vp, vp, vp, C.c_int,
+                                                     vp, dbl, vp]
+        L.csl_oracle_q_norm_rope_insert.restype = C.c_int
         L.csl_oracle_compress_rows.argtypes = [C.POINTER(Pool), C.c_int, vp, vp, vp, vp, dbl, vp]
         L.csl_oracle_compress_rows.restype = None
         L.csl_oracle_num_threads.argtypes = []
@@ -166,6 +169,24 @@ def compress_insert(pool: HostPool, bt, start_pos, cu_new, x, logits=None, gain=
     s = pool.struct()
     return lib().csl_oracle_compress_insert(C.byref(s), _p(bt), len(st), bt.shape[1], _p(st), _p(cu), _p(x),
                                             _p(lg), _p(g), float(eps))
+
+
+def q_norm_rope_insert(pool: HostPool, bt, start_pos, cu_new, x, q, gain=None, eps=1e-6):
+    """Query side of a step: every head of q [total][n_heads][dim] bf16 is
+    RMS-normed (gain [dim] or None) and rotated at its token's position with
+    the raw pool's RoPE; the raw rows RoPE(x_t, t) go into `pool` (ratio 1).
+    Returns (q_out [total][n_heads][dim] uint16 bf16 bits, faults)."""
+    bt = np.ascontiguousarray(bt, np.int32)
+    st = np.ascontiguousarray(start_pos, np.int64)
+    cu = np.ascontiguousarray(cu_new, np.int32)
+    x = np.ascontiguousarray(x, np.uint16)
+    q = np.ascontiguousarray(q, np.uint16)
+    g = None if gain is None else np.ascontiguousarray(gain, np.float32)
+    out = np.zeros_like(q)
+    s = pool.struct()
+    f = lib().csl_oracle_q_norm_rope_insert(C.byref(s), _p(bt), len(st), bt.shape[1], _p(st), _p(cu), _p(x), _p(q),
+                                            q.shape[1], _p(g), float(eps), _p(out))
+    return out, f
 
 
 def compress_rows(ratio, coff, dim, rope_dims, theta, dtype, ids, x_win, logits_win=None, gain=None, eps=1e-6):

@@ -42,6 +42,9 @@
  *       them and -1 padding; ids are emitted in ascending order.
  *   R17 fp8 = OCP e4m3fn, round-to-nearest-even, saturating at 448; one fp32
  *       scale = amax/448 per 64 elements (1 when amax = 0).
+ *   R21 the query-side norm is an RMSNorm per head over its dim entries
+ *       (eps 1e-6, one optional gain vector shared by the heads); the query
+ *       is then rotated at its own token's position with the raw pool's RoPE.
  *   R20 fp4 index rows = OCP MX "MXFP4": blocks of 32 elements share one
  *       E8M0 scale 2^(floor(log2 amax) - 2); elements are E2M1, rounded to
  *       nearest even, saturating at 6; an all-zero block has scale code 0.
@@ -458,6 +461,52 @@ int csl_oracle_compress_insert(const csl_oracle_pool* P, const int32_t* bt, int 
         free(y);
     }
     return faults;
+}
+
+/* ------------------------------------------------------------------ */
+/* Query side: Q RMSNorm + Q RoPE beside the raw-key RoPE + insert     */
+/* ------------------------------------------------------------------ */
+
+/* The step just before attention, which the pages fuse into one kernel
+ * ([Notes] 融合 3：Q Norm + KV RoPE + K Insert; [Summary] Kernel 融合):
+ * for new token j of sequence s, at position t = start_pos[s] + (j - cu_new[s]),
+ *   - every query head h (R21): y = q[j][h] / sqrt(mean(q[j][h]^2) + eps)
+ *     * gain, an RMSNorm over the head's dim entries with one gain vector
+ *     shared by all heads (unit when NULL); then y = RoPE(y, t) with the raw
+ *     pool's rope_dims and theta (queries and keys rotate alike, so the logit
+ *     depends on the query-key distance); stored as bf16 in q_out[j][h];
+ *   - the raw key row t = RoPE(x_j, t), exactly the ratio-1 insert above.
+ * q, q_out: [total][n_heads][dim] bf16, total = cu_new[num_seqs].  Returns
+ * the number of unmapped pages met by the insert (the queries are written
+ * regardless). */
+int csl_oracle_q_norm_rope_insert(const csl_oracle_pool* swa, const int32_t* bt, int num_seqs, int max_blocks,
+                                  const int64_t* start_pos, const int32_t* cu_new, const uint16_t* x,
+                                  const uint16_t* q, int n_heads, const float* gain, double eps, uint16_t* q_out)
+{
+    int D = swa->dim;
+#pragma omp parallel for schedule(dynamic)
+    for (int s = 0; s < num_seqs; s++) {
+        double* y = (double*)malloc(sizeof(double) * D);
+        for (int j = cu_new[s]; j < cu_new[s + 1]; j++) {
+            int64_t t = start_pos[s] + (j - cu_new[s]);
+            for (int h = 0; h < n_heads; h++) {
+                size_t off = ((size_t)j * n_heads + h) * (size_t)D;
+                double ms = 0.0;
+                for (int d = 0; d < D; d++) {
+                    y[d] = bf16_to_f64(q[off + d]);
+                    ms += y[d] * y[d];
+                }
+                ms /= D;
+                double inv = 1.0 / sqrt(ms + eps);
+                for (int d = 0; d < D; d++) y[d] = y[d] * inv * (gain ? (double)gain[d] : 1.0);
+                rope(y, D, swa->rope_dims, swa->rope_theta, (double)t);
+                for (int d = 0; d < D; d++) q_out[off + d] = f64_to_bf16(y[d]);
+            }
+        }
+        free(y);
+    }
+    if (swa->ratio != 1) return -1;
+    return csl_oracle_compress_insert(swa, bt, num_seqs, max_blocks, start_pos, cu_new, x, NULL, NULL, eps);
 }
 
 /* ------------------------------------------------------------------ */
