@@ -434,12 +434,110 @@ def run_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def run_qside(args):
+    """Query side of a step (per-head Q RMSNorm + Q RoPE, raw-key RoPE + insert,
+    one launch) at the decode or the prefill workload's shape: the new tokens'
+    64 query heads of 512 (pre-norm, ~N(0,1)) and their raw latent rows."""
+    import torch
+
+    import compressed_sparse_long_amd as csl
+    from synth import workloads as W
+
+    w = W.c4a_decode() if args.workload == "qside_decode" else W.prefill()
+    dev = "cuda"
+    ns, n, T, D, H = w.num_seqs, w.new_tokens, w.ctx, w.dim, w.n_heads
+    total = ns * n
+    bt = W.block_table(w).to(dev)
+    raw = csl.Pool(1, 1, D, w.rope_dims, w.theta, w.kv_dtype, w.num_pages, device=dev, state=False)
+    start = torch.full((ns,), T, dtype=torch.int64, device=dev)
+    cu = torch.arange(ns + 1, dtype=torch.int32, device=dev) * n
+    x = torch.cat([W.latent(w, s, T, n, device=dev) for s in range(ns)])
+    q = W.queries(w, device=dev)["q"]
+    assert q.shape == (total, H, D)
+    g = W.gain(w, D, tid=W.T_GAIN_Q, device=dev)
+    q_out = torch.empty_like(q)
+    log(f"q-side {w.name}: {total} tokens x {H} heads x {D}")
+
+    def launch():
+        csl.q_norm_rope_insert(raw, bt, start, cu, x, q, g, q_out=q_out)
+
+    K, warm = args.steps, args.warmup
+    for _ in range(warm):
+        launch()
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0
+    per = 10
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per):
+            launch()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, K // per)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / (reps * per)
+    csl.timer_read(csl.KERNEL_QSIDE)
+    csl.timer_enable(csl.KERNEL_QSIDE, True)
+    for _ in range(min(K, 500)):
+        launch()
+    torch.cuda.synchronize()
+    csl.timer_enable(csl.KERNEL_QSIDE, False)
+    k_ms, k_n = csl.timer_read(csl.KERNEL_QSIDE)
+    assert csl.read_device_error() == 0
+    k_avg = k_ms / max(1, k_n)
+    rb = csl.row_bytes(D, w.kv_dtype)
+    per_tok = 2 * H * D * 2 + D * 2 + rb
+    k_bytes = total * per_tok
+    ach = k_bytes / (k_avg * 1e-3) / 1e9
+    res = {
+        "metric": "query-side tokens/s (per-head Q RMSNorm + RoPE, raw-key RoPE + insert, one launch)",
+        "value": round(total / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": reps * per,
+        "warmup": warm, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"qside_{w.name}", "tokens": total, "heads": H, "latent_dim": D,
+                   "rope_dims": w.rope_dims, "q_gain": g is not None, "hip_graphs": True, "launches_per_graph": per},
+        "roofline": {"bound": "hbm", "kernel": "q_norm_rope_insert_kernel", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": k_bytes, "avg_launch_ms": round(k_avg, 5),
+                     "timed_launches": k_n,
+                     "timing": "hipExtLaunchKernel start/stop events stamped by each eager launch"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        import numpy as np
+
+        import oracle as O
+        m = min(total, 256)
+        hq = q[:m].cpu().view(torch.int16).numpy().view(np.uint16)
+        hx = x[:m].cpu().view(torch.int16).numpy().view(np.uint16)
+        hg = None if g is None else g.cpu().numpy()
+        hbt = bt.cpu().numpy()
+        hp = O.HostPool(1, 1, D, w.rope_dims, w.theta, w.kv_dtype, w.num_pages, state=False)
+        seqs = m // n if n > 1 else m
+        st = np.full(max(1, seqs), T, np.int64)
+        hcu = (np.arange(max(1, seqs) + 1) * (n if n > 1 else 1)).astype(np.int32)
+        hcu[-1] = m
+        done, t0 = 0, time.perf_counter()
+        while True:
+            O.q_norm_rope_insert(hp, hbt[:len(st)], st, hcu, hx, hq, hg)
+            done += m
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds / 4:
+                break
+        res["cpu_baseline"] = {"value": round(done / el, 1), "unit": "tokens/s", "cores": O.num_threads(),
+                               "kind": "oracle", "sample": f"the first {m} of the step's tokens, repeated for {el:.1f}s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c4a", choices=["c4a", "c4a_fp4", "c128a", "1m", "prefill"])
+    ap.add_argument("--workload", default="c4a", choices=["c4a", "c4a_fp4", "c128a", "1m", "prefill", "qside_decode", "qside_prefill"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=200,
@@ -468,6 +566,9 @@ def main():
 
     if args.workload == "prefill":
         run_prefill(args)
+        return
+    if args.workload.startswith("qside"):
+        run_qside(args)
         return
     w = {"c4a": W.c4a_decode, "c4a_fp4": W.c4a_decode_fp4, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libcsl.so")
 
 F32, BF16, FP8, FP4 = 0, 1, 2, 3
 BLOCK = 256
-KERNEL_COMPRESS, KERNEL_INDEX_SCORE, KERNEL_TOPK_SELECT, KERNEL_ATTN, KERNEL_ATTN_COMBINE = 0, 1, 2, 3, 4
+KERNEL_COMPRESS, KERNEL_INDEX_SCORE, KERNEL_TOPK_SELECT, KERNEL_ATTN, KERNEL_ATTN_COMBINE, KERNEL_QSIDE = 0, 1, 2, 3, 4, 5
 DEVERR_UNMAPPED_PAGE, DEVERR_TOPK_ID, DEVERR_POSITION, DEVERR_SEQ = 1, 2, 4, 8
 
 _STATUS = {0: "CSL_OK", -1: "CSL_EINVAL", -2: "CSL_ERANGE", -3: "CSL_EALIGN", -4: "CSL_EWORKSPACE",
@@ -68,6 +68,7 @@ _row_bytes = _sig("csl_row_bytes", _sz, [_i32, _i32])
 _compress_insert = _sig("csl_compress_insert", C.c_int, [_P, _G, _vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp])
 _compress_insert_multi = _sig("csl_compress_insert_multi", C.c_int,
                               [_i32, C.POINTER(_InsertJob), _G, _vp, _vp, _i32, _f32, _vp])
+_q_side = _sig("csl_q_norm_rope_insert", C.c_int, [_P, _G, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _f32, _vp, _vp])
 _index_topk_ws = _sig("csl_index_topk_workspace", _sz, [_i32, _i64, _i32])
 _index_topk = _sig("csl_index_topk", C.c_int,
                    [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
@@ -82,7 +83,8 @@ _read_dev_err = _sig("csl_read_device_error", C.c_int, [C.POINTER(C.c_uint32)])
 _timer_enable = _sig("csl_timer_enable", C.c_int, [_i32, _i32])
 _timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)])
 
-EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_index_topk_workspace", "csl_index_topk",
+EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_q_norm_rope_insert",
+           "csl_index_topk_workspace", "csl_index_topk",
            "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill", "csl_last_error",
            "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
 
@@ -155,6 +157,18 @@ def compress_insert_multi(jobs, block_table, start_pos, cu_new, eps=1e-6, stream
     total = int(jobs[0][1].shape[0])
     _check(_compress_insert_multi(len(jobs), arr, C.byref(pg), _ptr(start_pos), _ptr(cu_new), total, float(eps),
                                   _stream(stream)))
+
+
+def q_norm_rope_insert(swa: Pool, block_table, start_pos, cu_new, x, q, gain=None, eps=1e-6, q_out=None,
+                       stream=None):
+    """Per-head RMSNorm + RoPE of q [total][n_heads][dim] bf16 into q_out (default: in place) and the
+    raw-key insert of x [total][dim] into `swa`, one launch.  Returns q_out."""
+    q_out = q if q_out is None else q_out
+    ps = swa.struct()
+    pg = pages(block_table)
+    _check(_q_side(C.byref(ps), C.byref(pg), _ptr(start_pos), _ptr(cu_new), int(q.shape[0]), _ptr(x), _ptr(q),
+                   int(q.shape[1]), _ptr(gain), float(eps), _ptr(q_out), _stream(stream)))
+    return q_out
 
 
 def index_topk_workspace(num_q: int, max_q_pos: int, k: int) -> int:

@@ -63,7 +63,7 @@ struct Timer {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
     size_t used = 0;
 };
-constexpr int kNumKernels = 5;
+constexpr int kNumKernels = 6;
 constexpr size_t kMaxTimed = 65536;
 Timer g_timer[kNumKernels];
 std::mutex g_timer_mu;
@@ -363,6 +363,60 @@ csl_status csl_compress_insert(const csl_pool* pool, const csl_pages* pages, con
                                const float* gain, float eps, csl_stream_t stream) {
     csl_insert_job job = {pool, x, logits, gain};
     return csl_compress_insert_multi(1, &job, pages, start_pos, cu_new, total_new, eps, stream);
+}
+
+csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, const int64_t* start_pos,
+                                  const int32_t* cu_new, int32_t total_new, const uint16_t* x, const uint16_t* q,
+                                  int32_t n_heads, const float* q_gain, float eps, uint16_t* q_out,
+                                  csl_stream_t stream) {
+    csl_status st;
+    if ((st = check_pool(swa, "swa"))) return st;
+    if ((st = check_pages(pages))) return st;
+    if (swa->ratio != 1) return fail(CSL_EINVAL, "swa.ratio must be 1 (raw window keys)");
+    if (swa->dtype == CSL_MXFP4) return fail(CSL_EUNSUPPORTED, "raw window keys are bf16 or fp8, not fp4");
+    if (n_heads < 1 || n_heads > 1024) return fail(CSL_ERANGE, "n_heads = %d, supported 1..1024", n_heads);
+    if (total_new < 0) return fail(CSL_EINVAL, "total_new < 0");
+    if (!(eps >= 0.f)) return fail(CSL_EINVAL, "eps must be >= 0");
+    if (!start_pos || !cu_new) return fail(CSL_EINVAL, "start_pos or cu_new is NULL");
+    if (total_new == 0) return CSL_OK;
+    if (!x || !q || !q_out) return fail(CSL_EINVAL, "x, q or q_out is NULL");
+    if (!aligned16(x) || !aligned16(q) || !aligned16(q_out)) return fail(CSL_EALIGN, "x, q and q_out must be 16-byte aligned");
+    const int64_t n_q_rows = (int64_t)total_new * n_heads;
+    const int64_t n_items = n_q_rows + total_new;
+    if ((n_items + 15) / 16 > 0x7fffffff) return fail(CSL_ERANGE, "total_new * (n_heads + 1) too large");
+    if (q_out != q) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(q), b0 = reinterpret_cast<uintptr_t>(q_out);
+        const uintptr_t len = (uintptr_t)n_q_rows * swa->dim * 2;
+        if (a0 < b0 + len && b0 < a0 + len) return fail(CSL_EINVAL, "q_out overlaps q without being equal to it");
+    }
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    QSideArgs a;
+    a.q = q;
+    a.q_out = q_out;
+    a.x = x;
+    a.gain = q_gain;
+    a.rows = static_cast<uint8_t*>(swa->rows);
+    a.bt = pages->block_table;
+    a.start_pos = start_pos;
+    a.cu_new = cu_new;
+    a.err = err;
+    a.n_q_rows = n_q_rows;
+    a.n_items = n_items;
+    a.n_heads = n_heads;
+    a.dim = swa->dim;
+    a.rope_dims = swa->rope_dims;
+    a.dtype = swa->dtype;
+    a.num_pages = swa->num_pages;
+    a.row_bytes = (int)row_bytes_of(swa->dim, swa->dtype);
+    a.num_seqs = pages->num_seqs;
+    a.max_blocks = pages->max_blocks;
+    a.eps = eps;
+    a.rf = make_freqs(swa->rope_dims, swa->rope_theta);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(CSL_KERNEL_QSIDE, [&](const LaunchEvents& ev) { return launch_qside(a, s, ev); });
+    if (e != hipSuccess) return hip_fail(e, "q_norm_rope_insert launch");
+    return CSL_OK;
 }
 
 size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k) {

@@ -252,7 +252,109 @@ __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs 
     store8(row, a.dtype, D, lane, active, u);
 }
 
+// ---------------------------------------------------------------- query side
+
+// The step before attention ([Notes] 融合 3：Q Norm + KV RoPE + K Insert;
+// [Summary] Kernel 融合): every query head of a new token is RMS-normed and
+// rotated at the token's position, and the token's raw key is rotated and
+// inserted into the ratio-1 pool.  Work items are the flattened rows
+// [total_new*n_heads Q rows | total_new K rows]; wave w of workgroup b owns the
+// kQItems consecutive items from (4b + w) * kQItems and branches per item on
+// its kind, with no communication between waves (the pages' one-warp-per-head
+// dispatch).  A wave issues the loads of all its items first, so each lane has
+// kQItems 16-byte reads in flight.  cos/sin are recomputed only when the token
+// changes (the Q rows of a token are consecutive).  HBM-bound: read q and x,
+// write q_out and the key row.
+constexpr int kQItems = 4;
+
+__global__ void __launch_bounds__(kThreads) q_norm_rope_insert_kernel(QSideArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int D = a.dim;
+    const bool active = lane * 8 < D;
+    const int64_t g0 = ((int64_t)blockIdx.x * 4 + wave) * kQItems;
+    if (g0 >= a.n_items) return;
+
+    float v[kQItems][8];
+#pragma unroll
+    for (int u = 0; u < kQItems; ++u) {
+        const int64_t g = g0 + u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[u][c] = 0.f;
+        if (g < a.n_items && active) {
+            const uint16_t* src = g < a.n_q_rows ? a.q + g * D : a.x + (g - a.n_q_rows) * D;
+            load8(src + 8 * lane, v[u]);
+        }
+    }
+    float gn[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gn[c] = (a.gain && active) ? a.gain[8 * lane + c] : 1.0f;
+
+    const int base = D - a.rope_dims;
+    int64_t cur_j = -1, t = 0;
+    int cur_s = 0;
+    float cs[4], sn[4];
+#pragma unroll
+    for (int u = 0; u < kQItems; ++u) {
+        const int64_t g = g0 + u;
+        if (g >= a.n_items) break;  // wave-uniform
+        const bool is_q = g < a.n_q_rows;
+        const int64_t j = is_q ? g / a.n_heads : g - a.n_q_rows;
+        if (j != cur_j) {  // wave-uniform: the token's position and its rotation
+            cur_j = j;
+            cur_s = find_seq(a.cu_new, a.num_seqs, (int)j);
+            t = a.start_pos[cur_s] + (j - a.cu_new[cur_s]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int d = 8 * lane + 2 * c;
+                cs[c] = 1.f;
+                sn[c] = 0.f;
+                if (active && d >= base) rope_cs(t, a.rf.inv_freq[(d - base) >> 1], cs[c], sn[c]);
+            }
+        }
+        float* w = v[u];
+        if (is_q) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) ss = fmaf(w[c], w[c], ss);
+            ss = wave_sum(ss);
+            const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) w[c] = w[c] * inv * gn[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float x0 = w[2 * c], x1 = w[2 * c + 1];
+            w[2 * c] = x0 * cs[c] - x1 * sn[c];
+            w[2 * c + 1] = x0 * sn[c] + x1 * cs[c];
+        }
+        if (is_q) {
+            if (active) {
+                u32x4 o;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(w[2 * c], w[2 * c + 1]);
+                *reinterpret_cast<u32x4*>(a.q_out + g * D + 8 * lane) = o;
+            }
+        } else {
+            const int32_t pg = page_of(a.bt, a.max_blocks, a.num_pages, cur_s, t);
+            if (pg < 0) {
+                if (lane == 0) raise_error(a.err, (t < 0 || (t >> 8) >= a.max_blocks) ? kErrPos : kErrPage);
+                continue;
+            }
+            uint8_t* row = a.rows + ((int64_t)pg * kBlockPositions + (t & 255)) * a.row_bytes;
+            store8(row, a.dtype, D, lane, active, w);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_qside(const QSideArgs& a, hipStream_t st, const LaunchEvents& ev) {
+    if (a.n_items <= 0) return hipSuccess;
+    const int64_t waves = (a.n_items + kQItems - 1) / kQItems;
+    launch_kernel(ev, true, true, q_norm_rope_insert_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(kThreads), st,
+                  a);
+    return hipGetLastError();
+}
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.total_new <= 0 || a.n_jobs <= 0) return hipSuccess;

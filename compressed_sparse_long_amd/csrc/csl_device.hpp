@@ -58,7 +58,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 // the saturation, and NaN is passed through by hand.
 __device__ __forceinline__ float e4m3_clamp(float x) { return x != x ? x : fminf(fmaxf(x, -448.0f), 448.0f); }
 __device__ __forceinline__ uint32_t e4m3_nan_fix(float x, uint32_t code, int byte) {
-    return x != x ? (code & ~(0xffu << (8 * byte))) | (((__float_as_uint(x) >> 24) & 0x80u | 0x7fu) << (8 * byte)) : code;
+    return x != x ? (code & ~(0xffu << (8 * byte))) | ((((__float_as_uint(x) >> 24) & 0x80u) | 0x7fu) << (8 * byte)) : code;
 }
 // codes of a, b, c, d in bytes 0..3
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {

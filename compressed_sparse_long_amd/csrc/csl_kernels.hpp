@@ -32,6 +32,25 @@ struct CompressArgs {
     float eps;
 };
 
+// Query side: per-head Q RMSNorm + Q RoPE and the raw-key RoPE + insert of
+// the same new tokens, one launch.
+struct QSideArgs {
+    const uint16_t* q;  // [total_new][n_heads][dim] bf16
+    uint16_t* q_out;    // same shape; may equal q
+    const uint16_t* x;  // [total_new][dim] bf16 raw keys
+    const float* gain;  // [dim] or null
+    uint8_t* rows;      // ratio-1 pool rows
+    const int32_t* bt;
+    const int64_t* start_pos;
+    const int32_t* cu_new;
+    uint32_t* err;
+    int64_t n_q_rows;  // total_new * n_heads
+    int64_t n_items;   // n_q_rows + total_new
+    int n_heads, dim, rope_dims, dtype, num_pages, row_bytes, num_seqs, max_blocks;
+    float eps;
+    RopeFreqs rf;
+};
+
 struct IndexArgs {
     const uint8_t* rows;  // ratio-4 index pool: bf16 rows, or MXFP4 rows (fp4 = 1, dim 128: 68 bytes)
     const int32_t* bt;
@@ -94,6 +113,7 @@ inline void launch_kernel(const LaunchEvents& ev, bool first, bool last, F kerne
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+hipError_t launch_qside(const QSideArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 bool index_use_tiled(int num_q);

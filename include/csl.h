@@ -6,7 +6,8 @@
  *   [Notes]   "DeepSeek V4 in vLLM 技术博客详尽笔记"
  *   [Summary] "vLLM DeepSeek V4 支援：高效長上下文注意力"
  * in four calls: compress_insert, index_topk, hybrid_attn_decode and
- * hybrid_attn_prefill, over caches paged in blocks of 256 native positions.
+ * hybrid_attn_prefill, over caches paged in blocks of 256 native positions,
+ * plus the query-side step before them (q_norm_rope_insert).
  *
  * Conventions for every call:
  *  - Pointers are DEVICE memory unless marked "host".  The caller owns every
@@ -144,6 +145,29 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs 
                                      const int32_t* cu_new, int32_t total_new, float eps, csl_stream_t stream);
 
 /*
+ * The query side of a step, fused with the raw-key insert ([Notes] 融合 3：
+ * Q Norm + KV RoPE + K Insert; [Summary] Kernel 融合: queries and raw window
+ * keys prepared in one kernel).  For new token j of sequence s, at position
+ * t = start_pos[s] + (j - cu_new[s]):
+ *  - every head h: y = q[j][h] / sqrt(mean(q[j][h]^2) + eps) * q_gain (an
+ *    RMSNorm over the head's dim entries; q_gain [dim] fp32 shared by all
+ *    heads, NULL = unit gain), then y = RoPE(y, t) with swa's rope_dims and
+ *    rope_theta, stored as bf16 in q_out[j][h] -- the already normed and
+ *    rotated q that the attention calls take;
+ *  - raw key row t of `swa` = RoPE(x_j, t), exactly as csl_compress_insert
+ *    does for a ratio-1 pool.
+ * q, q_out: [total_new][n_heads][swa->dim] bf16; q_out may be q itself (in
+ * place) but must not overlap it otherwise.  x: [total_new][swa->dim] bf16.
+ * start_pos, cu_new as in csl_compress_insert.  swa: ratio 1, bf16 or fp8
+ * rows.  Limits: 1 <= n_heads <= 1024.  An unmapped page skips that key row
+ * (device error bit); the queries are written regardless.
+ */
+csl_status csl_q_norm_rope_insert(const csl_pool* swa /* host */, const csl_pages* pages /* host */,
+                                  const int64_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                  const uint16_t* x, const uint16_t* q, int32_t n_heads, const float* q_gain,
+                                  float eps, uint16_t* q_out, csl_stream_t stream);
+
+/*
  * Steps 2-3 -- DSA indexer scores and causal top-k ([Summary] DeepSeek V4
  * 注意力架構: DSA keeps only the top-k compressed tokens; [Notes] 压缩参数细节:
  * k = 512 on c4a layers).
@@ -233,6 +257,7 @@ csl_status csl_read_device_error(uint32_t* flags);
 #define CSL_KERNEL_TOPK_SELECT 2
 #define CSL_KERNEL_ATTN 3
 #define CSL_KERNEL_ATTN_COMBINE 4
+#define CSL_KERNEL_QSIDE 5
 csl_status csl_timer_enable(int32_t kernel_id, int32_t on);
 csl_status csl_timer_read(int32_t kernel_id, double* total_ms /* host */, int64_t* launches /* host */);
 

@@ -27,7 +27,7 @@ from . import rng
 
 # tensor ids (stable; changing one changes every derived input)
 T_X, T_LOGITS, T_XI, T_LOGITS_I, T_Q, T_QI, T_W, T_GAIN, T_GAIN_I = 1, 2, 3, 4, 5, 6, 7, 8, 9
-T_INDEX_KEYS, T_PERM, T_LOGITS_128, T_Q128 = 10, 11, 12, 13
+T_INDEX_KEYS, T_PERM, T_LOGITS_128, T_Q128, T_GAIN_Q = 10, 11, 12, 13, 14
 T_ROWS, T_TOPK = 20, 21
 
 

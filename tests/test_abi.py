@@ -124,3 +124,22 @@ def test_attn_validation(csl):
     assert attn(csl, comp, swa, pg(csl), ws_bytes=0) == -4
     for bad in (0.0, -0.04, float("inf"), float("nan")):                   # the logit scale must be > 0
         assert attn(csl, comp, swa, pg(csl), scale=bad) == -1
+
+
+def qside(csl, P, G, heads=64, total=2, x=FAKE, q=FAKE, q_out=FAKE, eps=1e-6):
+    return csl._q_side(C.byref(P), C.byref(G), FAKE, FAKE, total, x, q, heads, None, eps, q_out, None)
+
+
+def test_q_side_validation(csl):
+    swa = pool(csl, ratio=1, coff=1, state_x=None, state_logits=None)
+    assert qside(csl, pool(csl), pg(csl)) == -1                            # the key pool must be ratio 1
+    assert qside(csl, pool(csl, ratio=1, coff=1, dim=128, rope_dims=0, dtype=3), pg(csl)) == -6  # no fp4 keys
+    assert qside(csl, swa, pg(csl), heads=0) == -2
+    assert qside(csl, swa, pg(csl), heads=1025) == -2
+    assert qside(csl, swa, pg(csl), total=-1) == -1
+    assert qside(csl, swa, pg(csl), eps=-1.0) == -1
+    assert qside(csl, swa, pg(csl), q=None) == -1
+    assert qside(csl, swa, pg(csl), x=FAKE + 2) == -3
+    assert qside(csl, swa, pg(csl), q_out=FAKE + 1024) == -1               # overlaps q without being q
+    assert qside(csl, swa, pg(csl), total=0) == 0                          # nothing to do, nothing launched
+    assert csl.last_error() != ""

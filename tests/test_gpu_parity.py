@@ -160,6 +160,104 @@ def test_compress_insert_multi_parity(csl, orc):
 
 
 # ---------------------------------------------------------------------------
+# q_norm_rope_insert (query side + raw-key insert)
+# ---------------------------------------------------------------------------
+
+QSIDE_CASES = [
+    dict(name="d512_r64_h64_bf16_2seq_chunked", D=512, R=64, H=64, dtype=O.BF16, lens=[300, 77],
+         chunks=[[200, 100], [77, 0]], gain=True),
+    dict(name="d512_r64_h16_fp8_inplace", D=512, R=64, H=16, dtype=O.FP8, lens=[260], chunks=[[1, 259]],
+         in_place=True),
+    dict(name="d128_r32_h8_tiny", D=128, R=32, H=8, dtype=O.BF16, lens=[1024], chunks=[[1000, 24]]),
+    # 7 heads: a wave's four rows cross token boundaries
+    dict(name="d512_h7_rows_cross_tokens", D=512, R=64, H=7, dtype=O.BF16, lens=[33, 50], chunks=[[33], [50]],
+         gain=True),
+    dict(name="d64_r16_h1_3seq_one_empty", D=64, R=16, H=1, dtype=O.BF16, lens=[5, 0, 9], chunks=[[5], [0], [9]]),
+    # positions near 2^20: the angles of the fastest pairs reach ~1e6 rad
+    dict(name="d512_h64_pos_1m", D=512, R=64, H=64, dtype=O.BF16, lens=[40], chunks=[[40]], start=(1 << 20) - 17),
+]
+
+
+def sparse_table(seed, lens, start, extra=0):
+    """Block table mapping only the blocks that positions start .. start+len-1 touch (others -1)."""
+    mb = (start + max(lens)) // 256 + 1
+    bt = np.full((len(lens), mb), -1, np.int32)
+    nxt = 0
+    for s, n in enumerate(lens):
+        for b in range(start // 256, (start + n - 1) // 256 + 1 if n else start // 256):
+            bt[s, b] = nxt
+            nxt += 1
+    perm = np.random.default_rng(seed).permutation(nxt + extra).astype(np.int32)
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    return bt, nxt + extra
+
+
+@pytest.mark.parametrize("case", QSIDE_CASES, ids=[c["name"] for c in QSIDE_CASES])
+def test_q_norm_rope_insert_parity(csl, orc, case):
+    D, R, H, dt, lens, chunks = case["D"], case["R"], case["H"], case["dtype"], case["lens"], case["chunks"]
+    ns, start = len(lens), case.get("start", 0)
+    seed = zlib.crc32(case["name"].encode()) % 1000
+    bt, npages = sparse_table(seed, lens, start, extra=1)
+    hp = O.HostPool(1, 1, D, R, THETA, dt, npages, state=False)
+    gp = gpu_pool(csl, hp, state=False)
+    gbt = dev(bt)
+    xs = [randn_bf16(seed, 100 + s, (lens[s], D)) for s in range(ns)]
+    qs = [randn_bf16(seed, 150 + s, (lens[s], H, D)) for s in range(ns)]
+    gain = rand_u(seed, 300, (D,), 0.5, 1.5).astype(np.float32) if case.get("gain") else None
+    done = [0] * ns
+    for rnd in range(max(len(ch) for ch in chunks)):
+        sizes = [chunks[s][rnd] if rnd < len(chunks[s]) else 0 for s in range(ns)]
+        cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        st = np.array(done, np.int64) + start
+        x = np.concatenate([xs[s][done[s]:done[s] + sizes[s]] for s in range(ns)])
+        q = np.concatenate([qs[s][done[s]:done[s] + sizes[s]] for s in range(ns)])
+        want, f = O.q_norm_rope_insert(hp, bt, st, cu, x, q, gain)
+        assert f == 0
+        say(f"q_norm_rope_insert {case['name']} round {rnd} sizes {sizes}")
+        gq = dev_bf16(q)
+        out = None if case.get("in_place") else torch.empty_like(gq)
+        got = csl.q_norm_rope_insert(gp, gbt, dev(st), dev(cu), dev_bf16(x), gq, None if gain is None else dev(gain),
+                                     q_out=out)
+        if case.get("in_place"):
+            assert got is gq
+        torch.cuda.synchronize()
+        gotq = host_u16(got).reshape(want.shape)
+        assert_close(bf16_to_f64(gotq), bf16_to_f64(want), what=f"{case['name']} q round {rnd}")
+        if want.size:
+            assert np.mean(gotq == want) >= 0.99, f"{case['name']}: {np.mean(gotq == want):.4f} bit-exact"
+        done = [done[s] + sizes[s] for s in range(ns)]
+    assert csl.read_device_error() == 0
+    g_rows = host(gp.rows)
+    for s in range(ns):
+        go = gather_rows(g_rows, bt, s, 1, start, lens[s])
+        oo = gather_rows(hp.rows, bt, s, 1, start, lens[s])
+        if dt == O.BF16:
+            assert_close(O.decode_rows(go, D, dt), O.decode_rows(oo, D, dt), what=f"{case['name']} rows seq {s}")
+        else:
+            assert_fp8_close(orc, go[:, :D], go[:, D:].copy().view(np.float32), oo[:, :D],
+                             oo[:, D:].copy().view(np.float32), what=f"{case['name']} rows seq {s}")
+
+
+def test_q_side_unmapped_page_flags_and_writes_queries(csl, orc):
+    D, R, H = 512, 64, 4
+    bt = np.array([[0, -1]], np.int32)
+    hp = O.HostPool(1, 1, D, R, THETA, O.BF16, 2, state=False)
+    gp = gpu_pool(csl, hp, state=False)
+    x = randn_bf16(5, 1, (3, D))
+    q = randn_bf16(5, 2, (3, H, D))
+    st, cu = np.array([254], np.int64), np.array([0, 3], np.int32)
+    want, f = O.q_norm_rope_insert(hp, bt, st, cu, x, q)
+    assert f == 1
+    say("q_norm_rope_insert unmapped page")
+    got = csl.q_norm_rope_insert(gp, dev(bt), dev(st), dev(cu), dev_bf16(x), dev_bf16(q), q_out=torch.empty(
+        (3, H, D), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == csl.DEVERR_UNMAPPED_PAGE
+    assert_close(bf16_to_f64(host_u16(got).reshape(want.shape)), bf16_to_f64(want), what="q")
+    assert np.array_equal(host(gp.rows), hp.rows)
+
+
+# ---------------------------------------------------------------------------
 # index_topk
 # ---------------------------------------------------------------------------
 
