@@ -46,7 +46,7 @@ def log(msg):
 class DecodeSetup:
     """Pools, block table and step inputs of a decode workload, resident on the GPU."""
 
-    def __init__(self, w, replicas: int, device="cuda", side_stream: bool = False):
+    def __init__(self, w, replicas: int, device="cuda", side_stream: bool = False, qside: bool = False):
         import torch
 
         import compressed_sparse_long_amd as csl
@@ -130,10 +130,16 @@ class DecodeSetup:
                                if w.out_dtype == 2 else None) for l in w.layers}
         self.scale = D ** -0.5
         self.side = torch.cuda.Stream() if side_stream else None
+        # with the query side in the step, q is produced from pre-norm heads by the
+        # fused Q norm + RoPE + raw-key insert launch (which then owns the raw insert)
+        self.qside = qside
+        if qside:
+            self.q_pre = self.q.clone()
+            self.gain_q = W.gain(w, D, tid=W.T_GAIN_Q, device=device)
 
     def inserts(self, p):
         """The new token into every pool of the layer, one fused launch."""
-        jobs = [(p["raw"], self.x_new, None, None)]
+        jobs = [] if self.qside else [(p["raw"], self.x_new, None, None)]
         if "c4a" in self.layers:
             jobs += [(p["main4"], self.x_new, self.lg_new, self.gain), (p["idx"], self.xi_new, self.lgi_new, self.gain_i)]
         if "c128a" in self.layers:
@@ -145,6 +151,9 @@ class DecodeSetup:
         beside the indexer and attention (the query at p reads positions < p
         only), forked from and joined back into the current stream."""
         p, torch = self.reps[r], self.torch
+        if self.qside:
+            self.csl.q_norm_rope_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new, self.q_pre, self.gain_q,
+                                        q_out=self.q)
         if self.side is not None:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)
@@ -177,7 +186,7 @@ class DecodeSetup:
         rb = self.csl.row_bytes(D, w.kv_dtype)
         ob = {0: 4 * D, 1: 2 * D, 2: D + 4 * (D // 64)}[w.out_dtype]
         per_q = {}
-        qio = H * D * 2 + H * ob
+        qio = H * D * 2 + H * ob + (2 * H * D * 2 if self.qside else 0)
         ins = 2 * D * 2 + rb  # raw insert: x read, state x write (c4a/c128a), raw row write
         if "c4a" in w.layers:
             irb = self.csl.row_bytes(w.idx_dim, w.idx_dtype)
@@ -544,6 +553,9 @@ def main():
                     help="eager steps after the graph replays that time the dominant kernel")
     ap.add_argument("--side-stream", action="store_true",
                     help="run the inserts on a side stream beside the indexer and attention")
+    ap.add_argument("--qside", action="store_true",
+                    help="start the step from pre-norm query heads: the fused Q norm + RoPE + raw-key insert launch "
+                         "produces q and writes the raw key")
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -572,7 +584,7 @@ def main():
         return
     w = {"c4a": W.c4a_decode, "c4a_fp4": W.c4a_decode_fp4, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)
-    setup = DecodeSetup(w, R, side_stream=args.side_stream)
+    setup = DecodeSetup(w, R, side_stream=args.side_stream, qside=args.qside)
     log(f"workload {w.name}: {w.num_seqs} x {w.ctx} tokens, {R} replicas")
 
     for i in range(args.warmup):
@@ -648,6 +660,7 @@ def main():
                    "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
                    "out_dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.out_dtype], "replicas": R,
                    "hip_graphs": bool(graphs), "steps_per_graph": per_graph, "insert_stream": "side" if args.side_stream else "main",
+                   "query_side_in_step": bool(args.qside),
                    "algorithmic_bytes_per_step": step_bytes},
         "roofline": roof,
     }

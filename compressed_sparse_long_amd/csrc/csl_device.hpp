@@ -114,6 +114,23 @@ __device__ __forceinline__ float sum_xor32(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum over the 64 lanes, identical in every lane: quad_perm swaps (lane ^ 1,
+// lane ^ 2), row_half_mirror and row_mirror (the other quad, the other half
+// row), then the row-pair and half-wave swaps.  Each step adds a pair of
+// values that both partner lanes see, so every lane ends with the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+    v += dpp_f32<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x141>(v);  // row_half_mirror
+    v += dpp_f32<0x140>(v);  // row_mirror
+    v = sum_xor16(v);
+    return sum_xor32(v);
+}
+
 // Prefix scans over the 64 lanes (lane 0 first) on DPP moves, no LDS: shifts
 // by 1, 2, 4, 8 lanes inside each 16-lane row, then the last lane of rows 0
 // and 2 into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3

@@ -163,6 +163,8 @@ def test_compress_insert_multi_parity(csl, orc):
 # q_norm_rope_insert (query side + raw-key insert)
 # ---------------------------------------------------------------------------
 
+# Launch forms by rows (tokens x (heads + 1)): one row per wave below 4096, two
+# below 16384, four from there on; the cases below cover all three.
 QSIDE_CASES = [
     dict(name="d512_r64_h64_bf16_2seq_chunked", D=512, R=64, H=64, dtype=O.BF16, lens=[300, 77],
          chunks=[[200, 100], [77, 0]], gain=True),
@@ -173,6 +175,9 @@ QSIDE_CASES = [
     dict(name="d512_h7_rows_cross_tokens", D=512, R=64, H=7, dtype=O.BF16, lens=[33, 50], chunks=[[33], [50]],
          gain=True),
     dict(name="d64_r16_h1_3seq_one_empty", D=64, R=16, H=1, dtype=O.BF16, lens=[5, 0, 9], chunks=[[5], [0], [9]]),
+    # 297 tokens x 65 rows: four rows per wave (the large-launch form), fp8 key rows, ragged tail
+    dict(name="d512_h64_fp8_four_rows_per_wave", D=512, R=64, H=64, dtype=O.FP8, lens=[257, 40],
+         chunks=[[257], [40]], gain=True),
     # positions near 2^20: the angles of the fastest pairs reach ~1e6 rad
     dict(name="d512_h64_pos_1m", D=512, R=64, H=64, dtype=O.BF16, lens=[40], chunks=[[40]], start=(1 << 20) - 17),
 ]
