@@ -46,7 +46,8 @@ def log(msg):
 class DecodeSetup:
     """Pools, block table and step inputs of a decode workload, resident on the GPU."""
 
-    def __init__(self, w, replicas: int, device="cuda", side_stream: bool = False, qside: bool = False):
+    def __init__(self, w, replicas: int, device="cuda", side_stream: bool = False, qside: bool = False,
+                 fused_inserts: bool = False):
         import torch
 
         import compressed_sparse_long_amd as csl
@@ -133,27 +134,37 @@ class DecodeSetup:
         # with the query side in the step, q is produced from pre-norm heads by the
         # fused Q norm + RoPE + raw-key insert launch (which then owns the raw insert)
         self.qside = qside
+        self.fused_inserts = fused_inserts and not side_stream
         if qside:
             self.q_pre = self.q.clone()
             self.gain_q = W.gain(w, D, tid=W.T_GAIN_Q, device=device)
 
-    def inserts(self, p):
-        """The new token into every pool of the layer, one fused launch."""
+    def insert_jobs(self, p):
+        """The new token's insert into every pool of the layer."""
         jobs = [] if self.qside else [(p["raw"], self.x_new, None, None)]
         if "c4a" in self.layers:
             jobs += [(p["main4"], self.x_new, self.lg_new, self.gain), (p["idx"], self.xi_new, self.lgi_new, self.gain_i)]
         if "c128a" in self.layers:
             jobs += [(p["main128"], self.x_new, self.lg128_new, None)]
-        self.csl.compress_insert_multi(jobs, self.bt, self.start, self.cu1)
+        return jobs
+
+    def inserts(self, p):
+        """The new token into every pool of the layer, one fused launch."""
+        self.csl.compress_insert_multi(self.insert_jobs(p), self.bt, self.start, self.cu1)
 
     def step(self, r: int):
-        """One decode step.  With side streams, the inserts of the new token run
-        beside the indexer and attention (the query at p reads positions < p
-        only), forked from and joined back into the current stream."""
+        """One decode step.  By default the inserts ride in the indexer's top-k
+        launch (index_topk_insert; the query at p reads positions < p only).
+        Otherwise they go first in a launch of their own, or, with side streams,
+        beside the indexer and attention, forked from and joined back into the
+        current stream."""
         p, torch = self.reps[r], self.torch
         if self.qside:
             self.csl.q_norm_rope_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new, self.q_pre, self.gain_q,
                                         q_out=self.q)
+        if self.fused_inserts and "c4a" in self.layers:
+            self.attend(r, with_inserts=True)
+            return
         if self.side is not None:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)
@@ -165,12 +176,17 @@ class DecodeSetup:
         if self.side is not None:
             torch.cuda.current_stream().wait_stream(self.side)
 
-    def attend(self, r: int):
-        """The query side of a step: index top-k and attention of every layer."""
+    def attend(self, r: int, with_inserts: bool = False):
+        """The query side of a step: index top-k and attention of every layer
+        (with_inserts: the step's inserts in the top-k launch)."""
         csl, w, p = self.csl, self.w, self.reps[r]
         if "c4a" in self.layers:
-            csl.index_topk(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx, w.topk,
-                           self.topk, None, self.ws_idx)
+            if with_inserts:
+                csl.index_topk_insert(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx,
+                                      w.topk, self.topk, self.insert_jobs(p), self.start, self.cu1, None, self.ws_idx)
+            else:
+                csl.index_topk(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx, w.topk,
+                               self.topk, None, self.ws_idx)
             csl.hybrid_attn_decode(p["main4"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q,
                                    self.topk, w.topk, w.swa, self.scale, w.out_dtype, self.out["c4a"],
                                    self.out_scales["c4a"], self.ws_attn)
@@ -553,6 +569,8 @@ def main():
                     help="eager steps after the graph replays that time the dominant kernel")
     ap.add_argument("--side-stream", action="store_true",
                     help="run the inserts on a side stream beside the indexer and attention")
+    ap.add_argument("--separate-inserts", action="store_true",
+                    help="launch the inserts on their own before the indexer instead of inside its top-k launch")
     ap.add_argument("--qside", action="store_true",
                     help="start the step from pre-norm query heads: the fused Q norm + RoPE + raw-key insert launch "
                          "produces q and writes the raw key")
@@ -584,7 +602,8 @@ def main():
         return
     w = {"c4a": W.c4a_decode, "c4a_fp4": W.c4a_decode_fp4, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)
-    setup = DecodeSetup(w, R, side_stream=args.side_stream, qside=args.qside)
+    setup = DecodeSetup(w, R, side_stream=args.side_stream, qside=args.qside,
+                        fused_inserts=not args.separate_inserts)
     log(f"workload {w.name}: {w.num_seqs} x {w.ctx} tokens, {R} replicas")
 
     for i in range(args.warmup):
@@ -660,6 +679,8 @@ def main():
                    "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
                    "out_dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.out_dtype], "replicas": R,
                    "hip_graphs": bool(graphs), "steps_per_graph": per_graph, "insert_stream": "side" if args.side_stream else "main",
+                   "inserts": ("in the top-k launch" if setup.fused_inserts and "c4a" in w.layers else
+                               "own launch" + (" (side stream)" if args.side_stream else "")),
                    "query_side_in_step": bool(args.qside),
                    "algorithmic_bytes_per_step": step_bytes},
         "roofline": roof,

@@ -72,6 +72,9 @@ _q_side = _sig("csl_q_norm_rope_insert", C.c_int, [_P, _G, _vp, _vp, _i32, _vp, 
 _index_topk_ws = _sig("csl_index_topk_workspace", _sz, [_i32, _i64, _i32])
 _index_topk = _sig("csl_index_topk", C.c_int,
                    [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
+_index_topk_insert = _sig("csl_index_topk_insert", C.c_int,
+                          [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _i32,
+                           C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, _vp])
 _attn_ws = _sig("csl_hybrid_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i64])
 _attn_decode = _sig("csl_hybrid_attn_decode", C.c_int,
                     [_P, _P, _G, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz,
@@ -84,7 +87,7 @@ _timer_enable = _sig("csl_timer_enable", C.c_int, [_i32, _i32])
 _timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)])
 
 EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_q_norm_rope_insert",
-           "csl_index_topk_workspace", "csl_index_topk",
+           "csl_index_topk_workspace", "csl_index_topk", "csl_index_topk_insert",
            "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill", "csl_last_error",
            "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
 
@@ -183,6 +186,23 @@ def index_topk(pool: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k, to
     _check(_index_topk(C.byref(ps), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos), _ptr(q_idx), _ptr(w),
                        nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                        _stream(stream)))
+
+
+def index_topk_insert(pool: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k, topk, jobs, start_pos, cu_new,
+                      kth_score=None, ws=None, eps=1e-6, stream=None):
+    """index_topk, then compress_insert_multi(jobs, ...) on the same stream, the inserts riding in the
+    top-k launch.  jobs: list of (pool, x, logits or None, gain or None)."""
+    ps = pool.struct()
+    pg = pages(block_table)
+    nq, nh = int(w.shape[0]), int(w.shape[1])
+    structs = [p.struct() for p, _, _, _ in jobs]
+    arr = (_InsertJob * len(jobs))(*[_InsertJob(C.addressof(structs[i]), _ptr(x), _ptr(lg), _ptr(g))
+                                     for i, (_, x, lg, g) in enumerate(jobs)])
+    total = int(jobs[0][1].shape[0])
+    _check(_index_topk_insert(C.byref(ps), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos), _ptr(q_idx),
+                              _ptr(w), nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), len(jobs), arr, _ptr(start_pos),
+                              _ptr(cu_new), total, float(eps), _stream(stream)))
 
 
 def hybrid_attn_workspace(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos) -> int:

@@ -300,9 +300,10 @@ csl_status csl_timer_read(int32_t kid, double* total_ms, int64_t* launches) {
     return CSL_OK;
 }
 
-csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs, const csl_pages* pages,
-                                     const int64_t* start_pos, const int32_t* cu_new, int32_t total_new, float eps,
-                                     csl_stream_t stream) {
+// Validates an insert batch and fills its kernel arguments (a.total_new = 0:
+// nothing to launch).  Launches nothing.
+csl_status prepare_inserts(int32_t n_jobs, const csl_insert_job* jobs, const csl_pages* pages, const int64_t* start_pos,
+                           const int32_t* cu_new, int32_t total_new, float eps, CompressArgs& a) {
     csl_status st;
     if (n_jobs < 1 || n_jobs > kMaxInsertJobs) return fail(CSL_ERANGE, "n_jobs = %d, supported 1..%d", n_jobs, kMaxInsertJobs);
     if (!jobs) return fail(CSL_EINVAL, "jobs is NULL");
@@ -310,7 +311,8 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs,
     if (total_new < 0) return fail(CSL_EINVAL, "total_new < 0");
     if (!start_pos || !cu_new) return fail(CSL_EINVAL, "start_pos or cu_new is NULL");
     if (!(eps >= 0.f)) return fail(CSL_EINVAL, "eps must be >= 0");
-    CompressArgs a;
+    a.total_new = 0;
+    a.n_jobs = n_jobs;
     for (int i = 0; i < n_jobs; ++i) {
         const csl_pool* pool = jobs[i].pool;
         if ((st = check_pool(pool, "pool"))) return st;
@@ -341,17 +343,24 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs,
         a.rf[i] = make_freqs(pool->rope_dims, pool->rope_theta);
     }
     if (total_new == 0) return CSL_OK;
-    uint32_t* err = nullptr;
-    if ((st = device_error_ptr(&err))) return st;
     a.bt = pages->block_table;
     a.start_pos = start_pos;
     a.cu_new = cu_new;
-    a.err = err;
-    a.n_jobs = n_jobs;
+    a.err = nullptr;  // set by the caller once every check has passed
     a.num_seqs = pages->num_seqs;
     a.max_blocks = pages->max_blocks;
     a.total_new = total_new;
     a.eps = eps;
+    return CSL_OK;
+}
+
+csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs, const csl_pages* pages,
+                                     const int64_t* start_pos, const int32_t* cu_new, int32_t total_new, float eps,
+                                     csl_stream_t stream) {
+    CompressArgs a;
+    csl_status st = prepare_inserts(n_jobs, jobs, pages, start_pos, cu_new, total_new, eps, a);
+    if (st || a.total_new == 0) return st;
+    if ((st = device_error_ptr(&a.err))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed(CSL_KERNEL_COMPRESS, [&](const LaunchEvents& ev) { return launch_compress(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "compress_insert launch");
@@ -426,11 +435,14 @@ size_t csl_index_topk_workspace(int32_t num_q, int64_t max_q_pos, int32_t k) {
     return (size_t)num_q * ((size_t)stride * sizeof(float) + (kl > 0 ? (size_t)nchunks * (kl + 1) * 8 : 0));
 }
 
-csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
-                          const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q_idx, const float* w,
-                          int32_t n_heads, int32_t k, int32_t* topk, float* kth_score, void* ws, size_t ws_bytes,
-                          csl_stream_t stream) {
+// Validates an indexer call and fills its kernel arguments (a.num_q = 0:
+// nothing to launch).  Launches nothing.
+csl_status prepare_index(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
+                         const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q_idx, const float* w,
+                         int32_t n_heads, int32_t k, int32_t* topk, float* kth_score, void* ws, size_t ws_bytes,
+                         IndexArgs& a) {
     csl_status st;
+    a.num_q = 0;
     if ((st = check_pool(index_pool, "index"))) return st;
     if ((st = check_pages(pages))) return st;
     if (index_pool->ratio != 4) return fail(CSL_EUNSUPPORTED, "the indexer runs on ratio-4 (c4a) pools only");
@@ -450,9 +462,6 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     size_t need = csl_index_topk_workspace(num_q, max_q_pos, k);
     if (!ws || ws_bytes < need) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     if (!aligned16(ws)) return fail(CSL_EALIGN, "ws is not 16-byte aligned");
-    uint32_t* err = nullptr;
-    if ((st = device_error_ptr(&err))) return st;
-    IndexArgs a;
     a.rows = static_cast<const uint8_t*>(index_pool->rows);
     a.bt = pages->block_table;
     a.q_seq = q_seq;
@@ -462,7 +471,7 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     a.scores = static_cast<float*>(ws);
     a.topk = topk;
     a.kth = kth_score;
-    a.err = err;
+    a.err = nullptr;  // set by the caller once every check has passed
     a.max_q_pos = max_q_pos;
     a.stride = index_stride(max_q_pos);
     a.nchunks = (int)(a.stride / kIndexChunk);
@@ -478,11 +487,56 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     a.num_pages = index_pool->num_pages;
     a.num_seqs = pages->num_seqs;
     a.max_blocks = pages->max_blocks;
+    return CSL_OK;
+}
+
+csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
+                          const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q_idx, const float* w,
+                          int32_t n_heads, int32_t k, int32_t* topk, float* kth_score, void* ws, size_t ws_bytes,
+                          csl_stream_t stream) {
+    IndexArgs a;
+    csl_status st = prepare_index(index_pool, pages, num_q, q_seq, q_pos, max_q_pos, q_idx, w, n_heads, k, topk,
+                                  kth_score, ws, ws_bytes, a);
+    if (st || a.num_q == 0) return st;
+    if ((st = device_error_ptr(&a.err))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
     e = timed(CSL_KERNEL_TOPK_SELECT, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "topk_select launch");
+    return CSL_OK;
+}
+
+csl_status csl_index_topk_insert(const csl_pool* index_pool, const csl_pages* pages, int32_t num_q,
+                                 const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q_idx,
+                                 const float* w, int32_t n_heads, int32_t k, int32_t* topk, float* kth_score,
+                                 void* ws, size_t ws_bytes, int32_t n_jobs, const csl_insert_job* jobs,
+                                 const int64_t* start_pos, const int32_t* cu_new, int32_t total_new, float eps,
+                                 csl_stream_t stream) {
+    IndexArgs a;
+    CompressArgs c;
+    csl_status st = prepare_index(index_pool, pages, num_q, q_seq, q_pos, max_q_pos, q_idx, w, n_heads, k, topk,
+                                  kth_score, ws, ws_bytes, a);
+    if (st) return st;
+    if ((st = prepare_inserts(n_jobs, jobs, pages, start_pos, cu_new, total_new, eps, c))) return st;
+    if (a.num_q == 0 && c.total_new == 0) return CSL_OK;
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    a.err = err;
+    c.err = err;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (a.num_q > 0) {
+        e = timed(CSL_KERNEL_INDEX_SCORE, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
+        if (e != hipSuccess) return hip_fail(e, "index_score launch");
+    }
+    if (c.total_new == 0) {
+        if (a.num_q > 0) e = timed(CSL_KERNEL_TOPK_SELECT, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
+    } else {
+        e = timed(CSL_KERNEL_TOPK_SELECT,
+                  [&](const LaunchEvents& ev) { return launch_topk_select_insert(a, c, s, ev); });
+    }
+    if (e != hipSuccess) return hip_fail(e, "topk_select / insert launch");
     return CSL_OK;
 }
 

@@ -13,243 +13,15 @@
 // stores the token's row.  A lane owns 8 consecutive dims (one 16-byte
 // load/store per row), so a wave covers a row of up to 512 dims and RoPE pairs
 // never straddle lanes.  Elementwise and HBM-bound: no MFMA.
-#include "csl_kernels.hpp"
+#include "csl_insert.hpp"
 
 namespace csl {
 
 namespace {
 
-constexpr int kThreads = 256;
-
-// Sequence s with cu[s] <= j < cu[s+1]: the wave reads 64 boundaries per step
-// in parallel and counts the ones <= j (cu is non-decreasing).  Wave-uniform.
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int num_seqs, int j) {
-    const int lane = threadIdx.x & 63;
-    int s = -1;
-    for (int base = 1; base <= num_seqs; base += 64) {
-        const int i = base + lane;
-        const bool le = i <= num_seqs && cu[i] <= j;
-        s += (int)__popcll(__ballot(le));
-        if (!__ballot(i <= num_seqs && !le)) continue;
-        break;
-    }
-    s += 1;
-    return s < num_seqs ? s : num_seqs - 1;
-}
-
-__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
-    u32x4 r = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        v[2 * c] = __uint_as_float(r[c] << 16);
-        v[2 * c + 1] = __uint_as_float(r[c] & 0xffff0000u);
-    }
-}
-
-// Rotate the lane's 8 dims [d0, d0+8) at position `pos` (pairs in the last R dims).
-__device__ __forceinline__ void rope8(float* v, int d0, int dim, int rope_dims, const RopeFreqs& rf, int64_t pos) {
-    int base = dim - rope_dims;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        int d = d0 + 2 * c;
-        if (d >= base) {
-            float cs, sn;
-            rope_cs(pos, rf.inv_freq[(d - base) >> 1], cs, sn);
-            float a = v[2 * c], b = v[2 * c + 1];
-            v[2 * c] = a * cs - b * sn;
-            v[2 * c + 1] = a * sn + b * cs;
-        }
-    }
-}
-
-// Store the lane's 8 values of a row; every lane of the wave must call this
-// (fp8 reduces the group amax across 8 lanes, fp4 the block max across 4).  `active` = lane owns dims.
-__device__ __forceinline__ void store8(uint8_t* row, int dtype, int dim, int lane, bool active, const float* v) {
-    if (dtype == kBF16) {
-        if (active) {
-            u32x4 o;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
-            *reinterpret_cast<u32x4*>(row + 16 * lane) = o;
-        }
-        return;
-    }
-    if (dtype == kFP4) {
-        // MXFP4: the 32-element block is 4 lanes.  Scale 2^(floor(log2 amax) - 2)
-        // as an E8M0 byte; each element scaled by a power of two (exact) and
-        // rounded to E2M1 by counting the midpoints it passes (a tie sits at
-        // the even code: strict at 0.25, 1.25, 2.5, 5; inclusive at 0.75,
-        // 1.75, 3.5), saturating at 6.
-        float bmax = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) bmax = fmaxf(bmax, fabsf(v[c]));
-        bmax = active ? bmax : 0.f;
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
-        int sh = bmax > 0.f ? __builtin_amdgcn_frexp_expf(bmax) - 3 : -127;
-        sh = sh < -127 ? -127 : (sh > 127 ? 127 : sh);
-        if (active) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float q = __builtin_amdgcn_ldexpf(v[c], -sh);
-                const float r = fabsf(q);
-                const uint32_t code = (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) +
-                                      (uint32_t)(r >= 1.75f) + (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) +
-                                      (uint32_t)(r > 5.0f);
-                word |= (code | ((__float_as_uint(q) >> 28) & 8u)) << (4 * c);
-            }
-            *reinterpret_cast<uint32_t*>(row + 4 * lane) = word;
-            if ((lane & 3) == 0) row[dim / 2 + (lane >> 2)] = (uint8_t)(sh + 127);
-        }
-        return;
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[c]));
-    amax = group8_max(active ? amax : 0.f);
-    float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-    if (active) {
-        const float r = 1.0f / scale;
-        const u32x2 o = {e4m3_pack4(v[0] * r, v[1] * r, v[2] * r, v[3] * r),
-                         e4m3_pack4(v[4] * r, v[5] * r, v[6] * r, v[7] * r)};
-        *reinterpret_cast<u32x2*>(row + 8 * lane) = o;
-        if ((lane & 7) == 0) *reinterpret_cast<float*>(row + dim + 4 * (lane >> 3)) = scale;
-    }
-}
-
 __global__ void __launch_bounds__(kThreads) compress_insert_kernel(CompressArgs args) {
-    const CompressJob& a = args.job[blockIdx.y];
-    const RopeFreqs& rf = args.rf[blockIdx.y];
-    __shared__ float s_w[kThreads];
-    __shared__ const uint16_t* s_ptr[kThreads];
-    __shared__ float s_red[4][512];
-    __shared__ float s_tmp[8];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int D = a.dim;
-    const bool active = lane * 8 < D;
-
-    if (a.ratio == 1) {
-        const int j = blockIdx.x;
-        if (wave != 0) return;
-        int s = find_seq(args.cu_new, args.num_seqs, j);
-        int64_t t = args.start_pos[s] + (j - args.cu_new[s]);
-        int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, t);
-        if (pg < 0) {
-            if (lane == 0) raise_error(args.err, (t < 0 || (t >> 8) >= args.max_blocks) ? kErrPos : kErrPage);
-            return;
-        }
-        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (active) load8(a.x + (int64_t)j * D + 8 * lane, v);
-        rope8(v, 8 * lane, D, a.rope_dims, rf, t);
-        uint8_t* row = a.rows + ((int64_t)pg * kBlockPositions + (t & 255)) * a.row_bytes;
-        store8(row, a.dtype, D, lane, active, v);
-        return;
-    }
-
-    const int j = blockIdx.x;
-    const int s = find_seq(args.cu_new, args.num_seqs, j);
-    const int64_t start = args.start_pos[s];
-    const int cbase = args.cu_new[s];
-    const int64_t t = start + (j - cbase);
-    const int r = a.ratio, W = a.coff * a.ratio;
-
-    // 1. append the token to the compressor state
-    if (wave == 0) {
-        int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, t);
-        if (pg < 0) {
-            if (lane == 0) raise_error(args.err, (t < 0 || (t >> 8) >= args.max_blocks) ? kErrPos : kErrPage);
-        } else {
-            int64_t tok = (int64_t)pg * kBlockPositions + (t & 255);
-            if (active)
-                *reinterpret_cast<u32x4*>(a.state_x + tok * D + 8 * lane) =
-                    *reinterpret_cast<const u32x4*>(a.x + (int64_t)j * D + 8 * lane);
-            if (lane < a.coff) a.state_logits[tok * a.coff + lane] = a.logits[(int64_t)j * a.coff + lane];
-        }
-    }
-    if ((t + 1) % r != 0) return;  // uniform across the workgroup
-    const int64_t i = (t + 1) / r - 1;
-
-    // 2. window weights: thread k owns window slot k
-    float lg = -INFINITY;
-    const uint16_t* ptr = nullptr;
-    if (tid < W) {
-        int64_t tk = (int64_t)r * (i + 1) - W + tid;
-        int col = tid / r;
-        if (tk >= start) {
-            int64_t jj = cbase + (tk - start);
-            lg = a.logits[jj * a.coff + col];
-            ptr = a.x + jj * D;
-        } else if (tk >= 0) {
-            int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, tk);
-            if (pg < 0) {
-                raise_error(args.err, kErrPage);
-            } else {
-                int64_t tok = (int64_t)pg * kBlockPositions + (tk & 255);
-                lg = a.state_logits[tok * a.coff + col];
-                ptr = a.state_x + tok * D;
-            }
-        }
-    }
-    float m = wave_max(lg);
-    if (lane == 0) s_tmp[wave] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(s_tmp[0], s_tmp[1]), fmaxf(s_tmp[2], s_tmp[3]));
-    float e = ptr ? __expf(lg - m) : 0.f;
-    float den = wave_sum(e);
-    __syncthreads();
-    if (lane == 0) s_tmp[4 + wave] = den;
-    s_w[tid] = e;
-    s_ptr[tid] = ptr;
-    __syncthreads();
-    den = s_tmp[4] + s_tmp[5] + s_tmp[6] + s_tmp[7];
-    const float inv_den = den > 0.f ? 1.0f / den : 0.f;
-
-    // 3. weighted sum: wave w takes window slots w, w+4, w+8, ...
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (active) {
-#pragma unroll 4
-        for (int k = wave; k < W; k += 4) {
-            const uint16_t* p = s_ptr[k];
-            if (!p) continue;
-            float wk = s_w[k] * inv_den;
-            float v[8];
-            load8(p + 8 * lane, v);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[c] = fmaf(wk, v[c], acc[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s_red[wave][8 * lane + c] = acc[c];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-
-    // 4. RMSNorm, RoPE at r*i, store
-    float u[8];
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        int d = 8 * lane + c;
-        u[c] = active ? (s_red[0][d] + s_red[1][d]) + (s_red[2][d] + s_red[3][d]) : 0.f;
-        ss = fmaf(u[c], u[c], ss);
-    }
-    ss = wave_sum(ss);
-    float inv = 1.0f / sqrtf(ss / (float)D + args.eps);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        float g = (a.gain && active) ? a.gain[8 * lane + c] : 1.0f;
-        u[c] = u[c] * inv * g;
-    }
-    rope8(u, 8 * lane, D, a.rope_dims, rf, (int64_t)r * i);
-    int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, (int64_t)r * i);
-    if (pg < 0) {
-        if (lane == 0) raise_error(args.err, kErrPage);
-        return;
-    }
-    const int per_page = kBlockPositions / r;
-    uint8_t* row = a.rows + ((int64_t)pg * per_page + (i % per_page)) * a.row_bytes;
-    store8(row, a.dtype, D, lane, active, u);
+    __shared__ InsertSmem sm;
+    insert_block(args, blockIdx.y, blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------- query side

@@ -18,7 +18,7 @@
 // then an order-preserving pass in which each wave owns a contiguous range of
 // ids and emits the selected ids in ascending order with ballots; ties at the
 // k-th score go to the lower ids.
-#include "csl_kernels.hpp"
+#include "csl_insert.hpp"
 
 namespace csl {
 
@@ -1113,7 +1113,7 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
 // too.  Otherwise, or when the candidates cannot hold k ids (short rows), the
 // full select runs on the score row and overwrites the output.
 template <int NT>
-__global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
+__device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
     constexpr int NW = NT / 64;
     __shared__ uint32_t s_hist[2048];
     __shared__ uint32_t s_cand[kCandCap];
@@ -1121,7 +1121,7 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
     __shared__ uint32_t s_sel[8 + NW];
     __shared__ float s_min[NW];
     __shared__ uint32_t s_fail;
-    const int n = blockIdx.x, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     int s;
     int64_t p;
     const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
@@ -1175,6 +1175,25 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
         return;
     }
     if (tid == 0 && kth) *kth = key_score(T);
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
+    merge_query<NT>(a, blockIdx.x);
+}
+
+// The merge with the inserts of the same step in its grid: workgroups past
+// num_q each insert one (new token, pool).  The merge reads only the score
+// workspace, so the inserts cannot change what the queries select, and they
+// fill the CUs that the few merge workgroups leave idle.
+__global__ void __launch_bounds__(256) topk_merge_insert_kernel(IndexArgs a, CompressArgs c) {
+    if ((int)blockIdx.x >= a.num_q) {
+        __shared__ InsertSmem sm;
+        const int i = (int)blockIdx.x - a.num_q;
+        insert_block(c, i / c.total_new, i % c.total_new, sm);
+        return;
+    }
+    merge_query<256>(a, blockIdx.x);
 }
 
 }  // namespace
@@ -1242,6 +1261,29 @@ hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEv
         launch_kernel(ev, true, true, topk_select_kernel, dim3((unsigned)a.num_q), dim3(kSelThreads), st, a);
     }
     return hipGetLastError();
+}
+
+// The select, then the inserts; when the select ends in the 256-thread merge,
+// the inserts ride in its launch (one workgroup per token and pool).
+hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, hipStream_t st,
+                                     const LaunchEvents& ev) {
+    const int64_t n_ins = (int64_t)c.total_new * c.n_jobs;
+    if (a.num_q <= 0 || n_ins <= 0) {
+        hipError_t e = launch_topk_select(a, st, ev);
+        if (e != hipSuccess) return e;
+        return launch_compress(c, st);
+    }
+    if (a.kl > 0 && (int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256 && a.num_q + n_ins <= 0x7fffffff) {
+        if (a.tiled)
+            launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)((a.nchunks + 3) / 4), (unsigned)a.num_q),
+                          dim3(256), st, a);
+        launch_kernel(ev, !a.tiled, true, topk_merge_insert_kernel, dim3((unsigned)(a.num_q + n_ins)), dim3(256), st, a,
+                      c);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_topk_select(a, st, ev);
+    if (e != hipSuccess) return e;
+    return launch_compress(c, st);
 }
 
 bool index_use_tiled(int num_q) { return num_q >= kTiledMinQueries; }

@@ -198,6 +198,24 @@ csl_status csl_index_topk(const csl_pool* index_pool /* host */, const csl_pages
                           float* kth_score, void* ws, size_t ws_bytes, csl_stream_t stream);
 
 /*
+ * Steps 1-3 of a decode step with the inserts overlapped with the indexer
+ * ([Notes] 优化二：多 CUDA 流并行: the indexer branch runs beside the main KV
+ * compression and the raw-window insert; [Summary] 多串流分割).  Exactly
+ * csl_index_topk followed by csl_compress_insert_multi on `stream`, with the
+ * same arguments and results: the inserts run after the index scores are
+ * computed, inside the top-k selection's launch (whose few workgroups leave
+ * most of the GPU idle) when the selection ends in the two-stage merge, else
+ * in a launch of their own after it.  Validation covers both parts before
+ * anything is launched.  1 <= n_jobs <= 4.
+ */
+csl_status csl_index_topk_insert(const csl_pool* index_pool /* host */, const csl_pages* pages /* host */,
+                                 int32_t num_q, const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos,
+                                 const uint16_t* q_idx, const float* w, int32_t n_heads, int32_t k, int32_t* topk,
+                                 float* kth_score, void* ws, size_t ws_bytes, int32_t n_jobs,
+                                 const csl_insert_job* jobs /* host */, const int64_t* start_pos,
+                                 const int32_t* cu_new, int32_t total_new, float eps, csl_stream_t stream);
+
+/*
  * Steps 4-6 -- hybrid attention, inverse RoPE, optional fp8 output.
  *
  * Query n (sequence s, position p) attends with ONE softmax over

@@ -143,3 +143,22 @@ def test_q_side_validation(csl):
     assert qside(csl, swa, pg(csl), q_out=FAKE + 1024) == -1               # overlaps q without being q
     assert qside(csl, swa, pg(csl), total=0) == 0                          # nothing to do, nothing launched
     assert csl.last_error() != ""
+
+
+def test_index_topk_insert_validation(csl):
+    ip = pool(csl, dim=128, rope_dims=0)
+    job_pool = pool(csl, ratio=1, coff=1, state_x=None, state_logits=None)
+    jobs = (csl._InsertJob * 1)(csl._InsertJob(C.addressof(job_pool), FAKE, None, None))
+
+    def call(n_jobs=1, k=64, x_ok=True, total=1):
+        if not x_ok:
+            jobs[0].x = FAKE + 2
+        r = csl._index_topk_insert(C.byref(ip), C.byref(pg(csl)), 4, FAKE, FAKE, 1000, FAKE, FAKE, 16, k, FAKE,
+                                   None, FAKE, 1 << 30, n_jobs, jobs, FAKE, FAKE, total, 1e-6, None)
+        jobs[0].x = FAKE
+        return r
+    assert call(k=0) == -2            # the indexer's checks
+    assert call(n_jobs=0) == -2       # the inserts' checks
+    assert call(n_jobs=5) == -2
+    assert call(x_ok=False) == -3
+    assert call(total=-1) == -1

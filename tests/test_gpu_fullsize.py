@@ -183,7 +183,7 @@ def decode_query_check(csl, w, st, s, layer, theta=10000.0):
 def run_decode(csl, w):
     from bench import DecodeSetup
     say(f"{w.name}: building caches")
-    st = DecodeSetup(w, 1)
+    st = DecodeSetup(w, 1, fused_inserts=True)
     say(f"{w.name}: one decode step")
     st.step(0)
     torch.cuda.synchronize()

@@ -350,6 +350,82 @@ def test_index_topk_parity(csl, orc, case):
 
 
 # ---------------------------------------------------------------------------
+# index_topk_insert: the indexer with the step's inserts in its top-k launch
+# ---------------------------------------------------------------------------
+
+FUSED_CASES = [
+    # decode: one new token per sequence at the query's position; the index pool is
+    # also an insert target (token 9003 closes entry 2250, not visible at p = 9003)
+    dict(name="decode_two_stage_merge", pos=[[9003], [20000]], k=512),
+    # short rows: a one-pass select, the inserts in a launch of their own
+    dict(name="decode_short_rows", pos=[[1000], [700]], k=512),
+    # 100 queries: the query-blocked scores, then the merge with 100 x 3 inserts
+    dict(name="tiled_100_queries", pos=[list(range(9000, 9100))], k=512),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c["name"] for c in FUSED_CASES])
+def test_index_topk_insert_equals_separate_calls(csl, orc, case):
+    seed = zlib.crc32(case["name"].encode()) % 1000
+    H, DI, D, R, k = 16, 128, 512, 64, case["k"]
+    ns = len(case["pos"])
+    max_pos = max(max(p) for p in case["pos"])
+    mb = (max_pos + 256) // 256 + 1
+    bt = block_table(seed, ns, mb, extra_pages=1)
+    P = ns * mb + 1
+    idx = O.HostPool(4, 2, DI, 0, THETA, O.BF16, P)
+    for s in range(ns):
+        scatter_rows(idx.rows, bt, s, 4, randn_bf16(seed, 10 + s, (64 * mb, DI)).view(np.uint8).reshape(64 * mb, -1))
+    idx.state_x[:] = randn_bf16(seed, 11, idx.state_x.shape)
+    idx.state_logits[:] = randn_f32(seed, 12, idx.state_logits.shape).astype(np.float32)
+    raw = O.HostPool(1, 1, D, R, THETA, O.BF16, P, state=False)
+    main = O.HostPool(4, 2, D, R, THETA, O.FP8, P)
+    main.state_x[:] = randn_bf16(seed, 13, main.state_x.shape)
+    main.state_logits[:] = randn_f32(seed, 14, main.state_logits.shape).astype(np.float32)
+    q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
+    q_pos = np.concatenate(case["pos"]).astype(np.int64)
+    nq = len(q_pos)
+    qi = randn_bf16(seed, 20, (nq, H, DI))
+    w = rand_u(seed, 21, (nq, H)).astype(np.float32)
+    # the new tokens: each sequence's queries' positions, in order
+    lens = [len(p) for p in case["pos"]]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    st = np.array([p[0] for p in case["pos"]], np.int64)
+    x = randn_bf16(seed, 30, (nq, D))
+    xi = randn_bf16(seed, 31, (nq, DI))
+    lg = randn_f32(seed, 32, (nq, 2)).astype(np.float32)
+    li = randn_f32(seed, 33, (nq, 2)).astype(np.float32)
+    gain = rand_u(seed, 34, (D,), 0.5, 1.5).astype(np.float32)
+    outs = []
+    for fused in (False, True):
+        gi, gr, gm = gpu_pool(csl, idx), gpu_pool(csl, raw, state=False), gpu_pool(csl, main)
+        topk = torch.full((nq, k), -7, dtype=torch.int32, device=DEV)
+        kth = torch.empty(nq, dtype=torch.float32, device=DEV)
+        ws = torch.empty(csl.index_topk_workspace(nq, max_pos, k) // 4, dtype=torch.float32, device=DEV)
+        jobs = [(gr, dev_bf16(x), None, None), (gm, dev_bf16(x), dev(lg), dev(gain)), (gi, dev_bf16(xi), dev(li), None)]
+        gbt, gq, gw = dev(bt), dev_bf16(qi), dev(w)
+        say(f"index_topk_insert {case['name']} fused={fused}")
+        if fused:
+            csl.index_topk_insert(gi, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, jobs, dev(st), dev(cu),
+                                  kth, ws)
+        else:
+            csl.index_topk(gi, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, kth, ws)
+            csl.compress_insert_multi(jobs, gbt, dev(st), dev(cu))
+        torch.cuda.synchronize()
+        assert csl.read_device_error() == 0
+        outs.append([host(topk), host(kth), host(gi.rows), host_u16(gi.state_x), host(gi.state_logits), host(gr.rows),
+                     host(gm.rows), host_u16(gm.state_x), host(gm.state_logits)])
+    names = ["topk", "kth", "index rows", "index state_x", "index state_logits", "raw rows", "main rows",
+             "main state_x", "main state_logits"]
+    for nm, a, b in zip(names, outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{case['name']}: {nm} differ"
+    # and the selection against the oracle on the pre-insert index pool
+    o_topk, o_kth, o_sc, f = O.index_topk(idx, bt, q_seq, q_pos, qi, w, k, want_scores=True, max_cand=max_pos // 4)
+    assert f == 0
+    assert_topk_equivalent(outs[1][0], o_topk, o_sc, o_kth, what=case["name"])
+
+
+# ---------------------------------------------------------------------------
 # hybrid attention
 # ---------------------------------------------------------------------------
 
