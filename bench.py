@@ -354,23 +354,36 @@ def cpu_baseline(setup: DecodeSetup, n_seqs: int, seconds: float) -> dict:
     q_pos = np.full(n, T, np.int64)
     st1 = np.full(n, T, np.int64)
     cu1 = np.arange(n + 1, dtype=np.int32)
-    reps, t_start = 0, time.perf_counter()
-    while True:
-        O.compress_insert(raw, bt, st1, cu1, x_new)
-        O.compress_insert(main, bt, st1, cu1, x_new, lg_new)
-        O.compress_insert(idx, bt, st1, cu1, xi_new, lgi_new)
-        topk, _, _, _ = O.index_topk(idx, bt, q_seq, q_pos, qi, wi, w.topk)
-        O.hybrid_attn(main, raw, bt, q_seq, q_pos, q, topk=topk, swa_window=w.swa, softmax_scale=setup.scale,
-                      out_dtype=w.out_dtype)
-        reps += 1
-        el = time.perf_counter() - t_start
-        if el >= seconds:
-            break
+    def run(secs):
+        reps, t_start = 0, time.perf_counter()
+        while True:
+            O.compress_insert(raw, bt, st1, cu1, x_new)
+            O.compress_insert(main, bt, st1, cu1, x_new, lg_new)
+            O.compress_insert(idx, bt, st1, cu1, xi_new, lgi_new)
+            topk, _, _, _ = O.index_topk(idx, bt, q_seq, q_pos, qi, wi, w.topk)
+            O.hybrid_attn(main, raw, bt, q_seq, q_pos, q, topk=topk, swa_window=w.swa, softmax_scale=setup.scale,
+                          out_dtype=w.out_dtype)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= secs:
+                return reps, el
+
     threads = O.num_threads()
+    reps, el = run(seconds)
+    O.set_threads(1)
+    reps1, el1 = run(seconds / 4)
+    O.set_threads(threads)
+    model = ""
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(n * reps / el, 3), "unit": "queries/s", "cores": min(threads, n), "kind": "oracle",
             "sample": f"{n} of the {w.num_seqs} sequences (one query each) x {reps} full decode steps "
                       f"(compress_insert x3, index_topk, hybrid_attn) in {el:.1f}s, fp64, OpenMP over queries "
-                      f"({threads} threads available)"}
+                      f"({threads} threads available)",
+            "one_thread_value": round(n * reps1 / el1, 3), "cpu_model": model, "nproc": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 # ---------------------------------------------------------------------------
@@ -399,6 +412,41 @@ def copy_calibration(mb: int, iters: int):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"kernel": "neg", "read_bytes": n, "write_bytes": n, "iters": iters}))
+
+
+def probe():
+    """Ceilings of this GPU as plain library kernels reach them: a 4 GiB
+    device-to-device copy (read + write bytes / time) and a bf16 GEMM of
+    8192^3 (2 * 8192^3 flops / time), each the median of 20 timed runs."""
+    import torch
+    res = {}
+    n = 1 << 30  # fp32 elements: 4 GiB per buffer
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def med(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+    t = med(lambda: dst.copy_(src))
+    res["copy_GBps"] = round(2 * 4 * n / t / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    t = med(lambda: torch.matmul(a, b))
+    res["bf16_gemm_TFLOPs"] = round(2 * m ** 3 / t / 1e12, 1)
+    res["peaks"] = {"hbm_GBps": HBM_PEAK_GBPS, "bf16_mfma_TFLOPs": BF16_MFMA_PEAK_TFLOPS}
+    print(json.dumps(res), flush=True)
 
 
 def run_prefill(args):
@@ -577,6 +625,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="only measure this GPU's ceilings: a large device copy (HBM) and a large bf16 GEMM (MFMA)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -587,6 +637,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb, 10)
+        return
+    if args.probe:
+        probe()
         return
 
     import torch
@@ -641,6 +694,22 @@ def main():
             setup.step(i % R)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_dist = None
+    if graphs:
+        # per-replay durations (HIP events on the replay stream) for the spread
+        # of step times; a separate pass, so the timed loop above carries no events
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(200, K // per_graph))]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record()
+            graphs[i % len(graphs)].replay()
+            e1.record()
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in evs)
+        if us:
+            q = lambda f: round(us[min(len(us) - 1, int(f * len(us)))], 2)
+            step_dist = {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "replays": len(us),
+                         "timing": f"HIP events around each replay of a {per_graph}-step graph"}
     if graphs:
         # The kernel's own start/end stamps (hipExtLaunchKernel events) are not
         # kept by graph capture, so the dominant kernel's duration comes from
@@ -671,6 +740,7 @@ def main():
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == 1 else "fp8-kv/bf16-mfma", "data": "synthetic",
+        "step_us": step_dist,
         "hbm_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "context": w.ctx, "layers": list(w.layers),

@@ -465,27 +465,29 @@ hybrid_attn_kernel(AttnArgs a) {
     }
 }
 
-// Merge the splits of one (query, head): one wave, 8 dims per lane.
+// Merge the splits of one (query, head): one workgroup; wave w takes splits
+// w, w + 4, ... (8 dims per lane), the four running (max, sum, output) meet in
+// LDS and wave 0 finishes.  Splitting the split list over the waves keeps
+// each wave's chain of dependent batches short when there are many splits.
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
+    __shared__ float s_o[4][64][8];
+    __shared__ float s_ml[4][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = blockIdx.x / ((a.n_heads + 3) / 4);
-    const int head = (blockIdx.x % ((a.n_heads + 3) / 4)) * 4 + wave;
-    if (head >= a.n_heads) return;
+    const int n = blockIdx.x / a.n_heads;
+    const int head = blockIdx.x % a.n_heads;
     const bool active = 8 * lane < D;
-    QueryInfo qi = query_info(a, n);
-    const int64_t p = qi.ok ? qi.p : 0;
 
     const float* ml = a.part_ml + ((int64_t)n * a.n_splits * a.n_heads + head) * 2;
     const int64_t mstride = (int64_t)a.n_heads * 2;
     const float* po = a.part_o + ((int64_t)n * a.n_splits * a.n_heads + head) * D + 8 * (active ? lane : 0);
     const int64_t pstride = (int64_t)a.n_heads * D;
-    // one pass, batches of 16 splits: all loads of a batch are issued before
+    // batches of 8 of this wave's splits: all loads of a batch are issued before
     // any use; the running max M rescales what earlier batches accumulated
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float Lsum = 0.f, M = -INFINITY;
-    constexpr int kB = 16;
-    for (int sp0 = 0; sp0 < a.n_splits; sp0 += kB) {
+    constexpr int kB = 8;
+    for (int sp0 = wave; sp0 < a.n_splits; sp0 += 4 * kB) {
         f32x4 v0[kB], v1[kB];
         float msp[kB], lsp[kB];
 #pragma unroll
@@ -493,8 +495,8 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
             msp[u] = -INFINITY;
             lsp[u] = 0.f;
             v0[u] = v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (sp0 + u < a.n_splits) {
-                const int sp = sp0 + u;
+            const int sp = sp0 + 4 * u;
+            if (sp < a.n_splits) {
                 msp[u] = ml[sp * mstride];
                 lsp[u] = ml[sp * mstride + 1];
                 v0[u] = *reinterpret_cast<const f32x4*>(po + sp * pstride);
@@ -522,6 +524,28 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
         }
         M = Mb;
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s_o[wave][lane][c] = o[c];
+    if (lane == 0) {
+        s_ml[wave][0] = M;
+        s_ml[wave][1] = Lsum;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
+    const float Mu = M == -INFINITY ? 0.f : M;
+    Lsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float r = exp2f(s_ml[w][0] - Mu);  // a wave without splits holds -inf: weight 0
+        Lsum = fmaf(s_ml[w][1], r, Lsum);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = fmaf(r, s_o[w][lane][c], o[c]);
+    }
+    QueryInfo qi = query_info(a, n);
+    const int64_t p = qi.ok ? qi.p : 0;
     const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     const int rbase = D - a.rope_dims;
 #pragma unroll
@@ -1068,7 +1092,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0 || a.n_splits <= 1) return hipSuccess;
-    dim3 grid((unsigned)((int64_t)a.num_q * ((a.n_heads + 3) / 4)));
+    dim3 grid((unsigned)((int64_t)a.num_q * a.n_heads));
     if (a.dim == 512) launch_kernel(ev, true, true, attn_combine_kernel<512>, grid, dim3(kThreads), st, a);
     else if (a.dim == 128) launch_kernel(ev, true, true, attn_combine_kernel<128>, grid, dim3(kThreads), st, a);
     else return hipErrorInvalidValue;

@@ -80,6 +80,8 @@ def lib():
         L.csl_oracle_q_norm_rope_insert.restype = C.c_int
         L.csl_oracle_compress_rows.argtypes = [C.POINTER(Pool), C.c_int, vp, vp, vp, vp, dbl, vp]
         L.csl_oracle_compress_rows.restype = None
+        L.csl_oracle_set_threads.argtypes = [C.c_int]
+        L.csl_oracle_set_threads.restype = None
         L.csl_oracle_num_threads.argtypes = []
         L.csl_oracle_num_threads.restype = C.c_int
         _lib = L
@@ -253,6 +255,11 @@ def hybrid_attn(comp: HostPool | None, swa: HostPool, bt, q_seq, q_pos, q, topk=
                                      _p(q_seq), _p(q_pos), _p(q), nh, _p(topk), int(k), int(swa_window),
                                      float(softmax_scale), out_dtype, _p(out), _p(scales), _p(o64))
     return out, scales, o64, f
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only)."""
+    lib().csl_oracle_set_threads(int(n))
 
 
 def num_threads() -> int:

@@ -686,3 +686,14 @@ int csl_oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the parallel loops that follow (timing only; results do not
+ * depend on it). */
+void csl_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
