@@ -465,17 +465,21 @@ hybrid_attn_kernel(AttnArgs a) {
     }
 }
 
-// Merge the splits of one (query, head): one workgroup; wave w takes splits
-// w, w + 4, ... (8 dims per lane), the four running (max, sum, output) meet in
-// LDS and wave 0 finishes.  Splitting the split list over the waves keeps
-// each wave's chain of dependent batches short when there are many splits.
-template <int D>
+// Merge the splits of (query, head), 8 dims per lane.  SHARE (many splits):
+// one workgroup per (query, head); wave w takes splits w, w + 4, ..., the four
+// running (max, sum, output) meet in LDS and wave 0 finishes, so that each
+// wave's chain of dependent batches stays short.  Otherwise one wave per
+// (query, head) takes every split (four heads per workgroup).
+template <int D, bool SHARE>
 __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_o[4][64][8];
+    __shared__ float s_o[SHARE ? 4 : 1][64][8];
     __shared__ float s_ml[4][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = blockIdx.x / a.n_heads;
-    const int head = blockIdx.x % a.n_heads;
+    const int hpb = SHARE ? 1 : 4;  // heads per workgroup
+    const int n = blockIdx.x / ((a.n_heads + hpb - 1) / hpb);
+    const int head = (blockIdx.x % ((a.n_heads + hpb - 1) / hpb)) * hpb + (SHARE ? 0 : wave);
+    if (head >= a.n_heads) return;
+    const int w0 = SHARE ? wave : 0, wstep = SHARE ? 4 : 1;
     const bool active = 8 * lane < D;
 
     const float* ml = a.part_ml + ((int64_t)n * a.n_splits * a.n_heads + head) * 2;
@@ -486,8 +490,8 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
     // any use; the running max M rescales what earlier batches accumulated
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float Lsum = 0.f, M = -INFINITY;
-    constexpr int kB = 8;
-    for (int sp0 = wave; sp0 < a.n_splits; sp0 += 4 * kB) {
+    constexpr int kB = SHARE ? 8 : 16;
+    for (int sp0 = w0; sp0 < a.n_splits; sp0 += wstep * kB) {
         f32x4 v0[kB], v1[kB];
         float msp[kB], lsp[kB];
 #pragma unroll
@@ -495,7 +499,7 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
             msp[u] = -INFINITY;
             lsp[u] = 0.f;
             v0[u] = v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int sp = sp0 + 4 * u;
+            const int sp = sp0 + wstep * u;
             if (sp < a.n_splits) {
                 msp[u] = ml[sp * mstride];
                 lsp[u] = ml[sp * mstride + 1];
@@ -524,25 +528,27 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
         }
         M = Mb;
     }
+    if constexpr (SHARE) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_o[wave][lane][c] = o[c];
-    if (lane == 0) {
-        s_ml[wave][0] = M;
-        s_ml[wave][1] = Lsum;
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
-    const float Mu = M == -INFINITY ? 0.f : M;
-    Lsum = 0.f;
+        for (int c = 0; c < 8; ++c) s_o[wave][lane][c] = o[c];
+        if (lane == 0) {
+            s_ml[wave][0] = M;
+            s_ml[wave][1] = Lsum;
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
+        const float Mu = M == -INFINITY ? 0.f : M;
+        Lsum = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[c] = 0.f;
+        for (int c = 0; c < 8; ++c) o[c] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const float r = exp2f(s_ml[w][0] - Mu);  // a wave without splits holds -inf: weight 0
-        Lsum = fmaf(s_ml[w][1], r, Lsum);
+        for (int w = 0; w < 4; ++w) {
+            const float r = exp2f(s_ml[w][0] - Mu);  // a wave without splits holds -inf: weight 0
+            Lsum = fmaf(s_ml[w][1], r, Lsum);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = fmaf(r, s_o[w][lane][c], o[c]);
+            for (int c = 0; c < 8; ++c) o[c] = fmaf(r, s_o[w][lane][c], o[c]);
+        }
     }
     QueryInfo qi = query_info(a, n);
     const int64_t p = qi.ok ? qi.p : 0;
@@ -1092,10 +1098,19 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0 || a.n_splits <= 1) return hipSuccess;
-    dim3 grid((unsigned)((int64_t)a.num_q * a.n_heads));
-    if (a.dim == 512) launch_kernel(ev, true, true, attn_combine_kernel<512>, grid, dim3(kThreads), st, a);
-    else if (a.dim == 128) launch_kernel(ev, true, true, attn_combine_kernel<128>, grid, dim3(kThreads), st, a);
-    else return hipErrorInvalidValue;
+    // up to 16 splits: one batch per wave, four heads per workgroup; more: the
+    // split list shared by the four waves of a (query, head) workgroup
+    const bool share = a.n_splits > 16;
+    const dim3 grid((unsigned)((int64_t)a.num_q * (share ? a.n_heads : (a.n_heads + 3) / 4)));
+    if (a.dim == 512) {
+        if (share) launch_kernel(ev, true, true, attn_combine_kernel<512, true>, grid, dim3(kThreads), st, a);
+        else launch_kernel(ev, true, true, attn_combine_kernel<512, false>, grid, dim3(kThreads), st, a);
+    } else if (a.dim == 128) {
+        if (share) launch_kernel(ev, true, true, attn_combine_kernel<128, true>, grid, dim3(kThreads), st, a);
+        else launch_kernel(ev, true, true, attn_combine_kernel<128, false>, grid, dim3(kThreads), st, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -375,13 +375,12 @@ __device__ void select_all(const float* sc, int64_t nv, int k, int32_t* out, flo
     }
 }
 
-__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
+__device__ __forceinline__ void select_query(const IndexArgs& a, const int n) {
     __shared__ uint32_t s_hist[2048];
     __shared__ uint32_t s_cand[kCandCap];
     __shared__ uint32_t s_wave[kSelWaves];
     __shared__ uint32_t s_sel[8 + kSelWaves];
     __shared__ float s_min[kSelWaves];
-    const int n = blockIdx.x;
     int s;
     int64_t p;
     const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;  // the score kernel reports bad queries
@@ -391,6 +390,8 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
     if (nv <= a.k) select_all(sc, nv, a.k, out, kth, s_min);
     else select_full<kSelThreads>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
 }
+
+__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) { select_query(a, blockIdx.x); }
 
 // ---------------------------------------------------------------- two-stage select
 
@@ -1182,18 +1183,23 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
     merge_query<NT>(a, blockIdx.x);
 }
 
-// The merge with the inserts of the same step in its grid: workgroups past
-// num_q each insert one (new token, pool).  The merge reads only the score
-// workspace, so the inserts cannot change what the queries select, and they
-// fill the CUs that the few merge workgroups leave idle.
-__global__ void __launch_bounds__(256) topk_merge_insert_kernel(IndexArgs a, CompressArgs c) {
+// The select with the inserts of the same step in its grid: workgroups past
+// num_q each insert one (new token, pool) with their first 256 threads (the
+// other waves end at once; a barrier waits only for the waves still running).
+// The select reads only the score workspace, so the inserts cannot change
+// what the queries select, and they fill the CUs that the few select
+// workgroups leave idle.  MERGE: the two-stage merge, else the full select.
+template <int NT, bool MERGE>
+__global__ void __launch_bounds__(NT) topk_select_insert_kernel(IndexArgs a, CompressArgs c) {
     if ((int)blockIdx.x >= a.num_q) {
+        if (threadIdx.x >= 256) return;
         __shared__ InsertSmem sm;
         const int i = (int)blockIdx.x - a.num_q;
         insert_block(c, i / c.total_new, i % c.total_new, sm);
         return;
     }
-    merge_query<256>(a, blockIdx.x);
+    if constexpr (MERGE) merge_query<NT>(a, blockIdx.x);
+    else select_query(a, blockIdx.x);
 }
 
 }  // namespace
@@ -1263,27 +1269,30 @@ hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEv
     return hipGetLastError();
 }
 
-// The select, then the inserts; when the select ends in the 256-thread merge,
-// the inserts ride in its launch (one workgroup per token and pool).
+// The select with the inserts riding in its last launch (one workgroup per
+// token and pool after the queries' workgroups).
 hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, hipStream_t st,
                                      const LaunchEvents& ev) {
     const int64_t n_ins = (int64_t)c.total_new * c.n_jobs;
-    if (a.num_q <= 0 || n_ins <= 0) {
+    if (a.num_q <= 0 || n_ins <= 0 || a.num_q + n_ins > 0x7fffffff) {
         hipError_t e = launch_topk_select(a, st, ev);
         if (e != hipSuccess) return e;
         return launch_compress(c, st);
     }
-    if (a.kl > 0 && (int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256 && a.num_q + n_ins <= 0x7fffffff) {
+    const dim3 grid((unsigned)(a.num_q + n_ins));
+    if (a.kl > 0) {
         if (a.tiled)
             launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)((a.nchunks + 3) / 4), (unsigned)a.num_q),
                           dim3(256), st, a);
-        launch_kernel(ev, !a.tiled, true, topk_merge_insert_kernel, dim3((unsigned)(a.num_q + n_ins)), dim3(256), st, a,
-                      c);
-        return hipGetLastError();
+        if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256)
+            launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<256, true>, grid, dim3(256), st, a, c);
+        else
+            launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<kSelThreads, true>, grid, dim3(kSelThreads), st,
+                          a, c);
+    } else {
+        launch_kernel(ev, true, true, topk_select_insert_kernel<kSelThreads, false>, grid, dim3(kSelThreads), st, a, c);
     }
-    hipError_t e = launch_topk_select(a, st, ev);
-    if (e != hipSuccess) return e;
-    return launch_compress(c, st);
+    return hipGetLastError();
 }
 
 bool index_use_tiled(int num_q) { return num_q >= kTiledMinQueries; }

@@ -361,13 +361,16 @@ FUSED_CASES = [
     dict(name="decode_short_rows", pos=[[1000], [700]], k=512),
     # 100 queries: the query-blocked scores, then the merge with 100 x 3 inserts
     dict(name="tiled_100_queries", pos=[list(range(9000, 9100))], k=512),
+    # 150 000 visible entries: 148 chunks x 32 candidates, the 1024-thread merge
+    # (the inserts' workgroups run with their first 256 threads)
+    dict(name="decode_merge_1024_threads", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32),
 ]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES, ids=[c["name"] for c in FUSED_CASES])
 def test_index_topk_insert_equals_separate_calls(csl, orc, case):
     seed = zlib.crc32(case["name"].encode()) % 1000
-    H, DI, D, R, k = 16, 128, 512, 64, case["k"]
+    H, DI, D, R, k = 16, 128, case.get("D", 512), case.get("R", 64), case["k"]
     ns = len(case["pos"])
     max_pos = max(max(p) for p in case["pos"])
     mb = (max_pos + 256) // 256 + 1
@@ -379,7 +382,7 @@ def test_index_topk_insert_equals_separate_calls(csl, orc, case):
     idx.state_x[:] = randn_bf16(seed, 11, idx.state_x.shape)
     idx.state_logits[:] = randn_f32(seed, 12, idx.state_logits.shape).astype(np.float32)
     raw = O.HostPool(1, 1, D, R, THETA, O.BF16, P, state=False)
-    main = O.HostPool(4, 2, D, R, THETA, O.FP8, P)
+    main = O.HostPool(4, 2, D, R, THETA, case.get("main_dtype", O.FP8), P)
     main.state_x[:] = randn_bf16(seed, 13, main.state_x.shape)
     main.state_logits[:] = randn_f32(seed, 14, main.state_logits.shape).astype(np.float32)
     q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
