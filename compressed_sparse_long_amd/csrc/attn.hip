@@ -629,6 +629,14 @@ constexpr int kT2 = 32;          // keys per tile
 constexpr int kRow2 = 1040;      // LDS stride of a staged row (1024 B + 16: spreads the S-operand reads)
 constexpr int kMaxKeys2 = 1024;  // key addresses resolved per pass
 constexpr int kRing2 = 4;        // staged tiles: one computed, up to three in flight
+// fp8 keys: 544-byte rows (512 e4m3 codes, 8 fp32 group scales) land in a
+// 3-slot ring and are widened to exact bf16 codes in two bf16 tiles; the
+// group scales go to a [8][32] table per tile
+constexpr int kRow8 = 560;       // LDS stride of a staged fp8 row (544 B + 16)
+constexpr int kFp8Ring = 3 * kT2 * kRow8;
+constexpr int kFp8Bf16 = kFp8Ring;                      // offset of the two bf16 tiles
+constexpr int kFp8Scales = kFp8Bf16 + 2 * kT2 * kRow2;  // offset of the two scale tables
+static_assert(kFp8Scales + 2 * 8 * kT2 * 4 <= kRing2 * kT2 * kRow2, "fp8 staging fits the ring");
 
 // Source of masked key rows (zeros: a masked key then contributes 0 * 0).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_kv_row[1024];
@@ -673,11 +681,21 @@ __device__ __forceinline__ void scale_agpr16(f32x16& acc, float f) {
     acc = f32x16{e0, e1, e2, e3, e4, e5, e6, e7, e8, e9, e10, e11, e12, e13, e14, e15};
 }
 
-template <bool PREC>
+template <bool PREC, bool KV8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 hybrid_attn_mqa512_kernel(AttnArgs a) {
     constexpr int D = 512;
-    __shared__ __attribute__((aligned(16))) uint8_t s_kt[kRing2][kT2 * kRow2];
+    // bf16 keys: 4 ring slots of 32 rows.  fp8 keys: 3 slots of raw rows, 2
+    // bf16 tiles, 2 scale tables (see kFp8*).  Also the epilogue's staging area.
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing2 * kT2 * kRow2];
+    constexpr int kSlots = KV8 ? 3 : kRing2;
+    constexpr int kRowDma = KV8 ? kRow8 : kRow2;
+    // where the DMA of tile tl lands, the bf16 tile S and PV read, its scale table
+    auto dma_slot = [&](int tl) { return s_ring + (tl % kSlots) * (kT2 * kRowDma); };
+    auto kt_of = [&](int tl) -> const uint8_t* {
+        return KV8 ? s_ring + kFp8Bf16 + (tl & 1) * (kT2 * kRow2) : s_ring + (tl % kRing2) * (kT2 * kRow2);
+    };
+    auto sc_of = [&](int tl) { return reinterpret_cast<float*>(s_ring + kFp8Scales + (tl & 1) * (8 * kT2 * 4)); };
     __shared__ __attribute__((aligned(16))) float s_sx[4][64 * 16];  // S^T partials, one per wave
     __shared__ const uint8_t* s_rows[kMaxKeys2];
     __shared__ uint32_t s_vbits[kMaxKeys2 / 32];
@@ -751,12 +769,42 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     // (all 8 row addresses are read before the first copy is issued: the
     // copies' memory clobber would otherwise order each read behind them)
     auto issue_tile = [&](int tl) {
-        const uint8_t* buf = s_kt[tl % kRing2];
+        const uint8_t* buf = dma_slot(tl);
         const uint8_t* row[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) row[i] = s_rows[tl * kT2 + 8 * wave_u + i];
+        if (!KV8 || lane < 34) {  // an fp8 row is 34 x 16 bytes
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds_dma_row(lds_addr(buf + (8 * wave_u + i) * kRow2), row[i] + 16 * lane);
+            for (int i = 0; i < 8; ++i) lds_dma_row(lds_addr(buf + (8 * wave_u + i) * kRowDma), row[i] + 16 * lane);
+        }
+    };
+    // fp8 keys: tile tl's codes widened to bf16 (e4m3 values are exact in bf16:
+    // the conversion unit with scale 1) and its group scales into the table;
+    // thread = (row tid / 8, 64-code group tid % 8)
+    auto convert = [&](int tl) {
+        const int row = tid >> 3, g = tid & 7;
+        const uint8_t* src = dma_slot(tl) + row * kRow8;
+        uint8_t* dst = const_cast<uint8_t*>(kt_of(tl)) + row * kRow2 + 128 * g;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + 64 * g + 16 * q);
+            u32x4 o0, o1;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[c], 1.0f, false));
+                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[c], 1.0f, true));
+                if (c < 2) {
+                    o0[2 * c] = lo;
+                    o0[2 * c + 1] = hi;
+                } else {
+                    o1[2 * c - 4] = lo;
+                    o1[2 * c - 3] = hi;
+                }
+            }
+            *reinterpret_cast<u32x4*>(dst + 32 * q) = o0;
+            *reinterpret_cast<u32x4*>(dst + 32 * q + 16) = o1;
+        }
+        sc_of(tl)[g * kT2 + row] = *reinterpret_cast<const float*>(src + 512 + 4 * g);
     };
     // the wave's half of S^T for a staged tile (its 256 dims): A = key rows (LDS), B = q
     // accumulator row r = 8j + 4h + i holds key sigma(r) = 16h + 4i + j of the tile:
@@ -768,13 +816,43 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
     };
-    auto s_mfma = [&](const bf16x8 (&ka)[16]) {
-        // one accumulation chain (dependent 32x32x16 MFMAs issue back to back)
+    // the scales of the lane's 16 keys (16 h2 + 0..15) in 64-dim group g of the row
+    auto key_scales = [&](const float* sc, int g, float (&v)[16]) {
+        const float* p = sc + g * kT2 + 16 * h2;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * q);
+            v[4 * q] = x[0];
+            v[4 * q + 1] = x[1];
+            v[4 * q + 2] = x[2];
+            v[4 * q + 3] = x[3];
+        }
+    };
+    auto s_mfma = [&](const bf16x8 (&ka)[16], const float* sc) {
         f32x16 s0;
 #pragma unroll
         for (int c = 0; c < 16; ++c) s0[c] = 0.f;
+        if constexpr (!KV8) {
+            // one accumulation chain (dependent 32x32x16 MFMAs issue back to back)
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s0, 0, 0, 0);
+            for (int ks = 0; ks < 16; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s0, 0, 0, 0);
+        } else {
+            // one chain per 64-dim group over the exact codes, then the keys' group
+            // scales in fp32: value c is key 16 h2 + 4 (c % 4) + c / 4
+#pragma unroll
+            for (int lg = 0; lg < 4; ++lg) {
+                f32x16 acc;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[4 * lg + q], qb[4 * lg + q], acc, 0, 0, 0);
+                float v[16];
+                key_scales(sc, 4 * dh + lg, v);
+#pragma unroll
+                for (int c = 0; c < 16; ++c) s0[c] = fmaf(acc[c], v[4 * (c & 3) + (c >> 2)], s0[c]);
+            }
+        }
         return s0;
     };
     // the two halves of a head group meet in LDS (the lanes of waves w and w ^ 2
@@ -802,6 +880,7 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     // reference moved (alpha = 0 at the first move, which meets a zero accumulator)
     struct Soft {
         bf16x8 pb[2], plo[2];
+        float pf[KV8 ? 16 : 1];  // fp8 keys: P in fp32, scaled per group in the PV
         float alpha;
         bool rescale;
     };
@@ -843,6 +922,10 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * c], a.scale_log2, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * c + 1], a.scale_log2, -m_use));
             psum += p0 + p1;
+            if constexpr (KV8) {
+                o.pf[2 * c] = p0;
+                o.pf[2 * c + 1] = p1;
+            }
             pw[c] = pack_bf16x2(p0, p1);
             if constexpr (PREC)
                 pl[c] = pack_bf16x2(p0 - bf16_bits_to_f32(pw[c] & 0xffffu), p1 - bf16_bits_to_f32(pw[c] >> 16));
@@ -860,10 +943,59 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         return o;
     };
     // O^T += V^T . P^T for a staged tile (A = V^T by transposed LDS reads)
-    auto pv = [&](const Soft& sm, const uint8_t* kt) {
+    auto pv = [&](const Soft& sm, const uint8_t* kt, const float* sc) {
         if (__ballot(sm.rescale)) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) scale_agpr16(oacc[m], sm.alpha);
+        }
+        if constexpr (KV8) {
+            // V = codes x group scale: the scale of key j in group g moves onto
+            // P (B operand element e of k-step kk is key 16 h2 + 4 (e % 4) + 2 kk + e / 4),
+            // m-tiles 2 lg, 2 lg + 1 are the wave's group lg
+#pragma unroll
+            for (int lg = 0; lg < 4; ++lg) {
+                float v[16];
+                key_scales(sc, 4 * dh + lg, v);
+                bf16x8 va[2][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int mm = 0; mm < 2; ++mm) {
+                        const uint8_t* base = kt + (tr_row + 2 * kk) * kRow2 + tr_col + 64 * (2 * lg + mm);
+                        const u32x2 v0 = lds_read_tr16(base);
+                        const u32x2 v1 = lds_read_tr16(base + kRow2);
+                        va[mm][kk] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+                    }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        float x2[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int e = 2 * e2 + h;
+                            x2[h] = sm.pf[8 * kk + e] * v[4 * (e & 3) + 2 * kk + (e >> 2)];
+                        }
+                        hw[e2] = pack_bf16x2(x2[0], x2[1]);
+                        if constexpr (PREC)
+                            lw[e2] = pack_bf16x2(x2[0] - bf16_bits_to_f32(hw[e2] & 0xffffu),
+                                                 x2[1] - bf16_bits_to_f32(hw[e2] >> 16));
+                    }
+                    const bf16x8 pbh = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+#pragma unroll
+                    for (int mm = 0; mm < 2; ++mm)
+                        oacc[2 * lg + mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mm][kk], pbh, oacc[2 * lg + mm], 0, 0, 0);
+                    if constexpr (PREC) {
+                        const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+                        for (int mm = 0; mm < 2; ++mm)
+                            oacc[2 * lg + mm] =
+                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mm][kk], pbl, oacc[2 * lg + mm], 0, 0, 0);
+                    }
+                }
+            }
+            return;
         }
         bf16x8 va[8][2];
 #pragma unroll
@@ -898,11 +1030,12 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     // S of the next tile overlapped with the softmax of the current one: the 16
     // operand reads first, then each MFMA followed by a share of the softmax's
     // vector instructions
-    auto s_next_softmax = [&](const uint8_t* kt_next, uint32_t vb, const f32x16& sacc, f32x16& s_out) {
+    auto s_next_softmax = [&](const uint8_t* kt_next, const float* sc_next, uint32_t vb, const f32x16& sacc,
+                              f32x16& s_out) {
         bf16x8 ka[16];
         s_loads(kt_next, ka);
         const Soft sm = softmax(vb, sacc);
-        s_out = s_mfma(ka);
+        s_out = s_mfma(ka, sc_next);
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -938,11 +1071,15 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         else if (ntl == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if constexpr (KV8) {
+            convert(0);
+            __syncthreads();
+        }
         f32x16 s_cur;
         {
             bf16x8 ka[16];
-            s_loads(s_kt[0], ka);
-            s_cur = s_mfma(ka);
+            s_loads(kt_of(0), ka);
+            s_cur = s_mfma(ka, sc_of(0));
         }
         put_half(s_cur);
         __syncthreads();
@@ -955,15 +1092,19 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();  // tile t+1 complete; every wave is past tile t-1 (buffer t+3) and its S exchange
             if (t + 3 < ntl) issue_tile(t + 3);
+            if constexpr (KV8) {
+                convert(t + 1);  // (its bf16 tile held tile t-1, done with before the barrier above)
+                __syncthreads();
+            }
             f32x16 s_next;
-            const Soft sm = s_next_softmax(s_kt[(t + 1) % kRing2], s_vbits[t], s_cur, s_next);
-            pv(sm, s_kt[t % kRing2]);
+            const Soft sm = s_next_softmax(kt_of(t + 1), sc_of(t + 1), s_vbits[t], s_cur, s_next);
+            pv(sm, kt_of(t), sc_of(t));
             put_half(s_next);
             __syncthreads();
             add_other(s_next);
             s_cur = s_next;
         }
-        pv(softmax(s_vbits[ntl - 1], s_cur), s_kt[(ntl - 1) % kRing2]);
+        pv(softmax(s_vbits[ntl - 1], s_cur), kt_of(ntl - 1), sc_of(ntl - 1));
     }
 
     const float l_tot = sum_xor32(l_run);
@@ -996,7 +1137,7 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     const int rbase = D - a.rope_dims;
     const int esz = a.out_dtype == kF32 ? 4 : a.out_dtype == kBF16 ? 2 : 1;
     const int rstride = D * esz + 16;
-    uint8_t* stage = &s_kt[0][0];
+    uint8_t* stage = s_ring;
     auto rope_tile = [&](f32x16& v, int m) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1085,8 +1226,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev
     dim3 grid((unsigned)((int64_t)a.num_q * a.n_splits));
     const int kv = a.comp_rows ? a.comp_dtype : a.swa_dtype;
     if (a.dim == 512 && kv == kBF16) {
-        if (a.out_dtype == kFP8) launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<true>, grid, dim3(kThreads), st, a);
-        else launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<false>, grid, dim3(kThreads), st, a);
+        if (a.out_dtype == kFP8) launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<true, false>, grid, dim3(kThreads), st, a);
+        else launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<false, false>, grid, dim3(kThreads), st, a);
+        return hipGetLastError();
+    }
+    if (a.dim == 512 && kv == kFP8) {
+        if (a.out_dtype == kFP8) launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<true, true>, grid, dim3(kThreads), st, a);
+        else launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<false, true>, grid, dim3(kThreads), st, a);
         return hipGetLastError();
     }
     if (a.dim == 512 && kv == kBF16) launch_prec<512, kBF16>(a, grid, st, ev);

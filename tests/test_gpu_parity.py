@@ -494,6 +494,14 @@ ATTN_CASES = [
     # more keys than one pass of resolved addresses holds (1171 entries + 128 raw in one prefill split)
     dict(name="c128a_d512_h64_dense_bf16_long", D=512, R=64, H=64, ratio=128, k=0, dtype=O.BF16, out=O.FP8,
          pos=[[150000, 140001]]),
+    # fp8 keys in the 512-dim kernel: bf16 and f32 outputs, heads not a multiple of 32,
+    # two key passes, window keys only
+    dict(name="c4a_d512_h40_fp8kv_bf16out", D=512, R=64, H=40, ratio=4, k=512, dtype=O.FP8, out=O.BF16,
+         pos=[[3000, 2049], [4100]]),
+    dict(name="c128a_d512_h64_fp8kv_f32_long", D=512, R=64, H=64, ratio=128, k=0, dtype=O.FP8, out=O.F32,
+         pos=[[150000, 131000]]),
+    dict(name="swa_only_d512_h64_fp8kv_fp8out", D=512, R=64, H=64, ratio=4, k=0, dtype=O.FP8, out=O.FP8,
+         pos=[[5, 129, 1000]], no_comp=True),
 ]
 
 
