@@ -159,12 +159,12 @@ class DecodeSetup:
         beside the indexer and attention, forked from and joined back into the
         current stream."""
         p, torch = self.reps[r], self.torch
-        if self.qside:
-            self.csl.q_norm_rope_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new, self.q_pre, self.gain_q,
-                                        q_out=self.q)
         if self.fused_inserts and "c4a" in self.layers:
             self.attend(r, with_inserts=True)
             return
+        if self.qside:
+            self.csl.q_norm_rope_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new, self.q_pre, self.gain_q,
+                                        q_out=self.q)
         if self.side is not None:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)
@@ -182,8 +182,10 @@ class DecodeSetup:
         csl, w, p = self.csl, self.w, self.reps[r]
         if "c4a" in self.layers:
             if with_inserts:
+                qs = (p["raw"], self.x_new, self.q_pre, self.gain_q, self.q) if self.qside else None
                 csl.index_topk_insert(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx,
-                                      w.topk, self.topk, self.insert_jobs(p), self.start, self.cu1, None, self.ws_idx)
+                                      w.topk, self.topk, self.insert_jobs(p), self.start, self.cu1, None, self.ws_idx,
+                                      qside=qs)
             else:
                 csl.index_topk(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx, w.topk,
                                self.topk, None, self.ws_idx)
@@ -620,8 +622,9 @@ def main():
     ap.add_argument("--separate-inserts", action="store_true",
                     help="launch the inserts on their own before the indexer instead of inside its top-k launch")
     ap.add_argument("--qside", action="store_true",
-                    help="start the step from pre-norm query heads: the fused Q norm + RoPE + raw-key insert launch "
-                         "produces q and writes the raw key")
+                    help="start the step from pre-norm query heads: the Q norm + RoPE + raw-key insert (in the top-k "
+                         "launch with the other inserts, or its own launch with --separate-inserts) produces q and "
+                         "writes the raw key")
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")

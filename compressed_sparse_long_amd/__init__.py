@@ -72,9 +72,14 @@ _q_side = _sig("csl_q_norm_rope_insert", C.c_int, [_P, _G, _vp, _vp, _i32, _vp, 
 _index_topk_ws = _sig("csl_index_topk_workspace", _sz, [_i32, _i64, _i32])
 _index_topk = _sig("csl_index_topk", C.c_int,
                    [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
+class _QSideJob(C.Structure):
+    _fields_ = [("swa", C.c_void_p), ("x", C.c_void_p), ("q", C.c_void_p), ("n_heads", C.c_int32),
+                ("q_gain", C.c_void_p), ("q_out", C.c_void_p)]
+
+
 _index_topk_insert = _sig("csl_index_topk_insert", C.c_int,
                           [_P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _i32,
-                           C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, _vp])
+                           C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, C.POINTER(_QSideJob), _vp])
 _attn_ws = _sig("csl_hybrid_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i64])
 _attn_decode = _sig("csl_hybrid_attn_decode", C.c_int,
                     [_P, _P, _G, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz,
@@ -189,20 +194,26 @@ def index_topk(pool: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k, to
 
 
 def index_topk_insert(pool: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k, topk, jobs, start_pos, cu_new,
-                      kth_score=None, ws=None, eps=1e-6, stream=None):
-    """index_topk, then compress_insert_multi(jobs, ...) on the same stream, the inserts riding in the
-    top-k launch.  jobs: list of (pool, x, logits or None, gain or None)."""
+                      kth_score=None, ws=None, eps=1e-6, qside=None, stream=None):
+    """index_topk, then compress_insert_multi(jobs, ...), then (qside) q_norm_rope_insert on the same
+    stream, the writes riding in the top-k launch.  jobs: list of (pool, x, logits or None, gain or
+    None); qside: (swa pool, x, q, gain or None, q_out or None = in place)."""
     ps = pool.struct()
     pg = pages(block_table)
     nq, nh = int(w.shape[0]), int(w.shape[1])
     structs = [p.struct() for p, _, _, _ in jobs]
-    arr = (_InsertJob * len(jobs))(*[_InsertJob(C.addressof(structs[i]), _ptr(x), _ptr(lg), _ptr(g))
-                                     for i, (_, x, lg, g) in enumerate(jobs)])
-    total = int(jobs[0][1].shape[0])
+    arr = (_InsertJob * max(1, len(jobs)))(*[_InsertJob(C.addressof(structs[i]), _ptr(x), _ptr(lg), _ptr(g))
+                                             for i, (_, x, lg, g) in enumerate(jobs)])
+    qs, qsp = None, None
+    if qside is not None:
+        swa, qx, qq, qg, qo = qside
+        qsp = swa.struct()
+        qs = _QSideJob(C.addressof(qsp), _ptr(qx), _ptr(qq), int(qq.shape[1]), _ptr(qg), _ptr(qq if qo is None else qo))
+    total = int(jobs[0][1].shape[0]) if jobs else int(qside[1].shape[0])
     _check(_index_topk_insert(C.byref(ps), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos), _ptr(q_idx),
                               _ptr(w), nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(), len(jobs), arr, _ptr(start_pos),
-                              _ptr(cu_new), total, float(eps), _stream(stream)))
+                              _ptr(cu_new), total, float(eps), None if qs is None else C.byref(qs), _stream(stream)))
 
 
 def hybrid_attn_workspace(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos) -> int:

@@ -374,11 +374,13 @@ csl_status csl_compress_insert(const csl_pool* pool, const csl_pages* pages, con
     return csl_compress_insert_multi(1, &job, pages, start_pos, cu_new, total_new, eps, stream);
 }
 
-csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, const int64_t* start_pos,
-                                  const int32_t* cu_new, int32_t total_new, const uint16_t* x, const uint16_t* q,
-                                  int32_t n_heads, const float* q_gain, float eps, uint16_t* q_out,
-                                  csl_stream_t stream) {
+// Validates a query-side batch and fills its kernel arguments (a.n_items = 0:
+// nothing to launch; a.err set by the caller).  Launches nothing.
+csl_status prepare_qside(const csl_pool* swa, const csl_pages* pages, const int64_t* start_pos, const int32_t* cu_new,
+                         int32_t total_new, const uint16_t* x, const uint16_t* q, int32_t n_heads, const float* q_gain,
+                         float eps, uint16_t* q_out, QSideArgs& a) {
     csl_status st;
+    a.n_items = 0;
     if ((st = check_pool(swa, "swa"))) return st;
     if ((st = check_pages(pages))) return st;
     if (swa->ratio != 1) return fail(CSL_EINVAL, "swa.ratio must be 1 (raw window keys)");
@@ -398,9 +400,6 @@ csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, c
         const uintptr_t len = (uintptr_t)n_q_rows * swa->dim * 2;
         if (a0 < b0 + len && b0 < a0 + len) return fail(CSL_EINVAL, "q_out overlaps q without being equal to it");
     }
-    uint32_t* err = nullptr;
-    if ((st = device_error_ptr(&err))) return st;
-    QSideArgs a;
     a.q = q;
     a.q_out = q_out;
     a.x = x;
@@ -409,7 +408,7 @@ csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, c
     a.bt = pages->block_table;
     a.start_pos = start_pos;
     a.cu_new = cu_new;
-    a.err = err;
+    a.err = nullptr;
     a.n_q_rows = n_q_rows;
     a.n_items = n_items;
     a.n_heads = n_heads;
@@ -422,6 +421,17 @@ csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, c
     a.max_blocks = pages->max_blocks;
     a.eps = eps;
     a.rf = make_freqs(swa->rope_dims, swa->rope_theta);
+    return CSL_OK;
+}
+
+csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, const int64_t* start_pos,
+                                  const int32_t* cu_new, int32_t total_new, const uint16_t* x, const uint16_t* q,
+                                  int32_t n_heads, const float* q_gain, float eps, uint16_t* q_out,
+                                  csl_stream_t stream) {
+    QSideArgs a;
+    csl_status st = prepare_qside(swa, pages, start_pos, cu_new, total_new, x, q, n_heads, q_gain, eps, q_out, a);
+    if (st || a.n_items == 0) return st;
+    if ((st = device_error_ptr(&a.err))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed(CSL_KERNEL_QSIDE, [&](const LaunchEvents& ev) { return launch_qside(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "q_norm_rope_insert launch");
@@ -512,29 +522,44 @@ csl_status csl_index_topk_insert(const csl_pool* index_pool, const csl_pages* pa
                                  const float* w, int32_t n_heads, int32_t k, int32_t* topk, float* kth_score,
                                  void* ws, size_t ws_bytes, int32_t n_jobs, const csl_insert_job* jobs,
                                  const int64_t* start_pos, const int32_t* cu_new, int32_t total_new, float eps,
-                                 csl_stream_t stream) {
+                                 const csl_qside_job* qside, csl_stream_t stream) {
     IndexArgs a;
     CompressArgs c;
+    QSideArgs q;
     csl_status st = prepare_index(index_pool, pages, num_q, q_seq, q_pos, max_q_pos, q_idx, w, n_heads, k, topk,
                                   kth_score, ws, ws_bytes, a);
     if (st) return st;
-    if ((st = prepare_inserts(n_jobs, jobs, pages, start_pos, cu_new, total_new, eps, c))) return st;
-    if (a.num_q == 0 && c.total_new == 0) return CSL_OK;
+    c.total_new = 0;
+    c.n_jobs = 0;
+    if (n_jobs != 0 || !qside) {
+        if ((st = prepare_inserts(n_jobs, jobs, pages, start_pos, cu_new, total_new, eps, c))) return st;
+    }
+    q.n_items = 0;
+    if (qside && (st = prepare_qside(qside->swa, pages, start_pos, cu_new, total_new, qside->x, qside->q,
+                                     qside->n_heads, qside->q_gain, eps, qside->q_out, q)))
+        return st;
+    if (qside) {
+        for (int i = 0; i < n_jobs; ++i)
+            if (jobs[i].pool->rows == qside->swa->rows)
+                return fail(CSL_EINVAL, "job %d inserts into the query side's raw pool", i);
+    }
+    if (a.num_q == 0 && c.total_new == 0 && q.n_items == 0) return CSL_OK;
     uint32_t* err = nullptr;
     if ((st = device_error_ptr(&err))) return st;
     a.err = err;
     c.err = err;
+    q.err = err;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (a.num_q > 0) {
         e = timed(CSL_KERNEL_INDEX_SCORE, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "index_score launch");
     }
-    if (c.total_new == 0) {
+    if (c.total_new == 0 && q.n_items == 0) {
         if (a.num_q > 0) e = timed(CSL_KERNEL_TOPK_SELECT, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
     } else {
         e = timed(CSL_KERNEL_TOPK_SELECT,
-                  [&](const LaunchEvents& ev) { return launch_topk_select_insert(a, c, s, ev); });
+                  [&](const LaunchEvents& ev) { return launch_topk_select_insert(a, c, q, s, ev); });
     }
     if (e != hipSuccess) return hip_fail(e, "topk_select / insert launch");
     return CSL_OK;

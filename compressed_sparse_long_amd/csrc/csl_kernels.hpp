@@ -116,7 +116,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEv
 hipError_t launch_qside(const QSideArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
-hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, hipStream_t st,
+hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, const QSideArgs& q, hipStream_t st,
                                      const LaunchEvents& ev = {});
 bool index_use_tiled(int num_q);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});

@@ -1190,12 +1190,16 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
 // what the queries select, and they fill the CUs that the few select
 // workgroups leave idle.  MERGE: the two-stage merge, else the full select.
 template <int NT, bool MERGE>
-__global__ void __launch_bounds__(NT) topk_select_insert_kernel(IndexArgs a, CompressArgs c) {
+__global__ void __launch_bounds__(NT) topk_select_insert_kernel(IndexArgs a, CompressArgs c, QSideArgs q) {
     if ((int)blockIdx.x >= a.num_q) {
         if (threadIdx.x >= 256) return;
-        __shared__ InsertSmem sm;
-        const int i = (int)blockIdx.x - a.num_q;
-        insert_block(c, i / c.total_new, i % c.total_new, sm);
+        const int64_t i = (int64_t)blockIdx.x - a.num_q, n_ins = (int64_t)c.total_new * c.n_jobs;
+        if (i < n_ins) {
+            __shared__ InsertSmem sm;
+            insert_block(c, (int)(i / c.total_new), (int)(i % c.total_new), sm);
+        } else {
+            qside_block<1>(q, i - n_ins);  // one row per wave: decode-sized batches
+        }
         return;
     }
     if constexpr (MERGE) merge_query<NT>(a, blockIdx.x);
@@ -1269,28 +1273,32 @@ hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEv
     return hipGetLastError();
 }
 
-// The select with the inserts riding in its last launch (one workgroup per
-// token and pool after the queries' workgroups).
-hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, hipStream_t st,
+// The select with the inserts and the query-side rows riding in its last
+// launch (one workgroup per token and pool, then one per four query-side rows,
+// after the queries' workgroups).
+hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, const QSideArgs& q, hipStream_t st,
                                      const LaunchEvents& ev) {
     const int64_t n_ins = (int64_t)c.total_new * c.n_jobs;
-    if (a.num_q <= 0 || n_ins <= 0 || a.num_q + n_ins > 0x7fffffff) {
+    const int64_t n_qb = q.n_items > 0 ? (q.n_items + 3) / 4 : 0;
+    if (a.num_q <= 0 || n_ins + n_qb <= 0 || a.num_q + n_ins + n_qb > 0x7fffffff) {
         hipError_t e = launch_topk_select(a, st, ev);
-        if (e != hipSuccess) return e;
-        return launch_compress(c, st);
+        if (e == hipSuccess) e = launch_compress(c, st);
+        if (e == hipSuccess) e = launch_qside(q, st);
+        return e;
     }
-    const dim3 grid((unsigned)(a.num_q + n_ins));
+    const dim3 grid((unsigned)(a.num_q + n_ins + n_qb));
     if (a.kl > 0) {
         if (a.tiled)
             launch_kernel(ev, true, false, topk_local_kernel, dim3((unsigned)((a.nchunks + 3) / 4), (unsigned)a.num_q),
                           dim3(256), st, a);
         if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256)
-            launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<256, true>, grid, dim3(256), st, a, c);
+            launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<256, true>, grid, dim3(256), st, a, c, q);
         else
             launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<kSelThreads, true>, grid, dim3(kSelThreads), st,
-                          a, c);
+                          a, c, q);
     } else {
-        launch_kernel(ev, true, true, topk_select_insert_kernel<kSelThreads, false>, grid, dim3(kSelThreads), st, a, c);
+        launch_kernel(ev, true, true, topk_select_insert_kernel<kSelThreads, false>, grid, dim3(kSelThreads), st, a, c,
+                      q);
     }
     return hipGetLastError();
 }

@@ -197,23 +197,36 @@ csl_status csl_index_topk(const csl_pool* index_pool /* host */, const csl_pages
                           const uint16_t* q_idx, const float* w, int32_t n_heads, int32_t k, int32_t* topk,
                           float* kth_score, void* ws, size_t ws_bytes, csl_stream_t stream);
 
+/* The query side of a step, for csl_index_topk_insert: the arguments of
+ * csl_q_norm_rope_insert that the inserts do not share. */
+typedef struct {
+    const csl_pool* swa; /* host: ratio-1 pool that receives RoPE(x_t, t) */
+    const uint16_t* x;   /* [total_new][swa->dim] bf16 */
+    const uint16_t* q;   /* [total_new][n_heads][swa->dim] bf16, before the norm */
+    int32_t n_heads;
+    const float* q_gain; /* [swa->dim] fp32 or NULL (unit gain) */
+    uint16_t* q_out;     /* may equal q */
+} csl_qside_job;
+
 /*
- * Steps 1-3 of a decode step with the inserts overlapped with the indexer
- * ([Notes] 优化二：多 CUDA 流并行: the indexer branch runs beside the main KV
- * compression and the raw-window insert; [Summary] 多串流分割).  Exactly
- * csl_index_topk followed by csl_compress_insert_multi on `stream`, with the
- * same arguments and results: the inserts run after the index scores are
- * computed, inside the top-k selection's launch (whose few workgroups leave
- * most of the GPU idle) when the selection ends in the two-stage merge, else
- * in a launch of their own after it.  Validation covers both parts before
- * anything is launched.  1 <= n_jobs <= 4.
+ * Steps 1-3 of a decode step with the writes of the step overlapped with the
+ * indexer ([Notes] 优化二：多 CUDA 流并行: the indexer branch runs beside the
+ * main KV compression and the raw-window insert; [Summary] 多串流分割; the
+ * query side, [Notes] 融合 3).  Exactly csl_index_topk, then
+ * csl_compress_insert_multi (if n_jobs > 0), then csl_q_norm_rope_insert (if
+ * qside is not NULL) on `stream`, with the same arguments and results: the
+ * writes run after the index scores are computed, as extra workgroups of the
+ * top-k selection's last launch, whose few workgroups leave most of the GPU
+ * idle.  Validation covers every part before anything is launched.
+ * 0 <= n_jobs <= 4 (0 only with qside); no job may target qside->swa.
  */
 csl_status csl_index_topk_insert(const csl_pool* index_pool /* host */, const csl_pages* pages /* host */,
                                  int32_t num_q, const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos,
                                  const uint16_t* q_idx, const float* w, int32_t n_heads, int32_t k, int32_t* topk,
                                  float* kth_score, void* ws, size_t ws_bytes, int32_t n_jobs,
                                  const csl_insert_job* jobs /* host */, const int64_t* start_pos,
-                                 const int32_t* cu_new, int32_t total_new, float eps, csl_stream_t stream);
+                                 const int32_t* cu_new, int32_t total_new, float eps,
+                                 const csl_qside_job* qside /* host, nullable */, csl_stream_t stream);
 
 /*
  * Steps 4-6 -- hybrid attention, inverse RoPE, optional fp8 output.

@@ -150,11 +150,11 @@ def test_index_topk_insert_validation(csl):
     job_pool = pool(csl, ratio=1, coff=1, state_x=None, state_logits=None)
     jobs = (csl._InsertJob * 1)(csl._InsertJob(C.addressof(job_pool), FAKE, None, None))
 
-    def call(n_jobs=1, k=64, x_ok=True, total=1):
+    def call(n_jobs=1, k=64, x_ok=True, total=1, qs=None):
         if not x_ok:
             jobs[0].x = FAKE + 2
         r = csl._index_topk_insert(C.byref(ip), C.byref(pg(csl)), 4, FAKE, FAKE, 1000, FAKE, FAKE, 16, k, FAKE,
-                                   None, FAKE, 1 << 30, n_jobs, jobs, FAKE, FAKE, total, 1e-6, None)
+                                   None, FAKE, 1 << 30, n_jobs, jobs, FAKE, FAKE, total, 1e-6, qs, None)
         jobs[0].x = FAKE
         return r
     assert call(k=0) == -2            # the indexer's checks
@@ -162,3 +162,11 @@ def test_index_topk_insert_validation(csl):
     assert call(n_jobs=5) == -2
     assert call(x_ok=False) == -3
     assert call(total=-1) == -1
+    # the query side: its own checks, and no insert job into its raw pool
+    qs = csl._QSideJob(C.addressof(job_pool), FAKE, FAKE, 0, None, FAKE)
+    assert call(qs=C.byref(qs)) == -2                    # n_heads = 0
+    qs.n_heads = 8
+    assert call(qs=C.byref(qs)) == -1                    # job 0 targets the query side's raw pool
+    other = pool(csl, ratio=1, coff=1, state_x=None, state_logits=None, rows=FAKE + 4096)
+    qs.swa = C.addressof(other)
+    assert call(qs=C.byref(qs), x_ok=False) == -3        # the jobs' checks still apply

@@ -364,6 +364,10 @@ FUSED_CASES = [
     # 150 000 visible entries: 148 chunks x 32 candidates, the 1024-thread merge
     # (the inserts' workgroups run with their first 256 threads)
     dict(name="decode_merge_1024_threads", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32),
+    # the query side in the same launch (it owns the raw-window insert)
+    dict(name="decode_with_query_side", pos=[[9003], [20000]], k=512, qside=True),
+    dict(name="short_rows_with_query_side", pos=[[1000], [700]], k=512, qside=True),
+    dict(name="merge_1024_with_query_side", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32, qside=True),
 ]
 
 
@@ -399,6 +403,9 @@ def test_index_topk_insert_equals_separate_calls(csl, orc, case):
     lg = randn_f32(seed, 32, (nq, 2)).astype(np.float32)
     li = randn_f32(seed, 33, (nq, 2)).astype(np.float32)
     gain = rand_u(seed, 34, (D,), 0.5, 1.5).astype(np.float32)
+    qs = case.get("qside", False)
+    qh = randn_bf16(seed, 35, (nq, 8, D))
+    qg = rand_u(seed, 36, (D,), 0.5, 1.5).astype(np.float32)
     outs = []
     for fused in (False, True):
         gi, gr, gm = gpu_pool(csl, idx), gpu_pool(csl, raw, state=False), gpu_pool(csl, main)
@@ -407,20 +414,28 @@ def test_index_topk_insert_equals_separate_calls(csl, orc, case):
         ws = torch.empty(csl.index_topk_workspace(nq, max_pos, k) // 4, dtype=torch.float32, device=DEV)
         jobs = [(gr, dev_bf16(x), None, None), (gm, dev_bf16(x), dev(lg), dev(gain)), (gi, dev_bf16(xi), dev(li), None)]
         gbt, gq, gw = dev(bt), dev_bf16(qi), dev(w)
+        gqh, gqo = dev_bf16(qh), torch.empty((nq, 8, D), dtype=torch.bfloat16, device=DEV)
+        qside = (gr, dev_bf16(x), gqh, dev(qg), gqo) if qs else None
+        if qs:
+            jobs = jobs[1:]  # the query side writes the raw rows
         say(f"index_topk_insert {case['name']} fused={fused}")
         if fused:
             csl.index_topk_insert(gi, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, jobs, dev(st), dev(cu),
-                                  kth, ws)
+                                  kth, ws, qside=qside)
         else:
             csl.index_topk(gi, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, kth, ws)
             csl.compress_insert_multi(jobs, gbt, dev(st), dev(cu))
+            if qs:
+                csl.q_norm_rope_insert(gr, gbt, dev(st), dev(cu), qside[1], gqh, qside[3], q_out=gqo)
         torch.cuda.synchronize()
         assert csl.read_device_error() == 0
         outs.append([host(topk), host(kth), host(gi.rows), host_u16(gi.state_x), host(gi.state_logits), host(gr.rows),
-                     host(gm.rows), host_u16(gm.state_x), host(gm.state_logits)])
+                     host(gm.rows), host_u16(gm.state_x), host(gm.state_logits), host_u16(gqo)])
     names = ["topk", "kth", "index rows", "index state_x", "index state_logits", "raw rows", "main rows",
-             "main state_x", "main state_logits"]
+             "main state_x", "main state_logits", "q_out"]
     for nm, a, b in zip(names, outs[0], outs[1]):
+        if nm == "q_out" and not qs:
+            continue
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{case['name']}: {nm} differ"
     # and the selection against the oracle on the pre-insert index pool
     o_topk, o_kth, o_sc, f = O.index_topk(idx, bt, q_seq, q_pos, qi, w, k, want_scores=True, max_cand=max_pos // 4)
