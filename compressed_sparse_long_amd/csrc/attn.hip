@@ -1138,21 +1138,25 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     const int esz = a.out_dtype == kF32 ? 4 : a.out_dtype == kBF16 ? 2 : 1;
     const int rstride = D * esz + 16;
     uint8_t* stage = s_ring;
-    auto rope_tile = [&](f32x16& v, int m) {
+    // RoPE^-1 in place on a 32-dim tile m: skipped (uniformly) below the rotated
+    // tail; inside it each pair takes its cos/sin or (1, 0) by a select, so no
+    // lane-dependent branch splits the wave
+    auto rope_tile = [&](float (&v)[16], int m) {
+        const int t0 = 256 * dh + 32 * m;
+        if (t0 + 32 <= rbase) return;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d0 = 256 * dh + 32 * m + 8 * j + 4 * h2;
-            if (d0 >= rbase) {
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int pj = (d0 + 2 * c - rbase) >> 1;
-                    const float cs = s_rope[0][pj], sn = s_rope[1][pj];
-                    const float u = v[4 * j + 2 * c], w = v[4 * j + 2 * c + 1];
-                    v[4 * j + 2 * c] = u * cs - w * sn;
-                    v[4 * j + 2 * c + 1] = u * sn + w * cs;
-                }
+            for (int c = 0; c < 2; ++c) {
+                const int d = t0 + 8 * j + 4 * h2 + 2 * c;
+                const bool rot = d >= rbase;
+                const int pj = rot ? (d - rbase) >> 1 : 0;
+                const float cr = s_rope[0][pj], sr = s_rope[1][pj];
+                const float cs = rot ? cr : 1.f, sn = rot ? sr : 0.f;
+                const float u = v[4 * j + 2 * c], w = v[4 * j + 2 * c + 1];
+                v[4 * j + 2 * c] = u * cs - w * sn;
+                v[4 * j + 2 * c + 1] = u * sn + w * cs;
             }
-        }
     };
     __syncthreads();  // every wave is done with the ring
     uint8_t* srow = stage + head * rstride;
@@ -1160,7 +1164,12 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
         // 64-dim groups: tiles m = 2 g4, 2 g4 + 1 of the wave's 256 dims, halves h2 = 0, 1
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            f32x16 v0 = oacc[2 * g4], v1 = oacc[2 * g4 + 1];
+            float v0[16], v1[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                v0[c] = oacc[2 * g4][c];
+                v1[c] = oacc[2 * g4 + 1][c];
+            }
             rope_tile(v0, 2 * g4);
             rope_tile(v1, 2 * g4 + 1);
             float amax = 0.f;
@@ -1174,22 +1183,42 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
             const float scale = gmax > 0.f ? gmax / 448.0f : 1.0f;
             const float r = gmax > 0.f ? 448.0f / amax : 0.f;
             if (h2 == 0 && hv) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + 4 * dh + g4] = scale;
+            // NaN or infinity anywhere in the wave's group makes the sum of v * 0 a NaN:
+            // only then does the conversion need its per-value NaN handling
+            float nz = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) nz = fmaf(v1[c], 0.f, fmaf(v0[c], 0.f, nz));
+            const bool finite = __ballot(nz != nz) == 0;
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
-                const f32x16& v = mm ? v1 : v0;
+                const float* v = mm ? v1 : v0;
                 const int m = 2 * g4 + mm;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint32_t*>(srow + 256 * dh + 32 * m + 8 * j + 4 * h2) =
-                        e4m3_pack4(v[4 * j] * r, v[4 * j + 1] * r, v[4 * j + 2] * r, v[4 * j + 3] * r);
+                    *reinterpret_cast<uint32_t*>(srow + 256 * dh + 32 * m + 8 * j + 4 * h2) = e4m3_pack4_finite(
+                        v[4 * j] * r, v[4 * j + 1] * r, v[4 * j + 2] * r, v[4 * j + 3] * r);
+            }
+            if (__builtin_expect(!finite, 0)) {  // rare: the codes again, with the per-value NaN handling
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const float* v = mm ? v1 : v0;
+                    const int m = 2 * g4 + mm;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<uint32_t*>(srow + 256 * dh + 32 * m + 8 * j + 4 * h2) =
+                            e4m3_pack4(v[4 * j] * r, v[4 * j + 1] * r, v[4 * j + 2] * r, v[4 * j + 3] * r);
+                }
             }
         }
     } else {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            f32x16 v = oacc[m];
+            float v[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) v[c] = oacc[m][c];
             rope_tile(v, m);
-            v *= inv_l;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) v[c] *= inv_l;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d0 = 256 * dh + 32 * m + 8 * j + 4 * h2;

@@ -73,6 +73,12 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     }
     return code;
 }
+// e4m3_pack4 for values known to be finite: saturation only
+__device__ __forceinline__ uint32_t e4m3_pack4_finite(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(a, -448.0f), 448.0f), fminf(fmaxf(b, -448.0f), 448.0f), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(c, -448.0f), 448.0f), fminf(fmaxf(d, -448.0f), 448.0f), w, true);
+    return (uint32_t)w;
+}
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) { return e4m3_pack4(x, 0.f, 0.f, 0.f) & 0xffu; }
 
 // MXFP4 block -> bf16: 32 E2M1 codes (16 bytes, element 2i in the low nibble
