@@ -589,6 +589,49 @@ def test_unmapped_page_is_masked_and_flagged(csl, orc):
     assert_close(host(out), o64, what="unmapped")
 
 
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_nan_key_gives_nan_codes_only_where_seen(csl, orc, mode):
+    """A NaN in one raw key row makes every output of a query whose window holds that
+    row NaN (the fp8 NaN code, either sign), as in the oracle; the other queries stay
+    finite and match.  This covers the fp8 epilogue's non-finite path."""
+    D, R, H, k = 512, 64, 64, 64
+    comp, swa, bt = make_pools(31, 2, 1300, D, R, 4, O.BF16)
+    row = gather_rows(swa.rows, bt, 0, 1, 995, 1)
+    row.view(np.uint16)[0, 7] = 0x7FC0     # bf16 NaN in dim 7 of raw token 995 of sequence 0
+    scatter_rows(swa.rows, bt, 0, 1, row, i0=995)
+    pos_lists = [[1000, 1200], [1000]] if mode == "decode" else [[1000, 1001, 1002], [1000, 1001]]
+    q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(pos_lists)]).astype(np.int32)
+    q_pos = np.concatenate(pos_lists).astype(np.int64)
+    nq = len(q_pos)
+    q = randn_bf16(31, 80, (nq, H, D))
+    topk = random_topk(31, q_pos, 4, k)
+    o_out, o_sc, o64, f = O.hybrid_attn(comp, swa, bt, q_seq, q_pos, q, topk=topk, k=k, swa_window=128,
+                                        softmax_scale=D ** -0.5, out_dtype=O.FP8)
+    assert f == 0
+    seen = np.isnan(o64)
+    sees = (q_seq == 0) & (q_pos - 995 < 128)
+    assert np.array_equal(seen.all(axis=(1, 2)), sees) and not seen[~sees].any()
+    out = torch.empty((nq, H, D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((nq, H, D // 64), dtype=torch.float32, device=DEV)
+    say(f"nan key {mode} nq {nq}")
+    if mode == "decode":
+        ws = torch.empty(max(1, csl.hybrid_attn_workspace(nq, H, D, 4, k, 128, 1200) // 4), dtype=torch.float32,
+                         device=DEV)
+        csl.hybrid_attn_decode(gpu_pool(csl, comp, False), gpu_pool(csl, swa, False), dev(bt), dev(q_seq),
+                               dev(q_pos), 1200, dev_bf16(q), dev(topk), k, 128, D ** -0.5, O.FP8, out, scales, ws)
+    else:
+        cu = np.array([0, 3, 5], np.int32)
+        csl.hybrid_attn_prefill(gpu_pool(csl, comp, False), gpu_pool(csl, swa, False), dev(bt), dev(cu),
+                                dev(np.array([1000, 1000], np.int64)), 1002, dev_bf16(q), dev(topk), k, 128,
+                                D ** -0.5, O.FP8, out, scales)
+    torch.cuda.synchronize()
+    assert csl.read_device_error() == 0
+    codes = host(out)
+    assert np.array_equal((codes & 0x7F) == 0x7F, seen)
+    assert np.all(host(scales)[sees] == 1.0) and np.all(o_sc[sees] == 1.0)
+    assert_fp8_close(orc, codes[~sees], host(scales)[~sees], o_out[~sees], o_sc[~sees], what="nan key, unseen")
+
+
 # ---------------------------------------------------------------------------
 # the tiny workload end to end (compress x3 -> index_topk -> decode)
 # ---------------------------------------------------------------------------
