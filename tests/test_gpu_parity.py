@@ -517,6 +517,12 @@ ATTN_CASES = [
          pos=[[150000, 131000]]),
     dict(name="swa_only_d512_h64_fp8kv_fp8out", D=512, R=64, H=64, ratio=4, k=0, dtype=O.FP8, out=O.FP8,
          pos=[[5, 129, 1000]], no_comp=True),
+    # decode splits: at least as many splits as heads, and 32 queries x 10 splits
+    # (more workgroups than compute units)
+    dict(name="c128a_d512_h16_splits_over_heads_bf16", D=512, R=64, H=16, ratio=128, k=0, dtype=O.BF16, out=O.BF16,
+         pos=[[150000]]),
+    dict(name="c4a_d512_h64_k512_32q_fp8out", D=512, R=64, H=64, ratio=4, k=512, dtype=O.BF16, out=O.FP8,
+         pos=[[2100 + 37 * i for i in range(16)], [2500 + 53 * i for i in range(16)]]),
 ]
 
 
