@@ -53,6 +53,7 @@ struct QueryInfo {
     bool ok;
 };
 
+// (n: the same for every lane of the wave)
 __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int n) {
     QueryInfo qi;
     if (a.q_seq) {
@@ -68,6 +69,11 @@ __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int n) {
         qi.s = lo;
         qi.p = a.q_pos_start[lo] + (n - a.cu_q[lo]);
     }
+    // n is the same across the wave, so are s and p: scalar registers for them and
+    // for everything derived from them (key counts, tile loop bounds)
+    qi.s = __builtin_amdgcn_readfirstlane(qi.s);
+    qi.p = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)((uint64_t)qi.p >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qi.p));
     qi.ok = qi.s >= 0 && qi.s < a.num_seqs && qi.p >= 0 && qi.p <= a.max_q_pos;
     return qi;
 }
@@ -1047,7 +1053,7 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
 
     for (int64_t kb = t_begin * kT2; kb < k_end; kb += kMaxKeys2) {
         const int64_t ke = kb + kMaxKeys2 < k_end ? kb + kMaxKeys2 : k_end;
-        const int ntl = (int)((ke - kb + kT2 - 1) / kT2);
+        const int ntl = __builtin_amdgcn_readfirstlane((int)((ke - kb + kT2 - 1) / kT2));  // (uniform)
         const bool first = kb == t_begin * kT2;
         if (!first) __syncthreads();  // the previous pass is done with s_rows and the tiles
         {
