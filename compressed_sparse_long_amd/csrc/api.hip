@@ -176,9 +176,12 @@ int64_t decode_tiles(int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
 int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
     const int64_t tiles = decode_tiles(comp_ratio, k, swa_window, max_q_pos);
     // enough workgroups to spread over the CUs, but at least 2 tiles (64 keys)
-    // per split: every split writes a heads x dim fp32 partial
+    // per split: every split writes a heads x dim fp32 partial.  A launch that
+    // would still hold fewer than 32 workgroups (one or two queries) takes one
+    // tile per split: there the chip is idle and the extra partials are few.
     int64_t want = (512 + num_q - 1) / (num_q > 0 ? num_q : 1);
     int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
+    if ((int64_t)num_q * cap < 32) cap = tiles;
     int64_t sp = want < cap ? want : cap;
     if (sp > 1024) sp = 1024;
     return (int)(sp > 1 ? sp : 1);
