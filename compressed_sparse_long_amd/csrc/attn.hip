@@ -472,20 +472,21 @@ hybrid_attn_kernel(AttnArgs a) {
 }
 
 // Merge the splits of (query, head), 8 dims per lane.  SHARE (many splits):
-// one workgroup per (query, head); wave w takes splits w, w + 4, ..., the four
-// running (max, sum, output) meet in LDS and wave 0 finishes, so that each
-// wave's chain of dependent batches stays short.  Otherwise one wave per
-// (query, head) takes every split (four heads per workgroup).
-template <int D, bool SHARE>
-__global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_o[SHARE ? 4 : 1][64][8];
-    __shared__ float s_ml[4][2];
+// one workgroup of NW waves per (query, head); wave w takes splits w, w + NW,
+// ..., the NW running (max, sum, output) meet in LDS and wave 0 finishes, so
+// that each wave's chain of dependent batches stays short.  Otherwise one wave
+// per (query, head) takes every split (four heads per workgroup).
+template <int D, bool SHARE, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) attn_combine_kernel(AttnArgs a) {
+    static_assert(SHARE || NW == 4, "one wave per head: four heads per workgroup");
+    __shared__ float s_o[SHARE ? NW : 1][64][8];
+    __shared__ float s_ml[NW][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hpb = SHARE ? 1 : 4;  // heads per workgroup
     const int n = blockIdx.x / ((a.n_heads + hpb - 1) / hpb);
     const int head = (blockIdx.x % ((a.n_heads + hpb - 1) / hpb)) * hpb + (SHARE ? 0 : wave);
     if (head >= a.n_heads) return;
-    const int w0 = SHARE ? wave : 0, wstep = SHARE ? 4 : 1;
+    const int w0 = SHARE ? wave : 0, wstep = SHARE ? NW : 1;
     const bool active = 8 * lane < D;
 
     const float* ml = a.part_ml + ((int64_t)n * a.n_splits * a.n_heads + head) * 2;
@@ -543,13 +544,15 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
         }
         __syncthreads();
         if (wave != 0) return;
-        M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
+        M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0]);
         const float Mu = M == -INFINITY ? 0.f : M;
         Lsum = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) o[c] = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float r = exp2f(s_ml[w][0] - Mu);  // a wave without splits holds -inf: weight 0
             Lsum = fmaf(s_ml[w][1], r, Lsum);
 #pragma unroll
@@ -1284,7 +1287,9 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEv
     const bool share = a.n_splits > 16;
     const dim3 grid((unsigned)((int64_t)a.num_q * (share ? a.n_heads : (a.n_heads + 3) / 4)));
     if (a.dim == 512) {
-        if (share) launch_kernel(ev, true, true, attn_combine_kernel<512, true>, grid, dim3(kThreads), st, a);
+        // more than 64 splits: sixteen waves share them (a few batches per wave)
+        if (a.n_splits > 64) launch_kernel(ev, true, true, attn_combine_kernel<512, true, 16>, grid, dim3(1024), st, a);
+        else if (share) launch_kernel(ev, true, true, attn_combine_kernel<512, true>, grid, dim3(kThreads), st, a);
         else launch_kernel(ev, true, true, attn_combine_kernel<512, false>, grid, dim3(kThreads), st, a);
     } else if (a.dim == 128) {
         if (share) launch_kernel(ev, true, true, attn_combine_kernel<128, true>, grid, dim3(kThreads), st, a);
