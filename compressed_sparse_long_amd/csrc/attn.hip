@@ -1283,8 +1283,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev) {
     if (a.num_q <= 0 || a.n_splits <= 1) return hipSuccess;
     // up to 16 splits: one batch per wave, four heads per workgroup; more: the
-    // split list shared by the four waves of a (query, head) workgroup
-    const bool share = a.n_splits > 16;
+    // split list shared by the four waves of a (query, head) workgroup.  The
+    // shared form also takes 5..16 splits when the four-heads form would fill
+    // fewer than 256 workgroups: there more, shorter workgroups are faster.
+    const bool share = a.n_splits > 16 || (a.n_splits > 4 && (int64_t)a.num_q * ((a.n_heads + 3) / 4) < 256);
     const dim3 grid((unsigned)((int64_t)a.num_q * (share ? a.n_heads : (a.n_heads + 3) / 4)));
     if (a.dim == 512) {
         // more than 64 splits: sixteen waves share them (a few batches per wave)
