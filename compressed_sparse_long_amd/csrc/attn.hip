@@ -1120,13 +1120,17 @@ hybrid_attn_mqa512_kernel(AttnArgs a) {
     if (a.n_splits > 1) {
         if (!hv) return;
         // unnormalised partial relative to m_ref: dims 256 dh + 32 m + 8 j + 4 h2 .. +3 of this head
+        // (bf16 keys: non-temporal stores, which measured faster; the fp8-key
+        // launches measured slightly faster with ordinary stores)
         float* po = a.part_o + (((int64_t)n * a.n_splits + sp) * a.n_heads + head) * D + 256 * dh + 4 * h2;
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<f32x4*>(po + 32 * m + 8 * j) =
-                    f32x4{oacc[m][4 * j], oacc[m][4 * j + 1], oacc[m][4 * j + 2], oacc[m][4 * j + 3]};
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = {oacc[m][4 * j], oacc[m][4 * j + 1], oacc[m][4 * j + 2], oacc[m][4 * j + 3]};
+                if constexpr (KV8) *reinterpret_cast<f32x4*>(po + 32 * m + 8 * j) = v;
+                else __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(po + 32 * m + 8 * j));
+            }
         if (h2 == 0 && dh == 0) {
             float* ml = a.part_ml + (((int64_t)n * a.n_splits + sp) * a.n_heads + head) * 2;
             ml[0] = m_ref;
