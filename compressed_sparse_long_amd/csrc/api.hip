@@ -161,7 +161,7 @@ int index_local_k(int64_t max_q_pos, int k) {
     if (nv <= k) return 0;
     const double expect = (double)k * kIndexChunk / (double)nv;
     int kl = (int)std::ceil((expect + 5.0 * std::sqrt(expect) + 4.0) / 8.0) * 8;
-    kl = kl < 32 ? 32 : (kl > kIndexChunk ? kIndexChunk : kl);
+    kl = kl < 16 ? 16 : (kl > kIndexChunk ? kIndexChunk : kl);
     const int64_t nchunks = index_stride(max_q_pos) / kIndexChunk;
     return nchunks * kl <= 8192 ? kl : 0;
 }

@@ -1264,6 +1264,8 @@ hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEv
                           dim3(256), st, a);
         if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256)
             launch_kernel(ev, !a.tiled, true, topk_merge_kernel<256>, dim3((unsigned)a.num_q), dim3(256), st, a);
+        else if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 512)
+            launch_kernel(ev, !a.tiled, true, topk_merge_kernel<512>, dim3((unsigned)a.num_q), dim3(512), st, a);
         else
             launch_kernel(ev, !a.tiled, true, topk_merge_kernel<kSelThreads>, dim3((unsigned)a.num_q),
                           dim3(kSelThreads), st, a);
@@ -1293,6 +1295,8 @@ hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, 
                           dim3(256), st, a);
         if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 256)
             launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<256, true>, grid, dim3(256), st, a, c, q);
+        else if ((int64_t)a.nchunks * a.kl <= (int64_t)kMergeSlots * 512)
+            launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<512, true>, grid, dim3(512), st, a, c, q);
         else
             launch_kernel(ev, !a.tiled, true, topk_select_insert_kernel<kSelThreads, true>, grid, dim3(kSelThreads), st,
                           a, c, q);

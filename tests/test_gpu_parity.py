@@ -277,6 +277,8 @@ INDEX_CASES = [
     dict(name="h16_d128_k512_outliers", H=16, DI=128, k=512, pos=[[20000, 131072]], mode="outlier"),
     # more than 32768 candidates: the select reads its keys from global memory
     dict(name="h16_d128_k512_40k_candidates", H=16, DI=128, k=512, pos=[[160000, 150003]]),
+    # 400 000 visible entries: 392 chunks x 16 candidates, the 1024-thread merge
+    dict(name="h16_d128_k512_merge_1024_threads", H=16, DI=128, k=512, pos=[[1600003]]),
     # scores rise with the id (with bf16 ties): the top 512 crowd the last chunks, so the
     # two-stage select's check fails and the exact single-pass select takes over
     dict(name="h16_d128_k512_ramp", H=16, DI=128, k=512, pos=[[131072, 70001]], mode="ramp"),
@@ -361,13 +363,13 @@ FUSED_CASES = [
     dict(name="decode_short_rows", pos=[[1000], [700]], k=512),
     # 100 queries: the query-blocked scores, then the merge with 100 x 3 inserts
     dict(name="tiled_100_queries", pos=[list(range(9000, 9100))], k=512),
-    # 150 000 visible entries: 148 chunks x 32 candidates, the 1024-thread merge
+    # 150 000 visible entries: 148 chunks x 24 candidates, the 512-thread merge
     # (the inserts' workgroups run with their first 256 threads)
-    dict(name="decode_merge_1024_threads", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32),
+    dict(name="decode_wide_merge", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32),
     # the query side in the same launch (it owns the raw-window insert)
     dict(name="decode_with_query_side", pos=[[9003], [20000]], k=512, qside=True),
     dict(name="short_rows_with_query_side", pos=[[1000], [700]], k=512, qside=True),
-    dict(name="merge_1024_with_query_side", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32, qside=True),
+    dict(name="wide_merge_with_query_side", pos=[[600003]], k=512, D=64, main_dtype=O.BF16, R=32, qside=True),
 ]
 
 
