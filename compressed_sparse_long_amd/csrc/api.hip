@@ -173,15 +173,21 @@ int64_t decode_tiles(int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
     return (keys + 31) / 32;
 }
 
-int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
+// Splits of a decode launch.  Every split writes a heads x dim fp32 partial
+// that the merge reads back, so splits take several 32-key tiles: 4 for bf16
+// keys, 2 for fp8 keys (whose tiles cost more: the codes are widened in LDS).
+// A launch that would then hold fewer than 32 workgroups halves the tiles per
+// split until it does not (down to one), and there are at most 512 / num_q
+// splits.
+int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_q_pos, bool fp8_keys) {
     const int64_t tiles = decode_tiles(comp_ratio, k, swa_window, max_q_pos);
-    // enough workgroups to spread over the CUs, but at least 2 tiles (64 keys)
-    // per split: every split writes a heads x dim fp32 partial.  A launch that
-    // would still hold fewer than 32 workgroups (one or two queries) takes one
-    // tile per split: there the chip is idle and the extra partials are few.
-    int64_t want = (512 + num_q - 1) / (num_q > 0 ? num_q : 1);
-    int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
-    if ((int64_t)num_q * cap < 32) cap = tiles;
+    int64_t tps = fp8_keys ? 2 : 4;
+    int64_t cap = tiles / tps > 1 ? tiles / tps : 1;
+    while (tps > 1 && (int64_t)num_q * cap < 32) {
+        tps /= 2;
+        cap = tiles / tps > 1 ? tiles / tps : 1;
+    }
+    const int64_t want = (512 + num_q - 1) / (num_q > 0 ? num_q : 1);
     int64_t sp = want < cap ? want : cap;
     if (sp > 1024) sp = 1024;
     return (int)(sp > 1 ? sp : 1);
@@ -571,7 +577,10 @@ csl_status csl_index_topk_insert(const csl_pool* index_pool, const csl_pages* pa
 size_t csl_hybrid_attn_workspace(int32_t num_q, int32_t n_heads, int32_t dim, int32_t comp_ratio, int32_t k,
                                  int32_t swa_window, int64_t max_q_pos) {
     if (num_q <= 0 || n_heads <= 0 || dim <= 0) return 0;
-    int sp = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos);
+    // (the larger of the two key types' split counts: the key type is not an argument)
+    const int sp8 = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos, true);
+    const int sp16 = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos, false);
+    const int sp = sp8 > sp16 ? sp8 : sp16;
     if (sp <= 1) return 0;
     return (size_t)num_q * sp * n_heads * ((size_t)dim + 2) * sizeof(float);
 }
@@ -589,7 +598,7 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     if (!q_seq || !q_pos) return fail(CSL_EINVAL, "q_seq or q_pos is NULL");
     const int cr = comp ? comp->ratio : 0;
     const int kk = topk ? k : 0;
-    const int sp = decode_splits(num_q, cr, kk, swa_window, max_q_pos);
+    const int sp = decode_splits(num_q, cr, kk, swa_window, max_q_pos, swa->dtype == CSL_FP8_E4M3);
     if ((int64_t)num_q * sp > 0x7fffffff) return fail(CSL_ERANGE, "grid too large");
     size_t need = csl_hybrid_attn_workspace(num_q, n_heads, swa->dim, cr, kk, swa_window, max_q_pos);
     if (need > 0 && (!ws || ws_bytes < need)) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
