@@ -42,9 +42,14 @@ def test_workspace_sizes(csl):
     # 40 = 512*1024/32768 = 16 expected per chunk + 5 sqrt(16) + 4, rounded up to 8
     assert csl.index_topk_workspace(16, 131072, 512) == 16 * (32768 * 4 + 32 * 41 * 8)
     assert csl.index_topk_workspace(1, 100, 64) == 2048 * 4      # 25 entries <= k: one pass
-    # decode split-KV partials: num_q * splits * heads * (dim + 2) floats
-    ws = csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072)
-    assert ws > 0 and ws % (16 * 64 * 514 * 4) == 0
+    # decode split-KV partials: num_q * splits * heads * (dim + 2) floats, sized for the
+    # larger split count of the two key types (bf16: 4 tiles per split, fp8: 2; halved
+    # while the launch would hold fewer than 32 workgroups)
+    part = 64 * 514 * 4
+    assert csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072) == 16 * 10 * part  # 20 tiles: 10 fp8 splits
+    assert csl.hybrid_attn_workspace(1, 64, 512, 4, 512, 128, 1 << 20) == 20 * part      # one query: one-tile splits
+    assert csl.hybrid_attn_workspace(1, 64, 512, 128, 0, 128, 1 << 20) == 130 * part     # 260 tiles: 130 fp8 splits
+    assert csl.hybrid_attn_workspace(8, 64, 512, 128, 0, 128, 32768) == 8 * 6 * part     # 12 tiles: 6 splits
     assert csl.hybrid_attn_workspace(1, 64, 512, 0, 0, 0, 10) == 0
 
 
