@@ -635,8 +635,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path is data-parallel per sequence and this build runs on a "
-              "single MI355X; --gpus must be 1", file=sys.stderr)
+        print("bench.py measures one GPU: the path is data-parallel per sequence (sequences shard across GPUs "
+              "with no exchange), and the benchmark runs on a single MI355X; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb, 10)

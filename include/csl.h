@@ -60,7 +60,7 @@ typedef enum {
     CSL_EALIGN = -3,       /* a pointer not aligned to 16 bytes */
     CSL_EWORKSPACE = -4,   /* workspace smaller than the *_workspace() query */
     CSL_EHIP = -5,         /* the HIP runtime reported an error (text in csl_last_error) */
-    CSL_EUNSUPPORTED = -6  /* a valid combination this build does not implement */
+    CSL_EUNSUPPORTED = -6  /* a valid combination the library does not implement */
 } csl_status;
 
 /* Row formats.  CSL_FP8_E4M3 rows: dim e4m3fn codes, then dim/64 fp32 scales
