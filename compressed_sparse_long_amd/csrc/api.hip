@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -14,6 +15,10 @@
 #include "csl_kernels.hpp"
 
 __device__ uint32_t csl_device_error_word;
+
+namespace csl {
+thread_local unsigned g_events_used = 0;
+}
 
 namespace {
 
@@ -59,7 +64,7 @@ csl_status device_error_ptr(uint32_t** out) {
 // ---------------------------------------------------------------- timers
 
 struct Timer {
-    bool on = false;
+    std::atomic<bool> on{false};
     std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
     size_t used = 0;
 };
@@ -68,12 +73,18 @@ constexpr size_t kMaxTimed = 65536;
 Timer g_timer[kNumKernels];
 std::mutex g_timer_mu;
 
+// Runs launch(ev).  With the kernel's timer off (the normal case) no lock is
+// taken and no events are used.  With it on, the call takes the next event
+// pair; an event that no kernel took (a call that launched nothing, or fewer
+// kernels than the pair assumed) is recorded on the stream right away, so
+// every handed-out pair holds a valid interval.
 template <typename F>
-hipError_t timed(int kid, F&& launch) {
+hipError_t timed(int kid, hipStream_t st, F&& launch) {
+    Timer& t = g_timer[kid];
+    if (!t.on.load(std::memory_order_relaxed)) return launch(LaunchEvents{});
     hipEvent_t b = nullptr, e = nullptr;
     {
         std::lock_guard<std::mutex> lk(g_timer_mu);
-        Timer& t = g_timer[kid];
         if (t.on && t.used < kMaxTimed) {
             if (t.used == t.ev.size()) {
                 hipEvent_t x, y;
@@ -89,7 +100,11 @@ hipError_t timed(int kid, F&& launch) {
     LaunchEvents ev;
     ev.start = b;
     ev.stop = e;
-    return launch(ev);
+    g_events_used = 0;
+    hipError_t r = launch(ev);
+    if (b && !(g_events_used & 1u)) (void)hipEventRecord(b, st);
+    if (e && !(g_events_used & 2u)) (void)hipEventRecord(e, st);
+    return r;
 }
 
 // ---------------------------------------------------------------- validation
@@ -297,15 +312,16 @@ csl_status csl_timer_read(int32_t kid, double* total_ms, int64_t* launches) {
     std::lock_guard<std::mutex> lk(g_timer_mu);
     Timer& t = g_timer[kid];
     double sum = 0.0;
-    for (size_t i = 0; i < t.used; ++i) {
+    const size_t used = t.used;
+    t.used = 0;  // reset even if a query below fails, so later reads start clean
+    for (size_t i = 0; i < used; ++i) {
         float ms = 0.f;
         e = hipEventElapsedTime(&ms, t.ev[i].first, t.ev[i].second);
         if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
         sum += ms;
     }
     *total_ms = sum;
-    *launches = (int64_t)t.used;
-    t.used = 0;
+    *launches = (int64_t)used;
     return CSL_OK;
 }
 
@@ -371,7 +387,7 @@ csl_status csl_compress_insert_multi(int32_t n_jobs, const csl_insert_job* jobs,
     if (st || a.total_new == 0) return st;
     if ((st = device_error_ptr(&a.err))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_COMPRESS, [&](const LaunchEvents& ev) { return launch_compress(a, s, ev); });
+    hipError_t e = timed(CSL_KERNEL_COMPRESS, s, [&](const LaunchEvents& ev) { return launch_compress(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "compress_insert launch");
     return CSL_OK;
 }
@@ -442,7 +458,7 @@ csl_status csl_q_norm_rope_insert(const csl_pool* swa, const csl_pages* pages, c
     if (st || a.n_items == 0) return st;
     if ((st = device_error_ptr(&a.err))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_QSIDE, [&](const LaunchEvents& ev) { return launch_qside(a, s, ev); });
+    hipError_t e = timed(CSL_KERNEL_QSIDE, s, [&](const LaunchEvents& ev) { return launch_qside(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "q_norm_rope_insert launch");
     return CSL_OK;
 }
@@ -519,9 +535,9 @@ csl_status csl_index_topk(const csl_pool* index_pool, const csl_pages* pages, in
     if (st || a.num_q == 0) return st;
     if ((st = device_error_ptr(&a.err))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
+    hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, s, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
-    e = timed(CSL_KERNEL_TOPK_SELECT, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
+    e = timed(CSL_KERNEL_TOPK_SELECT, s, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "topk_select launch");
     return CSL_OK;
 }
@@ -561,14 +577,13 @@ csl_status csl_index_topk_insert(const csl_pool* index_pool, const csl_pages* pa
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (a.num_q > 0) {
-        e = timed(CSL_KERNEL_INDEX_SCORE, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
+        e = timed(CSL_KERNEL_INDEX_SCORE, s, [&](const LaunchEvents& ev) { return launch_index_score(a, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "index_score launch");
     }
     if (c.total_new == 0 && q.n_items == 0) {
-        if (a.num_q > 0) e = timed(CSL_KERNEL_TOPK_SELECT, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
+        if (a.num_q > 0) e = timed(CSL_KERNEL_TOPK_SELECT, s, [&](const LaunchEvents& ev) { return launch_topk_select(a, s, ev); });
     } else {
-        e = timed(CSL_KERNEL_TOPK_SELECT,
-                  [&](const LaunchEvents& ev) { return launch_topk_select_insert(a, c, q, s, ev); });
+        e = timed(CSL_KERNEL_TOPK_SELECT, s, [&](const LaunchEvents& ev) { return launch_topk_select_insert(a, c, q, s, ev); });
     }
     if (e != hipSuccess) return hip_fail(e, "topk_select / insert launch");
     return CSL_OK;
@@ -620,10 +635,10 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
         a.part_ml = a.part_o + (size_t)num_q * sp * n_heads * swa->dim;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_ATTN, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
+    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
     if (sp > 1) {
-        e = timed(CSL_KERNEL_ATTN_COMBINE, [&](const LaunchEvents& ev) { return launch_attn_combine(a, s, ev); });
+        e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&](const LaunchEvents& ev) { return launch_attn_combine(a, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
     }
     return CSL_OK;
@@ -653,7 +668,7 @@ csl_status csl_hybrid_attn_prefill(const csl_pool* comp, const csl_pool* swa, co
     a.n_splits = 1;
     a.tiles_per_split = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_ATTN, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
+    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
     return CSL_OK;
 }

@@ -265,8 +265,9 @@ __device__ __forceinline__ void store_slice(const Slice<D, KV>& sl, uint16_t* Kl
 }
 
 template <int D, int KV, bool PREC>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, D == 512 ? 1 : 4)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 hybrid_attn_kernel(AttnArgs a) {
+    static_assert(D == 128, "512-dim keys take hybrid_attn_mqa512_kernel; this kernel serves 128-dim keys");
     constexpr int KS = Cfg<D>::KS, MT = Cfg<D>::MT, KSTR = Cfg<D>::KSTR;
     constexpr bool SPLITKV = PREC && KV == kFP8;
     constexpr int NC = SPLITKV ? 2 : 1;
@@ -568,7 +569,7 @@ __global__ void __launch_bounds__(64 * NW) attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int d = 8 * lane + 2 * c;
-        if (d >= rbase) {
+        if (active && d >= rbase) {  // (a lane past the row has no pair: its index would leave the table)
             float cs, sn;
             rope_cs(-p, a.rf.inv_freq[(d - rbase) >> 1], cs, sn);
             float u = o[2 * c], v = o[2 * c + 1];
@@ -1277,9 +1278,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev
         else launch_kernel(ev, true, true, hybrid_attn_mqa512_kernel<false, true>, grid, dim3(kThreads), st, a);
         return hipGetLastError();
     }
-    if (a.dim == 512 && kv == kBF16) launch_prec<512, kBF16>(a, grid, st, ev);
-    else if (a.dim == 512 && kv == kFP8) launch_prec<512, kFP8>(a, grid, st, ev);
-    else if (a.dim == 128 && kv == kBF16) launch_prec<128, kBF16>(a, grid, st, ev);
+    // 128-dim keys (bf16 only: fp8 rows need dim % 256 == 0): the generic kernel
+    if (a.dim == 128 && kv == kBF16) launch_prec<128, kBF16>(a, grid, st, ev);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

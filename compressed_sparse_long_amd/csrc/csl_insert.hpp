@@ -39,12 +39,15 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
 }
 
 // Rotate the lane's 8 dims [d0, d0+8) at position `pos` (pairs in the last R dims).
-__device__ __forceinline__ void rope8(float* v, int d0, int dim, int rope_dims, const RopeFreqs& rf, int64_t pos) {
+// `active` = the lane owns dims (d0 < dim): a lane past the row rotates nothing,
+// so every frequency index stays below rope_dims / 2.
+__device__ __forceinline__ void rope8(float* v, int d0, int dim, int rope_dims, const RopeFreqs& rf, int64_t pos,
+                                      bool active) {
     int base = dim - rope_dims;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         int d = d0 + 2 * c;
-        if (d >= base) {
+        if (active && d >= base) {
             float cs, sn;
             rope_cs(pos, rf.inv_freq[(d - base) >> 1], cs, sn);
             float a = v[2 * c], b = v[2 * c + 1];
@@ -143,7 +146,7 @@ __device__ __forceinline__ void insert_block(const CompressArgs& args, int jb, i
         }
         float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (active) load8(a.x + (int64_t)j * D + 8 * lane, v);
-        rope8(v, 8 * lane, D, a.rope_dims, rf, t);
+        rope8(v, 8 * lane, D, a.rope_dims, rf, t, active);
         uint8_t* row = a.rows + ((int64_t)pg * kBlockPositions + (t & 255)) * a.row_bytes;
         store8(row, a.dtype, D, lane, active, v);
         return;
@@ -241,7 +244,7 @@ __device__ __forceinline__ void insert_block(const CompressArgs& args, int jb, i
         float g = (a.gain && active) ? a.gain[8 * lane + c] : 1.0f;
         u[c] = u[c] * inv * g;
     }
-    rope8(u, 8 * lane, D, a.rope_dims, rf, (int64_t)r * i);
+    rope8(u, 8 * lane, D, a.rope_dims, rf, (int64_t)r * i, active);
     int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, (int64_t)r * i);
     if (pg < 0) {
         if (lane == 0) raise_error(args.err, kErrPage);

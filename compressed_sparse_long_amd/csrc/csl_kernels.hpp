@@ -104,12 +104,20 @@ struct LaunchEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// Which events of the current timed call were handed to a kernel (bit 0:
+// start, bit 1: stop), so that the caller can record the ones no kernel took.
+extern thread_local unsigned g_events_used;
+
 template <typename F, typename... Args>
 inline void launch_kernel(const LaunchEvents& ev, bool first, bool last, F kernel, dim3 grid, dim3 block,
                           hipStream_t st, Args... args) {
     hipEvent_t b = first ? ev.start : nullptr, e = last ? ev.stop : nullptr;
-    if (b || e) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, b, e, 0, args...);
-    else hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    if (b || e) {
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, b, e, 0, args...);
+        g_events_used |= (b ? 1u : 0u) | (e ? 2u : 0u);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    }
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev = {});
