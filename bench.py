@@ -47,7 +47,7 @@ class DecodeSetup:
     """Pools, block table and step inputs of a decode workload, resident on the GPU."""
 
     def __init__(self, w, replicas: int, device="cuda", side_stream: bool = False, qside: bool = False,
-                 fused_inserts: bool = False):
+                 fused_inserts: bool = False, fused_call: bool = True):
         import torch
 
         import compressed_sparse_long_amd as csl
@@ -124,7 +124,11 @@ class DecodeSetup:
                                   device=device)
         ws4 = csl.hybrid_attn_workspace(nq, w.n_heads, D, 4, w.topk, w.swa, T) if "c4a" in w.layers else 0
         ws128 = csl.hybrid_attn_workspace(nq, w.n_heads, D, 128, 0, w.swa, T) if "c128a" in w.layers else 0
-        self.ws_attn = torch.empty(max(1, max(ws4, ws128) // 4), dtype=torch.float32, device=device)
+        self.ws_attn = torch.zeros(max(1, max(ws4, ws128) // 4), dtype=torch.float32, device=device)
+        # the two-launch step (index scores + inserts, then merge + attention): c4a layers with bf16 keys
+        self.fused = fused_call and "c4a" in w.layers and kv == 1
+        self.ws_fused = (csl.workspace(csl.index_attn_decode_workspace(nq, w.n_heads, T, w.topk, w.swa), device)
+                         if self.fused else None)
         odt = {0: torch.float32, 1: torch.bfloat16, 2: torch.uint8}[w.out_dtype]
         self.out = {l: torch.empty((nq, w.n_heads, D), dtype=odt, device=device) for l in w.layers}
         self.out_scales = {l: (torch.empty((nq, w.n_heads, D // 64), dtype=torch.float32, device=device)
@@ -153,11 +157,15 @@ class DecodeSetup:
         self.csl.compress_insert_multi(self.insert_jobs(p), self.bt, self.start, self.cu1)
 
     def step(self, r: int):
-        """One decode step.  By default the inserts ride in the indexer's top-k
-        launch (index_topk_insert; the query at p reads positions < p only).
-        Otherwise they go first in a launch of their own, or, with side streams,
-        beside the indexer and attention, forked from and joined back into the
-        current stream."""
+        """One decode step.  By default (c4a layers, bf16 keys) the step is the
+        two-launch call index_attn_decode: index scores with the raw and main
+        inserts riding in the score launch, then the candidates' merge and the
+        attention with the index insert riding in it (the query at p reads
+        positions < p only).  With --separate-calls the inserts ride in the
+        indexer's top-k launch (index_topk_insert) and attention is its own call;
+        or they go first in a launch of their own, or, with side streams, beside
+        the indexer and attention, forked from and joined back into the current
+        stream."""
         p, torch = self.reps[r], self.torch
         if self.fused_inserts and "c4a" in self.layers:
             self.attend(r, with_inserts=True)
@@ -180,7 +188,14 @@ class DecodeSetup:
         """The query side of a step: index top-k and attention of every layer
         (with_inserts: the step's inserts in the top-k launch)."""
         csl, w, p = self.csl, self.w, self.reps[r]
-        if "c4a" in self.layers:
+        if self.fused:
+            qs = (p["raw"], self.x_new, self.q_pre, self.gain_q, self.q) if (with_inserts and self.qside) else None
+            csl.index_attn_decode(p["idx"], p["main4"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos,
+                                  self.q_idx, self.w_idx, w.topk, self.topk, self.q, w.swa, self.scale, w.out_dtype,
+                                  self.out["c4a"], self.out_scales["c4a"],
+                                  self.insert_jobs(p) if with_inserts else (), self.start, self.cu1, None,
+                                  self.ws_fused, qside=qs)
+        elif "c4a" in self.layers:
             if with_inserts:
                 qs = (p["raw"], self.x_new, self.q_pre, self.gain_q, self.q) if self.qside else None
                 csl.index_topk_insert(p["idx"], self.bt, self.q_seq, self.q_pos, self.max_pos, self.q_idx, self.w_idx,
@@ -214,6 +229,14 @@ class DecodeSetup:
         if "c128a" in w.layers:
             per_q["c128a"] = (w.ctx // 128 + w.swa) * rb + qio + ins
         return {k: v * nq for k, v in per_q.items()}
+
+    def attention_bytes_per_launch(self, layer: str) -> int:
+        """Algorithmic bytes of one attention launch: the gathered key rows, q and the output."""
+        w = self.w
+        rb = self.csl.row_bytes(w.dim, w.kv_dtype)
+        ob = {0: 4 * w.dim, 1: 2 * w.dim, 2: w.dim + 4 * (w.dim // 64)}[w.out_dtype]
+        keys = (w.topk if layer == "c4a" else w.ctx // 128) + w.swa
+        return w.num_q * (keys * rb + w.n_heads * w.dim * 2 + w.n_heads * ob)
 
 
 class PrefillSetup:
@@ -621,6 +644,9 @@ def main():
                     help="run the inserts on a side stream beside the indexer and attention")
     ap.add_argument("--separate-inserts", action="store_true",
                     help="launch the inserts on their own before the indexer instead of inside its top-k launch")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="run the c4a step as index_topk_insert + hybrid_attn_decode instead of the two-launch "
+                         "index_attn_decode")
     ap.add_argument("--qside", action="store_true",
                     help="start the step from pre-norm query heads: the Q norm + RoPE + raw-key insert (in the top-k "
                          "launch with the other inserts, or its own launch with --separate-inserts) produces q and "
@@ -659,7 +685,8 @@ def main():
     w = {"c4a": W.c4a_decode, "c4a_fp4": W.c4a_decode_fp4, "c128a": W.c128a_decode, "1m": W.long_1m}[args.workload]()
     R = max(1, args.replicas)
     setup = DecodeSetup(w, R, side_stream=args.side_stream, qside=args.qside,
-                        fused_inserts=not args.separate_inserts)
+                        fused_inserts=not args.separate_inserts,
+                        fused_call=not (args.separate_calls or args.separate_inserts or args.side_stream))
     log(f"workload {w.name}: {w.num_seqs} x {w.ctx} tokens, {R} replicas")
 
     for i in range(args.warmup):
@@ -668,6 +695,11 @@ def main():
     assert csl.read_device_error() == 0, "device error flags after warm-up"
 
     timing_kernel = csl.KERNEL_INDEX_SCORE if "c4a" in w.layers else csl.KERNEL_ATTN
+    # every kernel of the step gets its own timer in the eager timing steps
+    step_kernels = {"index_score": csl.KERNEL_INDEX_SCORE, "topk_select": csl.KERNEL_TOPK_SELECT,
+                    "attention": csl.KERNEL_ATTN, "attn_combine": csl.KERNEL_ATTN_COMBINE}
+    if "c4a" not in w.layers:
+        step_kernels = {"attention": csl.KERNEL_ATTN, "attn_combine": csl.KERNEL_ATTN_COMBINE}
     graphs = None
     per_graph = 1
     if not args.no_graph:
@@ -692,7 +724,8 @@ def main():
         for i in range(K // per_graph):
             graphs[i % len(graphs)].replay()
     else:
-        csl.timer_enable(timing_kernel, True)
+        for kid in step_kernels.values():
+            csl.timer_enable(kid, True)
         for i in range(K):
             setup.step(i % R)
     torch.cuda.synchronize()
@@ -717,12 +750,16 @@ def main():
         # The kernel's own start/end stamps (hipExtLaunchKernel events) are not
         # kept by graph capture, so the dominant kernel's duration comes from
         # eager steps run right after the replays, on the same caches and stream.
-        csl.timer_enable(timing_kernel, True)
+        for kid in step_kernels.values():
+            csl.timer_enable(kid, True)
         for i in range(args.timing_steps):
             setup.step(i % R)
         torch.cuda.synchronize()
-    csl.timer_enable(timing_kernel, False)
-    k_ms, k_n = csl.timer_read(timing_kernel)
+    kern_times = {}
+    for name, kid in step_kernels.items():
+        csl.timer_enable(kid, False)
+        kern_times[name] = csl.timer_read(kid)
+    k_ms, k_n = kern_times["index_score" if "c4a" in w.layers else "attention"]
     assert csl.read_device_error() == 0, "device error flags after the timed steps"
     ms_per_step = (t1 - t0) * 1e3 / K
     qps = w.num_q / (ms_per_step * 1e-3)
@@ -739,6 +776,22 @@ def main():
             "timing": ("hipExtLaunchKernel start/stop events stamped by each launch of the kernel itself, over "
                        f"{k_n} eager steps right after the timed graph replays (graph capture drops the stamps)"
                        if graphs else "hipExtLaunchKernel start/stop events stamped by each launch in the timed steps")}
+    # one entry per step kernel: average duration, algorithmic bytes per launch and the
+    # fraction of the HBM peak they stand for (intermediate buffers are not counted)
+    kb = {"index_score": alg.get("index_score", 0),
+          # (the 1M workload's attention timer averages its two layers' launches: no byte figure)
+          "attention": (0 if len(w.layers) > 1 else setup.attention_bytes_per_launch(w.layers[0])),
+          "topk_select": 0, "attn_combine": 0}
+    kernels = {}
+    for name, (ms, n) in kern_times.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        e = {"avg_us": round(avg * 1e3, 2), "launches": n, "algorithmic_bytes_per_launch": kb[name]}
+        if kb[name]:
+            e["GBps"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
+            e["frac"] = round(kb[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        kernels[name] = e
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -752,11 +805,17 @@ def main():
                    "kv_dtype": {1: "bf16", 2: "fp8"}[w.kv_dtype],
                    "out_dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.out_dtype], "replicas": R,
                    "hip_graphs": bool(graphs), "steps_per_graph": per_graph, "insert_stream": "side" if args.side_stream else "main",
-                   "inserts": ("in the top-k launch" if setup.fused_inserts and "c4a" in w.layers else
+                   "inserts": ("raw + main in the score launch, index in the attention launch" if setup.fused else
+                               "in the top-k launch" if setup.fused_inserts and "c4a" in w.layers else
                                "own launch" + (" (side stream)" if args.side_stream else "")),
                    "query_side_in_step": bool(args.qside),
+                   "step_calls": ("index_attn_decode (2 launches)" if setup.fused else
+                                  "index_topk_insert + hybrid_attn_decode"),
                    "algorithmic_bytes_per_step": step_bytes},
         "roofline": roof,
+        "kernels": kernels,
+        "target": ("north star: the decode attention step (index top-k + hybrid attention) at >= 60% of the HBM "
+                   "peak: hbm_frac of the whole step; roofline.frac is the score kernel alone"),
     }
     if not args.no_cpu and w.layers == ("c4a",):
         log("timing the CPU oracle")

@@ -86,6 +86,10 @@ _attn_decode = _sig("csl_hybrid_attn_decode", C.c_int,
                      _vp])
 _attn_prefill = _sig("csl_hybrid_attn_prefill", C.c_int,
                      [_P, _P, _G, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp])
+_fused_ws = _sig("csl_index_attn_decode_workspace", _sz, [_i32, _i32, _i64, _i32, _i32])
+_fused = _sig("csl_index_attn_decode", C.c_int,
+              [_P, _P, _P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _f32, _i32,
+               _vp, _vp, _i32, C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, C.POINTER(_QSideJob), _vp, _sz, _vp])
 _last_error = _sig("csl_last_error", C.c_char_p, [])
 _read_dev_err = _sig("csl_read_device_error", C.c_int, [C.POINTER(C.c_uint32)])
 _timer_enable = _sig("csl_timer_enable", C.c_int, [_i32, _i32])
@@ -93,7 +97,8 @@ _timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.PO
 
 EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_q_norm_rope_insert",
            "csl_index_topk_workspace", "csl_index_topk", "csl_index_topk_insert",
-           "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill", "csl_last_error",
+           "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill",
+           "csl_index_attn_decode_workspace", "csl_index_attn_decode", "csl_last_error",
            "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
 
 
@@ -218,6 +223,41 @@ def index_topk_insert(pool: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w
 
 def hybrid_attn_workspace(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos) -> int:
     return int(_attn_ws(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace of at least `nbytes` (16-byte aligned): the
+    decode calls keep arrival counters in its first 16 KiB, which must start at zero."""
+    return torch.zeros(max(1, (int(nbytes) + 3) // 4), dtype=torch.float32, device=device)
+
+
+def index_attn_decode_workspace(num_q: int, n_heads: int, max_q_pos: int, k: int, swa_window: int) -> int:
+    return int(_fused_ws(num_q, n_heads, max_q_pos, k, swa_window))
+
+
+def index_attn_decode(index_pool: Pool, comp: Pool, swa: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k,
+                      topk, q, swa_window, softmax_scale, out_dtype, out, out_scales=None, jobs=(), start_pos=None,
+                      cu_new=None, kth_score=None, ws=None, eps=1e-6, qside=None, stream=None):
+    """index_topk_insert then hybrid_attn_decode in two launches (csl_index_attn_decode).  jobs and
+    qside as in index_topk_insert; ws from workspace(index_attn_decode_workspace(...))."""
+    ips, cs, ss = index_pool.struct(), comp.struct(), swa.struct()
+    pg = pages(block_table)
+    nq, nh = int(w.shape[0]), int(w.shape[1])
+    jobs = list(jobs)
+    structs = [p.struct() for p, _, _, _ in jobs]
+    arr = (_InsertJob * max(1, len(jobs)))(*[_InsertJob(C.addressof(structs[i]), _ptr(x), _ptr(lg), _ptr(g))
+                                             for i, (_, x, lg, g) in enumerate(jobs)])
+    qs, qsp = None, None
+    if qside is not None:
+        qswa, qx, qq, qg, qo = qside
+        qsp = qswa.struct()
+        qs = _QSideJob(C.addressof(qsp), _ptr(qx), _ptr(qq), int(qq.shape[1]), _ptr(qg), _ptr(qq if qo is None else qo))
+    total = int(jobs[0][1].shape[0]) if jobs else (int(qside[1].shape[0]) if qside is not None else 0)
+    _check(_fused(C.byref(ips), C.byref(cs), C.byref(ss), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos),
+                  _ptr(q_idx), _ptr(w), nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(q), int(q.shape[1]),
+                  int(swa_window), float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), len(jobs), arr,
+                  _ptr(start_pos), _ptr(cu_new), total, float(eps), None if qs is None else C.byref(qs), _ptr(ws),
+                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def hybrid_attn_decode(comp: Pool | None, swa: Pool, block_table, q_seq, q_pos, max_q_pos, q, topk, k, swa_window,

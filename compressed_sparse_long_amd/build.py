@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsl.so")
-SOURCES = ["api.hip", "compress.hip", "index_topk.hip", "attn.hip"]
+SOURCES = ["api.hip", "compress.hip", "index_topk.hip", "attn.hip", "decode_attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

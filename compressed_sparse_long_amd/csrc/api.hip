@@ -208,6 +208,61 @@ int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_
     return (int)(sp > 1 ? sp : 1);
 }
 
+// Decode attention on 512-dim bf16 keys (decode_attn_kernel): G head groups of
+// 16; the key list (rounded up to 32-key tiles) split so that the launch holds
+// about 256 workgroups, with 32..256 keys per split; at most 8 splits are
+// merged inside the launch by the last arriving split (more, or more than
+// kDecodeCounters (query, head group) pairs: partials for the combine kernel).
+struct DecodePlan {
+    int G, S, per, combine;
+};
+DecodePlan decode_plan(int num_q, int n_heads, int comp_ratio, int k, int swa_window, int64_t max_q_pos) {
+    DecodePlan pl;
+    pl.G = (n_heads + 15) / 16;
+    const int64_t keys = decode_tiles(comp_ratio, k, swa_window, max_q_pos) * 32;
+    const int64_t groups = (int64_t)(num_q > 0 ? num_q : 1) * pl.G;
+    const int64_t want = 256 / groups > 1 ? 256 / groups : 1;
+    auto round32 = [](int64_t x) { return (x + 31) / 32 * 32; };
+    int64_t per = round32((keys + want - 1) / want);
+    per = per < 32 ? 32 : (per > kDecodeMaxSplitKeys ? kDecodeMaxSplitKeys : per);
+    int64_t S = keys > 0 ? (keys + per - 1) / per : 1;
+    if (S > kDecodeMaxCombine && keys <= (int64_t)kDecodeMaxCombine * kDecodeMaxSplitKeys) {
+        per = round32((keys + kDecodeMaxCombine - 1) / kDecodeMaxCombine);
+        S = (keys + per - 1) / per;
+    }
+    pl.per = (int)per;
+    pl.S = (int)(S > 1 ? S : 1);
+    pl.combine = pl.S > 1 && pl.S <= kDecodeMaxCombine && groups <= kDecodeCounters;
+    return pl;
+}
+
+constexpr size_t kCounterBytes = (size_t)kDecodeCounters * sizeof(uint32_t);  // zero-on-entry block at ws offset 0
+
+// Bytes of split partials ([num_q][splits][n_heads][dim] fp32 and [..][2]).
+size_t partial_bytes(int num_q, int splits, int n_heads, int dim) {
+    return splits > 1 ? (size_t)num_q * splits * n_heads * ((size_t)dim + 2) * sizeof(float) : 0;
+}
+
+// Whether the decode call runs decode_attn_kernel (512-dim bf16 keys).
+bool use_decode_kernel(int dim, int key_dtype) { return dim == 512 && key_dtype == CSL_BF16; }
+
+// Workspace of a decode attention call: the counter block, then the partials
+// of the larger of the paths the key type could take (the key type is not an
+// argument of the query); 0 when no path needs partials.
+size_t attn_ws_bytes(int32_t num_q, int32_t n_heads, int32_t dim, int32_t comp_ratio, int32_t k, int32_t swa_window,
+                     int64_t max_q_pos) {
+    if (num_q <= 0 || n_heads <= 0 || dim <= 0) return 0;
+    const int sp8 = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos, true);
+    const int sp16 = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos, false);
+    size_t need = partial_bytes(num_q, sp8 > sp16 ? sp8 : sp16, n_heads, dim);
+    if (dim == 512) {
+        const DecodePlan pl = decode_plan(num_q, n_heads, comp_ratio, k, swa_window, max_q_pos);
+        const size_t b = partial_bytes(num_q, pl.S, n_heads, dim);
+        need = b > need ? b : need;
+    }
+    return need > 0 ? kCounterBytes + need : 0;
+}
+
 csl_status check_attn_common(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int n_heads,
                              const int32_t* topk, int k, int swa_window, int out_dtype, const void* out,
                              const float* out_scales, const uint16_t* q, int64_t max_q_pos, float softmax_scale) {
@@ -591,13 +646,7 @@ csl_status csl_index_topk_insert(const csl_pool* index_pool, const csl_pages* pa
 
 size_t csl_hybrid_attn_workspace(int32_t num_q, int32_t n_heads, int32_t dim, int32_t comp_ratio, int32_t k,
                                  int32_t swa_window, int64_t max_q_pos) {
-    if (num_q <= 0 || n_heads <= 0 || dim <= 0) return 0;
-    // (the larger of the two key types' split counts: the key type is not an argument)
-    const int sp8 = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos, true);
-    const int sp16 = decode_splits(num_q, comp_ratio, k, swa_window, max_q_pos, false);
-    const int sp = sp8 > sp16 ? sp8 : sp16;
-    if (sp <= 1) return 0;
-    return (size_t)num_q * sp * n_heads * ((size_t)dim + 2) * sizeof(float);
+    return attn_ws_bytes(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos);
 }
 
 csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int32_t num_q,
@@ -613,8 +662,6 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     if (!q_seq || !q_pos) return fail(CSL_EINVAL, "q_seq or q_pos is NULL");
     const int cr = comp ? comp->ratio : 0;
     const int kk = topk ? k : 0;
-    const int sp = decode_splits(num_q, cr, kk, swa_window, max_q_pos, swa->dtype == CSL_FP8_E4M3);
-    if ((int64_t)num_q * sp > 0x7fffffff) return fail(CSL_ERANGE, "grid too large");
     size_t need = csl_hybrid_attn_workspace(num_q, n_heads, swa->dim, cr, kk, swa_window, max_q_pos);
     if (need > 0 && (!ws || ws_bytes < need)) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     if (need > 0 && !aligned16(ws)) return fail(CSL_EALIGN, "ws is not 16-byte aligned");
@@ -628,17 +675,200 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     a.cu_q = nullptr;
     a.q_pos_start = nullptr;
     a.num_q = num_q;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    float* part = need > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
+    if (use_decode_kernel(swa->dim, swa->dtype)) {
+        const DecodePlan pl = decode_plan(num_q, n_heads, cr, kk, swa_window, max_q_pos);
+        if ((int64_t)(num_q * (int64_t)pl.S + 7) / 8 * 8 * pl.G > 0x7fffffff) return fail(CSL_ERANGE, "grid too large");
+        DecodeArgs d;
+        d.at = a;
+        d.G = pl.G;
+        d.S = pl.S;
+        d.per = pl.per;
+        d.combine = pl.combine;
+        d.cnt = static_cast<uint32_t*>(ws);
+        d.cand = nullptr;
+        d.c_next = nullptr;
+        d.scores = nullptr;
+        d.stride = 0;
+        d.nchunks = 0;
+        d.kl = 0;
+        d.topk_out = nullptr;
+        d.kth = nullptr;
+        d.at.n_splits = pl.S;
+        if (pl.S > 1) {
+            d.at.part_o = part;
+            d.at.part_ml = part + (size_t)num_q * pl.S * n_heads * swa->dim;
+        }
+        CompressArgs none;
+        none.total_new = 0;
+        none.n_jobs = 0;
+        e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_decode_attn(d, none, s, ev); });
+        if (e != hipSuccess) return hip_fail(e, "decode_attn launch");
+        if (pl.S > 1 && !pl.combine) {
+            e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&](const LaunchEvents& ev) { return launch_attn_combine(d.at, s, ev); });
+            if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
+        }
+        return CSL_OK;
+    }
+    const int sp = decode_splits(num_q, cr, kk, swa_window, max_q_pos, swa->dtype == CSL_FP8_E4M3);
+    if ((int64_t)num_q * sp > 0x7fffffff) return fail(CSL_ERANGE, "grid too large");
     a.n_splits = sp;
     a.tiles_per_split = (decode_tiles(cr, kk, swa_window, max_q_pos) + sp - 1) / sp;
     if (sp > 1) {
-        a.part_o = static_cast<float*>(ws);
+        a.part_o = part;
         a.part_ml = a.part_o + (size_t)num_q * sp * n_heads * swa->dim;
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
+    e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_attn(a, s, ev); });
     if (e != hipSuccess) return hip_fail(e, "hybrid_attn launch");
     if (sp > 1) {
         e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&](const LaunchEvents& ev) { return launch_attn_combine(a, s, ev); });
+        if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
+    }
+    return CSL_OK;
+}
+
+// Workspace of csl_index_attn_decode: [counters | attention partials | index scores and candidates].
+size_t fused_attn_part(int32_t num_q, int32_t n_heads, int64_t max_q_pos, int32_t k, int32_t swa_window) {
+    const DecodePlan pl = decode_plan(num_q, n_heads, 4, k, swa_window, max_q_pos);
+    return kCounterBytes + (partial_bytes(num_q, pl.S, n_heads, 512) + 255) / 256 * 256;
+}
+
+size_t csl_index_attn_decode_workspace(int32_t num_q, int32_t n_heads, int64_t max_q_pos, int32_t k,
+                                       int32_t swa_window) {
+    if (num_q <= 0 || n_heads <= 0 || max_q_pos < 0 || k < 1) return 0;
+    return fused_attn_part(num_q, n_heads, max_q_pos, k, swa_window) + csl_index_topk_workspace(num_q, max_q_pos, k);
+}
+
+csl_status csl_index_attn_decode(const csl_pool* index_pool, const csl_pool* comp, const csl_pool* swa,
+                                 const csl_pages* pages, int32_t num_q, const int32_t* q_seq, const int64_t* q_pos,
+                                 int64_t max_q_pos, const uint16_t* q_idx, const float* w, int32_t n_idx_heads,
+                                 int32_t k, int32_t* topk, float* kth_score, const uint16_t* q, int32_t n_heads,
+                                 int32_t swa_window, float softmax_scale, int32_t out_dtype, void* out,
+                                 float* out_scales, int32_t n_jobs, const csl_insert_job* jobs,
+                                 const int64_t* start_pos, const int32_t* cu_new, int32_t total_new, float eps,
+                                 const csl_qside_job* qside, void* ws, size_t ws_bytes, csl_stream_t stream) {
+    csl_status st;
+    if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
+    if (!comp) return fail(CSL_EINVAL, "the fused decode call needs the compressed pool");
+    if ((st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
+                                max_q_pos, softmax_scale)))
+        return st;
+    if (comp->ratio != 4) return fail(CSL_EINVAL, "comp.ratio must be 4: the indexer selects c4a entries");
+    if (!use_decode_kernel(swa->dim, swa->dtype))
+        return fail(CSL_EUNSUPPORTED, "the fused decode call takes 512-dim bf16 keys (fp8 keys: index_topk + hybrid_attn_decode)");
+    if (!topk) return fail(CSL_EINVAL, "topk is NULL");
+    const size_t need = csl_index_attn_decode_workspace(num_q, n_heads, max_q_pos, k, swa_window);
+    if (num_q > 0 && (!ws || ws_bytes < need)) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (ws && !aligned16(ws)) return fail(CSL_EALIGN, "ws is not 16-byte aligned");
+    const size_t attn_part = num_q > 0 ? fused_attn_part(num_q, n_heads, max_q_pos, k, swa_window) : 0;
+    IndexArgs ia;
+    CompressArgs c;
+    QSideArgs qa;
+    if ((st = prepare_index(index_pool, pages, num_q, q_seq, q_pos, max_q_pos, q_idx, w, n_idx_heads, k, topk,
+                            kth_score, num_q > 0 ? static_cast<uint8_t*>(ws) + attn_part : nullptr,
+                            num_q > 0 ? ws_bytes - attn_part : 0, ia)))
+        return st;
+    c.total_new = 0;
+    c.n_jobs = 0;
+    if (n_jobs != 0) {
+        if ((st = prepare_inserts(n_jobs, jobs, pages, start_pos, cu_new, total_new, eps, c))) return st;
+    }
+    // inserts into the index pool ride in the attention launch, which never reads index rows;
+    // the others (raw window, main) ride in the score launch, which reads only index rows
+    CompressArgs ci;
+    ci.total_new = 0;
+    ci.n_jobs = 0;
+    if (c.total_new > 0) {
+        ci = c;
+        int nk = 0, ni = 0;
+        for (int i = 0; i < c.n_jobs; ++i) {
+            const bool to_index = jobs[i].pool->rows == index_pool->rows;
+            CompressArgs& dst = to_index ? ci : c;
+            int& m = to_index ? ni : nk;
+            dst.job[m] = c.job[i];
+            dst.rf[m] = c.rf[i];
+            ++m;
+        }
+        c.n_jobs = nk;
+        ci.n_jobs = ni;
+        if (nk == 0) c.total_new = 0;
+        if (ni == 0) ci.total_new = 0;
+        if (ia.num_q == 0 && ni > 0) {  // no attention launch to carry them
+            for (int i = 0; i < ni; ++i) {
+                c.job[c.n_jobs] = ci.job[i];
+                c.rf[c.n_jobs] = ci.rf[i];
+                ++c.n_jobs;
+            }
+            c.total_new = ci.total_new;
+            ci.total_new = 0;
+            ci.n_jobs = 0;
+        }
+    }
+    qa.n_items = 0;
+    if (qside && (st = prepare_qside(qside->swa, pages, start_pos, cu_new, total_new, qside->x, qside->q,
+                                     qside->n_heads, qside->q_gain, eps, qside->q_out, qa)))
+        return st;
+    if (qside) {
+        for (int i = 0; i < n_jobs; ++i)
+            if (jobs[i].pool->rows == qside->swa->rows)
+                return fail(CSL_EINVAL, "job %d inserts into the query side's raw pool", i);
+    }
+    if (ia.num_q == 0 && c.total_new == 0 && ci.total_new == 0 && qa.n_items == 0) return CSL_OK;
+    uint32_t* err = nullptr;
+    if ((st = device_error_ptr(&err))) return st;
+    ia.err = err;
+    c.err = err;
+    ci.err = err;
+    qa.err = err;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(CSL_KERNEL_INDEX_SCORE, s, [&](const LaunchEvents& ev) {
+        return launch_index_score_insert(ia, c, qa, s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(e, "index_score launch");
+    if (ia.num_q == 0) return CSL_OK;
+    const bool merge = ia.kl > 0 && !ia.tiled;
+    if (!merge) {
+        // no first-stage candidates (short rows or many queries): the full select, then attention on its ids
+        e = timed(CSL_KERNEL_TOPK_SELECT, s, [&](const LaunchEvents& ev) { return launch_topk_select(ia, s, ev); });
+        if (e != hipSuccess) return hip_fail(e, "topk_select launch");
+    }
+    AttnArgs a;
+    fill_attn(a, comp, swa, pages, n_heads, topk, k, swa_window, softmax_scale, out_dtype, out, out_scales, q,
+              max_q_pos, err);
+    a.q_seq = q_seq;
+    a.q_pos = q_pos;
+    a.cu_q = nullptr;
+    a.q_pos_start = nullptr;
+    a.num_q = num_q;
+    const DecodePlan pl = decode_plan(num_q, n_heads, 4, k, swa_window, max_q_pos);
+    DecodeArgs d;
+    d.at = a;
+    d.G = pl.G;
+    d.S = pl.S;
+    d.per = pl.per;
+    d.combine = pl.combine;
+    d.cnt = static_cast<uint32_t*>(ws);
+    d.cand = merge ? ia.cand : nullptr;
+    d.c_next = ia.c_next;
+    d.scores = ia.scores;
+    d.stride = ia.stride;
+    d.nchunks = ia.nchunks;
+    d.kl = ia.kl;
+    d.topk_out = topk;
+    d.kth = kth_score;
+    if (merge) d.at.topk = nullptr;  // the ids come from the merge in the launch
+    d.at.n_splits = pl.S;
+    if (pl.S > 1) {
+        float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
+        d.at.part_o = part;
+        d.at.part_ml = part + (size_t)num_q * pl.S * n_heads * 512;
+    }
+    e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_decode_attn(d, ci, s, ev); });
+    if (e != hipSuccess) return hip_fail(e, "decode_attn launch");
+    if (pl.S > 1 && !pl.combine) {
+        e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&](const LaunchEvents& ev) { return launch_attn_combine(d.at, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
     }
     return CSL_OK;

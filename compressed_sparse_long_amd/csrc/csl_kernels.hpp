@@ -96,6 +96,29 @@ struct AttnArgs {
     RopeFreqs rf;
 };
 
+// Decode attention over 512-dim bf16 keys (decode_attn_kernel): the attention
+// arguments plus the work split and, when the launch also merges the
+// indexer's first-stage candidates, where they are.
+constexpr int kDecodeMaxSplitKeys = 256;  // keys of one split (8 tiles of 32)
+constexpr int kDecodeMaxCombine = 8;      // splits merged in the launch by the last arriver
+constexpr int kDecodeCounters = 4096;     // arrival counters at the start of the workspace (16 KiB)
+struct DecodeArgs {
+    AttnArgs at;
+    int G;        // head groups of 16
+    int S;        // key splits per (query, head group)
+    int per;      // keys per split (multiple of 32, <= kDecodeMaxSplitKeys)
+    int combine;  // S > 1: 1 = the last-arriving split merges (counters), 0 = partials for attn_combine_kernel
+    uint32_t* cnt;  // [num_q * G] arrival counters, zero on entry and left zero
+    // merge of first-stage candidates (the fused index + attention call); null cand = ids from at.topk
+    const uint2* cand;    // [num_q][nchunks][kl]
+    const uint2* c_next;  // [num_q][nchunks]
+    const float* scores;  // [num_q][stride]
+    int64_t stride;
+    int nchunks, kl;
+    int32_t* topk_out;  // [num_q][k] the merged top-k
+    float* kth;         // [num_q] or null
+};
+
 // Events of a timed launch.  A launcher hands `start` to the first kernel it
 // starts and `stop` to the last; the runtime stamps them with those kernels'
 // own begin and end times (no marker packets in the queue), so the interval
@@ -123,11 +146,15 @@ inline void launch_kernel(const LaunchEvents& ev, bool first, bool last, F kerne
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_qside(const QSideArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+hipError_t launch_index_score_insert(const IndexArgs& a, const CompressArgs& c, const QSideArgs& q, hipStream_t st,
+                                     const LaunchEvents& ev = {});
 hipError_t launch_topk_select(const IndexArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_topk_select_insert(const IndexArgs& a, const CompressArgs& c, const QSideArgs& q, hipStream_t st,
                                      const LaunchEvents& ev = {});
 bool index_use_tiled(int num_q);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEvents& ev = {});
+// c: inserts riding as extra workgroups (c.total_new = 0: none)
+hipError_t launch_decode_attn(const DecodeArgs& d, const CompressArgs& c, hipStream_t st, const LaunchEvents& ev = {});
 
 }  // namespace csl

@@ -1,0 +1,601 @@
+// Steps 4-6 for decode queries on gfx950, 512-dim bf16 keys: hybrid attention
+// over (top-k or every visible compressed entry) U raw window [p-S, p-1] with
+// one softmax and K = V ([Summary] 共享鍵和值向量, 短滑動窗口; [Notes] ⚠️ 注意：
+// C128A 的因果性约束), inverse RoPE at the query position and the output store
+// (fp32 / bf16 / fp8 + scales) as the epilogue ([Notes] Inverse RoPE 的数学原理,
+// 融合 2：Inverse RoPE + FP8 Quant).  Optionally the launch first merges the
+// indexer's first-stage candidates into the top-k ([Summary] DeepSeek V4 注意力
+// 架構: DSA), so that index scores -> top-k -> attention is two launches.
+//
+// Why this shape.  A decode step has few queries (16 in the 128K workload),
+// each with 640 keys of 1 KiB, and one workgroup gathers random rows at only
+// ~85 GB/s, so a query's keys are split over several workgroups.  With all 64
+// heads in one workgroup a split's fp32 partial (64 x 512 x 4 B) is larger
+// than the keys it read; so a workgroup takes 16 heads (one MFMA column
+// block) and a contiguous share of the key list, and its partial is 32 KiB.
+// Kernel boundaries and agent-scope fences each cost microseconds here, so
+// the splits are merged inside the launch: every split writes its partial
+// with device-coherent stores, waits for them, and counts itself in on an
+// arrival counter; the last of a (query, head group) reads the others'
+// partials with device-coherent loads and finishes the output.  Nothing
+// waits on another workgroup.
+//
+// Work mapping.  Workgroup = (query n, head group hg of 16 heads, split sp of
+// `per` keys); the G head groups of one (n, sp) get block indices equal mod 8
+// so that their shared key rows meet in one L2.  Wave w owns output dims
+// 128w .. 128w+127 and the same slice of every dot product.  Per 32-key tile
+// (staged by direct global->LDS loads in a 4-slot ring, three tiles in
+// flight):
+//   * S^T[32 keys x 16 heads] over the wave's 128 dims on
+//     v_mfma_f32_16x16x32_bf16 (A = key rows, LDS; B = the wave's q slice,
+//     registers); the four waves' partial sums meet in LDS and every wave
+//     adds them in the same order, so all hold the same S;
+//   * online softmax per head in the exp2 domain with a lazy reference max
+//     (rescale only when the max passes it by more than 8);
+//   * O^T[128 dims x 16 heads] += V^T . P^T: B = P straight from the S
+//     accumulator, A = V^T by transposing LDS reads (ds_read_b64_tr_b16) of
+//     the row-major tile.  Accumulator row a of S^T m-tile mt holds the key
+//     in LDS row 16 mt + 4 (a % 4) + a / 4 of the tile, which is the key
+//     order the transposed reads produce, and keeps both the S operand reads
+//     and the transposed reads free of bank conflicts (1040-byte rows).
+#include "csl_insert.hpp"
+#include "csl_select.hpp"
+
+namespace csl {
+
+namespace {
+
+constexpr int kDT = 256;           // threads per workgroup (4 waves)
+constexpr int kDTile = 32;         // keys per tile
+constexpr int kDRow = 1040;        // LDS stride of a staged 1 KiB row (260 words: 4 banks apart)
+constexpr int kDRing = 4;          // ring slots: one computed, up to three in flight
+constexpr int kDBt = 2048;         // block-table entries staged in LDS (contexts up to 512K positions)
+constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer descriptor word 3 (untyped dword access)
+constexpr int kSc1 = 16;                      // cache policy: device scope (coherent across the XCDs' L2s)
+
+// Source of masked key rows (zeros) and of q rows of heads past n_heads.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row512[1024];
+
+__device__ __forceinline__ void dma_row(uint32_t lds, const uint8_t* src) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)p);
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 tr_read(const uint8_t* p) {
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v*)(const_cast<uint8_t*>(p)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Writes the merged top-k: every position to the global row (when this
+// workgroup is the writer) and positions [lo, lo + cnt) to the workgroup's LDS slice.
+struct SliceOut {
+    int32_t* g;
+    int32_t* lds;
+    uint32_t lo, cnt;
+    __device__ __forceinline__ void operator()(uint32_t pos, int32_t id) const {
+        if (g) g[pos] = id;
+        if (pos - lo < cnt) lds[pos - lo] = id;
+    }
+};
+
+// Workgroups past the attention's take one (new token, pool) insert each of
+// `c` (the fused call's index-pool inserts: this launch never reads index rows).
+// MERGE: 0 = ids given (or dense); 1 / 2 = the workgroup merges the first-stage
+// candidates, 8 / 16 slots per thread (up to 2048 / 4096 slots).
+template <bool PREC, int MERGE>
+__global__ void __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_attn_kernel(DecodeArgs d, CompressArgs c) {
+    constexpr int D = 512;
+    constexpr int kBtPer = kDBt / kDT;  // block-table entries staged per thread
+    const AttnArgs& a = d.at;
+    // ring of staged key tiles; before the first tile it holds the merge's
+    // scratch, after the last one the epilogue's staging
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDRing * kDTile * kDRow];
+    static_assert(sizeof(InsertSmem) <= sizeof(s_ring), "the insert body fits the ring");
+    const int64_t n_attn = ((int64_t)a.num_q * d.S + 7) / 8 * 8 * d.G;
+    if ((int64_t)blockIdx.x >= n_attn) {
+        const int64_t i = (int64_t)blockIdx.x - n_attn;
+        if (i < (int64_t)c.total_new * c.n_jobs)
+            insert_block(c, (int)(i / c.total_new), (int)(i % c.total_new), *reinterpret_cast<InsertSmem*>(s_ring));
+        return;
+    }
+    __shared__ __attribute__((aligned(16))) f32x4 s_sx[2][4][2][64];  // S^T partials: [tile parity][wave][m-tile]
+    __shared__ const uint8_t* s_rows[kDecodeMaxSplitKeys];
+    __shared__ uint32_t s_vbits[kDecodeMaxSplitKeys / 32];
+    __shared__ int32_t s_ids[MERGE ? kDecodeMaxSplitKeys : 1];
+    __shared__ int32_t s_bt[kDBt];
+    __shared__ float s_rope[2][64];
+    __shared__ uint32_t s_flag;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+
+    // block -> (n, hg, sp); blocks 8G b .. 8G b + 8G - 1 hold pairs (n, sp) = 8b .. 8b + 7, head group
+    // by block / 8 within that range
+    const int B8 = 8 * d.G;
+    const int ublk = blockIdx.x / B8, rem = blockIdx.x - ublk * B8;
+    const int hg = rem >> 3;
+    const int u = ublk * 8 + (rem & 7);
+    const int n = u / d.S, sp = u - n * d.S;
+    if (n >= a.num_q) return;  // padding of the last block of eight pairs
+
+    const int head = 16 * hg + r16;
+    const bool hv = head < a.n_heads;
+    // the query (wave-uniform)
+    int s = __builtin_amdgcn_readfirstlane(a.q_seq[n]);
+    const int64_t p_raw = a.q_pos[n];
+    const int64_t p_in = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)((uint64_t)p_raw >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p_raw));
+    const bool ok = s >= 0 && s < a.num_seqs && p_in >= 0 && p_in <= a.max_q_pos;
+    if (!ok && hg == 0 && sp == 0 && tid == 0) raise_error(a.err, (s < 0 || s >= a.num_seqs) ? kErrSeq : kErrPos);
+    if (!ok) s = 0;
+    const int64_t p = ok ? p_in : 0;
+    const int64_t nv_c = (ok && a.comp_rows) ? p / a.comp_ratio : 0;
+    const int64_t Lc = a.comp_rows ? (a.topk || MERGE ? (int64_t)a.k : nv_c) : 0;
+    const int64_t lo = p - a.swa_window > 0 ? p - a.swa_window : 0;
+    const int64_t L = ok ? Lc + (p - lo) : 0;
+    const int64_t kb = (int64_t)sp * d.per;
+    const int64_t ke = kb + d.per < L ? kb + d.per : L;
+    const int64_t kce = ke < Lc ? ke : Lc;
+    const int nk = ke > kb ? (int)(ke - kb) : 0;     // keys of this split
+    const int nkc = kce > kb ? (int)(kce - kb) : 0;  // of them compressed
+
+    // every independent load first: q slice, the query's block-table row, the
+    // candidates (merge) or the given ids
+    // q slice of the wave as the B operand of S^T: column = head, k-step ks = dims 128 wave + 32 ks + 8 g .. +7
+    bf16x8 qb[4];
+    {
+        const uint16_t* qrow = (hv ? a.q + ((int64_t)n * a.n_heads + head) * D
+                                   : reinterpret_cast<const uint16_t*>(g_zero_row512)) + 128 * wave + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    }
+    const int64_t nbt64 = ok ? ((p + 255) >> 8 < (int64_t)a.max_blocks ? (p + 255) >> 8 : (int64_t)a.max_blocks) : 0;
+    const bool staged = nbt64 <= kDBt;
+    int32_t btv[kBtPer];
+    {
+        const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
+#pragma unroll
+        for (int i = 0; i < kBtPer; ++i) {
+            const int b = i * kDT + tid;
+            btv[i] = (staged && b < (int)nbt64) ? btrow[b] : -1;
+        }
+    }
+    MergeIn in;
+    in.nv = ok ? (p >> 2 < d.stride ? p >> 2 : d.stride) : 0;
+    in.sc = d.scores + (int64_t)n * d.stride;
+    in.cand = d.cand + (int64_t)n * d.nchunks * d.kl;
+    in.cnext = d.c_next + (int64_t)n * d.nchunks;
+    in.kl = d.kl;
+    in.k = a.k;
+    int32_t pre_id = -1;
+    if (!MERGE && a.topk && tid < nkc) pre_id = a.topk[(int64_t)n * a.k + kb + tid];
+
+#pragma unroll
+    for (int i = 0; i < kBtPer; ++i)
+        if (i * kDT + tid < (int)nbt64 && staged) s_bt[i * kDT + tid] = btv[i];
+    if (tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
+
+    if constexpr (MERGE > 0) {
+        // the top-k of the query from the first-stage candidates: every workgroup of the query
+        // runs the same deterministic merge; (hg 0, split 0) writes the top-k row and kth
+        uint32_t* sm = reinterpret_cast<uint32_t*>(s_ring);
+        const MergeLds m = {sm, sm + 2048, sm + 2048 + kCandCap, sm + 2048 + kCandCap + 4,
+                            reinterpret_cast<float*>(sm + 2048 + kCandCap + 16), sm + 2048 + kCandCap + 20};
+        const bool writer = hg == 0 && sp == 0;
+        const SliceOut out = {writer ? d.topk_out + (int64_t)n * a.k : nullptr, s_ids, (uint32_t)kb, (uint32_t)nkc};
+        float* kthp = writer && d.kth ? d.kth + n : nullptr;
+        if (in.nv <= a.k) {
+            select_all(in.sc, in.nv, a.k, out, kthp, m.min);
+        } else if constexpr (MERGE == 1) {
+            merge_candidates<kDT, 8>(in, out, kthp, m);
+        } else {
+            merge_candidates<kDT, 16>(in, out, kthp, m);
+        }
+    }
+    __syncthreads();  // s_bt, s_ids, s_rope; the merge is done with the ring
+
+    // the split's key rows: thread t resolves key kb + t
+    {
+        const uint8_t* row = nullptr;
+        if (tid < nk) {
+            const int64_t j = kb + tid;
+            int32_t pg = -1;
+            int64_t slot = 0;
+            const uint8_t* base = nullptr;
+            int per_page = 0, np = 0;
+            int64_t blk = -1;
+            if (j < Lc) {
+                const int64_t id = MERGE ? (int64_t)s_ids[tid] : (a.topk ? (int64_t)pre_id : j);
+                if (id >= nv_c) raise_error(a.err, kErrTopk);
+                if (id >= 0 && id < nv_c) {
+                    per_page = kBlockPositions / a.comp_ratio;
+                    blk = id / per_page;
+                    slot = id - blk * per_page;
+                    base = a.comp_rows;
+                    np = a.comp_pages;
+                }
+            } else {
+                const int64_t t = lo + (j - Lc);
+                blk = t >> 8;
+                slot = t & 255;
+                per_page = kBlockPositions;
+                base = a.swa_rows;
+                np = a.swa_pages;
+            }
+            if (blk >= 0) {
+                pg = blk < a.max_blocks ? (staged ? s_bt[blk] : a.bt[(int64_t)s * a.max_blocks + blk]) : -1;
+                if (pg < 0 || pg >= np) raise_error(a.err, kErrPage);
+                else row = base + ((int64_t)pg * per_page + slot) * (2 * D);
+            }
+        }
+        s_rows[tid] = row ? row : g_zero_row512;
+        const uint64_t bits = __ballot(row != nullptr);
+        if (lane == 0) {
+            s_vbits[2 * wave] = (uint32_t)bits;
+            s_vbits[2 * wave + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+    __syncthreads();
+
+    const int ntl = __builtin_amdgcn_readfirstlane((nk + kDTile - 1) / kDTile);
+    auto tile = [&](int t) { return s_ring + (t & (kDRing - 1)) * (kDTile * kDRow); };
+    auto issue = [&](int t) {
+        uint8_t* slot = s_ring + (t & (kDRing - 1)) * (kDTile * kDRow);
+        const uint8_t* src[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) src[i] = s_rows[t * kDTile + 8 * wave + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma_row(lds_off(slot + (8 * wave + i) * kDRow), src[i] + 16 * lane);
+    };
+    // the q loads retire here: the compiler's own wait for them would otherwise sit
+    // inside the tile loop and, counting the tiles' loads too, drain every tile in flight
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qb[ks]));
+    for (int t = 0; t < 3 && t < ntl; ++t) issue(t);
+
+    f32x4 oacc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    // S operand row of this lane (accumulator row r16 of an m-tile) and the
+    // transposed-read row (k-slot group g: LDS rows 4 i + g, + 16 for slots 4..7)
+    const int s_row = 4 * (r16 & 3) + (r16 >> 2);
+    const int tr_row = 4 * (r16 >> 2) + g;
+    const int tr_col = (128 * wave + 4 * (r16 & 3)) * 2;  // bytes, + 32 per m-tile of 16 dims
+
+    // the wave's S^T partial of tile t (two 16-key m-tiles over its 128 dims): operand reads, then MFMAs
+    auto s_reads = [&](int t, bf16x8 (&av)[2][4]) {
+        const uint8_t* kt = tile(t);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const uint8_t* ka = kt + (16 * mt + s_row) * kDRow + (128 * wave + 8 * g) * 2;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) av[mt][ks] = *reinterpret_cast<const bf16x8*>(ka + 64 * ks);
+        }
+    };
+    auto s_mfma = [&](const bf16x8 (&av)[2][4], f32x4 (&sa)[2]) {
+        sa[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sa[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) sa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][ks], qb[ks], sa[mt], 0, 0, 0);
+    };
+
+    if (ntl > 0) {
+        // tile 0's S partial before the loop
+        if (ntl >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (ntl == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        bf16x8 av[2][4];
+        f32x4 sa[2];
+        s_reads(0, av);
+        s_mfma(av, sa);
+        s_sx[0][wave][0][lane] = sa[0];
+        s_sx[0][wave][1][lane] = sa[1];
+    }
+    // iteration t: the softmax and P.V of tile t beside the S partial of tile t+1; one barrier:
+    // tile t+1 is in LDS, the partials of tile t are complete, tile t-1's slot is free
+    for (int t = 0; t < ntl; ++t) {
+        const bool next = t + 1 < ntl;
+        if (next) {
+            // tiles issued so far: min(ntl, t + 3); tile t+1 must have landed
+            if (t + 3 < ntl) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        if (t + 3 < ntl) issue(t + 3);
+        const int par = t & 1;
+        f32x4 sf[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            sf[mt] = ((s_sx[par][0][mt][lane] + s_sx[par][1][mt][lane]) + s_sx[par][2][mt][lane]) + s_sx[par][3][mt][lane];
+        bf16x8 av[2][4];
+        if (next) s_reads(t + 1, av);
+
+        // softmax: value (mt, i) is the key in LDS row 16 mt + 4 i + g of this head column
+        const uint32_t vb = s_vbits[t];
+        float x[8];
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+            const int mt = cc >> 2, i = cc & 3;
+            x[cc] = ((vb >> (16 * mt + 4 * i + g)) & 1u) ? sf[mt][i] : -INFINITY;
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) tmax = fmaxf(tmax, x[cc]);
+        tmax = max_xor32(max_xor16(tmax)) * a.scale_log2;
+        const bool move = tmax > m_ref + 8.0f;
+        const float alpha = __builtin_amdgcn_exp2f(move ? m_ref - tmax : 0.f);
+        const bool rescale = move && m_ref != -INFINITY;
+        l_run *= alpha;
+        m_ref = move ? tmax : m_ref;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float pf[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+            pf[cc] = __builtin_amdgcn_exp2f(fmaf(x[cc], a.scale_log2, -m_use));
+            psum += pf[cc];
+        }
+        l_run += psum;
+        uint32_t pw[4], pl[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            pw[cc] = pack_bf16x2(pf[2 * cc], pf[2 * cc + 1]);
+            if constexpr (PREC)
+                pl[cc] = pack_bf16x2(pf[2 * cc] - bf16_bits_to_f32(pw[cc] & 0xffffu),
+                                     pf[2 * cc + 1] - bf16_bits_to_f32(pw[cc] >> 16));
+        }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        bf16x8 plo = pb;
+        if constexpr (PREC) plo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+
+        f32x4 sa[2];
+        if (next) s_mfma(av, sa);
+
+        // O^T += V^T . P^T over the wave's 8 m-tiles of 16 dims
+        if (__ballot(rescale)) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
+        }
+        const uint8_t* kt = tile(t);
+        bf16x8 va[8];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+            const uint8_t* b0 = kt + tr_row * kDRow + tr_col + 32 * mm;
+            const u32x2 v0 = tr_read(b0), v1 = tr_read(b0 + 16 * kDRow);
+            va[mm] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        }
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+            oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], pb, oacc[mm], 0, 0, 0);
+            if constexpr (PREC) oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], plo, oacc[mm], 0, 0, 0);
+        }
+        if (next) {
+            s_sx[par ^ 1][wave][0][lane] = sa[0];
+            s_sx[par ^ 1][wave][1][lane] = sa[1];
+        }
+    }
+    // the head's sum over its four lanes (every wave holds the same softmax)
+    float l_tot = sum_xor16(l_run);
+    l_tot = sum_xor32(l_tot);
+
+    const int S = d.S;
+    bool last = true;
+    uint32_t* cnt = d.cnt + (int64_t)n * d.G + hg;
+    if (S > 1) {
+        const int64_t H = a.n_heads;
+        if (!d.combine) {
+            // partials for attn_combine_kernel: [n][S][H][D] fp32 and [n][S][H][2]
+            if (hv) {
+                float* po = a.part_o + (((int64_t)n * S + sp) * H + head) * D + 128 * wave + 4 * g;
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm) __builtin_nontemporal_store(oacc[mm], reinterpret_cast<f32x4*>(po + 16 * mm));
+                if (wave == 0 && g == 0) {
+                    float* ml = a.part_ml + (((int64_t)n * S + sp) * H + head) * 2;
+                    ml[0] = m_ref;
+                    ml[1] = l_tot;
+                }
+            }
+            return;
+        }
+        // this split's partial with device-scope stores (coherent across the XCDs' L2s), relative
+        // to the group's base: split x, head row h, dim c at ((x H + h) D + c) * 4 bytes
+        float* gbase_o = a.part_o + ((int64_t)n * S * H + 16 * hg) * D;
+        float* gbase_ml = a.part_ml + ((int64_t)n * S * H + 16 * hg) * 2;
+        const int rec_o = (int)((((int64_t)S - 1) * H + 16) * D * 4);
+        const int rec_ml = (int)((((int64_t)S - 1) * H + 16) * 2 * 4);
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(gbase_o, 0, rec_o, kBufDword3);
+        const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(gbase_ml, 0, rec_ml, kBufDword3);
+        const int row_o = ((sp * (int)H + r16) * D + 128 * wave + 4 * g) * 4;
+        if (hv) {
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[mm]), ro, row_o + 64 * mm, 0, kSc1);
+            if (wave == 0 && g == 0)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_ref), __float_as_uint(l_tot)}, rml,
+                                                      (sp * (int)H + r16) * 8, 0, kSc1);
+        }
+        // the stores are complete (visible device-wide) before the arrival is counted
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) s_flag = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_flag != (uint32_t)(S - 1)) return;  // another split finishes this (query, head group)
+        // last arriver: every other split has stored and counted; merge with device-scope loads,
+        // the splits in split order (this one's from registers) so that the result does not
+        // depend on which split arrived last; an empty split (m = -inf) weighs 0.  Loads of
+        // absent splits use an offset past the buffer's end (they return 0), so every load is
+        // issued unconditionally and a batch's loads are all in flight together.
+        constexpr int kOob = 0x7ffffff0;
+        float msx[kDecodeMaxCombine], lsx[kDecodeMaxCombine];
+        float M = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < kDecodeMaxCombine; ++x) {
+            const bool other = x < S && x != sp && hv;
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rml, other ? (x * (int)H + r16) * 8 : kOob, 0, kSc1);
+            msx[x] = x == sp ? m_ref : (x < S && hv ? __uint_as_float(v[0]) : -INFINITY);
+            lsx[x] = x == sp ? l_tot : __uint_as_float(v[1]);
+            M = fmaxf(M, msx[x]);
+        }
+        const float Mu = M == -INFINITY ? 0.f : M;
+        f32x4 acc[8];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
+        constexpr int kBatch = 4;
+#pragma unroll
+        for (int x0 = 0; x0 < kDecodeMaxCombine; x0 += kBatch) {
+            if (x0 >= S) break;
+            f32x4 v[kBatch][8];
+#pragma unroll
+            for (int xb = 0; xb < kBatch; ++xb) {
+                const int x = x0 + xb;
+                const bool other = x < S && x != sp && hv;
+                const int rx = other ? ((x * (int)H + r16) * D + 128 * wave + 4 * g) * 4 : kOob;
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm)
+                    v[xb][mm] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, other ? rx + 64 * mm : kOob, 0, kSc1));
+            }
+#pragma unroll
+            for (int xb = 0; xb < kBatch; ++xb) {
+                const int x = x0 + xb;
+                if (x >= S) break;
+                const float wx = __builtin_amdgcn_exp2f(msx[x] - Mu);
+                lsum = fmaf(lsx[x], wx, lsum);
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        acc[mm][cc] = fmaf(wx, x == sp ? oacc[mm][cc] : v[xb][mm][cc], acc[mm][cc]);
+            }
+        }
+        l_tot = lsum;
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) oacc[mm] = acc[mm];
+        last = true;
+    }
+
+    // epilogue: RoPE^-1 at p on the raw values of the rotated dims (pairs are
+    // adjacent values of a lane; the rotation commutes with the 1/l scaling),
+    // then 1/l and the conversion; for fp8 the 1/l cancels inside each 64-dim
+    // group: code = e4m3(v * 448 / amax(v)), scale = amax(v) / l / 448.  The
+    // group's rows are staged in the idle ring and leave in contiguous 16-byte stores.
+    const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const int rbase = D - a.rope_dims;
+    const int esz = a.out_dtype == kF32 ? 4 : a.out_dtype == kBF16 ? 2 : 1;
+    const int rstride = D * esz + 16;
+    __syncthreads();  // every wave is done with the ring
+    uint8_t* srow = s_ring + r16 * rstride;
+    float v[8][4];
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+        const int d0 = 128 * wave + 16 * mm + 4 * g;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) v[mm][cc] = oacc[mm][cc];
+        if (128 * wave + 16 * mm + 16 > rbase) {  // (uniform) a tile with rotated dims
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int dd = d0 + 2 * cc;
+                const bool rot = dd >= rbase;
+                const int pj = rot ? (dd - rbase) >> 1 : 0;
+                const float cs = rot ? s_rope[0][pj] : 1.f, sn = rot ? s_rope[1][pj] : 0.f;
+                const float x0 = v[mm][2 * cc], x1 = v[mm][2 * cc + 1];
+                v[mm][2 * cc] = x0 * cs - x1 * sn;
+                v[mm][2 * cc + 1] = x0 * sn + x1 * cs;
+            }
+        }
+    }
+    if (a.out_dtype == kFP8) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {  // 64-dim groups: m-tiles 4 gp .. 4 gp + 3
+            float amax = 0.f, nz = 0.f;
+#pragma unroll
+            for (int mm = 4 * gp; mm < 4 * gp + 4; ++mm)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    amax = fmaxf(amax, fabsf(v[mm][cc]));
+                    nz = fmaf(v[mm][cc], 0.f, nz);  // NaN or infinity anywhere makes this a NaN
+                }
+            amax = max_xor32(max_xor16(amax));
+            const float gmax = amax * inv_l;
+            const float scale = gmax > 0.f ? gmax / 448.0f : 1.0f;
+            const float r = gmax > 0.f ? 448.0f / amax : 0.f;
+            if (g == 0 && hv) a.out_scales[((int64_t)n * a.n_heads + head) * (D / 64) + 2 * wave + gp] = scale;
+            const bool finite = __ballot(nz != nz) == 0;
+#pragma unroll
+            for (int mm = 4 * gp; mm < 4 * gp + 4; ++mm) {
+                const int d0 = 128 * wave + 16 * mm + 4 * g;
+                *reinterpret_cast<uint32_t*>(srow + d0) =
+                    finite ? e4m3_pack4_finite(v[mm][0] * r, v[mm][1] * r, v[mm][2] * r, v[mm][3] * r)
+                           : e4m3_pack4(v[mm][0] * r, v[mm][1] * r, v[mm][2] * r, v[mm][3] * r);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+            const int d0 = 128 * wave + 16 * mm + 4 * g;
+            const float y0 = v[mm][0] * inv_l, y1 = v[mm][1] * inv_l, y2 = v[mm][2] * inv_l, y3 = v[mm][3] * inv_l;
+            if (a.out_dtype == kF32) *reinterpret_cast<f32x4*>(srow + 4 * d0) = f32x4{y0, y1, y2, y3};
+            else *reinterpret_cast<u32x2*>(srow + 2 * d0) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        }
+    }
+    __syncthreads();
+    // the group's head rows (contiguous in the output) in 16-byte chunks
+    const int nrows = a.n_heads - 16 * hg < 16 ? a.n_heads - 16 * hg : 16;
+    const int rchunks = D * esz / 16;
+    uint8_t* out = reinterpret_cast<uint8_t*>(a.out) + ((int64_t)n * a.n_heads + 16 * hg) * D * esz;
+    for (int cc = tid; cc < nrows * rchunks; cc += kDT) {
+        const int h = cc / rchunks, off = (cc - h * rchunks) * 16;
+        *reinterpret_cast<u32x4*>(out + (int64_t)cc * 16) = *reinterpret_cast<const u32x4*>(s_ring + h * rstride + off);
+    }
+    // the group's counter back to zero for the next call (last, so nothing above waits for it)
+    if (S > 1 && last && tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_decode_attn(const DecodeArgs& d, const CompressArgs& c, hipStream_t st, const LaunchEvents& ev) {
+    const AttnArgs& a = d.at;
+    if (a.num_q <= 0) return hipSuccess;
+    if (a.dim != 512) return hipErrorInvalidValue;
+    const int64_t pairs = (int64_t)a.num_q * d.S;
+    const int64_t n_ins = c.total_new > 0 ? (int64_t)c.total_new * c.n_jobs : 0;
+    if ((pairs + 7) / 8 * 8 * d.G + n_ins > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((pairs + 7) / 8 * 8 * d.G + n_ins));
+    const bool prec = a.out_dtype == kFP8;
+    const int64_t slots = (int64_t)d.nchunks * d.kl;
+    const int merge = d.cand == nullptr ? 0 : (slots <= 8 * kDT ? 1 : 2);
+    if (merge == 0) {
+        if (prec) launch_kernel(ev, true, true, decode_attn_kernel<true, 0>, grid, dim3(kDT), st, d, c);
+        else launch_kernel(ev, true, true, decode_attn_kernel<false, 0>, grid, dim3(kDT), st, d, c);
+    } else if (merge == 1) {
+        if (prec) launch_kernel(ev, true, true, decode_attn_kernel<true, 1>, grid, dim3(kDT), st, d, c);
+        else launch_kernel(ev, true, true, decode_attn_kernel<false, 1>, grid, dim3(kDT), st, d, c);
+    } else {
+        if (prec) launch_kernel(ev, true, true, decode_attn_kernel<true, 2>, grid, dim3(kDT), st, d, c);
+        else launch_kernel(ev, true, true, decode_attn_kernel<false, 2>, grid, dim3(kDT), st, d, c);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace csl

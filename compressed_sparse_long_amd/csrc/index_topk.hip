@@ -19,6 +19,7 @@
 // ids and emits the selected ids in ascending order with ballots; ties at the
 // k-th score go to the lower ids.
 #include "csl_insert.hpp"
+#include "csl_select.hpp"
 
 namespace csl {
 
@@ -39,341 +40,6 @@ __device__ __forceinline__ int64_t visible(const IndexArgs& a, int64_t p) {
     return nv < a.stride ? nv : a.stride;
 }
 
-// Order-preserving 32-bit key of an fp32 score (+0 and -0 share one key).
-__device__ __forceinline__ uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_score(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
-
-// Exclusive scan of one uint32 per thread over an NT-thread workgroup; also returns the total.
-template <int NT>
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t x = wave_scan_add(v);
-    if (lane == 63) s_wave[wave] = x;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        uint32_t c = s_wave[w];
-        before += w < wave ? c : 0u;
-        tot += c;
-    }
-    __syncthreads();
-    total = tot;
-    return before + x - v;
-}
-
-// Scan of a 2048-bin histogram from the top: the bin holding the `want`-th
-// largest key and the rank of that key inside the bin.  Every thread calls it;
-// the result lands in s_sel[0] (bin), s_sel[1] (rank), s_sel[2] (bin count),
-// and the histogram total is returned.
-template <int NT>
-__device__ uint32_t find_bin(const uint32_t* s_hist, uint32_t want, int nbins, uint32_t* s_wave, uint32_t* s_sel) {
-    constexpr int PER = 2048 / NT;  // bins per thread (2 for 1024 threads, 8 for 256)
-    const int tid = threadIdx.x;
-    const int top = nbins - 1 - PER * tid;  // this thread's bins top, top-1, ..., from the top
-    uint32_t c[PER], sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = top - i >= 0 ? s_hist[top - i] : 0u;
-        sum += c[i];
-    }
-    uint32_t tot;
-    uint32_t above = block_excl_scan<NT>(sum, s_wave, tot);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        if (top - i >= 0 && above < want && want <= above + c[i]) {
-            s_sel[0] = top - i;
-            s_sel[1] = want - above;
-            s_sel[2] = c[i];
-        }
-        above += c[i];
-    }
-    __syncthreads();
-    return tot;
-}
-
-// Keys of a query's scores read from global memory.
-struct GlobalKeys {
-    const float* sc;
-    __device__ __forceinline__ uint32_t operator()(int64_t e) const { return score_key(sc[e]); }
-};
-struct LdsKeys {
-    const uint32_t* k;
-    __device__ __forceinline__ uint32_t operator()(int64_t e) const { return k[e]; }
-};
-
-// Exact radix select (11/11/10-bit rounds) of the `want`-th largest among keys
-// [0, n) of `key_at`; *rem = copies of it that are taken.
-template <int NT, typename Keys>
-__device__ uint32_t radix_select(const Keys& key_at, int64_t n, uint32_t want, uint32_t* rem_out, uint32_t* s_hist,
-                                 uint32_t* s_wave, uint32_t* s_sel) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0, rem = want;
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int r = 0; r < 3; ++r) {
-        const int sh = shifts[r], nb = 1 << widths[r];
-        for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
-        __syncthreads();
-        for (int64_t e = tid; e < n; e += NT) {
-            uint32_t key = key_at(e);
-            if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> sh) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        find_bin<NT>(s_hist, rem, nb, s_wave, s_sel);
-        prefix |= s_sel[0] << sh;
-        rem = s_sel[1];
-        pmask |= (uint32_t)(nb - 1) << sh;
-        __syncthreads();
-    }
-    *rem_out = rem;
-    return prefix;
-}
-
-// The same over register-resident keys (slot i of a thread valid iff bit i of vmask).
-template <int NT, int KPT>
-__device__ __forceinline__ uint32_t radix_select_regs(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
-                                      uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0, rem = want;
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int r = 0; r < 3; ++r) {
-        const int sh = shifts[r], nb = 1 << widths[r];
-        for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            if (((vmask >> i) & 1u) && (key[i] & pmask) == prefix) atomicAdd(&s_hist[(key[i] >> sh) & (nb - 1)], 1u);
-        __syncthreads();
-        find_bin<NT>(s_hist, rem, nb, s_wave, s_sel);
-        prefix |= s_sel[0] << sh;
-        rem = s_sel[1];
-        pmask |= (uint32_t)(nb - 1) << sh;
-        __syncthreads();
-    }
-    *rem_out = rem;
-    return prefix;
-}
-
-constexpr int kCandCap = 4096;  // boundary-bin keys kept in LDS
-
-// Exact selection over register-resident keys (slot i valid iff bit i of vmask;
-// at least `want` valid keys in the workgroup): returns the `want`-th largest
-// key T and *rem, the number of its copies inside the top `want`.
-//  1. a 2048-bin histogram of the keys inside a window of 2^24 key units below
-//     the largest key (two octaves of fp32 score below the maximum; keys under
-//     the window are not counted, so crowded low bins cost nothing), scanned
-//     from the top: the bin b that holds the want-th key and its rank in b;
-//  2. b's keys (a few: bins are 2^13 key units wide) are compacted to LDS and T
-//     is the one with #(> T) < rank <= #(>= T).
-// If fewer than `want` keys fall in the window, or b is crowded, an exact
-// 3-round radix select over all keys is used instead.
-template <int NT, int KPT, int CAP = kCandCap>
-__device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
-                                 uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
-    constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
-    kmax = wave_max_u32(kmax);
-    if (lane == 0) s_sel[8 + wave] = kmax;
-    for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) kmax = max(kmax, s_sel[8 + w]);
-    constexpr uint32_t kWin = (1u << 24) - 1u;
-    const uint32_t lo = kmax > kWin ? kmax - kWin : 0u;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-        if (((vmask >> i) & 1u) && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
-    __syncthreads();
-    const uint32_t tot = find_bin<NT>(s_hist, want, 2048, s_wave, s_sel);
-    if (tot >= want && s_sel[2] <= (uint32_t)CAP) {
-        const uint32_t bsel = s_sel[0], rank = s_sel[1], cnt = s_sel[2];
-        uint32_t mine = 0;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            mine += (((vmask >> i) & 1u) && key[i] >= lo && ((key[i] - lo) >> 13) == bsel) ? 1u : 0u;
-        uint32_t t2;
-        uint32_t off = block_excl_scan<NT>(mine, s_wave, t2);
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            if (((vmask >> i) & 1u) && key[i] >= lo && ((key[i] - lo) >> 13) == bsel) s_cand[off++] = key[i];
-        __syncthreads();
-        if (cnt <= (uint32_t)NT) {
-            if ((uint32_t)tid < cnt) {
-                const uint32_t kc = s_cand[tid];
-                uint32_t gt = 0, ge = 0;
-                for (uint32_t j = 0; j < cnt; ++j) {
-                    const uint32_t kj = s_cand[j];
-                    gt += kj > kc ? 1u : 0u;
-                    ge += kj >= kc ? 1u : 0u;
-                }
-                if (gt < rank && rank <= ge) {  // every copy of T writes the same values
-                    s_sel[4] = kc;
-                    s_sel[5] = rank - gt;
-                }
-            }
-            __syncthreads();
-            *rem_out = s_sel[5];
-            const uint32_t T = s_sel[4];
-            __syncthreads();
-            return T;
-        }
-        return radix_select<NT>(LdsKeys{s_cand}, (int64_t)cnt, rank, rem_out, s_hist, s_wave, s_sel + 4);
-    }
-    return radix_select_regs<NT, KPT>(key, vmask, want, rem_out, s_hist, s_wave, s_sel + 4);
-}
-
-// Emit, in slot order (ids ascending by thread, then slot), the ids of keys > T
-// and of the first `rem` keys == T.  `ids(i)` gives slot i's id.  Writes
-// positions < k only.  Returns (through s_sel[6]) the id of the last taken copy
-// of T (the k-th element).
-template <int NT, int KPT, typename Ids>
-__device__ __forceinline__ void emit_selected(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t T, uint32_t rem, int k,
-                              const Ids& ids, int32_t* out, uint32_t* s_wave, uint32_t* s_sel, bool write) {
-    uint32_t ngt = 0, neq = 0;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const bool v = (vmask >> i) & 1u;
-        ngt += (v && key[i] > T) ? 1u : 0u;
-        neq += (v && key[i] == T) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan<NT>(ngt | (neq << 16), s_wave, tot);
-    uint32_t eq_before = pre >> 16;
-    uint32_t pos = (pre & 0xffffu) + (eq_before < rem ? eq_before : rem);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        if (!((vmask >> i) & 1u)) continue;
-        bool sel = key[i] > T;
-        if (key[i] == T) {
-            sel = eq_before < rem;
-            if (eq_before + 1 == rem) s_sel[6] = (uint32_t)ids(i);
-            ++eq_before;
-        }
-        if (sel) {
-            if (write && pos < (uint32_t)k) out[pos] = ids(i);
-            ++pos;
-        }
-    }
-}
-
-// ---------------------------------------------------------------- single-pass select
-
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRegKeys = 32;                     // keys per thread held in registers
-
-// Full select for one query by one NT-thread workgroup: thread t holds the
-// scores of ids [32t, 32t+32) in registers (nv <= 32*NT), else the keys are
-// read from global memory in radix rounds.  Used when the two-stage select
-// does not apply or its check fails.
-template <int NT>
-__device__ __forceinline__ void select_full(const float* sc, int64_t nv, int k, int32_t* out, float* kth, uint32_t* s_hist,
-                            uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
-    const int tid = threadIdx.x;
-    if (nv <= (int64_t)kRegKeys * NT) {
-        const int64_t e0 = (int64_t)tid * kRegKeys;
-        uint32_t key[kRegKeys];
-        if (e0 + kRegKeys <= nv) {
-            const float4* p4 = reinterpret_cast<const float4*>(sc + e0);
-#pragma unroll
-            for (int i = 0; i < kRegKeys / 4; ++i) {
-                const float4 v = p4[i];
-                key[4 * i] = score_key(v.x);
-                key[4 * i + 1] = score_key(v.y);
-                key[4 * i + 2] = score_key(v.z);
-                key[4 * i + 3] = score_key(v.w);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kRegKeys; ++i) key[i] = e0 + i < nv ? score_key(sc[e0 + i]) : 0u;
-        }
-        const int64_t nm = nv - e0 < 0 ? 0 : (nv - e0 < kRegKeys ? nv - e0 : kRegKeys);
-        const uint32_t vmask = nm >= 32 ? 0xffffffffu : ((1u << nm) - 1u);
-        uint32_t rem;
-        const uint32_t T = block_select<NT, kRegKeys>(key, vmask, (uint32_t)k, &rem, s_hist, s_wave, s_sel,
-                                                               s_cand);
-        emit_selected<NT, kRegKeys>(key, vmask, T, rem, k, [&](int i) { return (int32_t)(e0 + i); }, out,
-                                             s_wave, s_sel, true);
-        if (tid == 0 && kth) *kth = key_score(T);
-        return;
-    }
-    // long lists: radix rounds and an ordered emission over global memory;
-    // wave w owns ids [w*seg, (w+1)*seg)
-    uint32_t rem;
-    const uint32_t T = radix_select<NT>(GlobalKeys{sc}, nv, (uint32_t)k, &rem, s_hist, s_wave, s_sel);
-    const int lane = tid & 63, wave = tid >> 6;
-    constexpr int NW = NT / 64;
-    const int64_t seg = ((nv + NW - 1) / NW + 63) & ~(int64_t)63;
-    const int64_t lo = (int64_t)wave * seg;
-    const int64_t hi = lo + seg < nv ? lo + seg : nv;
-    uint32_t n_gt = 0, n_eq = 0;
-    for (int64_t e = lo + lane; e - lane < hi; e += 64) {
-        const bool in = e < hi;
-        const uint32_t key = in ? score_key(sc[e]) : 0u;
-        n_gt += __popcll(__ballot(in && key > T));
-        n_eq += __popcll(__ballot(in && key == T));
-    }
-    uint32_t* s_cnt = s_cand;  // [2][NW]
-    if (lane == 0) {
-        s_cnt[wave] = n_gt;
-        s_cnt[NW + wave] = n_eq;
-    }
-    __syncthreads();
-    uint32_t out_pos = 0, eq_seen = 0;
-    for (int w = 0; w < wave; ++w) {
-        const uint32_t eq_w = s_cnt[NW + w];
-        const uint32_t take_eq = eq_seen >= rem ? 0u : (eq_w < rem - eq_seen ? eq_w : rem - eq_seen);
-        out_pos += s_cnt[w] + take_eq;
-        eq_seen += eq_w;
-    }
-    for (int64_t e = lo + lane; e - lane < hi; e += 64) {
-        const bool in = e < hi;
-        const uint32_t key = in ? score_key(sc[e]) : 0u;
-        const bool gt = in && key > T, eq = in && key == T;
-        const uint64_t eqm = __ballot(eq);
-        const uint32_t eq_rank = eq_seen + __popcll(eqm & lanemask_lt(lane));
-        const bool sel = gt || (eq && eq_rank < rem);
-        const uint64_t selm = __ballot(sel);
-        const uint32_t dst = out_pos + __popcll(selm & lanemask_lt(lane));
-        if (sel && dst < (uint32_t)k) out[dst] = (int32_t)e;
-        out_pos += __popcll(selm);
-        eq_seen += __popcll(eqm);
-    }
-    if (tid == 0 && kth) *kth = key_score(T);
-}
-
-// Fewer visible entries than k: all of them, then -1; kth = the smallest score.
-__device__ void select_all(const float* sc, int64_t nv, int k, int32_t* out, float* kth, float* s_min) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nw = blockDim.x / 64;
-    for (int j = tid; j < k; j += blockDim.x) out[j] = j < nv ? j : -1;
-    if (!kth) return;
-    float m = INFINITY;
-    for (int64_t e = tid; e < nv; e += blockDim.x) m = fminf(m, sc[e]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fminf(m, __shfl_xor(m, o));
-    if (lane == 0) s_min[wave] = m;
-    __syncthreads();
-    if (tid == 0) {
-        float r = INFINITY;
-        for (int w = 0; w < nw; ++w) r = fminf(r, s_min[w]);
-        *kth = nv > 0 ? r : -INFINITY;
-    }
-}
 
 __device__ __forceinline__ void select_query(const IndexArgs& a, const int n) {
     __shared__ uint32_t s_hist[2048];
@@ -387,8 +53,8 @@ __device__ __forceinline__ void select_query(const IndexArgs& a, const int n) {
     const float* sc = a.scores + (int64_t)n * a.stride;
     int32_t* out = a.topk + (int64_t)n * a.k;
     float* kth = a.kth ? a.kth + n : nullptr;
-    if (nv <= a.k) select_all(sc, nv, a.k, out, kth, s_min);
-    else select_full<kSelThreads>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
+    if (nv <= a.k) select_all(sc, nv, a.k, GlobalOut{out}, kth, s_min);
+    else select_full<kSelThreads>(sc, nv, a.k, GlobalOut{out}, kth, s_hist, s_wave, s_sel, s_cand);
 }
 
 __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) { select_query(a, blockIdx.x); }
@@ -414,187 +80,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(IndexArgs a) {
 // reuses its LDS for the first stage of the top-k: the chunk's first kl ids in
 // (score desc, id asc) order -- written in ascending id order -- and the
 // (kl+1)-th, whose position the merge checks.
-constexpr int kChunk = 1024;        // ids per first-stage chunk (one workgroup of the score kernel)
 constexpr int kMergeSlots = 8;      // candidates per merge thread
-
-// ---- single-wave selection: no workgroup barriers.  A wave's LDS operations
-// execute in issue order, so after this point a lane reads what any lane of the
-// wave wrote before it; the fence keeps the compiler from moving them across.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-// An NB-bin histogram in LDS scanned from the top by one wave: the bin that
-// holds the rank-th largest counted key, the rank inside that bin and its
-// count (valid if total >= rank).  Lane l sums bins NB-1-PER*l downwards; the
-// hit lane's PER bins are then spread over lanes for a second scan.
-struct BinPick {
-    uint32_t bin, rank, cnt, total;
-};
-template <int NB>
-__device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t rank) {
-    constexpr int PER = NB >= 64 ? NB / 64 : 1;
-    const int lane = threadIdx.x & 63;
-    const int top = NB - 1 - PER * lane;
-    uint32_t sum = 0;
-    if constexpr (PER >= 4) {
-#pragma unroll
-        for (int v = 0; v < PER / 4; ++v) {
-            const u32x4 h = *reinterpret_cast<const u32x4*>(hist + top + 1 - PER + 4 * v);
-            sum += h[0] + h[1] + h[2] + h[3];
-        }
-    } else {
-        static_assert(PER == 1, "bins per lane: 1 or a multiple of 4");
-        sum = top >= 0 ? hist[top] : 0u;
-    }
-    const uint32_t incl = wave_scan_add(sum);
-    BinPick r = {0u, 0u, 0u, lane_value(incl, 63)};
-    if (r.total < rank) return r;
-    const uint32_t above = incl - sum;
-    const int L = __builtin_ctzll(__ballot(above < rank && rank <= incl));
-    const uint32_t above_l = lane_value(above, L);
-    if constexpr (PER == 1) {
-        r.bin = (uint32_t)(NB - 1 - L);
-        r.rank = rank - above_l;
-        r.cnt = lane_value(sum, L);
-    } else {
-        const int top_l = NB - 1 - PER * L;
-        const uint32_t c = lane < PER ? hist[top_l - lane] : 0u;
-        const uint32_t in2 = wave_scan_add(c) + above_l;
-        const int J = __builtin_ctzll(__ballot(lane < PER && in2 - c < rank && rank <= in2));
-        r.bin = (uint32_t)(top_l - J);
-        r.cnt = lane_value(c, J);
-        r.rank = rank - (lane_value(in2, J) - r.cnt);
-    }
-    return r;
-}
-
-// Lanes below this one whose bit is set in m.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// The rank-th largest of cn <= 64 keys in LDS, by one wave (lane j ranks key j
-// against all): T, and *rem = its copies among the top `rank`.
-__device__ __forceinline__ void pairwise_rank(const uint32_t* cbuf, uint32_t cn, uint32_t rank, uint32_t& T,
-                                              uint32_t& rem) {
-    const int lane = threadIdx.x & 63;
-    uint32_t kc = 0, gt = 0, ge = 0;
-    if ((uint32_t)lane < cn) {
-        kc = cbuf[lane];
-        for (uint32_t j = 0; j < cn; ++j) {
-            const uint32_t kj = cbuf[j];
-            gt += kj > kc ? 1u : 0u;
-            ge += kj >= kc ? 1u : 0u;
-        }
-    }
-    const int L = __builtin_ctzll(__ballot((uint32_t)lane < cn && gt < rank && rank <= ge));
-    T = lane_value(kc, L);
-    rem = rank - lane_value(gt, L);
-}
-
-// Emit of a first-stage chunk for slots of 64 consecutive ids (slot i of lane
-// l is id base + 64 (slot0 + i) + l), given T, rem, and the counts of keys > T
-// and == T among the chunk's ids before the first slot: candidates are the
-// keys > T and the first rem - 1 copies of T in id order, each at its rank in
-// id order among the candidates; the rem-th copy of T is the (kl+1)-th element.
-template <int NS>
-__device__ __forceinline__ void emit_first_stage(const uint32_t (&key)[NS], uint32_t vmask, int64_t base, int slot0,
-                                                 uint32_t T, uint32_t rem, uint32_t gt_before, uint32_t eq_before,
-                                                 int kl, uint2* cand, uint2* cnext) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        const bool v = (vmask >> i) & 1u;
-        const bool gt = v && key[i] > T, eq = v && key[i] == T;
-        const uint64_t mg = __ballot(gt), me = __ballot(eq);
-        const uint32_t e = eq_before + lanes_below(me);
-        const uint32_t pos = gt_before + lanes_below(mg) + (e < rem - 1 ? e : rem - 1);
-        const uint32_t id = (uint32_t)(base + 64 * (slot0 + i) + lane);
-        if ((gt || (eq && e + 1 < rem)) && pos < (uint32_t)kl) cand[pos] = make_uint2(key[i], id);
-        if (eq && e + 1 == rem) *cnext = make_uint2(T, id);
-        gt_before += (uint32_t)__popcll(mg);
-        eq_before += (uint32_t)__popcll(me);
-    }
-}
-
-// The want-th largest of a wave's keys (16 per lane, slot i valid iff bit i of
-// vmask), by one wave.  Radix rounds over rel = key - lo, counting only keys
-// >= lo: with WINDOW, lo = max - (2^24 - 1) (two octaves of fp32 score below
-// the maximum; digits at bits 13..23, 2..12, 0..1), else lo = 0 (bits 21..31,
-// 10..20, 0..9).  Each round histograms its digit in `hist` (2048 words of
-// LDS) and finds the bin of the rank; once that bin holds at most 64 keys they are
-// compacted to `cbuf` (64 words) and ranked pairwise.  Returns false (uniform)
-// if fewer than `want` keys are >= lo; else T and *rem, the number of copies
-// of T inside the top `want`.
-template <bool WINDOW>
-__device__ __forceinline__ bool wave_select(const uint32_t (&key)[16], uint32_t vmask, uint32_t want, uint32_t lo,
-                                            uint32_t* hist, uint32_t* cbuf, uint32_t& T, uint32_t& rem) {
-    const int lane = threadIdx.x & 63;
-    uint32_t rel[16], in = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        rel[i] = key[i] - lo;
-        in |= (((vmask >> i) & 1u) && key[i] >= lo ? 1u : 0u) << i;
-    }
-    uint32_t prefix = 0, pmask = 0, rank = want;
-    auto matches = [&](int i) { return ((in >> i) & 1u) && (rel[i] & pmask) == prefix; };
-    auto build = [&](int sh, int nb) {
-        for (int b = 4 * lane; b < nb; b += 256) *reinterpret_cast<u32x4*>(hist + b) = u32x4{0u, 0u, 0u, 0u};
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (matches(i)) atomicAdd(&hist[(rel[i] >> sh) & (uint32_t)(nb - 1)], 1u);
-        wave_lds_sync();
-    };
-    auto take = [&](const BinPick& b, int sh, int nb) {
-        prefix |= b.bin << sh;
-        pmask |= (uint32_t)(nb - 1) << sh;
-        rank = b.rank;
-    };
-    // the bin's keys (at most 64) ranked pairwise
-    auto finish = [&](uint32_t cn) {
-        uint32_t mine = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mine += matches(i) ? 1u : 0u;
-        uint32_t off = wave_scan_add(mine) - mine;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (matches(i)) {
-                if (off < 64u) cbuf[off] = rel[i];
-                ++off;
-            }
-        wave_lds_sync();
-        pairwise_rank(cbuf, cn, rank, T, rem);
-        T += lo;
-        wave_lds_sync();
-    };
-    constexpr int kSh0 = WINDOW ? 13 : 21, kSh1 = WINDOW ? 2 : 10;
-    build(kSh0, 2048);
-    BinPick b = wave_find_bin<2048>(hist, rank);
-    if (b.total < rank) return false;
-    take(b, kSh0, 2048);
-    if (b.cnt <= 64u) {
-        finish(b.cnt);
-        return true;
-    }
-    build(kSh1, 2048);
-    b = wave_find_bin<2048>(hist, rank);
-    take(b, kSh1, 2048);
-    if (b.cnt <= 64u) {
-        finish(b.cnt);
-        return true;
-    }
-    constexpr int kNb2 = WINDOW ? 4 : 1024;
-    build(0, kNb2);
-    b = wave_find_bin<kNb2>(hist, rank);
-    take(b, 0, kNb2);
-    T = prefix + lo;
-    rem = rank;
-    wave_lds_sync();
-    return true;
-}
 
 // First stage of the two-stage top-k over one 1024-id chunk of query n, by one
 // wave whose lane l holds the keys of ids base + 16 l .. +15 (ids at or past
@@ -691,8 +177,17 @@ __global__ void __launch_bounds__(256) topk_local_kernel(IndexArgs a) {
     wave_first_stage(a, n, blk, key, base, nvalid, s_hist[wave], s_cbuf[wave]);
 }
 
-template <int DI, int U, bool LOCAL, bool FP4 = false>
-__global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
+// LDS of one score workgroup (also the insert body's, when inserts ride in the launch).
+template <int DI>
+constexpr int score_smem_bytes() {
+    constexpr int kUnitBytes = 4 * 64 * (DI * 2 + 16);
+    constexpr int kSelBytes = (kChunk + 2048 + 64 + 8) * 4;
+    return kUnitBytes > kSelBytes ? kUnitBytes : kSelBytes;
+}
+
+// The score workgroup (chunk bx of query n).  Every thread calls it.
+template <int DI, int U, bool LOCAL, bool FP4>
+__device__ __forceinline__ void score_block(const IndexArgs& a, const int bx, const int n, uint8_t* s_mem) {
     constexpr int KS = DI / 32;          // MFMA k-steps per row
     constexpr int RB = DI * 2;           // bf16 row bytes (the LDS layout)
     constexpr int RBG = FP4 ? DI / 2 + DI / 32 : RB;  // stored row bytes
@@ -700,24 +195,20 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
     constexpr int CPR = RB / 16;         // 16-byte chunks per row
     constexpr int NLD = CPR;             // 1 KiB loads per 64-row unit
     constexpr int LROW = RB + 16;        // padded LDS row (spreads the banks of the MFMA-layout reads)
-    constexpr int kUnitBytes = 4 * 64 * LROW;
-    constexpr int kSelBytes = (kChunk + 2048 + 64 + 8) * 4;
     static_assert(!LOCAL || 4 * U * 64 == kChunk, "a first-stage chunk is one workgroup");
-    __shared__ __attribute__((aligned(16))) uint8_t s_mem[kUnitBytes > kSelBytes ? kUnitBytes : kSelBytes];
-    const int n = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     int s;
     int64_t p;
     if (!query_ok(a, n, s, p)) {
-        if (blockIdx.x == 0 && tid == 0) raise_error(a.err, (s < 0 || s >= a.num_seqs) ? kErrSeq : kErrPos);
+        if (bx == 0 && tid == 0) raise_error(a.err, (s < 0 || s >= a.num_seqs) ? kErrSeq : kErrPos);
         return;
     }
     const int64_t nv = visible(a, p);
-    const int64_t wg0 = (int64_t)blockIdx.x * 4 * U * 64;  // first entry of the workgroup
+    const int64_t wg0 = (int64_t)bx * 4 * U * 64;  // first entry of the workgroup
     if (wg0 >= nv) return;                                   // uniform over the workgroup
     // the wave's U consecutive 64-entry units; unit u is block u of the sequence
-    const int64_t u0 = ((int64_t)blockIdx.x * 4 + wave) * U;
+    const int64_t u0 = ((int64_t)bx * 4 + wave) * U;
     float mine_u[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) mine_u[j] = -INFINITY;
@@ -821,8 +312,8 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
         // each emits its own ids
         const int kl = a.kl;
         const int nvalid = (int)(nv - wg0 < kChunk ? nv - wg0 : kChunk);
-        uint2* cand = a.cand + ((int64_t)n * a.nchunks + blockIdx.x) * kl;
-        uint2* cnext = a.c_next + (int64_t)n * a.nchunks + blockIdx.x;
+        uint2* cand = a.cand + ((int64_t)n * a.nchunks + bx) * kl;
+        uint2* cnext = a.c_next + (int64_t)n * a.nchunks + bx;
         uint32_t kw[U], vmask = 0, kmax = 0u;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
@@ -880,7 +371,7 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
                 key[4 * v + 2] = kv.z;
                 key[4 * v + 3] = kv.w;
             }
-            wave_first_stage(a, n, blockIdx.x, key, wg0, nvalid, s_hist, s_cbuf);
+            wave_first_stage(a, n, bx, key, wg0, nvalid, s_hist, s_cbuf);
             return;
         }
 #pragma unroll
@@ -903,6 +394,35 @@ __global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
         emit_first_stage<U>(kw, vmask, wg0, wave * U, T, rem, before & 0xffffu, before >> 16, kl, cand, cnext);
     }
 }
+
+template <int DI, int U, bool LOCAL, bool FP4 = false>
+__global__ void __launch_bounds__(256) index_score_kernel(IndexArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[score_smem_bytes<DI>()];
+    score_block<DI, U, LOCAL, FP4>(a, blockIdx.x, blockIdx.y, s_mem);
+}
+
+// The decode score launch with the step's writes riding in it: rows y < num_q
+// of the grid are score workgroups; the rows after them take, in order, one
+// (new token, pool) insert per workgroup, then the query-side rows (four per
+// workgroup).  They are dispatched after every score workgroup, so they run
+// while the stream's last workgroups drain.  The writes touch positions the
+// step's queries do not read (the queries at p see entries and raw tokens
+// below p), so the scores are the same as without them.
+template <int DI, int U, bool LOCAL, bool FP4 = false>
+__global__ void __launch_bounds__(256) index_score_insert_kernel(IndexArgs a, CompressArgs c, QSideArgs q) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[score_smem_bytes<DI>()];
+    static_assert(sizeof(InsertSmem) <= score_smem_bytes<DI>(), "the insert body fits the score workgroup's LDS");
+    if ((int)blockIdx.y < a.num_q) {
+        score_block<DI, U, LOCAL, FP4>(a, blockIdx.x, blockIdx.y, s_mem);
+        return;
+    }
+    const int64_t i = ((int64_t)blockIdx.y - a.num_q) * gridDim.x + blockIdx.x;
+    const int64_t n_ins = (int64_t)c.total_new * c.n_jobs;
+    const int64_t n_qb = q.n_items > 0 ? (q.n_items + 3) / 4 : 0;
+    if (i < n_ins) insert_block(c, (int)(i / c.total_new), (int)(i % c.total_new), *reinterpret_cast<InsertSmem*>(s_mem));
+    else if (i < n_ins + n_qb) qside_block<1>(q, i - n_ins);
+}
+
 // index_score_tiled_kernel<DI, QW> -- scores for many queries (prefill chunks).
 // A workgroup takes a block of 4*QW queries and one 1024-entry chunk.  The
 // chunk's pages of the queries' sequence stream once through double-buffered
@@ -1106,13 +626,9 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
     }
 }
 
-// Stage 2: one NT-thread workgroup per query (8*NT candidate slots).  The
-// chunks' candidate lists, concatenated, are in ascending id order; thread t
-// holds slots [8t, 8t+8).  The top k of the candidates (score desc, id asc)
-// is exact when every chunk's (kl+1)-th element comes after the k-th selected
-// element in that order: every id outside the candidates then comes after it
-// too.  Otherwise, or when the candidates cannot hold k ids (short rows), the
-// full select runs on the score row and overwrites the output.
+// Stage 2: one NT-thread workgroup per query (merge_candidates, 8*NT
+// candidate slots), the full select on the score row when the candidates do
+// not decide the result.
 template <int NT>
 __device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
     constexpr int NW = NT / 64;
@@ -1122,60 +638,17 @@ __device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
     __shared__ uint32_t s_sel[8 + NW];
     __shared__ float s_min[NW];
     __shared__ uint32_t s_fail;
-    const int tid = threadIdx.x;
     int s;
     int64_t p;
-    const int64_t nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
-    const float* sc = a.scores + (int64_t)n * a.stride;
-    int32_t* out = a.topk + (int64_t)n * a.k;
-    float* kth = a.kth ? a.kth + n : nullptr;
-    if (nv <= a.k) {
-        select_all(sc, nv, a.k, out, kth, s_min);
-        return;
-    }
-    const int nch = (int)((nv + kChunk - 1) / kChunk);
-    const int64_t nslots = (int64_t)nch * a.kl;
-    // a chunk of L visible ids yields min(L, kl) candidates
-    const int64_t ncand = (nv / kChunk) * a.kl + (int64_t)min<int64_t>(a.kl, nv % kChunk);
-    if (nslots > (int64_t)kMergeSlots * NT || ncand < a.k) {
-        select_full<NT>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
-        return;
-    }
-    // the chunks' (kl+1)-th elements, fetched beside the candidates
-    const uint2* cnext = a.c_next + (int64_t)n * a.nchunks;
-    const uint2 nx = tid < nch ? cnext[tid] : make_uint2(0u, 0xffffffffu);
-    const uint2* cand = a.cand + (int64_t)n * a.nchunks * a.kl;
-    uint32_t key[kMergeSlots], id[kMergeSlots], vmask = 0;
-#pragma unroll
-    for (int i = 0; i < kMergeSlots; ++i) {
-        const int64_t f = (int64_t)tid * kMergeSlots + i;
-        uint2 c = make_uint2(0u, 0xffffffffu);
-        if (f < nslots) c = cand[f];
-        key[i] = c.x;
-        id[i] = c.y;
-        vmask |= (c.y != 0xffffffffu ? 1u : 0u) << i;
-    }
-    if (tid == 0) s_fail = 0;
-    uint32_t rem;
-    const uint32_t T = block_select<NT, kMergeSlots>(key, vmask, (uint32_t)a.k, &rem, s_hist, s_wave, s_sel, s_cand);
-    // emit, and learn the k-th element's id (s_sel[6]) for the check; a failed
-    // check rewrites every output position
-    emit_selected<NT, kMergeSlots>(key, vmask, T, rem, a.k, [&](int i) { return (int32_t)id[i]; }, out, s_wave, s_sel,
-                                   true);
-    __syncthreads();
-    const uint32_t idk = s_sel[6];
-    bool bad = nx.y != 0xffffffffu && !(nx.x < T || (nx.x == T && nx.y > idk));
-    for (int c = tid + NT; c < nch; c += NT) {
-        const uint2 x = cnext[c];
-        bad |= x.y != 0xffffffffu && !(x.x < T || (x.x == T && x.y > idk));
-    }
-    if (bad) s_fail = 1;
-    __syncthreads();
-    if (s_fail) {
-        select_full<NT>(sc, nv, a.k, out, kth, s_hist, s_wave, s_sel, s_cand);
-        return;
-    }
-    if (tid == 0 && kth) *kth = key_score(T);
+    MergeIn in;
+    in.nv = query_ok(a, n, s, p) ? visible(a, p) : 0;
+    in.sc = a.scores + (int64_t)n * a.stride;
+    in.cand = a.cand + (int64_t)n * a.nchunks * a.kl;
+    in.cnext = a.c_next + (int64_t)n * a.nchunks;
+    in.kl = a.kl;
+    in.k = a.k;
+    const MergeLds m = {s_hist, s_cand, s_wave, s_sel, s_min, &s_fail};
+    merge_candidates<NT, kMergeSlots>(in, GlobalOut{a.topk + (int64_t)n * a.k}, a.kth ? a.kth + n : nullptr, m);
 }
 
 template <int NT>
@@ -1247,6 +720,54 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t st, const LaunchEv
         case 128:
             if (local) launch_kernel(ev, true, true, index_score_kernel<128, U, true>, grid, dim3(256), st, a);
             else launch_kernel(ev, true, true, index_score_kernel<128, U, false>, grid, dim3(256), st, a);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// The decode score kernel with the step's inserts and query-side rows as
+// extra grid rows (launch_index_score's decode path otherwise).
+template <int DI, bool LOCAL, bool FP4>
+void launch_score_insert(const IndexArgs& a, const CompressArgs& c, const QSideArgs& q, dim3 grid, hipStream_t st,
+                         const LaunchEvents& ev) {
+    launch_kernel(ev, true, true, index_score_insert_kernel<DI, kScoreUnits, LOCAL, FP4>, grid, dim3(256), st, a, c, q);
+}
+
+hipError_t launch_index_score_insert(const IndexArgs& a, const CompressArgs& c, const QSideArgs& q, hipStream_t st,
+                                     const LaunchEvents& ev) {
+    const int64_t n_ins = (int64_t)c.total_new * c.n_jobs;
+    const int64_t n_qb = q.n_items > 0 ? (q.n_items + 3) / 4 : 0;
+    if (a.num_q <= 0 || a.tiled || n_ins + n_qb <= 0) {
+        // nothing rides along (or the query-blocked kernel scores): separate launches
+        hipError_t e = launch_index_score(a, st, ev);
+        if (e == hipSuccess) e = launch_compress(c, st);
+        if (e == hipSuccess) e = launch_qside(q, st);
+        return e;
+    }
+    const int64_t gx = a.stride / (256 * kScoreUnits);
+    const int64_t rows = (n_ins + n_qb + gx - 1) / gx;
+    if (a.num_q + rows > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)gx, (unsigned)(a.num_q + rows));
+    const bool local = a.kl > 0;
+    if (a.fp4) {
+        if (a.dim != 128) return hipErrorInvalidValue;
+        if (local) launch_score_insert<128, true, true>(a, c, q, grid, st, ev);
+        else launch_score_insert<128, false, true>(a, c, q, grid, st, ev);
+        return hipGetLastError();
+    }
+    switch (a.dim) {
+        case 32:
+            if (local) launch_score_insert<32, true, false>(a, c, q, grid, st, ev);
+            else launch_score_insert<32, false, false>(a, c, q, grid, st, ev);
+            break;
+        case 64:
+            if (local) launch_score_insert<64, true, false>(a, c, q, grid, st, ev);
+            else launch_score_insert<64, false, false>(a, c, q, grid, st, ev);
+            break;
+        case 128:
+            if (local) launch_score_insert<128, true, false>(a, c, q, grid, st, ev);
+            else launch_score_insert<128, false, false>(a, c, q, grid, st, ev);
             break;
         default: return hipErrorInvalidValue;
     }

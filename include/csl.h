@@ -253,6 +253,13 @@ csl_status csl_index_topk_insert(const csl_pool* index_pool /* host */, const cs
  *          are split across workgroups and merged (needs ws).
  * prefill: queries of sequence s are cu_q[s] .. cu_q[s+1]-1 at positions
  *          q_pos_start[s], q_pos_start[s]+1, ...; one workgroup per query.
+ *
+ * Decode workspace (device, caller-owned; csl_hybrid_attn_workspace() bytes,
+ * 0 = none needed and ws may be NULL): the first 16 KiB hold arrival counters
+ * of the splits and MUST BE ZERO before the first call that uses this ws
+ * (e.g. allocate it zero-filled); every call that completes leaves them zero
+ * again, so a ws can be reused by any later decode call, on one stream at a
+ * time.  The rest holds split partials (contents undefined on entry and exit).
  */
 size_t csl_hybrid_attn_workspace(int32_t num_q, int32_t n_heads, int32_t dim, int32_t comp_ratio, int32_t k,
                                  int32_t swa_window, int64_t max_q_pos);
@@ -268,6 +275,35 @@ csl_status csl_hybrid_attn_prefill(const csl_pool* comp /* host, nullable */, co
                                    const uint16_t* q, int32_t n_heads, const int32_t* topk, int32_t k,
                                    int32_t swa_window, float softmax_scale, int32_t out_dtype, void* out,
                                    float* out_scales, csl_stream_t stream);
+
+/*
+ * Steps 1-6 of a c4a decode step in two launches ([Summary] DeepSeek V4 注意力
+ * 架構: the indexer's top-k feeds the sparse attention; [Notes] 优化二：多 CUDA
+ * 流并行 for the writes that ride along): exactly csl_index_topk_insert(
+ * index_pool, ..., topk, kth_score, ..., n_jobs, jobs, ..., qside), then
+ * csl_hybrid_attn_decode(comp, swa, ..., topk, k, ...), with the same
+ * arguments and results (topk and kth_score are written as by the indexer).
+ * The first launch scores the index entries (with each 1024-entry chunk's
+ * first-stage candidates) and carries the inserts and query-side rows; the
+ * second merges each query's candidates into its top-k and runs the
+ * attention, splits merged in the launch.
+ * comp: ratio 4, dim 512, bf16 rows (fp8 keys: the two calls); swa: ratio 1,
+ * the same dim and dtype.  ws: csl_index_attn_decode_workspace() bytes, its
+ * first 16 KiB zero before the first use and left zero (as for
+ * csl_hybrid_attn_decode).  0 <= n_jobs <= 4.
+ */
+size_t csl_index_attn_decode_workspace(int32_t num_q, int32_t n_heads, int64_t max_q_pos, int32_t k,
+                                       int32_t swa_window);
+csl_status csl_index_attn_decode(const csl_pool* index_pool /* host */, const csl_pool* comp /* host */,
+                                 const csl_pool* swa /* host */, const csl_pages* pages /* host */, int32_t num_q,
+                                 const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos,
+                                 const uint16_t* q_idx, const float* w, int32_t n_idx_heads, int32_t k, int32_t* topk,
+                                 float* kth_score, const uint16_t* q, int32_t n_heads, int32_t swa_window,
+                                 float softmax_scale, int32_t out_dtype, void* out, float* out_scales, int32_t n_jobs,
+                                 const csl_insert_job* jobs /* host */, const int64_t* start_pos,
+                                 const int32_t* cu_new, int32_t total_new, float eps,
+                                 const csl_qside_job* qside /* host, nullable */, void* ws, size_t ws_bytes,
+                                 csl_stream_t stream);
 
 /* Message of the last failing call on the calling thread ("" if none). */
 const char* csl_last_error(void);

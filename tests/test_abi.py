@@ -42,15 +42,24 @@ def test_workspace_sizes(csl):
     # 40 = 512*1024/32768 = 16 expected per chunk + 5 sqrt(16) + 4, rounded up to 8
     assert csl.index_topk_workspace(16, 131072, 512) == 16 * (32768 * 4 + 32 * 41 * 8)
     assert csl.index_topk_workspace(1, 100, 64) == 2048 * 4      # 25 entries <= k: one pass
-    # decode split-KV partials: num_q * splits * heads * (dim + 2) floats, sized for the
-    # larger split count of the two key types (bf16: 4 tiles per split, fp8: 2; halved
-    # while the launch would hold fewer than 32 workgroups)
+    # decode split-KV partials: a 16 KiB block of arrival counters, then num_q * splits *
+    # heads * (dim + 2) floats, sized for the larger split count of the paths the key
+    # type could take (fp8 keys: 2 tiles per split, one while the launch would hold
+    # fewer than 32 workgroups; bf16 keys: 16-head groups with about 256 workgroups,
+    # 32..256 keys per split, at most 8 splits while the keys fit 8 x 256)
     part = 64 * 514 * 4
-    assert csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072) == 16 * 10 * part  # 20 tiles: 10 fp8 splits
-    assert csl.hybrid_attn_workspace(1, 64, 512, 4, 512, 128, 1 << 20) == 20 * part      # one query: one-tile splits
-    assert csl.hybrid_attn_workspace(1, 64, 512, 128, 0, 128, 1 << 20) == 130 * part     # 260 tiles: 130 fp8 splits
-    assert csl.hybrid_attn_workspace(8, 64, 512, 128, 0, 128, 32768) == 8 * 6 * part     # 12 tiles: 6 splits
+    cnt = 16384
+    assert csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072) == cnt + 16 * 10 * part  # fp8: 10 splits; bf16: 4
+    assert csl.hybrid_attn_workspace(1, 64, 512, 4, 512, 128, 1 << 20) == cnt + 20 * part      # fp8 one-tile splits; bf16: 7
+    assert csl.hybrid_attn_workspace(1, 64, 512, 128, 0, 128, 1 << 20) == cnt + 130 * part     # fp8: 130; bf16: 52
+    assert csl.hybrid_attn_workspace(8, 64, 512, 128, 0, 128, 32768) == cnt + 8 * 6 * part     # 12 tiles: 6 splits
     assert csl.hybrid_attn_workspace(1, 64, 512, 0, 0, 0, 10) == 0
+    # the fused decode call: counters, the bf16 plan's partials (16 queries x 4 splits of 160
+    # keys), then the indexer's scores and candidates
+    assert csl.index_attn_decode_workspace(16, 64, 131072, 512, 128) == (
+        cnt + 16 * 4 * part + csl.index_topk_workspace(16, 131072, 512))
+    assert csl.index_attn_decode_workspace(16, 8, 1024, 64, 128) == (
+        cnt + 16 * 6 * 8 * 514 * 4 + csl.index_topk_workspace(16, 1024, 64))  # 192 keys: 6 splits of 32
 
 
 FAKE = 0x100000  # a 16-byte aligned host address that is never dereferenced

@@ -446,6 +446,170 @@ def test_index_topk_insert_equals_separate_calls(csl, orc, case):
 
 
 # ---------------------------------------------------------------------------
+# index_attn_decode: index scores + inserts, then merge + attention, two launches
+# ---------------------------------------------------------------------------
+
+def tail_table(seed, ns, mb, first_low, tail):
+    """Block table in which blocks first_low[s] .. first_low[s] + tail - 1 of sequence s take
+    pages [0, ns*tail) and every other block a page above them, so that a pool only read
+    around the sequence's end (raw window, compressor state) can hold just the low pages
+    (the others lie beyond its num_pages)."""
+    lowp = np.random.default_rng(seed).permutation(ns * tail).astype(np.int32)
+    highp = (ns * tail + np.random.default_rng(seed + 1).permutation(ns * (mb - tail))).astype(np.int32)
+    bt = np.empty((ns, mb), np.int32)
+    for s in range(ns):
+        low = np.zeros(mb, bool)
+        low[first_low[s]:first_low[s] + tail] = True
+        bt[s, low] = lowp[s * tail:(s + 1) * tail]
+        bt[s, ~low] = highp[s * (mb - tail):(s + 1) * (mb - tail)]
+    return bt
+
+
+FUSED_ATTN_CASES = [
+    # two sequences, one query each: scores with first stage, inserts in the score launch,
+    # the merge in the attention launch (8 candidates per thread)
+    dict(name="two_stage_merge", pos=[[9003], [20000]]),
+    # short rows (visible entries <= k): no first stage; the select kernel, then attention
+    dict(name="short_rows", pos=[[1000], [700]]),
+    # the query side (Q norm + RoPE, raw-key insert) in the score launch too
+    dict(name="with_query_side", pos=[[9003], [20000]], qside=True),
+    # 16 sequences (one query and one new token each), fp8 output: the precision variant
+    dict(name="16_queries_fp8_out", pos=[[5000 + 700 * i] for i in range(16)], out=O.FP8),
+    # index keys rising with the id: the top-k crowds the last chunk, the candidates'
+    # check fails and every workgroup of the query takes the exact select on the score row
+    dict(name="ramp_fallback", pos=[[9000], [12001]], mode="ramp", out=O.F32),
+    # 150 000 visible entries: 148 chunks x 24 candidates, 16 candidates per merge thread;
+    # no inserts; 48 heads (three head groups)
+    dict(name="wide_merge_16_per_thread", pos=[[600003]], DI=32, H=48, jobs=False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_ATTN_CASES, ids=[c["name"] for c in FUSED_ATTN_CASES])
+def test_index_attn_decode_equals_separate_calls(csl, orc, case):
+    seed = zlib.crc32(("fused_attn_" + case["name"]).encode()) % 1000
+    HI, DI, D, R, k = 16, case.get("DI", 128), 512, 64, 512
+    H = case.get("H", 64)
+    od = case.get("out", O.BF16)
+    ns = len(case["pos"])
+    max_pos = max(max(p) for p in case["pos"])
+    mb = (max_pos + 256) // 256 + 1
+    # the window [p - 128, p - 1], the new token p and its entry's window [p - 7, p] lie in
+    # blocks (p - 128) / 256 .. p / 256: three blocks from max(0, p / 256 - 1)
+    tail = 3
+    first_low = [max(0, max(p) // 256 - 1) for p in case["pos"]]
+    bt = tail_table(seed, ns, mb, first_low, tail)
+    P, P_low = ns * mb, ns * tail
+    with_jobs = case.get("jobs", True)
+    idx = O.HostPool(4, 2, DI, 0, THETA, O.BF16, P, state=with_jobs)
+    for s in range(ns):
+        keys = randn_bf16(seed, 10 + s, (64 * mb, DI))
+        if case.get("mode") == "ramp":
+            ramp = (1.0 + np.arange(64 * mb) / 8192.0).astype(np.float32)
+            keys = (np.repeat(ramp[:, None], DI, 1).view(np.uint32) >> 16).astype(np.uint16)
+        scatter_rows(idx.rows, bt, s, 4, keys.view(np.uint8).reshape(64 * mb, -1))
+    main = O.HostPool(4, 2, D, R, THETA, O.BF16, P, state=with_jobs)
+    for s in range(ns):
+        scatter_rows(main.rows, bt, s, 4, randn_bf16(seed, 40 + s, (64 * mb, D)).view(np.uint8).reshape(64 * mb, -1))
+    raw = O.HostPool(1, 1, D, R, THETA, O.BF16, P_low, state=False)
+    for s in range(ns):
+        n_raw = 256 * tail
+        scatter_rows(raw.rows, bt, s, 1, randn_bf16(seed, 60 + s, (n_raw, D)).view(np.uint8).reshape(n_raw, -1),
+                     i0=256 * first_low[s])
+    if with_jobs:  # compressor state of the tail pages (the only pages the inserts read)
+        for hp, t0 in ((idx, 11), (main, 13)):
+            hp.state_x[:P_low] = randn_bf16(seed, t0, hp.state_x[:P_low].shape)
+            hp.state_logits[:P_low] = randn_f32(seed, t0 + 1, hp.state_logits[:P_low].shape).astype(np.float32)
+    q_seq = np.concatenate([[s] * len(p) for s, p in enumerate(case["pos"])]).astype(np.int32)
+    q_pos = np.concatenate(case["pos"]).astype(np.int64)
+    nq = len(q_pos)
+    qi = randn_bf16(seed, 20, (nq, HI, DI))
+    if case.get("mode") == "ramp":
+        qi = (np.abs(O.bf16_array_to_f64(qi)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = rand_u(seed, 21, (nq, HI)).astype(np.float32)
+    q = randn_bf16(seed, 22, (nq, H, D))
+    # new tokens: one per query, at the query's position (decode: the queries read below it)
+    lens = [len(p) for p in case["pos"]]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    st = np.array([p[0] for p in case["pos"]], np.int64)
+    x = randn_bf16(seed, 30, (nq, D))
+    xi = randn_bf16(seed, 31, (nq, DI))
+    lg = randn_f32(seed, 32, (nq, 2)).astype(np.float32)
+    li = randn_f32(seed, 33, (nq, 2)).astype(np.float32)
+    gain = rand_u(seed, 34, (D,), 0.5, 1.5).astype(np.float32)
+    qs = case.get("qside", False)
+    qh = randn_bf16(seed, 35, (nq, H, D))
+    qg = rand_u(seed, 36, (D,), 0.5, 1.5).astype(np.float32)
+    scale = D ** -0.5
+    odt = {O.F32: torch.float32, O.BF16: torch.bfloat16, O.FP8: torch.uint8}[od]
+    outs = []
+    for fused in (False, True):
+        gi, gr, gm = gpu_pool(csl, idx, state=with_jobs), gpu_pool(csl, raw, state=False), gpu_pool(csl, main, state=with_jobs)
+        topk = torch.full((nq, k), -7, dtype=torch.int32, device=DEV)
+        kth = torch.empty(nq, dtype=torch.float32, device=DEV)
+        out = torch.empty((nq, H, D), dtype=odt, device=DEV)
+        scales = torch.zeros((nq, H, D // 64), dtype=torch.float32, device=DEV) if od == O.FP8 else None
+        jobs = []
+        if with_jobs:
+            jobs = [(gr, dev_bf16(x), None, None), (gm, dev_bf16(x), dev(lg), dev(gain)),
+                    (gi, dev_bf16(xi), dev(li), None)]
+        gbt, gq, gw = dev(bt), dev_bf16(qi), dev(w)
+        gqh = dev_bf16(qh)
+        gqo = gqh.clone() if qs else dev_bf16(q)
+        qside = (gr, dev_bf16(x), gqh, dev(qg), gqo) if qs else None
+        if qs:
+            jobs = jobs[1:]  # the query side writes the raw rows
+        say(f"index_attn_decode {case['name']} fused={fused} nq {nq}")
+        if fused:
+            ws = csl.workspace(csl.index_attn_decode_workspace(nq, H, max_pos, k, 128))
+            csl.index_attn_decode(gi, gm, gr, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, gqo, 128, scale,
+                                  od, out, scales, jobs, dev(st), dev(cu), kth, ws, qside=qside)
+        else:
+            wsi = torch.empty(csl.index_topk_workspace(nq, max_pos, k) // 4, dtype=torch.float32, device=DEV)
+            wsa = csl.workspace(csl.hybrid_attn_workspace(nq, H, D, 4, k, 128, max_pos))
+            if jobs or qs:
+                csl.index_topk_insert(gi, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, jobs, dev(st),
+                                      dev(cu), kth, wsi, qside=qside)
+            else:
+                csl.index_topk(gi, gbt, dev(q_seq), dev(q_pos), max_pos, gq, gw, k, topk, kth, wsi)
+            csl.hybrid_attn_decode(gm, gr, gbt, dev(q_seq), dev(q_pos), max_pos, gqo, topk, k, 128, scale, od, out,
+                                   scales, wsa)
+        torch.cuda.synchronize()
+        assert csl.read_device_error() == 0
+        res = [host(topk), host(kth), host(out.view(torch.uint8)), host(gr.rows), host(gm.rows), host(gi.rows),
+               host_u16(gqo)]
+        if with_jobs:
+            res += [host_u16(gm.state_x), host(gm.state_logits), host_u16(gi.state_x), host(gi.state_logits)]
+        if od == O.FP8:
+            res.append(host(scales))
+        outs.append(res)
+        if fused:  # the counter block is left zero
+            assert not ws[:4096].any().item()
+    names = ["topk", "kth", "out", "raw rows", "main rows", "index rows", "q", "main state_x", "main state_logits",
+             "index state_x", "index state_logits", "out scales"]
+    if not with_jobs:
+        names = names[:7] + names[11:]
+    for nm, a, b in zip(names, outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{case['name']}: {nm} differ"
+    # against the oracle on the pre-insert pools: the selection, then the attention over the
+    # GPU's ids for every query (the sets may differ from the oracle's by allowed swaps)
+    o_topk, o_kth, o_sc, f = O.index_topk(idx, bt, q_seq, q_pos, qi, w, k, want_scores=True, max_cand=max_pos // 4)
+    assert f == 0
+    g_topk = outs[1][0]
+    assert_topk_equivalent(g_topk, o_topk, o_sc, o_kth, what=case["name"])
+    q_used = host_u16(gqo)
+    o_out, o_oscale, o64, f = O.hybrid_attn(main, raw, bt, q_seq, q_pos, q_used, topk=g_topk, k=k, swa_window=128,
+                                            softmax_scale=scale, out_dtype=od)
+    assert f == 0
+    g_out = outs[1][2]
+    if od == O.F32:
+        assert_close(g_out.view(np.float32).reshape(o64.shape), o64, what=case["name"])
+    elif od == O.BF16:
+        assert_close(O.bf16_array_to_f64(g_out.view(np.uint16).reshape(o64.shape)), o64, what=case["name"])
+    else:
+        assert_fp8_close(orc, g_out.reshape(o64.shape), outs[1][-1], o_out, o_oscale, what=case["name"])
+
+
+# ---------------------------------------------------------------------------
 # hybrid attention
 # ---------------------------------------------------------------------------
 
@@ -525,6 +689,16 @@ ATTN_CASES = [
          pos=[[150000]]),
     dict(name="c4a_d512_h64_k512_32q_fp8out", D=512, R=64, H=64, ratio=4, k=512, dtype=O.BF16, out=O.FP8,
          pos=[[2100 + 37 * i for i in range(16)], [2500 + 53 * i for i in range(16)]]),
+    # bf16 keys, more keys than 8 splits of 256 hold: the splits leave partials for the
+    # separate combine launch instead of merging in the launch
+    dict(name="c128a_d512_h64_dense_bf16_partials_path", D=512, R=64, H=64, ratio=128, k=0, dtype=O.BF16,
+         out=O.BF16, pos=[[300000]]),
+    # 128-dim keys with bf16 and fp8 output (the generic kernel's precision variant and the
+    # combine kernel's 128-dim stores)
+    dict(name="c4a_d128_h8_k64_bf16out", D=128, R=32, H=8, ratio=4, k=64, dtype=O.BF16, out=O.BF16,
+         pos=[[130, 600, 1023, 1024], [700]]),
+    dict(name="c4a_d128_h16_k64_fp8out", D=128, R=32, H=16, ratio=4, k=64, dtype=O.BF16, out=O.FP8,
+         pos=[[1, 300, 1023], [900, 1024]]),
 ]
 
 
@@ -557,7 +731,7 @@ def test_hybrid_attn_parity(csl, orc, case, mode):
     say(f"hybrid_attn {mode} {case['name']} nq {nq}")
     if mode == "decode":
         wsb = csl.hybrid_attn_workspace(nq, H, D, ratio if comp is not None else 0, k, 128, max_pos)
-        ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(max(1, wsb // 4), dtype=torch.float32, device=DEV)
         csl.hybrid_attn_decode(gcomp, gswa, dev(bt), dev(q_seq), dev(q_pos), max_pos, dev_bf16(q), gtopk, k, 128,
                                scale, od, out, scales, ws)
     else:
@@ -587,7 +761,7 @@ def test_unmapped_page_is_masked_and_flagged(csl, orc):
     _, _, o64, f = O.hybrid_attn(comp, swa, bt, [0], q_pos, q, topk=topk, out_dtype=O.F32)
     assert f > 0
     out = torch.empty((1, H, D), dtype=torch.float32, device=DEV)
-    ws = torch.empty(max(1, csl.hybrid_attn_workspace(1, H, D, 4, 5, 128, 1000) // 4), dtype=torch.float32,
+    ws = torch.zeros(max(1, csl.hybrid_attn_workspace(1, H, D, 4, 5, 128, 1000) // 4), dtype=torch.float32,
                      device=DEV)
     say("unmapped page masked")
     csl.hybrid_attn_decode(gpu_pool(csl, comp, False), gpu_pool(csl, swa, False), dev(bt), dev(np.zeros(1, np.int32)),
@@ -623,7 +797,7 @@ def test_nan_key_gives_nan_codes_only_where_seen(csl, orc, mode):
     scales = torch.empty((nq, H, D // 64), dtype=torch.float32, device=DEV)
     say(f"nan key {mode} nq {nq}")
     if mode == "decode":
-        ws = torch.empty(max(1, csl.hybrid_attn_workspace(nq, H, D, 4, k, 128, 1200) // 4), dtype=torch.float32,
+        ws = torch.zeros(max(1, csl.hybrid_attn_workspace(nq, H, D, 4, k, 128, 1200) // 4), dtype=torch.float32,
                          device=DEV)
         csl.hybrid_attn_decode(gpu_pool(csl, comp, False), gpu_pool(csl, swa, False), dev(bt), dev(q_seq),
                                dev(q_pos), 1200, dev_bf16(q), dev(topk), k, 128, D ** -0.5, O.FP8, out, scales, ws)
@@ -681,7 +855,7 @@ def test_tiny_workload_end_to_end(csl, orc):
     say("tiny workload: index_topk")
     csl.index_topk(g_idx, gbt, dev(q_seq), dev(q_pos), T, dev_bf16(qi), dev(wi), k, topk, None, ws)
     out = torch.empty((nq, H, D), dtype=torch.float32, device=DEV)
-    wsa = torch.empty(max(1, csl.hybrid_attn_workspace(nq, H, D, 4, k, w.swa, T) // 4), dtype=torch.float32,
+    wsa = torch.zeros(max(1, csl.hybrid_attn_workspace(nq, H, D, 4, k, w.swa, T) // 4), dtype=torch.float32,
                       device=DEV)
     say("tiny workload: hybrid_attn_decode")
     csl.hybrid_attn_decode(g_main, g_raw, gbt, dev(q_seq), dev(q_pos), T, dev_bf16(q), topk, k, w.swa, D ** -0.5,
