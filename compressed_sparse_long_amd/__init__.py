@@ -90,6 +90,9 @@ _fused_ws = _sig("csl_index_attn_decode_workspace", _sz, [_i32, _i32, _i64, _i32
 _fused = _sig("csl_index_attn_decode", C.c_int,
               [_P, _P, _P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _f32, _i32,
                _vp, _vp, _i32, C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, C.POINTER(_QSideJob), _vp, _sz, _vp])
+_fused_noalloc = _sig("csl_index_attn_decode_noalloc", C.c_int,
+                      [_P, _P, _P, _G, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _f32,
+                       _i32, _vp, _vp, _i32, C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, C.POINTER(_QSideJob), _vp])
 _last_error = _sig("csl_last_error", C.c_char_p, [])
 _read_dev_err = _sig("csl_read_device_error", C.c_int, [C.POINTER(C.c_uint32)])
 _timer_enable = _sig("csl_timer_enable", C.c_int, [_i32, _i32])
@@ -98,7 +101,8 @@ _timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.PO
 EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_q_norm_rope_insert",
            "csl_index_topk_workspace", "csl_index_topk", "csl_index_topk_insert",
            "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill",
-           "csl_index_attn_decode_workspace", "csl_index_attn_decode", "csl_last_error",
+           "csl_index_attn_decode_workspace", "csl_index_attn_decode", "csl_index_attn_decode_noalloc",
+           "csl_last_error",
            "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
 
 
@@ -237,9 +241,10 @@ def index_attn_decode_workspace(num_q: int, n_heads: int, max_q_pos: int, k: int
 
 def index_attn_decode(index_pool: Pool, comp: Pool, swa: Pool, block_table, q_seq, q_pos, max_q_pos, q_idx, w, k,
                       topk, q, swa_window, softmax_scale, out_dtype, out, out_scales=None, jobs=(), start_pos=None,
-                      cu_new=None, kth_score=None, ws=None, eps=1e-6, qside=None, stream=None):
+                      cu_new=None, kth_score=None, ws=None, eps=1e-6, qside=None, stream=None, noalloc=False):
     """index_topk_insert then hybrid_attn_decode in two launches (csl_index_attn_decode).  jobs and
-    qside as in index_topk_insert; ws from workspace(index_attn_decode_workspace(...))."""
+    qside as in index_topk_insert; ws from workspace(index_attn_decode_workspace(...)).  noalloc=True
+    calls csl_index_attn_decode_noalloc instead (no ws: the library's static scratch)."""
     ips, cs, ss = index_pool.struct(), comp.struct(), swa.struct()
     pg = pages(block_table)
     nq, nh = int(w.shape[0]), int(w.shape[1])
@@ -253,11 +258,16 @@ def index_attn_decode(index_pool: Pool, comp: Pool, swa: Pool, block_table, q_se
         qsp = qswa.struct()
         qs = _QSideJob(C.addressof(qsp), _ptr(qx), _ptr(qq), int(qq.shape[1]), _ptr(qg), _ptr(qq if qo is None else qo))
     total = int(jobs[0][1].shape[0]) if jobs else (int(qside[1].shape[0]) if qside is not None else 0)
-    _check(_fused(C.byref(ips), C.byref(cs), C.byref(ss), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos),
-                  _ptr(q_idx), _ptr(w), nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(q), int(q.shape[1]),
-                  int(swa_window), float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), len(jobs), arr,
-                  _ptr(start_pos), _ptr(cu_new), total, float(eps), None if qs is None else C.byref(qs), _ptr(ws),
-                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    args = (C.byref(ips), C.byref(cs), C.byref(ss), C.byref(pg), nq, _ptr(q_seq), _ptr(q_pos), int(max_q_pos),
+            _ptr(q_idx), _ptr(w), nh, int(k), _ptr(topk), _ptr(kth_score), _ptr(q), int(q.shape[1]),
+            int(swa_window), float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), len(jobs), arr,
+            _ptr(start_pos), _ptr(cu_new), total, float(eps), None if qs is None else C.byref(qs))
+    if noalloc:
+        if ws is not None:
+            raise ValueError("noalloc=True takes no ws")
+        _check(_fused_noalloc(*args, _stream(stream)))
+    else:
+        _check(_fused(*args, _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def hybrid_attn_decode(comp: Pool | None, swa: Pool, block_table, q_seq, q_pos, max_q_pos, q, topk, k, swa_window,

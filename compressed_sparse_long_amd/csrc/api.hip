@@ -61,6 +61,53 @@ csl_status device_error_ptr(uint32_t** out) {
     return CSL_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+
+// Scratch of the no-allocation fused decode call: one copy per device, held
+// until the process ends, shared by every such call on that device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The device address of `scratch` on the current device (the host-side name is
+// only a stand-in), taken once per device.  The first call on a device also
+// clears the arrival counters at the start of the scratch (on `st`, before the
+// caller's launches); every call that completes leaves them zero again.
+csl_status static_scratch(hipStream_t st, void** out) {
+    static void* ptrs[kMaxDevices] = {};
+    static hipError_t errs[kMaxDevices] = {};
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CSL_EUNSUPPORTED, "device id %d beyond %d", dev, kMaxDevices);
+    std::call_once(once[dev], [&] {
+        void* ptr = nullptr;
+        hipError_t se = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+        if (se == hipSuccess && ptr) {
+            constexpr int words = kDecodeCounters;
+            hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+                               static_cast<uint32_t*>(ptr), words);
+            se = hipGetLastError();
+        }
+        errs[dev] = se;
+        if (se == hipSuccess) ptrs[dev] = ptr;
+    });
+    if (errs[dev] != hipSuccess) return hip_fail(errs[dev], "static scratch set-up");
+    if (!ptrs[dev]) return fail(CSL_EHIP, "static scratch of device %d is unavailable", dev);
+    *out = ptrs[dev];
+    return CSL_OK;
+}
+
 // ---------------------------------------------------------------- timers
 
 struct Timer {
@@ -872,6 +919,29 @@ csl_status csl_index_attn_decode(const csl_pool* index_pool, const csl_pool* com
         if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
     }
     return CSL_OK;
+}
+
+csl_status csl_index_attn_decode_noalloc(const csl_pool* index_pool, const csl_pool* comp, const csl_pool* swa,
+                                         const csl_pages* pages, int32_t num_q, const int32_t* q_seq,
+                                         const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q_idx,
+                                         const float* w, int32_t n_idx_heads, int32_t k, int32_t* topk,
+                                         float* kth_score, const uint16_t* q, int32_t n_heads, int32_t swa_window,
+                                         float softmax_scale, int32_t out_dtype, void* out, float* out_scales,
+                                         int32_t n_jobs, const csl_insert_job* jobs, const int64_t* start_pos,
+                                         const int32_t* cu_new, int32_t total_new, float eps,
+                                         const csl_qside_job* qside, csl_stream_t stream) {
+    if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
+    const size_t need = csl_index_attn_decode_workspace(num_q, n_heads, max_q_pos, k, swa_window);
+    if (need > kStaticScratchBytes)
+        return fail(CSL_ERANGE, "the call needs %zu bytes of scratch, the static scratch holds %zu", need,
+                    kStaticScratchBytes);
+    void* ws = nullptr;
+    csl_status st;
+    if ((st = static_scratch(static_cast<hipStream_t>(stream), &ws))) return st;
+    return csl_index_attn_decode(index_pool, comp, swa, pages, num_q, q_seq, q_pos, max_q_pos, q_idx, w, n_idx_heads,
+                                 k, topk, kth_score, q, n_heads, swa_window, softmax_scale, out_dtype, out,
+                                 out_scales, n_jobs, jobs, start_pos, cu_new, total_new, eps, qside, ws,
+                                 kStaticScratchBytes, stream);
 }
 
 csl_status csl_hybrid_attn_prefill(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages,

@@ -305,6 +305,32 @@ csl_status csl_index_attn_decode(const csl_pool* index_pool /* host */, const cs
                                  const csl_qside_job* qside /* host, nullable */, void* ws, size_t ws_bytes,
                                  csl_stream_t stream);
 
+/*
+ * csl_index_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus ws, ws_bytes),
+ * kernels and results as csl_index_attn_decode; its scratch is a static device
+ * array of 64 MiB in the library, one copy per device, held until the process
+ * ends.  A call whose csl_index_attn_decode_workspace() exceeds 64 MiB returns
+ * CSL_ERANGE and launches nothing (16 queries of 64 heads fit up to 1M
+ * positions).  The first call on a device also launches, on `stream`, the
+ * clearing of the scratch's arrival counters.  The library allocates nothing
+ * in this call.  Every call on one device shares that device's scratch: calls
+ * that overlap on one device (different streams, or different host threads
+ * without ordering) race and give undefined results.
+ */
+csl_status csl_index_attn_decode_noalloc(const csl_pool* index_pool /* host */, const csl_pool* comp /* host */,
+                                         const csl_pool* swa /* host */, const csl_pages* pages /* host */,
+                                         int32_t num_q, const int32_t* q_seq, const int64_t* q_pos,
+                                         int64_t max_q_pos, const uint16_t* q_idx, const float* w,
+                                         int32_t n_idx_heads, int32_t k, int32_t* topk, float* kth_score,
+                                         const uint16_t* q, int32_t n_heads, int32_t swa_window,
+                                         float softmax_scale, int32_t out_dtype, void* out, float* out_scales,
+                                         int32_t n_jobs, const csl_insert_job* jobs /* host */,
+                                         const int64_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                         float eps, const csl_qside_job* qside /* host, nullable */,
+                                         csl_stream_t stream);
+
 /* Message of the last failing call on the calling thread ("" if none). */
 const char* csl_last_error(void);
 
