@@ -550,6 +550,28 @@ struct MergeIn {
     int64_t nv;          // visible ids
     int kl, k;
 };
+// The candidate slots a merge thread holds (KPT of them) and the (kl+1)-th
+// element of chunk `thread`, loaded before the query's visible count is known.
+template <int KPT>
+struct CandRegs {
+    uint2 c[KPT];
+    uint2 nx;
+};
+// Thread t loads slots [KPT t, KPT t + KPT) of the first nslots_max and chunk t's
+// next element if t < nch_max; slots past the query's chunks are masked by the merge.
+template <int KPT>
+__device__ __forceinline__ void cand_load(const MergeIn& in, int64_t nslots_max, int nch_max, CandRegs<KPT>& r) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int64_t f = (int64_t)tid * KPT + i;
+        r.c[i] = make_uint2(0u, 0xffffffffu);
+        if (f < nslots_max) r.c[i] = in.cand[f];
+    }
+    r.nx = make_uint2(0u, 0xffffffffu);
+    if (tid < nch_max) r.nx = in.cnext[tid];
+}
+
 // LDS of one merge: hist[2048], cand[kCandCap], wave[NT/64], sel[8 + NT/64], min[NT/64], fail[1].
 struct MergeLds {
     uint32_t* hist;
@@ -572,7 +594,8 @@ struct MergeLds {
 // position may be written twice when the fallback runs); kth (nullable) the
 // k-th score.
 template <int NT, int KPT, typename Out>
-__device__ __forceinline__ void merge_candidates(const MergeIn& in, const Out& out, float* kth, const MergeLds& m) {
+__device__ __forceinline__ void merge_candidates(const MergeIn& in, const CandRegs<KPT>& r, const Out& out, float* kth,
+                                                 const MergeLds& m) {
     const int tid = threadIdx.x;
     const int64_t nv = in.nv;
     if (nv <= in.k) {
@@ -588,13 +611,13 @@ __device__ __forceinline__ void merge_candidates(const MergeIn& in, const Out& o
         return;
     }
     // the chunks' (kl+1)-th elements, fetched beside the candidates
-    const uint2 nx = tid < nch ? in.cnext[tid] : make_uint2(0u, 0xffffffffu);
+    const uint2 nx = tid < nch ? r.nx : make_uint2(0u, 0xffffffffu);
     uint32_t key[KPT], id[KPT], vmask = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int64_t f = (int64_t)tid * KPT + i;
         uint2 c = make_uint2(0u, 0xffffffffu);
-        if (f < nslots) c = in.cand[f];
+        if (f < nslots) c = r.c[i];
         key[i] = c.x;
         id[i] = c.y;
         vmask |= (c.y != 0xffffffffu ? 1u : 0u) << i;

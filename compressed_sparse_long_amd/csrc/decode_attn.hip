@@ -136,9 +136,33 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
 
     const int head = 16 * hg + r16;
     const bool hv = head < a.n_heads;
-    // the query (wave-uniform)
-    int s = __builtin_amdgcn_readfirstlane(a.q_seq[n]);
+    const int64_t kb = (int64_t)sp * d.per;
+
+    // every load that needs only n first, in one round trip: the query's sequence and
+    // position, the wave's q slice, and the given ids or the first-stage candidates
+    const int s_raw = a.q_seq[n];
     const int64_t p_raw = a.q_pos[n];
+    // q slice of the wave as the B operand of S^T: column = head, k-step ks = dims 128 wave + 32 ks + 8 g .. +7
+    bf16x8 qb[4];
+    {
+        const uint16_t* qrow = (hv ? a.q + ((int64_t)n * a.n_heads + head) * D
+                                   : reinterpret_cast<const uint16_t*>(g_zero_row512)) + 128 * wave + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    }
+    int32_t pre_id = -1;
+    if (!MERGE && a.topk && tid < d.per && kb + tid < a.k) pre_id = a.topk[(int64_t)n * a.k + kb + tid];
+    MergeIn in;
+    in.sc = d.scores + (int64_t)n * d.stride;
+    in.cand = d.cand + (int64_t)n * d.nchunks * d.kl;
+    in.cnext = d.c_next + (int64_t)n * d.nchunks;
+    in.kl = d.kl;
+    in.k = a.k;
+    CandRegs<MERGE == 2 ? 16 : 8> cr;
+    if (MERGE) cand_load(in, (int64_t)d.nchunks * d.kl, d.nchunks, cr);
+
+    // the query (wave-uniform)
+    int s = __builtin_amdgcn_readfirstlane(s_raw);
     const int64_t p_in = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)((uint64_t)p_raw >> 32)) << 32) |
                                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p_raw));
     const bool ok = s >= 0 && s < a.num_seqs && p_in >= 0 && p_in <= a.max_q_pos;
@@ -149,22 +173,12 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     const int64_t Lc = a.comp_rows ? (a.topk || MERGE ? (int64_t)a.k : nv_c) : 0;
     const int64_t lo = p - a.swa_window > 0 ? p - a.swa_window : 0;
     const int64_t L = ok ? Lc + (p - lo) : 0;
-    const int64_t kb = (int64_t)sp * d.per;
     const int64_t ke = kb + d.per < L ? kb + d.per : L;
     const int64_t kce = ke < Lc ? ke : Lc;
     const int nk = ke > kb ? (int)(ke - kb) : 0;     // keys of this split
     const int nkc = kce > kb ? (int)(kce - kb) : 0;  // of them compressed
+    in.nv = ok ? (p >> 2 < d.stride ? p >> 2 : d.stride) : 0;
 
-    // every independent load first: q slice, the query's block-table row, the
-    // candidates (merge) or the given ids
-    // q slice of the wave as the B operand of S^T: column = head, k-step ks = dims 128 wave + 32 ks + 8 g .. +7
-    bf16x8 qb[4];
-    {
-        const uint16_t* qrow = (hv ? a.q + ((int64_t)n * a.n_heads + head) * D
-                                   : reinterpret_cast<const uint16_t*>(g_zero_row512)) + 128 * wave + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-    }
     const int64_t nbt64 = ok ? ((p + 255) >> 8 < (int64_t)a.max_blocks ? (p + 255) >> 8 : (int64_t)a.max_blocks) : 0;
     const bool staged = nbt64 <= kDBt;
     int32_t btv[kBtPer];
@@ -176,19 +190,6 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
             btv[i] = (staged && b < (int)nbt64) ? btrow[b] : -1;
         }
     }
-    MergeIn in;
-    in.nv = ok ? (p >> 2 < d.stride ? p >> 2 : d.stride) : 0;
-    in.sc = d.scores + (int64_t)n * d.stride;
-    in.cand = d.cand + (int64_t)n * d.nchunks * d.kl;
-    in.cnext = d.c_next + (int64_t)n * d.nchunks;
-    in.kl = d.kl;
-    in.k = a.k;
-    int32_t pre_id = -1;
-    if (!MERGE && a.topk && tid < nkc) pre_id = a.topk[(int64_t)n * a.k + kb + tid];
-
-#pragma unroll
-    for (int i = 0; i < kBtPer; ++i)
-        if (i * kDT + tid < (int)nbt64 && staged) s_bt[i * kDT + tid] = btv[i];
     if (tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
 
     if constexpr (MERGE > 0) {
@@ -200,14 +201,13 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         const bool writer = hg == 0 && sp == 0;
         const SliceOut out = {writer ? d.topk_out + (int64_t)n * a.k : nullptr, s_ids, (uint32_t)kb, (uint32_t)nkc};
         float* kthp = writer && d.kth ? d.kth + n : nullptr;
-        if (in.nv <= a.k) {
-            select_all(in.sc, in.nv, a.k, out, kthp, m.min);
-        } else if constexpr (MERGE == 1) {
-            merge_candidates<kDT, 8>(in, out, kthp, m);
-        } else {
-            merge_candidates<kDT, 16>(in, out, kthp, m);
-        }
+        if (in.nv <= a.k) select_all(in.sc, in.nv, a.k, out, kthp, m.min);
+        else merge_candidates<kDT, MERGE == 2 ? 16 : 8>(in, cr, out, kthp, m);
     }
+    // the block-table row lands after the merge, which does not need it
+#pragma unroll
+    for (int i = 0; i < kBtPer; ++i)
+        if (i * kDT + tid < (int)nbt64 && staged) s_bt[i * kDT + tid] = btv[i];
     __syncthreads();  // s_bt, s_ids, s_rope; the merge is done with the ring
 
     // the split's key rows: thread t resolves key kb + t
@@ -224,9 +224,9 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
                 const int64_t id = MERGE ? (int64_t)s_ids[tid] : (a.topk ? (int64_t)pre_id : j);
                 if (id >= nv_c) raise_error(a.err, kErrTopk);
                 if (id >= 0 && id < nv_c) {
-                    per_page = kBlockPositions / a.comp_ratio;
-                    blk = id / per_page;
-                    slot = id - blk * per_page;
+                    per_page = kBlockPositions / a.comp_ratio;  // 64 or 2: a power of two
+                    blk = id >> (31 - __builtin_clz((unsigned)per_page));
+                    slot = id & (per_page - 1);
                     base = a.comp_rows;
                     np = a.comp_pages;
                 }

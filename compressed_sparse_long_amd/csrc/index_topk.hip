@@ -648,7 +648,12 @@ __device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
     in.kl = a.kl;
     in.k = a.k;
     const MergeLds m = {s_hist, s_cand, s_wave, s_sel, s_min, &s_fail};
-    merge_candidates<NT, kMergeSlots>(in, GlobalOut{a.topk + (int64_t)n * a.k}, a.kth ? a.kth + n : nullptr, m);
+    CandRegs<kMergeSlots> cr;
+    if (in.nv > in.k) {
+        const int nch = (int)((in.nv + kChunk - 1) / kChunk);
+        cand_load(in, (int64_t)nch * in.kl, nch, cr);
+    }
+    merge_candidates<NT, kMergeSlots>(in, cr, GlobalOut{a.topk + (int64_t)n * a.k}, a.kth ? a.kth + n : nullptr, m);
 }
 
 template <int NT>
