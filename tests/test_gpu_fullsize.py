@@ -146,12 +146,13 @@ def decode_query_check(csl, w, st, s, layer, theta=10000.0):
                                               host(st.w_idx[s:s + 1]), w.topk, want_scores=True, max_cand=nv)
         g_topk = host(st.topk[s:s + 1])
         assert_topk_equivalent(g_topk, o_topk, o_sc, o_kth, what=f"c4a seq {s}")
-        ids = o_topk[0][o_topk[0] >= 0].astype(np.int64)
+        # the attention is checked over the GPU's ids (the oracle's up to allowed swaps)
+        ids = g_topk[0][g_topk[0] >= 0].astype(np.int64)
         lg_seq = W.logits(w, s, 0, T + 1, 2, device=DEV)
         main_o = oracle_rows(rep["main4"], ids, x_seq, lg_seq, st.gain, theta)
         check_rows(gpu_rows(rep["main4"], bt_row, ids), main_o, D, w.kv_dtype, f"c4a seq {s}: top-k entries")
         comp = host_pool(4, 2, D, R, theta, w.kv_dtype, mb, ids, main_o)
-        topk_arg = o_topk
+        topk_arg = g_topk
         same = np.array_equal(g_topk, o_topk)
     else:
         ids = np.arange(p // 128, dtype=np.int64)
@@ -173,10 +174,9 @@ def decode_query_check(csl, w, st, s, layer, theta=10000.0):
         st.attend(0)
         torch.cuda.synchronize()
         assert csl.read_device_error() == 0
-    if same:
-        sc = st.out_scales[layer]
-        check_out(csl, st.out[layer][s:s + 1], None if sc is None else sc[s:s + 1], o_out, o_sc8, o64, w.out_dtype,
-                  f"{layer} seq {s}: attention output")
+    sc = st.out_scales[layer]
+    check_out(csl, st.out[layer][s:s + 1], None if sc is None else sc[s:s + 1], o_out, o_sc8, o64, w.out_dtype,
+              f"{layer} seq {s}: attention output")
     return same
 
 
@@ -204,11 +204,9 @@ def test_c128a_decode_full_size(csl):
 def test_c4a_decode_full_size(csl):
     w = W.c4a_decode()
     st = run_decode(csl, w)
-    same = 0
-    for s in (0, 7, 15):
+    for s in range(w.num_seqs):
         say(f"{w.name}: oracle check of sequence {s}")
-        same += decode_query_check(csl, w, st, s, "c4a")
-    assert same >= 2, "top-k sets differ by allowed ties on most sampled queries"
+        decode_query_check(csl, w, st, s, "c4a")
     del st
     torch.cuda.empty_cache()
 
@@ -216,11 +214,9 @@ def test_c4a_decode_full_size(csl):
 def test_c4a_fp4_index_decode_full_size(csl):
     w = W.c4a_decode_fp4()
     st = run_decode(csl, w)
-    same = 0
     for s in (0, 15):
         say(f"{w.name}: oracle check of sequence {s}")
-        same += decode_query_check(csl, w, st, s, "c4a")
-    assert same >= 1, "top-k sets differ by allowed ties on every sampled query"
+        decode_query_check(csl, w, st, s, "c4a")
     del st
     torch.cuda.empty_cache()
 
@@ -274,7 +270,8 @@ def test_c4a_prefill_full_size(csl):
     say(f"{w.name}: oracle rows of the sampled queries")
     x_seq = W.latent(w, 0, 0, Tn, device=DEV)
     lg_seq = W.logits(w, 0, 0, Tn, 2, device=DEV)
-    ids = np.unique(o_topk[o_topk >= 0]).astype(np.int64)
+    # the attention is checked over the GPU's ids (the oracle's up to allowed swaps)
+    ids = np.unique(g_topk[g_topk >= 0]).astype(np.int64)
     main_o = oracle_rows(st.main, ids, x_seq, lg_seq, st.gain, theta)
     check_rows(gpu_rows(st.main, bt_row, ids), main_o, D, w.kv_dtype, "prefill top-k entries")
     raw_ids = np.unique(np.concatenate([np.arange(max(0, p - w.swa), p) for p in pos])).astype(np.int64)
@@ -283,7 +280,7 @@ def test_c4a_prefill_full_size(csl):
     comp = host_pool(4, 2, D, R, theta, w.kv_dtype, mb, ids, main_o)
     raw_pool = host_pool(1, 1, D, R, theta, w.kv_dtype, mb, raw_ids, raw_o)
     say(f"{w.name}: oracle attention of {len(js)} queries")
-    o_out, o_sc8, o64, f = O.hybrid_attn(comp, raw_pool, bt_o, q_seq, pos, host_u16(st.q[jt]), topk=o_topk,
+    o_out, o_sc8, o64, f = O.hybrid_attn(comp, raw_pool, bt_o, q_seq, pos, host_u16(st.q[jt]), topk=g_topk,
                                          swa_window=w.swa, softmax_scale=st.scale, out_dtype=w.out_dtype)
     assert f == 0
     # fp8 outputs: the sampled queries' attention re-run over the oracle's rows
@@ -293,10 +290,6 @@ def test_c4a_prefill_full_size(csl):
     st.attend()
     torch.cuda.synchronize()
     assert csl.read_device_error() == 0
-    same = [m for m in range(len(js)) if np.array_equal(g_topk[m], o_topk[m])]
-    assert len(same) >= len(js) * 3 // 4
-    sel = jt[torch.tensor(same, device=DEV)]
-    check_out(csl, st.out[sel], st.out_scales[sel], o_out[same], o_sc8[same], o64[same], w.out_dtype,
-              "prefill attention output")
+    check_out(csl, st.out[jt], st.out_scales[jt], o_out, o_sc8, o64, w.out_dtype, "prefill attention output")
     del st
     torch.cuda.empty_cache()

@@ -840,8 +840,6 @@ def test_tiny_workload_end_to_end(csl, orc):
     for pool, xx, ll in ((o_main, x, lg), (o_idx, xi, lgi), (o_raw, x, None)):
         assert O.compress_insert(pool, bt, [0], [0, T], xx, ll) == 0
     o_topk, o_kth, o_sc, _ = O.index_topk(o_idx, bt, q_seq, q_pos, qi, wi, k, want_scores=True, max_cand=T // 4)
-    o_out, _, o64, _ = O.hybrid_attn(o_main, o_raw, bt, q_seq, q_pos, q, topk=o_topk, swa_window=w.swa,
-                                     out_dtype=O.F32)
     g_main = csl.Pool(4, 2, D, R, THETA, csl.BF16, P)
     g_idx = csl.Pool(4, 2, DI, 0, THETA, csl.BF16, P)
     g_raw = csl.Pool(1, 1, D, R, THETA, csl.BF16, P)
@@ -864,6 +862,7 @@ def test_tiny_workload_end_to_end(csl, orc):
     assert csl.read_device_error() == 0
     g_topk = host(topk)
     assert_topk_equivalent(g_topk, o_topk, o_sc, o_kth, what="tiny")
-    same = [n for n in range(nq) if np.array_equal(g_topk[n], o_topk[n])]
-    assert len(same) >= nq * 3 // 4
-    assert_close(host(out)[same], o64[same], what="tiny attention")
+    # every query's attention against the oracle's over the GPU's ids (the oracle's up to allowed swaps)
+    _, _, o64g, f = O.hybrid_attn(o_main, o_raw, bt, q_seq, q_pos, q, topk=g_topk, swa_window=w.swa, out_dtype=O.F32)
+    assert f == 0
+    assert_close(host(out), o64g, what="tiny attention")
