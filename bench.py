@@ -31,8 +31,16 @@ sys.path.insert(0, ROOT)
 METRIC = "decode queries/s + HBM GB/s, c4a top-k512+SWA128 at 128K ctx, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_c4a_decode_b16_128k.pmc.json")
-SCORE_SOURCE = os.path.join(ROOT, "compressed_sparse_long_amd", "csrc", "index_topk.hip")
+CSRC = os.path.join(ROOT, "compressed_sparse_long_amd", "csrc")
+# committed HBM counter runs: (summary json, kernel source it was taken on)
+TRAFFIC = {
+    "index_score": (os.path.join(ROOT, "profiles", "index_score_c4a_decode_b16_128k.pmc.json"),
+                    os.path.join(CSRC, "index_topk.hip")),
+    "decode_attention": (os.path.join(ROOT, "profiles", "decode_attn_c4a_decode_b16_128k.pmc.json"),
+                         os.path.join(CSRC, "decode_attn.hip")),
+    "prefill_attention": (os.path.join(ROOT, "profiles", "attention_prefill_c4a_8k_on_64k.pmc.json"),
+                          os.path.join(CSRC, "attn.hip")),
+}
 
 
 def log(msg):
@@ -411,15 +419,92 @@ def cpu_baseline(setup: DecodeSetup, n_seqs: int, seconds: float) -> dict:
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
+def cpu_baseline_prefill(w, n_sample: int, seconds: float, device="cuda") -> dict:
+    """The oracle on the prefill chunk: the prefix cache is built untimed; then the
+    chunk's inserts (all new tokens, three pools) are timed once, and the index
+    top-k plus attention of evenly spaced sampled queries, in batches of 16 (the
+    oracle spreads a batch's queries over its threads), for `seconds`.  tokens/s =
+    1 / (insert time per token + top-k and attention time per query)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from synth import workloads as W
+
+    T0, n, D, R, DI = w.ctx, w.new_tokens, w.dim, w.rope_dims, w.idx_dim
+    mb = w.max_blocks
+    bt = np.arange(mb, dtype=np.int32)[None]
+    main = O.HostPool(4, 2, D, R, w.theta, w.kv_dtype, mb)
+    raw = O.HostPool(1, 1, D, R, w.theta, w.kv_dtype, mb)
+    idx = O.HostPool(4, 2, DI, 0, w.theta, O.BF16, mb)
+
+    def u16(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    gain = W.gain(w, D).numpy()
+    gain_i = W.gain(w, DI, tid=W.T_GAIN_I).numpy()
+
+    def inputs(t0, cnt):
+        return (u16(W.latent(w, 0, t0, cnt, device=device)), W.logits(w, 0, t0, cnt, 2, device=device).cpu().numpy(),
+                u16(W.latent(w, 0, t0, cnt, dim=DI, tid=W.T_XI, device=device)),
+                W.logits(w, 0, t0, cnt, 2, tid=W.T_LOGITS_I, device=device).cpu().numpy())
+
+    def insert(t0, cnt, x, lg, xi, lgi):
+        st, cu = np.array([t0], np.int64), np.array([0, cnt], np.int32)
+        assert O.compress_insert(raw, bt, st, cu, x) == 0
+        assert O.compress_insert(main, bt, st, cu, x, lg, gain) == 0
+        assert O.compress_insert(idx, bt, st, cu, xi, lgi, gain_i) == 0
+
+    t_build = time.time()
+    insert(0, T0, *inputs(0, T0))
+    log(f"oracle prefix of {T0} tokens built in {time.time() - t_build:.1f}s")
+    new = inputs(T0, n)
+    t_ins = time.perf_counter()
+    insert(T0, n, *new)
+    t_ins = time.perf_counter() - t_ins
+    qd = W.queries(w, device=device)
+    q, qi, wi = u16(qd["q"]), u16(qd["q_idx"]), qd["w_idx"].cpu().numpy()
+    pos = w.query_positions().numpy()
+    order = np.linspace(0, n - 1, max(16, n_sample)).astype(np.int64)
+    scale = D ** -0.5
+
+    def run(secs):
+        done, t_start, b = 0, time.perf_counter(), 0
+        while True:
+            js = order[(16 * b + np.arange(16)) % len(order)]
+            b += 1
+            seqs = np.zeros(16, np.int32)
+            topk, _, _, _ = O.index_topk(idx, bt, seqs, pos[js], qi[js], wi[js], w.topk)
+            O.hybrid_attn(main, raw, bt, seqs, pos[js], q[js], topk=topk, swa_window=w.swa, softmax_scale=scale,
+                          out_dtype=w.out_dtype)
+            done += 16
+            el = time.perf_counter() - t_start
+            if el >= secs:
+                return done, el
+
+    threads = O.num_threads()
+    done, el = run(seconds)
+    O.set_threads(1)
+    done1, el1 = run(seconds / 4)
+    O.set_threads(threads)
+    per_tok = t_ins / n
+    return {"value": round(1.0 / (per_tok + el / done), 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"insert of all {n} new tokens (3 pools) in {t_ins:.1f}s, then index_topk + hybrid_attn of "
+                      f"{done} queries (batches of 16 of {len(order)} evenly spaced ones) in {el:.1f}s; fp64, "
+                      f"OpenMP over a batch's queries",
+            "one_thread_value": round(1.0 / (per_tok + el1 / done1), 1), "nproc": os.cpu_count()}
+
+
 # ---------------------------------------------------------------------------
 
-def traffic_from_profile(launch_kind: str):
-    """HBM bytes per launch of the index score kernel from committed rocprofv3 counter runs,
-    or None when the kernel source changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_from_profile(kernel: str, launch_kind: str):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, or None
+    when there are none for this launch or the kernel source changed since."""
+    path, source = TRAFFIC[kernel]
+    if not os.path.exists(path):
         return None
-    d = json.load(open(TRAFFIC_FILE))
-    sha = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
+    d = json.load(open(path))
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
     if d.get("source_sha256") != sha or d.get("launch") != launch_kind:
         return None
     return float(d["hbm_bytes_per_launch"])
@@ -524,10 +609,11 @@ def run_prefill(args):
                    "heads": w.n_heads, "latent_dim": w.dim, "indexer": f"{w.idx_heads}x{w.idx_dim}",
                    "kv_dtype": "bf16", "out_dtype": "fp8", "hip_graphs": False},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profile("prefill_attention", w.name) if dom == "attention" else None,
                      "timing": "hipExtLaunchKernel start/stop events stamped by each launch in the timed steps"},
         "kernels": kern,
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu else cpu_baseline_prefill(w, 256, args.cpu_seconds),
     }
     print(json.dumps(res), flush=True)
 
@@ -771,7 +857,7 @@ def main():
     achieved = k_bytes / (k_avg_ms * 1e-3) / 1e9 if k_n else None
     roof = {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-            "traffic": traffic_from_profile(w.name) if "c4a" in w.layers else None,
+            "traffic": traffic_from_profile("index_score", w.name) if "c4a" in w.layers else None,
             "algorithmic_bytes_per_launch": k_bytes, "avg_launch_ms": round(k_avg_ms, 5), "timed_launches": k_n,
             "timing": ("hipExtLaunchKernel start/stop events stamped by each launch of the kernel itself, over "
                        f"{k_n} eager steps right after the timed graph replays (graph capture drops the stamps)"
@@ -791,6 +877,10 @@ def main():
         if kb[name]:
             e["GBps"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
             e["frac"] = round(kb[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if name == "index_score" and "c4a" in w.layers:
+            e["traffic"] = traffic_from_profile("index_score", w.name)
+        if name == "attention" and setup.fused:
+            e["traffic"] = traffic_from_profile("decode_attention", w.name)
         kernels[name] = e
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": K,
