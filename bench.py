@@ -134,7 +134,7 @@ class DecodeSetup:
         ws128 = csl.hybrid_attn_workspace(nq, w.n_heads, D, 128, 0, w.swa, T) if "c128a" in w.layers else 0
         self.ws_attn = torch.zeros(max(1, max(ws4, ws128) // 4), dtype=torch.float32, device=device)
         # the two-launch step (index scores + inserts, then merge + attention): c4a layers with bf16 keys
-        self.fused = fused_call and "c4a" in w.layers and kv == 1
+        self.fused = fused_call and "c4a" in w.layers
         self.ws_fused = (csl.workspace(csl.index_attn_decode_workspace(nq, w.n_heads, T, w.topk, w.swa), device)
                          if self.fused else None)
         odt = {0: torch.float32, 1: torch.bfloat16, 2: torch.uint8}[w.out_dtype]
@@ -165,7 +165,7 @@ class DecodeSetup:
         self.csl.compress_insert_multi(self.insert_jobs(p), self.bt, self.start, self.cu1)
 
     def step(self, r: int):
-        """One decode step.  By default (c4a layers, bf16 keys) the step is the
+        """One decode step.  By default (c4a layers) the step is the
         two-launch call index_attn_decode: index scores with the raw and main
         inserts riding in the score launch, then the candidates' merge and the
         attention with the index insert riding in it (the query at p reads

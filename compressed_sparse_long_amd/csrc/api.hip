@@ -255,7 +255,7 @@ int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_
     return (int)(sp > 1 ? sp : 1);
 }
 
-// Decode attention on 512-dim bf16 keys (decode_attn_kernel): G head groups of
+// Decode attention on 512-dim bf16 or fp8 keys (decode_attn_kernel): G head groups of
 // 16; the key list (rounded up to 32-key tiles) split so that the launch holds
 // about 256 workgroups, with 32..256 keys per split; at most 8 splits are
 // merged inside the launch by the last arriving split (more, or more than
@@ -290,8 +290,8 @@ size_t partial_bytes(int num_q, int splits, int n_heads, int dim) {
     return splits > 1 ? (size_t)num_q * splits * n_heads * ((size_t)dim + 2) * sizeof(float) : 0;
 }
 
-// Whether the decode call runs decode_attn_kernel (512-dim bf16 keys).
-bool use_decode_kernel(int dim, int key_dtype) { return dim == 512 && key_dtype == CSL_BF16; }
+// Whether the decode call runs decode_attn_kernel (512-dim bf16 or fp8 keys).
+bool use_decode_kernel(int dim, int key_dtype) { return dim == 512 && (key_dtype == CSL_BF16 || key_dtype == CSL_FP8_E4M3); }
 
 // Workspace of a decode attention call: the counter block, then the partials
 // of the larger of the paths the key type could take (the key type is not an
@@ -804,7 +804,7 @@ csl_status csl_index_attn_decode(const csl_pool* index_pool, const csl_pool* com
         return st;
     if (comp->ratio != 4) return fail(CSL_EINVAL, "comp.ratio must be 4: the indexer selects c4a entries");
     if (!use_decode_kernel(swa->dim, swa->dtype))
-        return fail(CSL_EUNSUPPORTED, "the fused decode call takes 512-dim bf16 keys (fp8 keys: index_topk + hybrid_attn_decode)");
+        return fail(CSL_EUNSUPPORTED, "the fused decode call takes 512-dim bf16 or fp8 keys");
     if (!topk) return fail(CSL_EINVAL, "topk is NULL");
     const size_t need = csl_index_attn_decode_workspace(num_q, n_heads, max_q_pos, k, swa_window);
     if (num_q > 0 && (!ws || ws_bytes < need)) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -96,7 +96,7 @@ struct AttnArgs {
     RopeFreqs rf;
 };
 
-// Decode attention over 512-dim bf16 keys (decode_attn_kernel): the attention
+// Decode attention over 512-dim bf16 or fp8 keys (decode_attn_kernel): the attention
 // arguments plus the work split and, when the launch also merges the
 // indexer's first-stage candidates, where they are.
 constexpr int kDecodeMaxSplitKeys = 256;  // keys of one split (8 tiles of 32)

@@ -1,4 +1,4 @@
-// Steps 4-6 for decode queries on gfx950, 512-dim bf16 keys: hybrid attention
+// Steps 4-6 for decode queries on gfx950, 512-dim bf16 or fp8 keys: hybrid attention
 // over (top-k or every visible compressed entry) U raw window [p-S, p-1] with
 // one softmax and K = V ([Summary] 共享鍵和值向量, 短滑動窗口; [Notes] ⚠️ 注意：
 // C128A 的因果性约束), inverse RoPE at the query position and the output store
@@ -38,6 +38,12 @@
 //     in LDS row 16 mt + 4 (a % 4) + a / 4 of the tile, which is the key
 //     order the transposed reads produce, and keeps both the S operand reads
 //     and the transposed reads free of bank conflicts (1040-byte rows).
+// fp8 keys (544-byte rows: 512 e4m3 codes, then one fp32 scale per 64-dim
+// group) are staged as stored, seven slots deep, and widened to their exact
+// bf16 values on the way to the MFMAs (the conversion unit with scale 1); the
+// V^T operands come from 8-bit transposing reads.  S runs one MFMA chain per
+// 64-dim group and adds the chains times the keys' group scales in fp32; in
+// P.V the group scale of each key moves onto P, so V needs no rounding.
 #include "csl_insert.hpp"
 #include "csl_select.hpp"
 
@@ -49,6 +55,10 @@ constexpr int kDT = 256;           // threads per workgroup (4 waves)
 constexpr int kDTile = 32;         // keys per tile
 constexpr int kDRow = 1040;        // LDS stride of a staged 1 KiB row (260 words: 4 banks apart)
 constexpr int kDRing = 4;          // ring slots: one computed, up to three in flight
+// fp8 keys: 544-byte rows (512 e4m3 codes, then the 8 fp32 scales of the 64-dim groups)
+constexpr int kDRowBytes8 = 544;
+constexpr int kDRow8 = 560;        // LDS stride of a staged fp8 row (140 words)
+constexpr int kDRing8 = 7;         // ring slots for fp8 rows: one computed, up to six in flight
 constexpr int kDBt = 2048;         // block-table entries staged in LDS (contexts up to 512K positions)
 constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer descriptor word 3 (untyped dword access)
 constexpr int kSc1 = 16;                      // cache policy: device scope (coherent across the XCDs' L2s)
@@ -62,6 +72,37 @@ __device__ __forceinline__ void dma_row(uint32_t lds, const uint8_t* src) {
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)p);
+}
+
+// eight e4m3 codes (bytes of w, in order) to their exact bf16 values
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+    u32x4 o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
+    return __builtin_bit_cast(bf16x8, o);
+}
+
+// transposing 8-bit LDS read: in each 16-lane group, lane j receives byte j % 8 of the
+// 8-byte words read by lanes 2c + j / 8 (c = 0..7) of the group
+typedef int int2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 tr8_read(const uint8_t* p) {
+    const int2v v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2v*)(const_cast<uint8_t*>(p)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// tiles of n 8-load issues each may stay in flight (n <= 6)
+__device__ __forceinline__ void wait_tiles(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    }
 }
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -96,15 +137,18 @@ struct SliceOut {
 // `c` (the fused call's index-pool inserts: this launch never reads index rows).
 // MERGE: 0 = ids given (or dense); 1 / 2 = the workgroup merges the first-stage
 // candidates, 8 / 16 slots per thread (up to 2048 / 4096 slots).
-template <bool PREC, int MERGE>
+template <bool PREC, int MERGE, bool KV8>
 __global__ void __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     constexpr int D = 512;
+    constexpr int ROW = KV8 ? kDRow8 : kDRow;           // LDS stride of a staged row
+    constexpr int RING = KV8 ? kDRing8 : kDRing;        // ring slots
+    constexpr int RB = KV8 ? kDRowBytes8 : 2 * D;       // stored row bytes
     constexpr int kBtPer = kDBt / kDT;  // block-table entries staged per thread
     const AttnArgs& a = d.at;
     // ring of staged key tiles; before the first tile it holds the merge's
     // scratch, after the last one the epilogue's staging
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDRing * kDTile * kDRow];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[RING * kDTile * ROW];
     static_assert(sizeof(InsertSmem) <= sizeof(s_ring), "the insert body fits the ring");
     const int64_t n_attn = ((int64_t)a.num_q * d.S + 7) / 8 * 8 * d.G;
     if ((int64_t)blockIdx.x >= n_attn) {
@@ -241,7 +285,7 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
             if (blk >= 0) {
                 pg = blk < a.max_blocks ? (staged ? s_bt[blk] : a.bt[(int64_t)s * a.max_blocks + blk]) : -1;
                 if (pg < 0 || pg >= np) raise_error(a.err, kErrPage);
-                else row = base + ((int64_t)pg * per_page + slot) * (2 * D);
+                else row = base + ((int64_t)pg * per_page + slot) * RB;
             }
         }
         s_rows[tid] = row ? row : g_zero_row512;
@@ -254,20 +298,23 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     __syncthreads();
 
     const int ntl = __builtin_amdgcn_readfirstlane((nk + kDTile - 1) / kDTile);
-    auto tile = [&](int t) { return s_ring + (t & (kDRing - 1)) * (kDTile * kDRow); };
+    auto tile = [&](int t) { return s_ring + (t % RING) * (kDTile * ROW); };
     auto issue = [&](int t) {
-        uint8_t* slot = s_ring + (t & (kDRing - 1)) * (kDTile * kDRow);
+        uint8_t* slot = s_ring + (t % RING) * (kDTile * ROW);
         const uint8_t* src[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) src[i] = s_rows[t * kDTile + 8 * wave + i];
+        if (!KV8 || lane < kDRowBytes8 / 16) {  // an fp8 row is 34 x 16 bytes
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dma_row(lds_off(slot + (8 * wave + i) * kDRow), src[i] + 16 * lane);
+            for (int i = 0; i < 8; ++i) dma_row(lds_off(slot + (8 * wave + i) * ROW), src[i] + 16 * lane);
+        }
     };
     // the q loads retire here: the compiler's own wait for them would otherwise sit
     // inside the tile loop and, counting the tiles' loads too, drain every tile in flight
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qb[ks]));
-    for (int t = 0; t < 3 && t < ntl; ++t) issue(t);
+    const int pre = ntl < RING - 1 ? ntl : RING - 1;  // tiles issued before the loop
+    for (int t = 0; t < pre; ++t) issue(t);
 
     f32x4 oacc[8];
 #pragma unroll
@@ -275,40 +322,76 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     float m_ref = -INFINITY, l_run = 0.f;
 
     // S operand row of this lane (accumulator row r16 of an m-tile) and the
-    // transposed-read row (k-slot group g: LDS rows 4 i + g, + 16 for slots 4..7)
-    const int s_row = 4 * (r16 & 3) + (r16 >> 2);
+    // transposed-read row.  bf16 keys: k-slot group g of the PV reads LDS rows
+    // 4 i + g (+ 16 for slots 4..7), and accumulator row a of m-tile mt is the
+    // key in LDS row 16 mt + 4 (a % 4) + a / 4.  fp8 keys: lane L of the PV's
+    // 8-bit transposed read takes row L / 2 (so lane 16 g + r gets keys 8 g .. 8 g + 7
+    // of dim r), and accumulator row a of m-tile mt is the key in LDS row
+    // 8 (a / 4) + 4 mt + a % 4: softmax value 4 mt + i of a lane is key 8 g + 4 mt + i.
+    const int s_row = KV8 ? 8 * (r16 >> 2) + (r16 & 3) : 4 * (r16 & 3) + (r16 >> 2);  // + 4 mt (fp8) / 16 mt
     const int tr_row = 4 * (r16 >> 2) + g;
     const int tr_col = (128 * wave + 4 * (r16 & 3)) * 2;  // bytes, + 32 per m-tile of 16 dims
+    auto key_bit = [&](int mt, int i) { return KV8 ? 8 * g + 4 * mt + i : 16 * mt + 4 * i + g; };
 
-    // the wave's S^T partial of tile t (two 16-key m-tiles over its 128 dims): operand reads, then MFMAs
-    auto s_reads = [&](int t, bf16x8 (&av)[2][4]) {
+    // the wave's S^T partial of tile t (two 16-key m-tiles over its 128 dims): operand reads, then MFMAs.
+    // fp8 keys: codes widened to bf16 on the way; one MFMA chain per 64-dim group (k-steps 0, 1 and
+    // 2, 3), each times its keys' group scale (the lane's keys: rows 8 g + 4 mt + i)
+    struct SOps {
+        bf16x8 av[2][4];
+        float s0[2][4], s1[2][4];
+    };
+    auto s_reads = [&](int t, SOps& o) {
         const uint8_t* kt = tile(t);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const uint8_t* ka = kt + (16 * mt + s_row) * kDRow + (128 * wave + 8 * g) * 2;
+            if constexpr (KV8) {
+                const uint8_t* ka = kt + (s_row + 4 * mt) * ROW + 128 * wave + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) av[mt][ks] = *reinterpret_cast<const bf16x8*>(ka + 64 * ks);
+                for (int ks = 0; ks < 4; ++ks) o.av[mt][ks] = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(ka + 32 * ks));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float2 v = *reinterpret_cast<const float2*>(kt + (8 * g + 4 * mt + i) * ROW + 512 + 8 * wave);
+                    o.s0[mt][i] = v.x;
+                    o.s1[mt][i] = v.y;
+                }
+            } else {
+                const uint8_t* ka = kt + (16 * mt + s_row) * ROW + (128 * wave + 8 * g) * 2;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) o.av[mt][ks] = *reinterpret_cast<const bf16x8*>(ka + 64 * ks);
+            }
         }
     };
-    auto s_mfma = [&](const bf16x8 (&av)[2][4], f32x4 (&sa)[2]) {
-        sa[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sa[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto s_mfma = [&](const SOps& o, f32x4 (&sa)[2]) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int mt = 0; mt < 2; ++mt) sa[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (KV8) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) sa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][ks], qb[ks], sa[mt], 0, 0, 0);
+            for (int mt = 0; mt < 2; ++mt) {
+                f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.av[mt][0], qb[0], c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.av[mt][2], qb[2], c1, 0, 0, 0);
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.av[mt][1], qb[1], c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.av[mt][3], qb[3], c1, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sa[mt][i] = fmaf(c0[i], o.s0[mt][i], c1[i] * o.s1[mt][i]);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    sa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.av[mt][ks], qb[ks], sa[mt], 0, 0, 0);
+        }
     };
 
     if (ntl > 0) {
         // tile 0's S partial before the loop
-        if (ntl >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (ntl == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_tiles(pre - 1);
         __syncthreads();
-        bf16x8 av[2][4];
+        SOps so;
         f32x4 sa[2];
-        s_reads(0, av);
-        s_mfma(av, sa);
+        s_reads(0, so);
+        s_mfma(so, sa);
         s_sx[0][wave][0][lane] = sa[0];
         s_sx[0][wave][1][lane] = sa[1];
     }
@@ -317,27 +400,27 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     for (int t = 0; t < ntl; ++t) {
         const bool next = t + 1 < ntl;
         if (next) {
-            // tiles issued so far: min(ntl, t + 3); tile t+1 must have landed
-            if (t + 3 < ntl) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // tiles issued so far: min(ntl, t + RING - 1); tile t+1 must have landed
+            const int issued = ntl < t + RING - 1 ? ntl : t + RING - 1;
+            wait_tiles(issued - (t + 2));
         }
         __syncthreads();
-        if (t + 3 < ntl) issue(t + 3);
+        if (t + RING - 1 < ntl) issue(t + RING - 1);
         const int par = t & 1;
         f32x4 sf[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
             sf[mt] = ((s_sx[par][0][mt][lane] + s_sx[par][1][mt][lane]) + s_sx[par][2][mt][lane]) + s_sx[par][3][mt][lane];
-        bf16x8 av[2][4];
-        if (next) s_reads(t + 1, av);
+        SOps so;
+        if (next) s_reads(t + 1, so);
 
-        // softmax: value (mt, i) is the key in LDS row 16 mt + 4 i + g of this head column
+        // softmax: value (mt, i) is the key in LDS row key_bit(mt, i) of this head column
         const uint32_t vb = s_vbits[t];
         float x[8];
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
             const int mt = cc >> 2, i = cc & 3;
-            x[cc] = ((vb >> (16 * mt + 4 * i + g)) & 1u) ? sf[mt][i] : -INFINITY;
+            x[cc] = ((vb >> key_bit(mt, i)) & 1u) ? sf[mt][i] : -INFINITY;
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -357,20 +440,43 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
             psum += pf[cc];
         }
         l_run += psum;
-        uint32_t pw[4], pl[4];
+        // the P operands (hi and, for fp8 output, lo parts); fp8 keys: one per 64-dim group of
+        // the wave, P times the key's group scale (V = codes x scale), element cc = key 8 g + cc
+        bf16x8 pb[2], plo[2];
+        {
+            float sc[2][8];
+            if constexpr (KV8) {
+                const uint8_t* kt = tile(t);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            pw[cc] = pack_bf16x2(pf[2 * cc], pf[2 * cc + 1]);
-            if constexpr (PREC)
-                pl[cc] = pack_bf16x2(pf[2 * cc] - bf16_bits_to_f32(pw[cc] & 0xffffu),
-                                     pf[2 * cc + 1] - bf16_bits_to_f32(pw[cc] >> 16));
+                for (int cc = 0; cc < 8; ++cc) {
+                    const float2 v = *reinterpret_cast<const float2*>(kt + (8 * g + cc) * ROW + 512 + 8 * wave);
+                    sc[0][cc] = v.x;
+                    sc[1][cc] = v.y;
+                }
+            }
+#pragma unroll
+            for (int gp = 0; gp < (KV8 ? 2 : 1); ++gp) {
+                uint32_t pw[4], pl[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const float p0 = KV8 ? pf[2 * cc] * sc[gp][2 * cc] : pf[2 * cc];
+                    const float p1 = KV8 ? pf[2 * cc + 1] * sc[gp][2 * cc + 1] : pf[2 * cc + 1];
+                    pw[cc] = pack_bf16x2(p0, p1);
+                    if constexpr (PREC)
+                        pl[cc] = pack_bf16x2(p0 - bf16_bits_to_f32(pw[cc] & 0xffffu), p1 - bf16_bits_to_f32(pw[cc] >> 16));
+                }
+                pb[gp] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+                plo[gp] = pb[gp];
+                if constexpr (PREC) plo[gp] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+            }
+            if constexpr (!KV8) {
+                pb[1] = pb[0];
+                plo[1] = plo[0];
+            }
         }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-        bf16x8 plo = pb;
-        if constexpr (PREC) plo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 
         f32x4 sa[2];
-        if (next) s_mfma(av, sa);
+        if (next) s_mfma(so, sa);
 
         // O^T += V^T . P^T over the wave's 8 m-tiles of 16 dims
         if (__ballot(rescale)) {
@@ -381,14 +487,19 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         bf16x8 va[8];
 #pragma unroll
         for (int mm = 0; mm < 8; ++mm) {
-            const uint8_t* b0 = kt + tr_row * kDRow + tr_col + 32 * mm;
-            const u32x2 v0 = tr_read(b0), v1 = tr_read(b0 + 16 * kDRow);
-            va[mm] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+            if constexpr (KV8) {
+                va[mm] = fp8x8_to_bf16(tr8_read(kt + (lane >> 1) * ROW + 128 * wave + 16 * mm + 8 * (lane & 1)));
+            } else {
+                const uint8_t* b0 = kt + tr_row * ROW + tr_col + 32 * mm;
+                const u32x2 v0 = tr_read(b0), v1 = tr_read(b0 + 16 * ROW);
+                va[mm] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+            }
         }
 #pragma unroll
         for (int mm = 0; mm < 8; ++mm) {
-            oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], pb, oacc[mm], 0, 0, 0);
-            if constexpr (PREC) oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], plo, oacc[mm], 0, 0, 0);
+            // m-tiles 0..3 are the wave's first 64-dim group, 4..7 its second
+            oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], pb[mm >> 2], oacc[mm], 0, 0, 0);
+            if constexpr (PREC) oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], plo[mm >> 2], oacc[mm], 0, 0, 0);
         }
         if (next) {
             s_sx[par ^ 1][wave][0][lane] = sa[0];
@@ -583,18 +694,20 @@ hipError_t launch_decode_attn(const DecodeArgs& d, const CompressArgs& c, hipStr
     if ((pairs + 7) / 8 * 8 * d.G + n_ins > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((pairs + 7) / 8 * 8 * d.G + n_ins));
     const bool prec = a.out_dtype == kFP8;
+    const bool kv8 = a.swa_dtype == kFP8;
+    if (kv8 != (a.comp_rows ? a.comp_dtype == kFP8 : kv8) || (!kv8 && a.swa_dtype != kBF16)) return hipErrorInvalidValue;
     const int64_t slots = (int64_t)d.nchunks * d.kl;
     const int merge = d.cand == nullptr ? 0 : (slots <= 8 * kDT ? 1 : 2);
-    if (merge == 0) {
-        if (prec) launch_kernel(ev, true, true, decode_attn_kernel<true, 0>, grid, dim3(kDT), st, d, c);
-        else launch_kernel(ev, true, true, decode_attn_kernel<false, 0>, grid, dim3(kDT), st, d, c);
-    } else if (merge == 1) {
-        if (prec) launch_kernel(ev, true, true, decode_attn_kernel<true, 1>, grid, dim3(kDT), st, d, c);
-        else launch_kernel(ev, true, true, decode_attn_kernel<false, 1>, grid, dim3(kDT), st, d, c);
-    } else {
-        if (prec) launch_kernel(ev, true, true, decode_attn_kernel<true, 2>, grid, dim3(kDT), st, d, c);
-        else launch_kernel(ev, true, true, decode_attn_kernel<false, 2>, grid, dim3(kDT), st, d, c);
-    }
+    auto go = [&](auto kern) { launch_kernel(ev, true, true, kern, grid, dim3(kDT), st, d, c); };
+#define CSL_DECODE_VARIANT(P, M, K) \
+    if (prec == P && merge == M && kv8 == K) go(decode_attn_kernel<P, M, K>);
+    CSL_DECODE_VARIANT(false, 0, false) CSL_DECODE_VARIANT(true, 0, false)
+    CSL_DECODE_VARIANT(false, 1, false) CSL_DECODE_VARIANT(true, 1, false)
+    CSL_DECODE_VARIANT(false, 2, false) CSL_DECODE_VARIANT(true, 2, false)
+    CSL_DECODE_VARIANT(false, 0, true) CSL_DECODE_VARIANT(true, 0, true)
+    CSL_DECODE_VARIANT(false, 1, true) CSL_DECODE_VARIANT(true, 1, true)
+    CSL_DECODE_VARIANT(false, 2, true) CSL_DECODE_VARIANT(true, 2, true)
+#undef CSL_DECODE_VARIANT
     return hipGetLastError();
 }
 

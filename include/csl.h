@@ -287,7 +287,7 @@ csl_status csl_hybrid_attn_prefill(const csl_pool* comp /* host, nullable */, co
  * first-stage candidates) and carries the inserts and query-side rows; the
  * second merges each query's candidates into its top-k and runs the
  * attention, splits merged in the launch.
- * comp: ratio 4, dim 512, bf16 rows (fp8 keys: the two calls); swa: ratio 1,
+ * comp: ratio 4, dim 512, bf16 or fp8 rows; swa: ratio 1,
  * the same dim and dtype.  ws: csl_index_attn_decode_workspace() bytes, its
  * first 16 KiB zero before the first use and left zero (as for
  * csl_hybrid_attn_decode).  0 <= n_jobs <= 4.

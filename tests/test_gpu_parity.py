@@ -481,6 +481,8 @@ FUSED_ATTN_CASES = [
     # 150 000 visible entries: 148 chunks x 24 candidates, 16 candidates per merge thread;
     # no inserts; 48 heads (three head groups)
     dict(name="wide_merge_16_per_thread", pos=[[600003]], DI=32, H=48, jobs=False),
+    # fp8 keys (raw and c4a-main pools), with inserts into them, and fp8 output
+    dict(name="fp8_keys_fp8_out", pos=[[9003], [20000], [14001]], kv=O.FP8, out=O.FP8),
 ]
 
 
@@ -507,14 +509,20 @@ def test_index_attn_decode_equals_separate_calls(csl, orc, case):
             ramp = (1.0 + np.arange(64 * mb) / 8192.0).astype(np.float32)
             keys = (np.repeat(ramp[:, None], DI, 1).view(np.uint32) >> 16).astype(np.uint16)
         scatter_rows(idx.rows, bt, s, 4, keys.view(np.uint8).reshape(64 * mb, -1))
-    main = O.HostPool(4, 2, D, R, THETA, O.BF16, P, state=with_jobs)
+    kv = case.get("kv", O.BF16)
+
+    def kv_rows(tid, n):
+        if kv == O.FP8:
+            return fp8_random_rows(seed, tid, n, D)
+        return randn_bf16(seed, tid, (n, D)).view(np.uint8).reshape(n, -1)
+
+    main = O.HostPool(4, 2, D, R, THETA, kv, P, state=with_jobs)
     for s in range(ns):
-        scatter_rows(main.rows, bt, s, 4, randn_bf16(seed, 40 + s, (64 * mb, D)).view(np.uint8).reshape(64 * mb, -1))
-    raw = O.HostPool(1, 1, D, R, THETA, O.BF16, P_low, state=False)
+        scatter_rows(main.rows, bt, s, 4, kv_rows(40 + 2 * s, 64 * mb))
+    raw = O.HostPool(1, 1, D, R, THETA, kv, P_low, state=False)
     for s in range(ns):
         n_raw = 256 * tail
-        scatter_rows(raw.rows, bt, s, 1, randn_bf16(seed, 60 + s, (n_raw, D)).view(np.uint8).reshape(n_raw, -1),
-                     i0=256 * first_low[s])
+        scatter_rows(raw.rows, bt, s, 1, kv_rows(100 + 2 * s, n_raw), i0=256 * first_low[s])
     if with_jobs:  # compressor state of the tail pages (the only pages the inserts read)
         for hp, t0 in ((idx, 11), (main, 13)):
             hp.state_x[:P_low] = randn_bf16(seed, t0, hp.state_x[:P_low].shape)
