@@ -260,6 +260,8 @@ int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_
 // about 256 workgroups, with 32..256 keys per split; at most 8 splits are
 // merged inside the launch by the last arriving split (more, or more than
 // kDecodeCounters (query, head group) pairs: partials for the combine kernel).
+// (Fewer, longer splits measured slower: eight fp8 splits of 1040 keys for the
+// 1M c128a layer took the step from 72 to 115 us.)
 struct DecodePlan {
     int G, S, per, combine;
 };

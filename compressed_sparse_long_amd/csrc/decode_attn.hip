@@ -39,7 +39,7 @@
 //     order the transposed reads produce, and keeps both the S operand reads
 //     and the transposed reads free of bank conflicts (1040-byte rows).
 // fp8 keys (544-byte rows: 512 e4m3 codes, then one fp32 scale per 64-dim
-// group) are staged as stored, seven slots deep, and widened to their exact
+// group) are staged as stored, six slots deep, and widened to their exact
 // bf16 values on the way to the MFMAs (the conversion unit with scale 1); the
 // V^T operands come from 8-bit transposing reads.  S runs one MFMA chain per
 // 64-dim group and adds the chains times the keys' group scales in fp32; in
@@ -58,7 +58,7 @@ constexpr int kDRing = 4;          // ring slots: one computed, up to three in f
 // fp8 keys: 544-byte rows (512 e4m3 codes, then the 8 fp32 scales of the 64-dim groups)
 constexpr int kDRowBytes8 = 544;
 constexpr int kDRow8 = 560;        // LDS stride of a staged fp8 row (140 words)
-constexpr int kDRing8 = 7;         // ring slots for fp8 rows: one computed, up to six in flight
+constexpr int kDRing8 = 6;         // ring slots for fp8 rows: one computed, up to five in flight
 constexpr int kDBt = 2048;         // block-table entries staged in LDS (contexts up to 512K positions)
 constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer descriptor word 3 (untyped dword access)
 constexpr int kSc1 = 16;                      // cache policy: device scope (coherent across the XCDs' L2s)
@@ -144,6 +144,8 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     constexpr int ROW = KV8 ? kDRow8 : kDRow;           // LDS stride of a staged row
     constexpr int RING = KV8 ? kDRing8 : kDRing;        // ring slots
     constexpr int RB = KV8 ? kDRowBytes8 : 2 * D;       // stored row bytes
+    constexpr int KMAX = kDecodeMaxSplitKeys;           // keys of one split
+    constexpr int KR = (KMAX + kDT - 1) / kDT;          // rounds of address resolution (one thread per key)
     constexpr int kBtPer = kDBt / kDT;  // block-table entries staged per thread
     const AttnArgs& a = d.at;
     // ring of staged key tiles; before the first tile it holds the merge's
@@ -158,9 +160,9 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         return;
     }
     __shared__ __attribute__((aligned(16))) f32x4 s_sx[2][4][2][64];  // S^T partials: [tile parity][wave][m-tile]
-    __shared__ const uint8_t* s_rows[kDecodeMaxSplitKeys];
-    __shared__ uint32_t s_vbits[kDecodeMaxSplitKeys / 32];
-    __shared__ int32_t s_ids[MERGE ? kDecodeMaxSplitKeys : 1];
+    __shared__ const uint8_t* s_rows[KMAX];
+    __shared__ uint32_t s_vbits[KMAX / 32];
+    __shared__ int32_t s_ids[MERGE ? KMAX : 1];
     __shared__ int32_t s_bt[kDBt];
     __shared__ float s_rope[2][64];
     __shared__ uint32_t s_flag;
@@ -194,8 +196,13 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
     }
-    int32_t pre_id = -1;
-    if (!MERGE && a.topk && tid < d.per && kb + tid < a.k) pre_id = a.topk[(int64_t)n * a.k + kb + tid];
+    int32_t pre_id[KR];
+#pragma unroll
+    for (int u = 0; u < KR; ++u) {
+        const int j = u * kDT + tid;
+        pre_id[u] = -1;
+        if (!MERGE && a.topk && j < d.per && kb + j < a.k) pre_id[u] = a.topk[(int64_t)n * a.k + kb + j];
+    }
     MergeIn in;
     in.sc = d.scores + (int64_t)n * d.stride;
     in.cand = d.cand + (int64_t)n * d.nchunks * d.kl;
@@ -254,18 +261,21 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         if (i * kDT + tid < (int)nbt64 && staged) s_bt[i * kDT + tid] = btv[i];
     __syncthreads();  // s_bt, s_ids, s_rope; the merge is done with the ring
 
-    // the split's key rows: thread t resolves key kb + t
-    {
+    // the split's key rows: in round u thread t resolves key kb + 256 u + t
+#pragma unroll
+    for (int u = 0; u < KR; ++u) {
+        const int jj = u * kDT + tid;
+        if (u * kDT >= nk) break;  // (uniform)
         const uint8_t* row = nullptr;
-        if (tid < nk) {
-            const int64_t j = kb + tid;
+        if (jj < nk) {
+            const int64_t j = kb + jj;
             int32_t pg = -1;
             int64_t slot = 0;
             const uint8_t* base = nullptr;
             int per_page = 0, np = 0;
             int64_t blk = -1;
             if (j < Lc) {
-                const int64_t id = MERGE ? (int64_t)s_ids[tid] : (a.topk ? (int64_t)pre_id : j);
+                const int64_t id = MERGE ? (int64_t)s_ids[jj] : (a.topk ? (int64_t)pre_id[u] : j);
                 if (id >= nv_c) raise_error(a.err, kErrTopk);
                 if (id >= 0 && id < nv_c) {
                     per_page = kBlockPositions / a.comp_ratio;  // 64 or 2: a power of two
@@ -288,12 +298,12 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
                 else row = base + ((int64_t)pg * per_page + slot) * RB;
             }
         }
-        s_rows[tid] = row ? row : g_zero_row512;
+        // every row of the round's tiles gets an address (masked keys copy the zero row)
+        if (jj < KMAX) s_rows[jj] = row ? row : g_zero_row512;
         const uint64_t bits = __ballot(row != nullptr);
-        if (lane == 0) {
-            s_vbits[2 * wave] = (uint32_t)bits;
-            s_vbits[2 * wave + 1] = (uint32_t)(bits >> 32);
-        }
+        const int vw = (u * kDT + 64 * wave) / 32;
+        if (lane == 0 && vw < KMAX / 32) s_vbits[vw] = (uint32_t)bits;
+        if (lane == 0 && vw + 1 < KMAX / 32) s_vbits[vw + 1] = (uint32_t)(bits >> 32);
     }
     __syncthreads();
 

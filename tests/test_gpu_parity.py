@@ -701,6 +701,10 @@ ATTN_CASES = [
     # separate combine launch instead of merging in the launch
     dict(name="c128a_d512_h64_dense_bf16_partials_path", D=512, R=64, H=64, ratio=128, k=0, dtype=O.BF16,
          out=O.BF16, pos=[[300000]]),
+    # fp8 keys, one query over 2343 + 128 keys: more splits than the launch merges, so
+    # the partials go to the combine kernel
+    dict(name="c128a_d512_h64_fp8kv_partials_path_bf16out", D=512, R=64, H=64, ratio=128, k=0, dtype=O.FP8,
+         out=O.BF16, pos=[[300000]]),
     # 128-dim keys with bf16 and fp8 output (the generic kernel's precision variant and the
     # combine kernel's 128-dim stores)
     dict(name="c4a_d128_h8_k64_bf16out", D=128, R=32, H=8, ratio=4, k=64, dtype=O.BF16, out=O.BF16,
