@@ -877,9 +877,13 @@ csl_status csl_index_attn_decode(const csl_pool* index_pool, const csl_pool* com
     });
     if (e != hipSuccess) return hip_fail(e, "index_score launch");
     if (ia.num_q == 0) return CSL_OK;
-    const bool merge = ia.kl > 0 && !ia.tiled;
+    // the attention launch merges up to 2048 candidate slots per query (8 per thread); every
+    // workgroup of a query repeats the merge, which past that size costs more than the select
+    // launch (1M positions, 4096 slots: 29.3 us fused against 8.9 + 15.4 us)
+    const bool merge = ia.kl > 0 && !ia.tiled && (int64_t)ia.nchunks * ia.kl <= kDecodeMergeSlots;
     if (!merge) {
-        // no first-stage candidates (short rows or many queries): the full select, then attention on its ids
+        // no first-stage candidates (short rows or many queries) or too many: the select launch,
+        // then attention on its ids
         e = timed(CSL_KERNEL_TOPK_SELECT, s, [&](const LaunchEvents& ev) { return launch_topk_select(ia, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "topk_select launch");
     }

@@ -102,6 +102,7 @@ struct AttnArgs {
 constexpr int kDecodeMaxSplitKeys = 256;  // keys of one split (8 tiles of 32)
 constexpr int kDecodeMaxCombine = 8;      // splits merged in the launch by the last arriver
 constexpr int kDecodeCounters = 4096;     // arrival counters at the start of the workspace (16 KiB)
+constexpr int kDecodeMergeSlots = 2048;   // first-stage candidate slots one attention workgroup merges
 struct DecodeArgs {
     AttnArgs at;
     int G;        // head groups of 16

@@ -135,8 +135,8 @@ struct SliceOut {
 
 // Workgroups past the attention's take one (new token, pool) insert each of
 // `c` (the fused call's index-pool inserts: this launch never reads index rows).
-// MERGE: 0 = ids given (or dense); 1 / 2 = the workgroup merges the first-stage
-// candidates, 8 / 16 slots per thread (up to 2048 / 4096 slots).
+// MERGE: 0 = ids given (or dense); 1 = the workgroup merges the first-stage
+// candidates, 8 slots per thread (up to kDecodeMergeSlots).
 template <bool PREC, int MERGE, bool KV8>
 __global__ void __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_attn_kernel(DecodeArgs d, CompressArgs c) {
@@ -209,7 +209,7 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     in.cnext = d.c_next + (int64_t)n * d.nchunks;
     in.kl = d.kl;
     in.k = a.k;
-    CandRegs<MERGE == 2 ? 16 : 8> cr;
+    CandRegs<8> cr;
     if (MERGE) cand_load(in, (int64_t)d.nchunks * d.kl, d.nchunks, cr);
 
     // the query (wave-uniform)
@@ -253,7 +253,7 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         const SliceOut out = {writer ? d.topk_out + (int64_t)n * a.k : nullptr, s_ids, (uint32_t)kb, (uint32_t)nkc};
         float* kthp = writer && d.kth ? d.kth + n : nullptr;
         if (in.nv <= a.k) select_all(in.sc, in.nv, a.k, out, kthp, m.min);
-        else merge_candidates<kDT, MERGE == 2 ? 16 : 8>(in, cr, out, kthp, m);
+        else merge_candidates<kDT, 8>(in, cr, out, kthp, m);
     }
     // the block-table row lands after the merge, which does not need it
 #pragma unroll
@@ -707,16 +707,16 @@ hipError_t launch_decode_attn(const DecodeArgs& d, const CompressArgs& c, hipStr
     const bool kv8 = a.swa_dtype == kFP8;
     if (kv8 != (a.comp_rows ? a.comp_dtype == kFP8 : kv8) || (!kv8 && a.swa_dtype != kBF16)) return hipErrorInvalidValue;
     const int64_t slots = (int64_t)d.nchunks * d.kl;
-    const int merge = d.cand == nullptr ? 0 : (slots <= 8 * kDT ? 1 : 2);
+    if (d.cand != nullptr && slots > kDecodeMergeSlots) return hipErrorInvalidValue;
+    static_assert(kDecodeMergeSlots == 8 * kDT, "one merge slot group of 8 per thread");
+    const int merge = d.cand == nullptr ? 0 : 1;
     auto go = [&](auto kern) { launch_kernel(ev, true, true, kern, grid, dim3(kDT), st, d, c); };
 #define CSL_DECODE_VARIANT(P, M, K) \
     if (prec == P && merge == M && kv8 == K) go(decode_attn_kernel<P, M, K>);
     CSL_DECODE_VARIANT(false, 0, false) CSL_DECODE_VARIANT(true, 0, false)
     CSL_DECODE_VARIANT(false, 1, false) CSL_DECODE_VARIANT(true, 1, false)
-    CSL_DECODE_VARIANT(false, 2, false) CSL_DECODE_VARIANT(true, 2, false)
     CSL_DECODE_VARIANT(false, 0, true) CSL_DECODE_VARIANT(true, 0, true)
     CSL_DECODE_VARIANT(false, 1, true) CSL_DECODE_VARIANT(true, 1, true)
-    CSL_DECODE_VARIANT(false, 2, true) CSL_DECODE_VARIANT(true, 2, true)
 #undef CSL_DECODE_VARIANT
     return hipGetLastError();
 }

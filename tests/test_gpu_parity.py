@@ -478,9 +478,9 @@ FUSED_ATTN_CASES = [
     # index keys rising with the id: the top-k crowds the last chunk, the candidates'
     # check fails and every workgroup of the query takes the exact select on the score row
     dict(name="ramp_fallback", pos=[[9000], [12001]], mode="ramp", out=O.F32),
-    # 150 000 visible entries: 148 chunks x 24 candidates, 16 candidates per merge thread;
-    # no inserts; 48 heads (three head groups)
-    dict(name="wide_merge_16_per_thread", pos=[[600003]], DI=32, H=48, jobs=False),
+    # 150 000 visible entries: 148 chunks x 24 candidates, more than the attention launch
+    # merges: the select launch runs between the two; no inserts; 48 heads (three head groups)
+    dict(name="wide_candidates_select_launch", pos=[[600003]], DI=32, H=48, jobs=False),
     # fp8 keys (raw and c4a-main pools), with inserts into them, and fp8 output
     dict(name="fp8_keys_fp8_out", pos=[[9003], [20000], [14001]], kv=O.FP8, out=O.FP8),
 ]
