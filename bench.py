@@ -904,7 +904,7 @@ def main():
                    "algorithmic_bytes_per_step": step_bytes},
         "roofline": roof,
         "kernels": kernels,
-        "target": ("north star: the decode attention step (index top-k + hybrid attention) at >= 60% of the HBM "
+        "target": ("the decode attention step (index top-k + hybrid attention) at >= 60% of the HBM "
                    "peak: hbm_frac of the whole step; roofline.frac is the score kernel alone"),
     }
     if not args.no_cpu and w.layers == ("c4a",):

@@ -1,6 +1,6 @@
 """GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
 
-Sizes span several tiles and ragged tails; tolerances are the north-star's:
+Sizes span several tiles and ragged tails; tolerances are those of the method's acceptance rules:
 rows and outputs rtol 1e-2 / atol 1e-2, fp8 within one e4m3 ULP of the
 oracle's quantisation, top-k sets equal up to swaps within 1e-4 of the k-th
 score.  Every case prints its name before its GPU step.
