@@ -32,15 +32,23 @@ METRIC = "decode queries/s + HBM GB/s, c4a top-k512+SWA128 at 128K ctx, 1 MI355X
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "compressed_sparse_long_amd", "csrc")
-# committed HBM counter runs: (summary json, kernel source it was taken on)
+# committed HBM counter runs: (summary json, kernel source file it was taken on)
 TRAFFIC = {
-    "index_score": (os.path.join(ROOT, "profiles", "index_score_c4a_decode_b16_128k.pmc.json"),
-                    os.path.join(CSRC, "index_topk.hip")),
+    "index_score": (os.path.join(ROOT, "profiles", "index_score_c4a_decode_b16_128k.pmc.json"), "index_topk.hip"),
     "decode_attention": (os.path.join(ROOT, "profiles", "decode_attn_c4a_decode_b16_128k.pmc.json"),
-                         os.path.join(CSRC, "decode_attn.hip")),
-    "prefill_attention": (os.path.join(ROOT, "profiles", "attention_prefill_c4a_8k_on_64k.pmc.json"),
-                          os.path.join(CSRC, "attn.hip")),
+                         "decode_attn.hip"),
+    "prefill_attention": (os.path.join(ROOT, "profiles", "attention_prefill_c4a_8k_on_64k.pmc.json"), "attn.hip"),
 }
+# headers the kernel files include: a change to any of them changes the kernels
+KERNEL_HEADERS = ["csl_device.hpp", "csl_kernels.hpp", "csl_select.hpp", "csl_insert.hpp"]
+
+
+def source_digest(source: str) -> str:
+    """sha256 over a kernel source file and the shared kernel headers, in that order."""
+    h = hashlib.sha256()
+    for f in [source] + KERNEL_HEADERS:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
 def log(msg):
@@ -504,8 +512,7 @@ def traffic_from_profile(kernel: str, launch_kind: str):
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    if d.get("source_sha256") != sha or d.get("launch") != launch_kind:
+    if d.get("source_sha256") != source_digest(source) or d.get("launch") != launch_kind:
         return None
     return float(d["hbm_bytes_per_launch"])
 
@@ -526,8 +533,9 @@ def copy_calibration(mb: int, iters: int):
 
 def probe():
     """Ceilings of this GPU as plain library kernels reach them: a 4 GiB
-    device-to-device copy (read + write bytes / time) and a bf16 GEMM of
-    8192^3 (2 * 8192^3 flops / time), each the median of 20 timed runs."""
+    device-to-device copy (read + write bytes / time), a sum over the same
+    4 GiB (read bytes / time) and a bf16 GEMM of 8192^3 (2 * 8192^3 flops /
+    time), each the median of 20 timed runs."""
     import torch
     res = {}
     n = 1 << 30  # fp32 elements: 4 GiB per buffer
@@ -548,6 +556,8 @@ def probe():
         return sorted(ts)[len(ts) // 2]
     t = med(lambda: dst.copy_(src))
     res["copy_GBps"] = round(2 * 4 * n / t / 1e9, 1)
+    t = med(lambda: torch.sum(src))
+    res["read_GBps"] = round(4 * n / t / 1e9, 1)
     del src, dst
     torch.cuda.empty_cache()
     m = 8192

@@ -143,6 +143,75 @@ __device__ __forceinline__ uint32_t radix_select_regs(const uint32_t (&key)[KPT]
     return prefix;
 }
 
+// An NB-bin histogram in LDS scanned from the top by one wave: the bin that
+// holds the rank-th largest counted key, the rank inside that bin and its
+// count (valid if total >= rank).  Lane l sums bins NB-1-PER*l downwards; the
+// hit lane's PER bins are then spread over lanes for a second scan.
+struct BinPick {
+    uint32_t bin, rank, cnt, total;
+};
+template <int NB>
+__device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t rank) {
+    constexpr int PER = NB >= 64 ? NB / 64 : 1;
+    const int lane = threadIdx.x & 63;
+    const int top = NB - 1 - PER * lane;
+    uint32_t sum = 0;
+    if constexpr (PER >= 4) {
+#pragma unroll
+        for (int v = 0; v < PER / 4; ++v) {
+            const u32x4 h = *reinterpret_cast<const u32x4*>(hist + top + 1 - PER + 4 * v);
+            sum += h[0] + h[1] + h[2] + h[3];
+        }
+    } else {
+        static_assert(PER == 1, "bins per lane: 1 or a multiple of 4");
+        sum = top >= 0 ? hist[top] : 0u;
+    }
+    const uint32_t incl = wave_scan_add(sum);
+    BinPick r = {0u, 0u, 0u, lane_value(incl, 63)};
+    if (r.total < rank) return r;
+    const uint32_t above = incl - sum;
+    const int L = __builtin_ctzll(__ballot(above < rank && rank <= incl));
+    const uint32_t above_l = lane_value(above, L);
+    if constexpr (PER == 1) {
+        r.bin = (uint32_t)(NB - 1 - L);
+        r.rank = rank - above_l;
+        r.cnt = lane_value(sum, L);
+    } else {
+        const int top_l = NB - 1 - PER * L;
+        const uint32_t c = lane < PER ? hist[top_l - lane] : 0u;
+        const uint32_t in2 = wave_scan_add(c) + above_l;
+        const int J = __builtin_ctzll(__ballot(lane < PER && in2 - c < rank && rank <= in2));
+        r.bin = (uint32_t)(top_l - J);
+        r.cnt = lane_value(c, J);
+        r.rank = rank - (lane_value(in2, J) - r.cnt);
+    }
+    return r;
+}
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The rank-th largest of cn <= 64 keys in LDS, by one wave (lane j ranks key j
+// against all): T, and *rem = its copies among the top `rank`.
+__device__ __forceinline__ void pairwise_rank(const uint32_t* cbuf, uint32_t cn, uint32_t rank, uint32_t& T,
+                                              uint32_t& rem) {
+    const int lane = threadIdx.x & 63;
+    uint32_t kc = 0, gt = 0, ge = 0;
+    if ((uint32_t)lane < cn) {
+        kc = cbuf[lane];
+        for (uint32_t j = 0; j < cn; ++j) {
+            const uint32_t kj = cbuf[j];
+            gt += kj > kc ? 1u : 0u;
+            ge += kj >= kc ? 1u : 0u;
+        }
+    }
+    const int L = __builtin_ctzll(__ballot((uint32_t)lane < cn && gt < rank && rank <= ge));
+    T = lane_value(kc, L);
+    rem = rank - lane_value(gt, L);
+}
+
 constexpr int kCandCap = 4096;  // boundary-bin keys kept in LDS
 
 // Exact selection over register-resident keys (slot i valid iff bit i of vmask;
@@ -154,8 +223,11 @@ constexpr int kCandCap = 4096;  // boundary-bin keys kept in LDS
 //     from the top: the bin b that holds the want-th key and its rank in b;
 //  2. b's keys (a few: bins are 2^13 key units wide) are compacted to LDS and T
 //     is the one with #(> T) < rank <= #(>= T).
-// If fewer than `want` keys fall in the window, or b is crowded, an exact
-// 3-round radix select over all keys is used instead.
+// Every wave scans the histogram itself, and when b holds at most 64 keys
+// every wave ranks them itself, so that common case takes three workgroup
+// barriers.  A crowded b goes through workgroup scans; if fewer than `want`
+// keys fall in the window, an exact 3-round radix select over all keys is used
+// instead.  s_hist must be 16-byte aligned.
 template <int NT, int KPT, int CAP = kCandCap>
 __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
                                  uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
@@ -166,7 +238,8 @@ __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uin
     for (int i = 0; i < KPT; ++i) kmax = ((vmask >> i) & 1u) ? max(kmax, key[i]) : kmax;
     kmax = wave_max_u32(kmax);
     if (lane == 0) s_sel[8 + wave] = kmax;
-    for (int b = tid; b < 2048; b += NT) s_hist[b] = 0;
+    if (tid == 0) s_sel[3] = 0u;  // compaction count
+    for (int b = tid; b < 512; b += NT) reinterpret_cast<u32x4*>(s_hist)[b] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) kmax = max(kmax, s_sel[8 + w]);
@@ -176,6 +249,19 @@ __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uin
     for (int i = 0; i < KPT; ++i)
         if (((vmask >> i) & 1u) && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
     __syncthreads();
+    // the same pick in every wave (every wave reads the same histogram)
+    const BinPick bp = wave_find_bin<2048>(s_hist, want);
+    if (bp.total >= want && bp.cnt <= 64u) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            if (((vmask >> i) & 1u) && key[i] >= lo && ((key[i] - lo) >> 13) == bp.bin)
+                s_cand[atomicAdd(&s_sel[3], 1u)] = key[i];
+        __syncthreads();
+        uint32_t T, rem;
+        pairwise_rank(s_cand, bp.cnt, bp.rank, T, rem);
+        *rem_out = rem;
+        return T;
+    }
     const uint32_t tot = find_bin<NT>(s_hist, want, 2048, s_wave, s_sel);
     if (tot >= want && s_sel[2] <= (uint32_t)CAP) {
         const uint32_t bsel = s_sel[0], rank = s_sel[1], cnt = s_sel[2];
@@ -360,75 +446,6 @@ __device__ __forceinline__ void select_all(const float* sc, int64_t nv, int k, c
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-}
-
-// An NB-bin histogram in LDS scanned from the top by one wave: the bin that
-// holds the rank-th largest counted key, the rank inside that bin and its
-// count (valid if total >= rank).  Lane l sums bins NB-1-PER*l downwards; the
-// hit lane's PER bins are then spread over lanes for a second scan.
-struct BinPick {
-    uint32_t bin, rank, cnt, total;
-};
-template <int NB>
-__device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t rank) {
-    constexpr int PER = NB >= 64 ? NB / 64 : 1;
-    const int lane = threadIdx.x & 63;
-    const int top = NB - 1 - PER * lane;
-    uint32_t sum = 0;
-    if constexpr (PER >= 4) {
-#pragma unroll
-        for (int v = 0; v < PER / 4; ++v) {
-            const u32x4 h = *reinterpret_cast<const u32x4*>(hist + top + 1 - PER + 4 * v);
-            sum += h[0] + h[1] + h[2] + h[3];
-        }
-    } else {
-        static_assert(PER == 1, "bins per lane: 1 or a multiple of 4");
-        sum = top >= 0 ? hist[top] : 0u;
-    }
-    const uint32_t incl = wave_scan_add(sum);
-    BinPick r = {0u, 0u, 0u, lane_value(incl, 63)};
-    if (r.total < rank) return r;
-    const uint32_t above = incl - sum;
-    const int L = __builtin_ctzll(__ballot(above < rank && rank <= incl));
-    const uint32_t above_l = lane_value(above, L);
-    if constexpr (PER == 1) {
-        r.bin = (uint32_t)(NB - 1 - L);
-        r.rank = rank - above_l;
-        r.cnt = lane_value(sum, L);
-    } else {
-        const int top_l = NB - 1 - PER * L;
-        const uint32_t c = lane < PER ? hist[top_l - lane] : 0u;
-        const uint32_t in2 = wave_scan_add(c) + above_l;
-        const int J = __builtin_ctzll(__ballot(lane < PER && in2 - c < rank && rank <= in2));
-        r.bin = (uint32_t)(top_l - J);
-        r.cnt = lane_value(c, J);
-        r.rank = rank - (lane_value(in2, J) - r.cnt);
-    }
-    return r;
-}
-
-// Lanes below this one whose bit is set in m.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// The rank-th largest of cn <= 64 keys in LDS, by one wave (lane j ranks key j
-// against all): T, and *rem = its copies among the top `rank`.
-__device__ __forceinline__ void pairwise_rank(const uint32_t* cbuf, uint32_t cn, uint32_t rank, uint32_t& T,
-                                              uint32_t& rem) {
-    const int lane = threadIdx.x & 63;
-    uint32_t kc = 0, gt = 0, ge = 0;
-    if ((uint32_t)lane < cn) {
-        kc = cbuf[lane];
-        for (uint32_t j = 0; j < cn; ++j) {
-            const uint32_t kj = cbuf[j];
-            gt += kj > kc ? 1u : 0u;
-            ge += kj >= kc ? 1u : 0u;
-        }
-    }
-    const int L = __builtin_ctzll(__ballot((uint32_t)lane < cn && gt < rank && rank <= ge));
-    T = lane_value(kc, L);
-    rem = rank - lane_value(gt, L);
 }
 
 // Emit of a first-stage chunk for slots of 64 consecutive ids (slot i of lane

@@ -42,7 +42,7 @@ __device__ __forceinline__ int64_t visible(const IndexArgs& a, int64_t p) {
 
 
 __device__ __forceinline__ void select_query(const IndexArgs& a, const int n) {
-    __shared__ uint32_t s_hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2048];
     __shared__ uint32_t s_cand[kCandCap];
     __shared__ uint32_t s_wave[kSelWaves];
     __shared__ uint32_t s_sel[8 + kSelWaves];
@@ -632,7 +632,7 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
 template <int NT>
 __device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
     constexpr int NW = NT / 64;
-    __shared__ uint32_t s_hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2048];
     __shared__ uint32_t s_cand[kCandCap];
     __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_sel[8 + NW];
