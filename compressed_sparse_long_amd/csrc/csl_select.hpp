@@ -223,12 +223,14 @@ constexpr int kCandCap = 4096;  // boundary-bin keys kept in LDS
 //     from the top: the bin b that holds the want-th key and its rank in b;
 //  2. b's keys (a few: bins are 2^13 key units wide) are compacted to LDS and T
 //     is the one with #(> T) < rank <= #(>= T).
-// Every wave scans the histogram itself, and when b holds at most 64 keys
-// every wave ranks them itself, so that common case takes three workgroup
-// barriers.  A crowded b goes through workgroup scans; if fewer than `want`
-// keys fall in the window, an exact 3-round radix select over all keys is used
-// instead.  s_hist must be 16-byte aligned.
-template <int NT, int KPT, int CAP = kCandCap>
+// With WAVE_PICK every wave scans the histogram itself and, when b holds at
+// most 64 keys, ranks them itself, so that common case takes three workgroup
+// barriers instead of ten: shorter for a lone workgroup on a CU, dearer where
+// many share one (the repeated scans cost more than the barriers save).  A
+// crowded b goes through workgroup scans; if fewer than `want` keys fall in
+// the window, an exact 3-round radix select over all keys is used instead.
+// s_hist must be 16-byte aligned.
+template <int NT, int KPT, bool WAVE_PICK = false, int CAP = kCandCap>
 __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uint32_t vmask, uint32_t want, uint32_t* rem_out,
                                  uint32_t* s_hist, uint32_t* s_wave, uint32_t* s_sel, uint32_t* s_cand) {
     constexpr int NW = NT / 64;
@@ -250,8 +252,8 @@ __device__ __forceinline__ uint32_t block_select(const uint32_t (&key)[KPT], uin
         if (((vmask >> i) & 1u) && key[i] >= lo) atomicAdd(&s_hist[(key[i] - lo) >> 13], 1u);
     __syncthreads();
     // the same pick in every wave (every wave reads the same histogram)
-    const BinPick bp = wave_find_bin<2048>(s_hist, want);
-    if (bp.total >= want && bp.cnt <= 64u) {
+    const BinPick bp = WAVE_PICK ? wave_find_bin<2048>(s_hist, want) : BinPick{0u, 0u, 0u, 0u};
+    if (WAVE_PICK && bp.total >= want && bp.cnt <= 64u) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i)
             if (((vmask >> i) & 1u) && key[i] >= lo && ((key[i] - lo) >> 13) == bp.bin)
@@ -610,7 +612,7 @@ struct MergeLds {
 // Every thread calls it; out(pos, id) receives each position 0..k-1 (a
 // position may be written twice when the fallback runs); kth (nullable) the
 // k-th score.
-template <int NT, int KPT, typename Out>
+template <int NT, int KPT, bool WAVE_PICK, typename Out>
 __device__ __forceinline__ void merge_candidates(const MergeIn& in, const CandRegs<KPT>& r, const Out& out, float* kth,
                                                  const MergeLds& m) {
     const int tid = threadIdx.x;
@@ -641,7 +643,7 @@ __device__ __forceinline__ void merge_candidates(const MergeIn& in, const CandRe
     }
     if (tid == 0) *m.fail = 0;
     uint32_t rem;
-    const uint32_t T = block_select<NT, KPT>(key, vmask, (uint32_t)in.k, &rem, m.hist, m.wave, m.sel, m.cand);
+    const uint32_t T = block_select<NT, KPT, WAVE_PICK>(key, vmask, (uint32_t)in.k, &rem, m.hist, m.wave, m.sel, m.cand);
     // emit, and learn the k-th element's id (sel[6]) for the check
     emit_selected<NT, KPT>(key, vmask, T, rem, in.k, [&](int i) { return (int32_t)id[i]; }, out, m.wave, m.sel, true);
     __syncthreads();

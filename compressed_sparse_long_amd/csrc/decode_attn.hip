@@ -253,7 +253,7 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         const SliceOut out = {writer ? d.topk_out + (int64_t)n * a.k : nullptr, s_ids, (uint32_t)kb, (uint32_t)nkc};
         float* kthp = writer && d.kth ? d.kth + n : nullptr;
         if (in.nv <= a.k) select_all(in.sc, in.nv, a.k, out, kthp, m.min);
-        else merge_candidates<kDT, 8>(in, cr, out, kthp, m);
+        else merge_candidates<kDT, 8, true>(in, cr, out, kthp, m);  // one workgroup per CU: per-wave picks
     }
     // the block-table row lands after the merge, which does not need it
 #pragma unroll

@@ -653,7 +653,8 @@ __device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
         const int nch = (int)((in.nv + kChunk - 1) / kChunk);
         cand_load(in, (int64_t)nch * in.kl, nch, cr);
     }
-    merge_candidates<NT, kMergeSlots>(in, cr, GlobalOut{a.topk + (int64_t)n * a.k}, a.kth ? a.kth + n : nullptr, m);
+    merge_candidates<NT, kMergeSlots, false>(in, cr, GlobalOut{a.topk + (int64_t)n * a.k}, a.kth ? a.kth + n : nullptr,
+                                             m);
 }
 
 template <int NT>
