@@ -610,6 +610,9 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
                     mine[pp][t] = h2 == 0 ? va : vb;
                 }
             }
+            // the next page into LDS before this page's scores go out: its wait for the page's
+            // loads (a count of outstanding memory operations) then does not include the stores
+            if (j + 1 < npages) store_page((j + 1) & 1);
 #pragma unroll
             for (int pp = 0; pp < PP; ++pp) {
                 const int qi = QW * wave + 2 * pp + h2;
@@ -620,7 +623,6 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
                     if (store && e0 + 32 * t + r32 < nvl[pp])
                         __builtin_nontemporal_store(pg < 0 ? -INFINITY : mine[pp][t], row + 32 * t);
             }
-            if (j + 1 < npages) store_page((j + 1) & 1);
             __syncthreads();
         }
     }
