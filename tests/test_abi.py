@@ -45,8 +45,9 @@ def test_workspace_sizes(csl):
     # decode split-KV partials: a 16 KiB block of arrival counters, then num_q * splits *
     # heads * (dim + 2) floats, sized for the larger split count of the paths the key
     # type could take (fp8 keys: 2 tiles per split, one while the launch would hold
-    # fewer than 32 workgroups; bf16 keys: 16-head groups with about 256 workgroups,
-    # 32..256 keys per split, at most 8 splits while the keys fit 8 x 256)
+    # fewer than 32 workgroups; bf16 keys: 16-head groups with about 256 workgroups but
+    # about three tiles or more per split, 32..256 keys per split, at most 8 splits
+    # while the keys fit 8 x 256)
     part = 64 * 514 * 4
     cnt = 16384
     assert csl.hybrid_attn_workspace(16, 64, 512, 4, 512, 128, 131072) == cnt + 16 * 10 * part  # fp8: 10 splits; bf16: 4
@@ -59,7 +60,7 @@ def test_workspace_sizes(csl):
     assert csl.index_attn_decode_workspace(16, 64, 131072, 512, 128) == (
         cnt + 16 * 4 * part + csl.index_topk_workspace(16, 131072, 512))
     assert csl.index_attn_decode_workspace(16, 8, 1024, 64, 128) == (
-        cnt + 16 * 6 * 8 * 514 * 4 + csl.index_topk_workspace(16, 1024, 64))  # 192 keys: 6 splits of 32
+        cnt + 16 * 2 * 8 * 514 * 4 + csl.index_topk_workspace(16, 1024, 64))  # 192 keys: 2 splits of 96
 
 
 FAKE = 0x100000  # a 16-byte aligned host address that is never dereferenced
