@@ -489,6 +489,8 @@ __global__ void __launch_bounds__(64 * NW) attn_combine_kernel(AttnArgs a) {
     if (head >= a.n_heads) return;
     const int w0 = SHARE ? wave : 0, wstep = SHARE ? NW : 1;
     const bool active = 8 * lane < D;
+    // the query's position (for the inverse RoPE) is loaded beside the partials
+    QueryInfo qi = query_info(a, n);
 
     const float* ml = a.part_ml + ((int64_t)n * a.n_splits * a.n_heads + head) * 2;
     const int64_t mstride = (int64_t)a.n_heads * 2;
@@ -560,7 +562,6 @@ __global__ void __launch_bounds__(64 * NW) attn_combine_kernel(AttnArgs a) {
             for (int c = 0; c < 8; ++c) o[c] = fmaf(r, s_o[w][lane][c], o[c]);
         }
     }
-    QueryInfo qi = query_info(a, n);
     const int64_t p = qi.ok ? qi.p : 0;
     const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     const int rbase = D - a.rope_dims;
@@ -1293,8 +1294,10 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st, const LaunchEv
     const bool share = a.n_splits > 16 || (a.n_splits > 4 && (int64_t)a.num_q * ((a.n_heads + 3) / 4) < 256);
     const dim3 grid((unsigned)((int64_t)a.num_q * (share ? a.n_heads : (a.n_heads + 3) / 4)));
     if (a.dim == 512) {
-        // more than 64 splits: sixteen waves share them (a few batches per wave)
+        // more than 64 splits: sixteen waves share them (a few batches per wave); 33..64: eight
+        // waves, so that each takes one batch of at most 8
         if (a.n_splits > 64) launch_kernel(ev, true, true, attn_combine_kernel<512, true, 16>, grid, dim3(1024), st, a);
+        else if (a.n_splits > 32) launch_kernel(ev, true, true, attn_combine_kernel<512, true, 8>, grid, dim3(512), st, a);
         else if (share) launch_kernel(ev, true, true, attn_combine_kernel<512, true>, grid, dim3(kThreads), st, a);
         else launch_kernel(ev, true, true, attn_combine_kernel<512, false>, grid, dim3(kThreads), st, a);
     } else if (a.dim == 128) {
