@@ -177,7 +177,9 @@ class DecodeSetup:
         two-launch call index_attn_decode: index scores with the raw and main
         inserts riding in the score launch, then the candidates' merge and the
         attention with the index insert riding in it (the query at p reads
-        positions < p only).  With --separate-calls the inserts ride in the
+        positions < p only); a dense c128a layer's step is one launch,
+        hybrid_attn_decode_insert, whose attention workgroups carry the
+        inserts.  With --separate-calls the inserts ride in the
         indexer's top-k launch (index_topk_insert) and attention is its own call;
         or they go first in a launch of their own, or, with side streams, beside
         the indexer and attention, forked from and joined back into the current
@@ -185,6 +187,14 @@ class DecodeSetup:
         p, torch = self.reps[r], self.torch
         if self.fused_inserts and "c4a" in self.layers:
             self.attend(r, with_inserts=True)
+            return
+        if self.fused_inserts and tuple(self.layers) == ("c128a",) and not self.qside:
+            # the dense step in one launch: the inserts ride in the attention launch
+            w = self.w
+            self.csl.hybrid_attn_decode_insert(p["main128"], p["raw"], self.bt, self.q_seq, self.q_pos, self.max_pos,
+                                               self.q, None, 0, w.swa, self.scale, w.out_dtype, self.out["c128a"],
+                                               self.insert_jobs(p), self.start, self.cu1, self.out_scales["c128a"],
+                                               self.ws_attn)
             return
         if self.qside:
             self.csl.q_norm_rope_insert(p["raw"], self.bt, self.start, self.cu1, self.x_new, self.q_pre, self.gain_q,

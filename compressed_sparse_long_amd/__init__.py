@@ -84,6 +84,9 @@ _attn_ws = _sig("csl_hybrid_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32,
 _attn_decode = _sig("csl_hybrid_attn_decode", C.c_int,
                     [_P, _P, _G, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz,
                      _vp])
+_attn_decode_insert = _sig("csl_hybrid_attn_decode_insert", C.c_int,
+                           [_P, _P, _G, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _i32,
+                            C.POINTER(_InsertJob), _vp, _vp, _i32, _f32, _vp, _sz, _vp])
 _attn_prefill = _sig("csl_hybrid_attn_prefill", C.c_int,
                      [_P, _P, _G, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _vp, _vp])
 _fused_ws = _sig("csl_index_attn_decode_workspace", _sz, [_i32, _i32, _i64, _i32, _i32])
@@ -100,7 +103,8 @@ _timer_read = _sig("csl_timer_read", C.c_int, [_i32, C.POINTER(C.c_double), C.PO
 
 EXPORTS = ["csl_row_bytes", "csl_compress_insert", "csl_compress_insert_multi", "csl_q_norm_rope_insert",
            "csl_index_topk_workspace", "csl_index_topk", "csl_index_topk_insert",
-           "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_prefill",
+           "csl_hybrid_attn_workspace", "csl_hybrid_attn_decode", "csl_hybrid_attn_decode_insert",
+           "csl_hybrid_attn_prefill",
            "csl_index_attn_decode_workspace", "csl_index_attn_decode", "csl_index_attn_decode_noalloc",
            "csl_last_error",
            "csl_read_device_error", "csl_timer_enable", "csl_timer_read"]
@@ -280,6 +284,27 @@ def hybrid_attn_decode(comp: Pool | None, swa: Pool, block_table, q_seq, q_pos, 
                         _ptr(q_pos), int(max_q_pos), _ptr(q), nh, _ptr(topk), int(k), int(swa_window),
                         float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), _ptr(ws),
                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hybrid_attn_decode_insert(comp: Pool | None, swa: Pool, block_table, q_seq, q_pos, max_q_pos, q, topk, k,
+                              swa_window, softmax_scale, out_dtype, out, jobs, start_pos, cu_new, out_scales=None,
+                              ws=None, eps=1e-6, stream=None):
+    """compress_insert_multi(jobs, ...) and hybrid_attn_decode(...) with the inserts riding in the
+    attention launch (csl_hybrid_attn_decode_insert); jobs as in compress_insert_multi."""
+    cs = comp.struct() if comp is not None else None
+    ss = swa.struct()
+    pg = pages(block_table)
+    nq, nh = int(q.shape[0]), int(q.shape[1])
+    jobs = list(jobs)
+    structs = [p.struct() for p, _, _, _ in jobs]
+    arr = (_InsertJob * max(1, len(jobs)))(*[_InsertJob(C.addressof(structs[i]), _ptr(x), _ptr(lg), _ptr(g))
+                                             for i, (_, x, lg, g) in enumerate(jobs)])
+    total = int(jobs[0][1].shape[0]) if jobs else 0
+    _check(_attn_decode_insert(C.byref(cs) if cs is not None else None, C.byref(ss), C.byref(pg), nq, _ptr(q_seq),
+                               _ptr(q_pos), int(max_q_pos), _ptr(q), nh, _ptr(topk), int(k), int(swa_window),
+                               float(softmax_scale), int(out_dtype), _ptr(out), _ptr(out_scales), len(jobs), arr,
+                               _ptr(start_pos), _ptr(cu_new), total, float(eps), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def hybrid_attn_prefill(comp: Pool | None, swa: Pool, block_table, cu_q, q_pos_start, max_q_pos, q, topk, k,

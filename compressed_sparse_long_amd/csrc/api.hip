@@ -704,24 +704,45 @@ size_t csl_hybrid_attn_workspace(int32_t num_q, int32_t n_heads, int32_t dim, in
     return attn_ws_bytes(num_q, n_heads, dim, comp_ratio, k, swa_window, max_q_pos);
 }
 
-csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int32_t num_q,
-                                  const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q,
-                                  int32_t n_heads, const int32_t* topk, int32_t k, int32_t swa_window,
-                                  float softmax_scale, int32_t out_dtype, void* out, float* out_scales, void* ws,
-                                  size_t ws_bytes, csl_stream_t stream) {
-    if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
-    if (num_q == 0) return CSL_OK;
-    csl_status st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
-                                      max_q_pos, softmax_scale);
-    if (st) return st;
+}  // extern "C"
+
+namespace {
+
+// csl_hybrid_attn_decode, and with `ins` (inserts prepared by prepare_inserts,
+// total_new > 0) csl_hybrid_attn_decode_insert: on decode_attn_kernel the
+// inserts run as extra workgroups of the attention launch, otherwise in a
+// launch of their own before it.  Validation precedes every launch.
+csl_status hybrid_decode(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int32_t num_q,
+                         const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q,
+                         int32_t n_heads, const int32_t* topk, int32_t k, int32_t swa_window, float softmax_scale,
+                         int32_t out_dtype, void* out, float* out_scales, void* ws, size_t ws_bytes,
+                         CompressArgs* ins, csl_stream_t stream) {
+    if (num_q == 0 && !ins) return CSL_OK;
+    csl_status st;
+    hipError_t e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto inserts_alone = [&]() -> csl_status {
+        if (!ins) return CSL_OK;
+        e = timed(CSL_KERNEL_COMPRESS, s, [&](const LaunchEvents& ev) { return launch_compress(*ins, s, ev); });
+        return e == hipSuccess ? CSL_OK : hip_fail(e, "compress_insert launch");
+    };
+    uint32_t* err = nullptr;
+    if (num_q == 0) {
+        if ((st = device_error_ptr(&err))) return st;
+        ins->err = err;
+        return inserts_alone();
+    }
+    if ((st = check_attn_common(comp, swa, pages, n_heads, topk, k, swa_window, out_dtype, out, out_scales, q,
+                                max_q_pos, softmax_scale)))
+        return st;
     if (!q_seq || !q_pos) return fail(CSL_EINVAL, "q_seq or q_pos is NULL");
     const int cr = comp ? comp->ratio : 0;
     const int kk = topk ? k : 0;
     size_t need = csl_hybrid_attn_workspace(num_q, n_heads, swa->dim, cr, kk, swa_window, max_q_pos);
     if (need > 0 && (!ws || ws_bytes < need)) return fail(CSL_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     if (need > 0 && !aligned16(ws)) return fail(CSL_EALIGN, "ws is not 16-byte aligned");
-    uint32_t* err = nullptr;
     if ((st = device_error_ptr(&err))) return st;
+    if (ins) ins->err = err;
     AttnArgs a;
     fill_attn(a, comp, swa, pages, n_heads, topk, k, swa_window, softmax_scale, out_dtype, out, out_scales, q,
               max_q_pos, err);
@@ -730,8 +751,6 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     a.cu_q = nullptr;
     a.q_pos_start = nullptr;
     a.num_q = num_q;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
     float* part = need > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
     if (use_decode_kernel(swa->dim, swa->dtype)) {
         const DecodePlan pl = decode_plan(num_q, n_heads, cr, kk, swa_window, max_q_pos);
@@ -759,7 +778,8 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
         CompressArgs none;
         none.total_new = 0;
         none.n_jobs = 0;
-        e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_decode_attn(d, none, s, ev); });
+        const CompressArgs& ride = ins ? *ins : none;
+        e = timed(CSL_KERNEL_ATTN, s, [&](const LaunchEvents& ev) { return launch_decode_attn(d, ride, s, ev); });
         if (e != hipSuccess) return hip_fail(e, "decode_attn launch");
         if (pl.S > 1 && !pl.combine) {
             e = timed(CSL_KERNEL_ATTN_COMBINE, s, [&](const LaunchEvents& ev) { return launch_attn_combine(d.at, s, ev); });
@@ -769,6 +789,7 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
     }
     const int sp = decode_splits(num_q, cr, kk, swa_window, max_q_pos, swa->dtype == CSL_FP8_E4M3);
     if ((int64_t)num_q * sp > 0x7fffffff) return fail(CSL_ERANGE, "grid too large");
+    if ((st = inserts_alone())) return st;
     a.n_splits = sp;
     a.tiles_per_split = (decode_tiles(cr, kk, swa_window, max_q_pos) + sp - 1) / sp;
     if (sp > 1) {
@@ -782,6 +803,36 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, con
         if (e != hipSuccess) return hip_fail(e, "attn_combine launch");
     }
     return CSL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csl_status csl_hybrid_attn_decode(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages, int32_t num_q,
+                                  const int32_t* q_seq, const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q,
+                                  int32_t n_heads, const int32_t* topk, int32_t k, int32_t swa_window,
+                                  float softmax_scale, int32_t out_dtype, void* out, float* out_scales, void* ws,
+                                  size_t ws_bytes, csl_stream_t stream) {
+    if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
+    return hybrid_decode(comp, swa, pages, num_q, q_seq, q_pos, max_q_pos, q, n_heads, topk, k, swa_window,
+                         softmax_scale, out_dtype, out, out_scales, ws, ws_bytes, nullptr, stream);
+}
+
+csl_status csl_hybrid_attn_decode_insert(const csl_pool* comp, const csl_pool* swa, const csl_pages* pages,
+                                         int32_t num_q, const int32_t* q_seq, const int64_t* q_pos,
+                                         int64_t max_q_pos, const uint16_t* q, int32_t n_heads, const int32_t* topk,
+                                         int32_t k, int32_t swa_window, float softmax_scale, int32_t out_dtype,
+                                         void* out, float* out_scales, int32_t n_jobs, const csl_insert_job* jobs,
+                                         const int64_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                         float eps, void* ws, size_t ws_bytes, csl_stream_t stream) {
+    if (num_q < 0) return fail(CSL_EINVAL, "num_q < 0");
+    CompressArgs c;
+    csl_status st = prepare_inserts(n_jobs, jobs, pages, start_pos, cu_new, total_new, eps, c);
+    if (st) return st;
+    return hybrid_decode(comp, swa, pages, num_q, q_seq, q_pos, max_q_pos, q, n_heads, topk, k, swa_window,
+                         softmax_scale, out_dtype, out, out_scales, ws, ws_bytes, c.total_new > 0 ? &c : nullptr,
+                         stream);
 }
 
 // Workspace of csl_index_attn_decode: [counters | attention partials | index scores and candidates].

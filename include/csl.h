@@ -269,6 +269,29 @@ csl_status csl_hybrid_attn_decode(const csl_pool* comp /* host, nullable */, con
                                   const int32_t* topk, int32_t k, int32_t swa_window, float softmax_scale,
                                   int32_t out_dtype, void* out, float* out_scales, void* ws, size_t ws_bytes,
                                   csl_stream_t stream);
+/*
+ * A decode step's attention with the step's inserts riding along ([Notes]
+ * 优化二：多 CUDA 流并行: the writes of a step overlap its reads): the
+ * results of csl_compress_insert_multi(n_jobs, jobs, pages, start_pos,
+ * cu_new, total_new, eps) followed by csl_hybrid_attn_decode(comp, swa, ...),
+ * provided that no query reads what the inserts write: every inserted token's
+ * position is at least the position of each query of its sequence (a decode
+ * step inserts the token at the query's own position, and a query at p reads
+ * raw tokens below p and compressed entries that close below p).  Otherwise
+ * the results are undefined.  For 512-dim bf16 or fp8 keys the inserts run as
+ * extra workgroups of the attention launch (one launch for a dense c128a
+ * step); for other keys they run in a launch of their own first.  Arguments,
+ * limits and workspace as for the two calls (1 <= n_jobs <= 4); validation
+ * covers both before anything is launched.
+ */
+csl_status csl_hybrid_attn_decode_insert(const csl_pool* comp /* host, nullable */, const csl_pool* swa /* host */,
+                                         const csl_pages* pages /* host */, int32_t num_q, const int32_t* q_seq,
+                                         const int64_t* q_pos, int64_t max_q_pos, const uint16_t* q,
+                                         int32_t n_heads, const int32_t* topk, int32_t k, int32_t swa_window,
+                                         float softmax_scale, int32_t out_dtype, void* out, float* out_scales,
+                                         int32_t n_jobs, const csl_insert_job* jobs /* host */,
+                                         const int64_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                         float eps, void* ws, size_t ws_bytes, csl_stream_t stream);
 csl_status csl_hybrid_attn_prefill(const csl_pool* comp /* host, nullable */, const csl_pool* swa /* host */,
                                    const csl_pages* pages /* host */, const int32_t* cu_q,
                                    const int64_t* q_pos_start, int32_t total_q, int64_t max_q_pos,

@@ -141,6 +141,28 @@ def test_attn_validation(csl):
         assert attn(csl, comp, swa, pg(csl), scale=bad) == -1
 
 
+def test_attn_decode_insert_validation(csl):
+    comp = pool(csl, state_x=None, state_logits=None)
+    swa = pool(csl, ratio=1, coff=1, state_x=None, state_logits=None)
+    jobs = (csl._InsertJob * 1)(csl._InsertJob(C.addressof(swa), FAKE, None, None))
+
+    def call(n_jobs=1, heads=64, x_ok=True, total=1, ws_bytes=1 << 30):
+        if not x_ok:
+            jobs[0].x = FAKE + 2
+        r = csl._attn_decode_insert(C.byref(comp), C.byref(swa), C.byref(pg(csl)), 4, FAKE, FAKE, 1000, FAKE, heads,
+                                    FAKE, 512, 128, 0.04, 1, FAKE, None, n_jobs, jobs, FAKE, FAKE, total, 1e-6,
+                                    FAKE, ws_bytes, None)
+        jobs[0].x = FAKE
+        return r
+    # the inserts' checks, then the attention's; nothing runs before both pass
+    assert call(n_jobs=0) == -2
+    assert call(n_jobs=5) == -2
+    assert call(x_ok=False) == -3
+    assert call(total=-1) == -1
+    assert call(heads=65) == -2
+    assert call(ws_bytes=0) == -4
+
+
 def qside(csl, P, G, heads=64, total=2, x=FAKE, q=FAKE, q_out=FAKE, eps=1e-6):
     return csl._q_side(C.byref(P), C.byref(G), FAKE, FAKE, total, x, q, heads, None, eps, q_out, None)
 

@@ -618,6 +618,110 @@ def test_index_attn_decode_equals_separate_calls(csl, orc, case):
 
 
 # ---------------------------------------------------------------------------
+# hybrid_attn_decode_insert: the step's inserts riding in the attention launch
+# ---------------------------------------------------------------------------
+
+DECODE_INSERT_CASES = [
+    # the dense c128a step (every visible entry): raw and c128a-main inserts, one launch;
+    # the third sequence's new token closes an entry (p + 1 a multiple of 128)
+    dict(name="c128a_dense_bf16", ratio=128, coff=1, D=512, R=64, H=64, k=0, pos=[[9003], [20000], [12031]]),
+    # fp8 keys and fp8 output
+    dict(name="c128a_dense_fp8", ratio=128, coff=1, D=512, R=64, H=64, k=0, pos=[[9003], [16383]], kv=O.FP8,
+         out=O.FP8),
+    # c4a with given top-k ids (the index-free form of the step), 48 heads
+    dict(name="c4a_given_ids", ratio=4, coff=2, D=512, R=64, H=48, k=512, pos=[[9003], [20000]]),
+    # 128-dim keys: not the decode kernel; the inserts run first in a launch of their own
+    dict(name="c4a_d128_inserts_first", ratio=4, coff=2, D=128, R=32, H=8, k=64, pos=[[3001], [1024]],
+         out=O.F32),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_INSERT_CASES, ids=[c["name"] for c in DECODE_INSERT_CASES])
+def test_hybrid_attn_decode_insert_equals_separate_calls(csl, orc, case):
+    seed = zlib.crc32(("decode_insert_" + case["name"]).encode()) % 1000
+    D, R, H, k, r = case["D"], case["R"], case["H"], case["k"], case["ratio"]
+    kv, od = case.get("kv", O.BF16), case.get("out", O.BF16)
+    ns = len(case["pos"])
+    max_pos = max(max(p) for p in case["pos"])
+    mb = (max_pos + 256) // 256 + 1
+    tail = 3
+    first_low = [max(0, max(p) // 256 - 1) for p in case["pos"]]
+    bt = tail_table(seed, ns, mb, first_low, tail)
+    P, P_low = ns * mb, ns * tail
+    per_page = 256 // r
+
+    def kv_rows(tid, n):
+        if kv == O.FP8:
+            return fp8_random_rows(seed, tid, n, D)
+        return randn_bf16(seed, tid, (n, D)).view(np.uint8).reshape(n, -1)
+
+    main = O.HostPool(r, case["coff"], D, R, THETA, kv, P, state=True)
+    for s_ in range(ns):
+        scatter_rows(main.rows, bt, s_, r, kv_rows(40 + 2 * s_, per_page * mb))
+    raw = O.HostPool(1, 1, D, R, THETA, kv, P_low, state=False)
+    for s_ in range(ns):
+        scatter_rows(raw.rows, bt, s_, 1, kv_rows(100 + 2 * s_, 256 * tail), i0=256 * first_low[s_])
+    main.state_x[:P_low] = randn_bf16(seed, 13, main.state_x[:P_low].shape)
+    main.state_logits[:P_low] = randn_f32(seed, 14, main.state_logits[:P_low].shape).astype(np.float32)
+    q_seq = np.concatenate([[s_] * len(p) for s_, p in enumerate(case["pos"])]).astype(np.int32)
+    q_pos = np.concatenate(case["pos"]).astype(np.int64)
+    nq = len(q_pos)
+    q = randn_bf16(seed, 22, (nq, H, D))
+    topk = None
+    if k:  # valid distinct ids below each query's visible count, ascending
+        rng = np.random.default_rng(seed)
+        topk = np.stack([np.sort(rng.choice(int(p) // r, k, replace=False)) for p in q_pos]).astype(np.int32)
+    # new tokens: one per sequence, at the query's position (the queries read below it)
+    cu = np.arange(ns + 1, dtype=np.int32)
+    st = np.array([p[0] for p in case["pos"]], np.int64)
+    x = randn_bf16(seed, 30, (ns, D))
+    lg = randn_f32(seed, 32, (ns, case["coff"])).astype(np.float32)
+    gain = rand_u(seed, 34, (D,), 0.5, 1.5).astype(np.float32)
+    scale = D ** -0.5
+    odt = {O.F32: torch.float32, O.BF16: torch.bfloat16, O.FP8: torch.uint8}[od]
+    outs = []
+    for fused in (False, True):
+        gr, gm = gpu_pool(csl, raw, state=False), gpu_pool(csl, main)
+        out = torch.empty((nq, H, D), dtype=odt, device=DEV)
+        scales = torch.zeros((nq, H, D // 64), dtype=torch.float32, device=DEV) if od == O.FP8 else None
+        jobs = [(gr, dev_bf16(x), None, None), (gm, dev_bf16(x), dev(lg), dev(gain))]
+        gbt = dev(bt)
+        gtk = dev(topk) if k else None
+        ws = csl.workspace(csl.hybrid_attn_workspace(nq, H, D, r, k, 128, max_pos))
+        say(f"hybrid_attn_decode_insert {case['name']} fused={fused} nq {nq}")
+        if fused:
+            csl.hybrid_attn_decode_insert(gm, gr, gbt, dev(q_seq), dev(q_pos), max_pos, dev_bf16(q), gtk, k, 128,
+                                          scale, od, out, jobs, dev(st), dev(cu), scales, ws)
+        else:
+            csl.compress_insert_multi(jobs, gbt, dev(st), dev(cu))
+            csl.hybrid_attn_decode(gm, gr, gbt, dev(q_seq), dev(q_pos), max_pos, dev_bf16(q), gtk, k, 128, scale, od,
+                                   out, scales, ws)
+        torch.cuda.synchronize()
+        assert csl.read_device_error() == 0
+        res = [host(out.view(torch.uint8)), host(gr.rows), host(gm.rows), host_u16(gm.state_x), host(gm.state_logits)]
+        if od == O.FP8:
+            res.append(host(scales))
+        outs.append(res)
+        if ws is not None:  # the counter block is left zero
+            assert not ws[:4096].any().item()
+    names = ["out", "raw rows", "main rows", "main state_x", "main state_logits", "out scales"]
+    for nm, a, b in zip(names, outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{case['name']}: {nm} differ"
+    # the attention against the oracle on the pre-insert pools (the inserts write only rows
+    # and entries no query reads)
+    o_out, o_oscale, o64, f = O.hybrid_attn(main, raw, bt, q_seq, q_pos, q, topk=topk, k=k,
+                                            swa_window=128, softmax_scale=scale, out_dtype=od)
+    assert f == 0
+    g_out = outs[1][0]
+    if od == O.F32:
+        assert_close(g_out.view(np.float32).reshape(o64.shape), o64, what=case["name"])
+    elif od == O.BF16:
+        assert_close(O.bf16_array_to_f64(g_out.view(np.uint16).reshape(o64.shape)), o64, what=case["name"])
+    else:
+        assert_fp8_close(orc, g_out.reshape(o64.shape), outs[1][-1], o_out, o_oscale, what=case["name"])
+
+
+# ---------------------------------------------------------------------------
 # hybrid attention
 # ---------------------------------------------------------------------------
 
