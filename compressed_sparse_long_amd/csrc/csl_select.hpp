@@ -146,25 +146,37 @@ __device__ __forceinline__ uint32_t radix_select_regs(const uint32_t (&key)[KPT]
 // An NB-bin histogram in LDS scanned from the top by one wave: the bin that
 // holds the rank-th largest counted key, the rank inside that bin and its
 // count (valid if total >= rank).  Lane l sums bins NB-1-PER*l downwards; the
-// hit lane's PER bins are then spread over lanes for a second scan.
+// hit lane's PER bins are then spread over lanes for a second scan.  A packed
+// histogram holds two 16-bit counts per word (counts below 65536).
 struct BinPick {
     uint32_t bin, rank, cnt, total;
 };
-template <int NB>
+// Count of bin b in a histogram of NB bins, plain (one word per bin) or
+// packed (bins 2w and 2w+1 in the low and high halves of word w).
+template <bool PACKED>
+__device__ __forceinline__ uint32_t hist_bin(const uint32_t* hist, int b) {
+    if constexpr (PACKED) return (hist[b >> 1] >> (16 * (b & 1))) & 0xffffu;
+    else return hist[b];
+}
+template <int NB, bool PACKED = false>
 __device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t rank) {
     constexpr int PER = NB >= 64 ? NB / 64 : 1;
+    constexpr int WPER = PACKED ? PER / 2 : PER;  // words per lane
     const int lane = threadIdx.x & 63;
     const int top = NB - 1 - PER * lane;
     uint32_t sum = 0;
-    if constexpr (PER >= 4) {
+    if constexpr (WPER >= 4) {
+        const int w0 = PACKED ? (top + 1 - PER) >> 1 : top + 1 - PER;
 #pragma unroll
-        for (int v = 0; v < PER / 4; ++v) {
-            const u32x4 h = *reinterpret_cast<const u32x4*>(hist + top + 1 - PER + 4 * v);
-            sum += h[0] + h[1] + h[2] + h[3];
+        for (int v = 0; v < WPER / 4; ++v) {
+            const u32x4 h = *reinterpret_cast<const u32x4*>(hist + w0 + 4 * v);
+            sum += PACKED ? (h[0] & 0xffffu) + (h[0] >> 16) + (h[1] & 0xffffu) + (h[1] >> 16) + (h[2] & 0xffffu) +
+                                (h[2] >> 16) + (h[3] & 0xffffu) + (h[3] >> 16)
+                          : h[0] + h[1] + h[2] + h[3];
         }
     } else {
-        static_assert(PER == 1, "bins per lane: 1 or a multiple of 4");
-        sum = top >= 0 ? hist[top] : 0u;
+        static_assert(PER == 1, "bins per lane: 1 or a multiple of 4 words");
+        sum = top >= 0 ? hist_bin<PACKED>(hist, top) : 0u;
     }
     const uint32_t incl = wave_scan_add(sum);
     BinPick r = {0u, 0u, 0u, lane_value(incl, 63)};
@@ -178,7 +190,7 @@ __device__ __forceinline__ BinPick wave_find_bin(const uint32_t* hist, uint32_t 
         r.cnt = lane_value(sum, L);
     } else {
         const int top_l = NB - 1 - PER * L;
-        const uint32_t c = lane < PER ? hist[top_l - lane] : 0u;
+        const uint32_t c = lane < PER ? hist_bin<PACKED>(hist, top_l - lane) : 0u;
         const uint32_t in2 = wave_scan_add(c) + above_l;
         const int J = __builtin_ctzll(__ballot(lane < PER && in2 - c < rank && rank <= in2));
         r.bin = (uint32_t)(top_l - J);
@@ -479,8 +491,9 @@ __device__ __forceinline__ void emit_first_stage(const uint32_t (&key)[NS], uint
 // vmask), by one wave.  Radix rounds over rel = key - lo, counting only keys
 // >= lo: with WINDOW, lo = max - (2^24 - 1) (two octaves of fp32 score below
 // the maximum; digits at bits 13..23, 2..12, 0..1), else lo = 0 (bits 21..31,
-// 10..20, 0..9).  Each round histograms its digit in `hist` (2048 words of
-// LDS) and finds the bin of the rank; once that bin holds at most 64 keys they are
+// 10..20, 0..9).  Each round histograms its digit in `hist` (1024 words of
+// LDS: 2048 bins of 16 bits, two to a word, as a wave holds at most 2048 keys)
+// and finds the bin of the rank; once that bin holds at most 64 keys they are
 // compacted to `cbuf` (64 words) and ranked pairwise.  Returns false (uniform)
 // if fewer than `want` keys are >= lo; else T and *rem, the number of copies
 // of T inside the top `want`.
@@ -488,6 +501,7 @@ template <bool WINDOW, int NK = 16>
 __device__ __forceinline__ bool wave_select(const uint32_t (&key)[NK], uint32_t vmask, uint32_t want, uint32_t lo,
                                             uint32_t* hist, uint32_t* cbuf, uint32_t& T, uint32_t& rem) {
     static_assert(NK <= 32, "slot masks are 32 bits");
+    static_assert(NK * 64 < 65536, "bin counts fit 16 bits");
     const int lane = threadIdx.x & 63;
     uint32_t rel[NK], in = 0;
 #pragma unroll
@@ -498,11 +512,14 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[NK], uint32_t 
     uint32_t prefix = 0, pmask = 0, rank = want;
     auto matches = [&](int i) { return ((in >> i) & 1u) && (rel[i] & pmask) == prefix; };
     auto build = [&](int sh, int nb) {
-        for (int b = 4 * lane; b < nb; b += 256) *reinterpret_cast<u32x4*>(hist + b) = u32x4{0u, 0u, 0u, 0u};
+        for (int w = 4 * lane; w < nb / 2; w += 256) *reinterpret_cast<u32x4*>(hist + w) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < NK; ++i)
-            if (matches(i)) atomicAdd(&hist[(rel[i] >> sh) & (uint32_t)(nb - 1)], 1u);
+            if (matches(i)) {
+                const uint32_t bin = (rel[i] >> sh) & (uint32_t)(nb - 1);
+                atomicAdd(&hist[bin >> 1], 1u << (16 * (bin & 1u)));
+            }
         wave_lds_sync();
     };
     auto take = [&](const BinPick& b, int sh, int nb) {
@@ -529,7 +546,7 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[NK], uint32_t 
     };
     constexpr int kSh0 = WINDOW ? 13 : 21, kSh1 = WINDOW ? 2 : 10;
     build(kSh0, 2048);
-    BinPick b = wave_find_bin<2048>(hist, rank);
+    BinPick b = wave_find_bin<2048, true>(hist, rank);
     if (b.total < rank) return false;
     take(b, kSh0, 2048);
     if (b.cnt <= 64u) {
@@ -537,7 +554,7 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[NK], uint32_t 
         return true;
     }
     build(kSh1, 2048);
-    b = wave_find_bin<2048>(hist, rank);
+    b = wave_find_bin<2048, true>(hist, rank);
     take(b, kSh1, 2048);
     if (b.cnt <= 64u) {
         finish(b.cnt);
@@ -545,7 +562,7 @@ __device__ __forceinline__ bool wave_select(const uint32_t (&key)[NK], uint32_t 
     }
     constexpr int kNb2 = WINDOW ? 4 : 1024;
     build(0, kNb2);
-    b = wave_find_bin<kNb2>(hist, rank);
+    b = wave_find_bin<kNb2, true>(hist, rank);
     take(b, 0, kNb2);
     T = prefix + lo;
     rem = rank;

@@ -86,7 +86,7 @@ constexpr int kMergeSlots = 8;      // candidates per merge thread
 // wave whose lane l holds the keys of ids base + 16 l .. +15 (ids at or past
 // base + nvalid are invalid): the chunk's first kl ids in (score desc, id asc)
 // order, written in ascending id order, and the (kl+1)-th, whose position the
-// merge checks (none if nvalid <= kl).  hist / cbuf: LDS of 2048 and 64 words
+// merge checks (none if nvalid <= kl).  hist / cbuf: LDS of 1024 and 64 words
 // that only this wave uses.
 __device__ __forceinline__ void wave_first_stage(const IndexArgs& a, int n, int blk, const uint32_t (&key)[16],
                                                  int64_t base, int nvalid, uint32_t* hist, uint32_t* cbuf) {
@@ -148,7 +148,7 @@ __device__ __forceinline__ void wave_first_stage(const IndexArgs& a, int n, int 
 // Stand-alone first stage (after the query-blocked score kernel): each wave
 // takes one (query, chunk), keys read from the score row; no barriers.
 __global__ void __launch_bounds__(256) topk_local_kernel(IndexArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t s_hist[4][2048];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[4][1024];
     __shared__ uint32_t s_cbuf[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = blockIdx.y, blk = blockIdx.x * 4 + wave;
