@@ -541,26 +541,27 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
         __syncthreads();  // the previous pass's reads of s_pg and s_k are done
         if (tid < npages) s_pg[tid] = page_of(a.bt, a.max_blocks, a.num_pages, sg, (c0 + 64 * tid) * 4);
         __syncthreads();
-        u32x4 st[LPT];
-        uint32_t st_e8 = 0;  // fp4: the scale byte of the thread's block
-        auto load_page = [&](int j) {
-            const int32_t pg = s_pg[j];
+        const int32_t pgl = lane < npages ? s_pg[lane] : -1;  // lane j: page j of the pass (read with readlane)
+        u32x4 st[2][LPT];
+        uint32_t st_e8[2] = {0u, 0u};  // fp4: the scale byte of the thread's block
+        auto load_page = [&](int j, int b) {
+            const int32_t pg = __builtin_amdgcn_readlane(pgl, j);
             if constexpr (FP4) {
                 // thread = (row tid / 4, 32-element block tid % 4)
                 const uint8_t* r = a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT + (tid >> 2) * RBG;
-                st[0] = load16_a4(r + 16 * (tid & 3));
-                st_e8 = r[DI / 2 + (tid & 3)];
+                st[b][0] = load16_a4(r + 16 * (tid & 3));
+                st_e8[b] = r[DI / 2 + (tid & 3)];
             } else {
                 const u32x4* base = reinterpret_cast<const u32x4*>(a.rows + (int64_t)(pg < 0 ? 0 : pg) * UNIT);
 #pragma unroll
-                for (int q = 0; q < LPT; ++q) st[q] = base[q * 256 + tid];
+                for (int q = 0; q < LPT; ++q) st[b][q] = base[q * 256 + tid];
             }
         };
-        auto store_page = [&](int b) {
+        auto store_page = [&](int lb, int b) {
             if constexpr (FP4) {
                 uint32_t w[16];
-                mxfp4_to_bf16(st[0], st_e8, w);
-                uint8_t* dst = s_k[b] + (tid >> 2) * LROW + 64 * (tid & 3);
+                mxfp4_to_bf16(st[b][0], st_e8[b], w);
+                uint8_t* dst = s_k[lb] + (tid >> 2) * LROW + 64 * (tid & 3);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<u32x4*>(dst + 16 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
@@ -568,18 +569,20 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
 #pragma unroll
                 for (int q = 0; q < LPT; ++q) {
                     const int c = q * 256 + tid;  // 16-byte chunk of the page
-                    *reinterpret_cast<u32x4*>(s_k[b] + (c / CPR) * LROW + (c % CPR) * 16) = st[q];
+                    *reinterpret_cast<u32x4*>(s_k[lb] + (c / CPR) * LROW + (c % CPR) * 16) = st[b][q];
                 }
             }
         };
-        load_page(0);
-        store_page(0);
+        load_page(0, 0);
+        if (npages > 1) load_page(1, 1);
+        store_page(0, 0);
         __syncthreads();
-        for (int j = 0; j < npages; ++j) {
-            if (j + 1 < npages) load_page(j + 1);
-            const uint8_t* sk = s_k[j & 1];
+        // page j: registers st[j & 1] then LDS s_k[j & 1]; two pages' loads in flight
+        auto body = [&](int j, int b) {
+            if (j + 2 < npages) load_page(j + 2, b);
+            const uint8_t* sk = s_k[b];
             const int64_t e0 = c0 + 64 * j;
-            const int32_t pg = s_pg[j];
+            const int32_t pg = __builtin_amdgcn_readlane(pgl, j);
             if (pg < 0 && lane == 0 && ((gmask >> (QW * wave)) & ((1u << QW) - 1u))) raise_error(a.err, kErrPage);
             float mine[PP][2];  // the lane's score: query 2pp + h2, entry e0 + 32 t + r32
 #pragma unroll
@@ -612,7 +615,7 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
             }
             // the next page into LDS before this page's scores go out: its wait for the page's
             // loads (a count of outstanding memory operations) then does not include the stores
-            if (j + 1 < npages) store_page((j + 1) & 1);
+            if (j + 1 < npages) store_page(b ^ 1, b ^ 1);
 #pragma unroll
             for (int pp = 0; pp < PP; ++pp) {
                 const int qi = QW * wave + 2 * pp + h2;
@@ -624,6 +627,10 @@ __global__ void __launch_bounds__(256) index_score_tiled_kernel(IndexArgs a) {
                         __builtin_nontemporal_store(pg < 0 ? -INFINITY : mine[pp][t], row + 32 * t);
             }
             __syncthreads();
+        };
+        for (int j = 0; j < npages; j += 2) {
+            body(j, 0);
+            if (j + 1 < npages) body(j + 1, 1);
         }
     }
 }
