@@ -256,6 +256,134 @@ __device__ __forceinline__ void insert_block(const CompressArgs& args, int jb, i
 }
 
 
+// Windows of at most this many tokens (raw rows and c4a) are inserted by one wave.
+constexpr int kWaveWindow = 64;
+
+// The same insert as insert_block for a pool whose window holds at most
+// kWaveWindow tokens, by one wave with no LDS and no barrier, in the same
+// arithmetic order (lane k holds window slot k as thread k does there; the
+// weighted sum keeps four partial sums over the slots k = w mod 4 and adds
+// them as (0 + 1) + (2 + 3)), so the rows are bit-identical.  The token's row
+// and logits are requested before its sequence and page are known.
+__device__ __forceinline__ void insert_wave(const CompressArgs& args, int jb, int j) {
+    const CompressJob& a = args.job[jb];
+    const RopeFreqs& rf = args.rf[jb];
+    const int lane = threadIdx.x & 63;
+    const int D = a.dim;
+    const bool active = lane * 8 < D;
+    u32x4 xr = {0u, 0u, 0u, 0u};
+    if (active) xr = *reinterpret_cast<const u32x4*>(a.x + (int64_t)j * D + 8 * lane);
+    const float lgj = a.ratio > 1 && lane < a.coff ? a.logits[(int64_t)j * a.coff + lane] : 0.f;
+    const int s = find_seq(args.cu_new, args.num_seqs, j);
+    const int64_t start = args.start_pos[s];
+    const int cbase = args.cu_new[s];
+    const int64_t t = start + (j - cbase);
+    const int32_t pgt = page_of(args.bt, args.max_blocks, a.num_pages, s, t);
+    if (a.ratio == 1) {
+        if (pgt < 0) {
+            if (lane == 0) raise_error(args.err, (t < 0 || (t >> 8) >= args.max_blocks) ? kErrPos : kErrPage);
+            return;
+        }
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v[2 * c] = __uint_as_float(xr[c] << 16);
+            v[2 * c + 1] = __uint_as_float(xr[c] & 0xffff0000u);
+        }
+        rope8(v, 8 * lane, D, a.rope_dims, rf, t, active);
+        uint8_t* row = a.rows + ((int64_t)pgt * kBlockPositions + (t & 255)) * a.row_bytes;
+        store8(row, a.dtype, D, lane, active, v);
+        return;
+    }
+
+    // 1. append the token to the compressor state
+    if (pgt < 0) {
+        if (lane == 0) raise_error(args.err, (t < 0 || (t >> 8) >= args.max_blocks) ? kErrPos : kErrPage);
+    } else {
+        const int64_t tok = (int64_t)pgt * kBlockPositions + (t & 255);
+        if (active) *reinterpret_cast<u32x4*>(a.state_x + tok * D + 8 * lane) = xr;
+        if (lane < a.coff) a.state_logits[tok * a.coff + lane] = lgj;
+    }
+    const int r = a.ratio, W = a.coff * a.ratio;
+    if ((t + 1) % r != 0) return;  // uniform across the wave
+    const int64_t i = (t + 1) / r - 1;
+
+    // 2. window weights: lane k owns window slot k
+    float lg = -INFINITY;
+    const uint16_t* ptr = nullptr;
+    if (lane < W) {
+        const int64_t tk = (int64_t)r * (i + 1) - W + lane;
+        const int col = lane / r;
+        if (tk >= start) {
+            const int64_t jj = cbase + (tk - start);
+            lg = a.logits[jj * a.coff + col];
+            ptr = a.x + jj * D;
+        } else if (tk >= 0) {
+            const int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, tk);
+            if (pg < 0) {
+                raise_error(args.err, kErrPage);
+            } else {
+                const int64_t tok = (int64_t)pg * kBlockPositions + (tk & 255);
+                lg = a.state_logits[tok * a.coff + col];
+                ptr = a.state_x + tok * D;
+            }
+        }
+    }
+    const float m = wave_max(lg);
+    const float e = ptr ? __expf(lg - m) : 0.f;
+    const float den = wave_sum(e);
+    const float inv_den = den > 0.f ? 1.0f / den : 0.f;
+
+    // 3. weighted sum
+    float acc[4][8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[w][c] = 0.f;
+    const uint64_t pv = reinterpret_cast<uint64_t>(ptr);
+    for (int k0 = 0; k0 < W; k0 += 4) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int k = k0 + w;
+            if (k >= W) break;
+            const uint64_t pk = ((uint64_t)lane_value((uint32_t)(pv >> 32), k) << 32) | lane_value((uint32_t)pv, k);
+            if (!pk) continue;
+            const float wk = __uint_as_float(lane_value(__float_as_uint(e), k)) * inv_den;
+            if (active) {
+                float v[8];
+                load8(reinterpret_cast<const uint16_t*>(pk) + 8 * lane, v);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[w][c] = fmaf(wk, v[c], acc[w][c]);
+            }
+        }
+    }
+
+    // 4. RMSNorm, RoPE at r*i, store
+    float u[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        u[c] = active ? (acc[0][c] + acc[1][c]) + (acc[2][c] + acc[3][c]) : 0.f;
+        ss = fmaf(u[c], u[c], ss);
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + args.eps);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float g = (a.gain && active) ? a.gain[8 * lane + c] : 1.0f;
+        u[c] = u[c] * inv * g;
+    }
+    rope8(u, 8 * lane, D, a.rope_dims, rf, (int64_t)r * i, active);
+    const int32_t pg = page_of(args.bt, args.max_blocks, a.num_pages, s, (int64_t)r * i);
+    if (pg < 0) {
+        if (lane == 0) raise_error(args.err, kErrPage);
+        return;
+    }
+    const int per_page = kBlockPositions / r;
+    uint8_t* row = a.rows + ((int64_t)pg * per_page + (i % per_page)) * a.row_bytes;
+    store8(row, a.dtype, D, lane, active, u);
+}
+
 // ---------------------------------------------------------------- query side
 
 // Sequence s of new token j and its position t = start_pos[s] + (j - cu[s]).
