@@ -666,8 +666,13 @@ __device__ __forceinline__ void merge_query(const IndexArgs& a, const int n) {
                                              m);
 }
 
+// The 256-thread merge serves calls with many queries (a prefill chunk: one
+// workgroup per query): the compiler is held to six waves per SIMD instead of
+// the four its register use allows, at the price of some spills (0.050 -> 0.040
+// ms on an 8192-query chunk).
 template <int NT>
-__global__ void __launch_bounds__(NT) topk_merge_kernel(IndexArgs a) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 6 : 1, 8)))
+topk_merge_kernel(IndexArgs a) {
     merge_query<NT>(a, blockIdx.x);
 }
 
