@@ -291,6 +291,11 @@ INDEX_CASES = [
          pos=[[0, 3, 4, 5, 255, 256, 300] + list(range(4096, 4121)), list(range(1020, 1050)),
               [260 + 37 * i for i in range(20)]], shuffle=True),
     dict(name="tiled_h16_d64_k100_ties", H=16, DI=64, k=100, pos=[list(range(6000, 6070))], mode="equal"),
+    # scores rise with the id: the top 512 crowd the last chunk, so after the
+    # query-blocked scores and the stand-alone first stage the merge's candidate
+    # check fails and its exact select over the score rows takes over
+    dict(name="tiled_h16_d128_k512_ramp_fallback", H=16, DI=128, k=512, pos=[list(range(20000, 20070))],
+         mode="ramp"),
     # fp4 (MXFP4) index rows: one query per score row, and query-blocked
     dict(name="fp4_h16_d128_k512_2seq", H=16, DI=128, k=512, pos=[[2047, 2048, 2051, 9000, 20000], [4, 5000, 6000]],
          fp4=True),
