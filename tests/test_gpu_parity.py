@@ -777,6 +777,11 @@ def random_topk(seed, q_pos, ratio, k, invalid=False):
 ATTN_CASES = [
     dict(name="c4a_d128_h8_k64_f32", D=128, R=32, H=8, ratio=4, k=64, dtype=O.BF16, out=O.F32,
          pos=[[1, 5, 127, 128, 130, 600, 1023, 1024]]),
+    # the 128-dim kernel and the 128-dim combine with bf16 and fp8 output
+    dict(name="c4a_d128_h8_k64_bf16", D=128, R=32, H=8, ratio=4, k=64, dtype=O.BF16, out=O.BF16,
+         pos=[[1, 5, 127, 128, 130, 600, 1023, 1024]]),
+    dict(name="c4a_d128_h8_k64_fp8out", D=128, R=32, H=8, ratio=4, k=64, dtype=O.BF16, out=O.FP8,
+         pos=[[2, 64, 129, 700, 1024], [900, 3]]),
     dict(name="c4a_d512_h64_k512_bf16_split", D=512, R=64, H=64, ratio=4, k=512, dtype=O.BF16, out=O.BF16,
          pos=[[2048, 2049, 4099], [3000, 700]]),
     dict(name="c128a_d512_h64_dense_bf16", D=512, R=64, H=64, ratio=128, k=0, dtype=O.BF16, out=O.BF16,
