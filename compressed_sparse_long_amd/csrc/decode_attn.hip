@@ -23,9 +23,9 @@
 // Work mapping.  Workgroup = (query n, head group hg of 16 heads, split sp of
 // `per` keys); the G head groups of one (n, sp) get block indices equal mod 8
 // so that their shared key rows meet in one L2.  Wave w owns output dims
-// 128w .. 128w+127 and the same slice of every dot product.  Per 32-key tile
-// (staged by direct global->LDS loads in a 4-slot ring, three tiles in
-// flight):
+// 128w .. 128w+127 and the same slice of every dot product.  32-key tiles
+// are staged by direct global->LDS loads in a 4-slot ring (every slot filled
+// before the loop) and taken two per pass, one softmax over the pair; per tile:
 //   * S^T[32 keys x 16 heads] over the wave's 128 dims on
 //     v_mfma_f32_16x16x32_bf16 (A = key rows, LDS; B = the wave's q slice,
 //     registers); the four waves' partial sums meet in LDS and every wave
@@ -159,7 +159,7 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
             insert_block(c, (int)(i / c.total_new), (int)(i % c.total_new), *reinterpret_cast<InsertSmem*>(s_ring));
         return;
     }
-    __shared__ __attribute__((aligned(16))) f32x4 s_sx[2][4][2][64];  // S^T partials: [tile parity][wave][m-tile]
+    __shared__ __attribute__((aligned(16))) f32x4 s_sx[2][4][2][64];  // S^T partials: [tile of the pair][wave][m-tile]
     __shared__ const uint8_t* s_rows[KMAX];
     __shared__ uint32_t s_vbits[KMAX / 32];
     __shared__ int32_t s_ids[MERGE ? KMAX : 1];
@@ -188,6 +188,9 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     // position, the wave's q slice, and the given ids or the first-stage candidates
     const int s_raw = a.q_seq[n];
     const int64_t p_raw = a.q_pos[n];
+    // the inverse-RoPE frequency of the pair this thread rotates in the epilogue
+    const bool rope_lane = tid < a.rope_dims / 2;
+    const double inv_freq = rope_lane ? a.rf.inv_freq[tid] : 0.0;
     // q slice of the wave as the B operand of S^T: column = head, k-step ks = dims 128 wave + 32 ks + 8 g .. +7
     bf16x8 qb[4];
     {
@@ -241,7 +244,6 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
             btv[i] = (staged && b < (int)nbt64) ? btrow[b] : -1;
         }
     }
-    if (tid < a.rope_dims / 2) rope_cs(-p, a.rf.inv_freq[tid], s_rope[0][tid], s_rope[1][tid]);
 
     if constexpr (MERGE > 0) {
         // the top-k of the query from the first-stage candidates: every workgroup of the query
@@ -323,8 +325,13 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
     // inside the tile loop and, counting the tiles' loads too, drain every tile in flight
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qb[ks]));
-    const int pre = ntl < RING - 1 ? ntl : RING - 1;  // tiles issued before the loop
-    for (int t = 0; t < pre; ++t) issue(t);
+    double inv_freq_r = inv_freq;  // (likewise the frequency, used after the issue)
+    asm volatile("" : "+v"(inv_freq_r));
+    // every ring slot is filled before the loop; a pair of tiles frees two slots
+    int issued = ntl < RING ? ntl : RING;
+    for (int t = 0; t < issued; ++t) issue(t);
+    // the epilogue's inverse-RoPE angles while the first tiles are in flight
+    if (rope_lane) rope_cs(-p, inv_freq_r, s_rope[0][tid], s_rope[1][tid]);
 
     f32x4 oacc[8];
 #pragma unroll
@@ -394,47 +401,53 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         }
     };
 
-    if (ntl > 0) {
-        // tile 0's S partial before the loop
-        wait_tiles(pre - 1);
-        __syncthreads();
-        SOps so;
-        f32x4 sa[2];
-        s_reads(0, so);
-        s_mfma(so, sa);
-        s_sx[0][wave][0][lane] = sa[0];
-        s_sx[0][wave][1][lane] = sa[1];
-    }
-    // iteration t: the softmax and P.V of tile t beside the S partial of tile t+1; one barrier:
-    // tile t+1 is in LDS, the partials of tile t are complete, tile t-1's slot is free
-    for (int t = 0; t < ntl; ++t) {
-        const bool next = t + 1 < ntl;
-        if (next) {
-            // tiles issued so far: min(ntl, t + RING - 1); tile t+1 must have landed
-            const int issued = ntl < t + RING - 1 ? ntl : t + RING - 1;
-            wait_tiles(issued - (t + 2));
+    // iteration i takes tiles t = 2i and t + 1 (when there is one): both S^T partials, one
+    // barrier to meet the four waves' partials, one softmax over the pair's keys, both P.V
+    // products.  Two tiles per pass halve the passes' dependent chains (LDS round trips,
+    // barriers, the cross-lane max), which bound the loop at one wave per SIMD.
+    for (int t = 0; t < ntl; t += 2) {
+        const bool two = t + 1 < ntl;  // (uniform)
+        const int tl = two ? t + 1 : t;
+        // tiles t .. tl have landed: the loads of the tiles issued after them may still be in flight
+        wait_tiles(issued - (tl + 1));
+        __syncthreads();  // the pair is visible; every wave is done with the slots and the S partials before it
+        while (issued < ntl && issued < t + RING) issue(issued++);  // the slots the previous pair freed
+        {
+            SOps so0, so1;
+            f32x4 sa0[2], sa1[2];
+            s_reads(t, so0);
+            if (two) s_reads(t + 1, so1);
+            s_mfma(so0, sa0);
+            if (two) s_mfma(so1, sa1);
+            s_sx[0][wave][0][lane] = sa0[0];
+            s_sx[0][wave][1][lane] = sa0[1];
+            if (two) {
+                s_sx[1][wave][0][lane] = sa1[0];
+                s_sx[1][wave][1][lane] = sa1[1];
+            }
         }
-        __syncthreads();
-        if (t + RING - 1 < ntl) issue(t + RING - 1);
-        const int par = t & 1;
-        f32x4 sf[2];
+        __syncthreads();  // the four waves' S^T partials of the pair
+        f32x4 sf[2][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-            sf[mt] = ((s_sx[par][0][mt][lane] + s_sx[par][1][mt][lane]) + s_sx[par][2][mt][lane]) + s_sx[par][3][mt][lane];
-        SOps so;
-        if (next) s_reads(t + 1, so);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                sf[h][mt] = (h == 0 || two)
+                                ? ((s_sx[h][0][mt][lane] + s_sx[h][1][mt][lane]) + s_sx[h][2][mt][lane]) + s_sx[h][3][mt][lane]
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // softmax: value (mt, i) is the key in LDS row key_bit(mt, i) of this head column
-        const uint32_t vb = s_vbits[t];
-        float x[8];
+        // softmax over the pair: value 8 h + (mt, i) is the key in LDS row key_bit(mt, i) of tile t + h
+        const uint32_t vb0 = s_vbits[t], vb1 = two ? s_vbits[t + 1] : 0u;
+        float x[16];
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-            const int mt = cc >> 2, i = cc & 3;
-            x[cc] = ((vb >> key_bit(mt, i)) & 1u) ? sf[mt][i] : -INFINITY;
+        for (int cc = 0; cc < 16; ++cc) {
+            const int h = cc >> 3, mt = (cc >> 2) & 1, i = cc & 3;
+            const uint32_t vb = h ? vb1 : vb0;
+            x[cc] = ((vb >> key_bit(mt, i)) & 1u) ? sf[h][mt][i] : -INFINITY;
         }
         float tmax = -INFINITY;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) tmax = fmaxf(tmax, x[cc]);
+        for (int cc = 0; cc < 16; ++cc) tmax = fmaxf(tmax, x[cc]);
         tmax = max_xor32(max_xor16(tmax)) * a.scale_log2;
         const bool move = tmax > m_ref + 8.0f;
         const float alpha = __builtin_amdgcn_exp2f(move ? m_ref - tmax : 0.f);
@@ -442,78 +455,75 @@ decode_attn_kernel(DecodeArgs d, CompressArgs c) {
         l_run *= alpha;
         m_ref = move ? tmax : m_ref;
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        float pf[8];
+        float pf[16];
         float psum = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
+        for (int cc = 0; cc < 16; ++cc) {
             pf[cc] = __builtin_amdgcn_exp2f(fmaf(x[cc], a.scale_log2, -m_use));
             psum += pf[cc];
         }
         l_run += psum;
-        // the P operands (hi and, for fp8 output, lo parts); fp8 keys: one per 64-dim group of
-        // the wave, P times the key's group scale (V = codes x scale), element cc = key 8 g + cc
-        bf16x8 pb[2], plo[2];
-        {
-            float sc[2][8];
-            if constexpr (KV8) {
-                const uint8_t* kt = tile(t);
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const float2 v = *reinterpret_cast<const float2*>(kt + (8 * g + cc) * ROW + 512 + 8 * wave);
-                    sc[0][cc] = v.x;
-                    sc[1][cc] = v.y;
-                }
-            }
-#pragma unroll
-            for (int gp = 0; gp < (KV8 ? 2 : 1); ++gp) {
-                uint32_t pw[4], pl[4];
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const float p0 = KV8 ? pf[2 * cc] * sc[gp][2 * cc] : pf[2 * cc];
-                    const float p1 = KV8 ? pf[2 * cc + 1] * sc[gp][2 * cc + 1] : pf[2 * cc + 1];
-                    pw[cc] = pack_bf16x2(p0, p1);
-                    if constexpr (PREC)
-                        pl[cc] = pack_bf16x2(p0 - bf16_bits_to_f32(pw[cc] & 0xffffu), p1 - bf16_bits_to_f32(pw[cc] >> 16));
-                }
-                pb[gp] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-                plo[gp] = pb[gp];
-                if constexpr (PREC) plo[gp] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-            }
-            if constexpr (!KV8) {
-                pb[1] = pb[0];
-                plo[1] = plo[0];
-            }
-        }
-
-        f32x4 sa[2];
-        if (next) s_mfma(so, sa);
-
-        // O^T += V^T . P^T over the wave's 8 m-tiles of 16 dims
         if (__ballot(rescale)) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
         }
-        const uint8_t* kt = tile(t);
-        bf16x8 va[8];
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-            if constexpr (KV8) {
-                va[mm] = fp8x8_to_bf16(tr8_read(kt + (lane >> 1) * ROW + 128 * wave + 16 * mm + 8 * (lane & 1)));
-            } else {
-                const uint8_t* b0 = kt + tr_row * ROW + tr_col + 32 * mm;
-                const u32x2 v0 = tr_read(b0), v1 = tr_read(b0 + 16 * ROW);
-                va[mm] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        for (int h = 0; h < 2; ++h) {
+            if (h == 1 && !two) break;  // (uniform)
+            const uint8_t* kt = tile(t + h);
+            // the P operands of tile t + h (hi and, for fp8 output, lo parts); fp8 keys: one per
+            // 64-dim group of the wave, P times the key's group scale (V = codes x scale),
+            // element cc = key 8 g + cc
+            bf16x8 pb[2], plo[2];
+            {
+                float sc[2][8];
+                if constexpr (KV8) {
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) {
+                        const float2 v = *reinterpret_cast<const float2*>(kt + (8 * g + cc) * ROW + 512 + 8 * wave);
+                        sc[0][cc] = v.x;
+                        sc[1][cc] = v.y;
+                    }
+                }
+#pragma unroll
+                for (int gp = 0; gp < (KV8 ? 2 : 1); ++gp) {
+                    uint32_t pw[4], pl[4];
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        const float q0 = pf[8 * h + 2 * cc], q1 = pf[8 * h + 2 * cc + 1];
+                        const float p0 = KV8 ? q0 * sc[gp][2 * cc] : q0;
+                        const float p1 = KV8 ? q1 * sc[gp][2 * cc + 1] : q1;
+                        pw[cc] = pack_bf16x2(p0, p1);
+                        if constexpr (PREC)
+                            pl[cc] = pack_bf16x2(p0 - bf16_bits_to_f32(pw[cc] & 0xffffu), p1 - bf16_bits_to_f32(pw[cc] >> 16));
+                    }
+                    pb[gp] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+                    plo[gp] = pb[gp];
+                    if constexpr (PREC) plo[gp] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+                }
+                if constexpr (!KV8) {
+                    pb[1] = pb[0];
+                    plo[1] = plo[0];
+                }
             }
-        }
+            // O^T += V^T . P^T over the wave's 8 m-tiles of 16 dims
+            bf16x8 va[8];
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-            // m-tiles 0..3 are the wave's first 64-dim group, 4..7 its second
-            oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], pb[mm >> 2], oacc[mm], 0, 0, 0);
-            if constexpr (PREC) oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], plo[mm >> 2], oacc[mm], 0, 0, 0);
-        }
-        if (next) {
-            s_sx[par ^ 1][wave][0][lane] = sa[0];
-            s_sx[par ^ 1][wave][1][lane] = sa[1];
+            for (int mm = 0; mm < 8; ++mm) {
+                if constexpr (KV8) {
+                    va[mm] = fp8x8_to_bf16(tr8_read(kt + (lane >> 1) * ROW + 128 * wave + 16 * mm + 8 * (lane & 1)));
+                } else {
+                    const uint8_t* b0 = kt + tr_row * ROW + tr_col + 32 * mm;
+                    const u32x2 v0 = tr_read(b0), v1 = tr_read(b0 + 16 * ROW);
+                    va[mm] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+                }
+            }
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) {
+                // m-tiles 0..3 are the wave's first 64-dim group, 4..7 its second
+                oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], pb[mm >> 2], oacc[mm], 0, 0, 0);
+                if constexpr (PREC) oacc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mm], plo[mm >> 2], oacc[mm], 0, 0, 0);
+            }
         }
     }
     // the head's sum over its four lanes (every wave holds the same softmax)
