@@ -10,7 +10,7 @@ element d's fp4 error, ReLU being 1-Lipschitz gives
 
 and the candidates are the entries with sigma_fp4 + eps >= tau, tau the k-th
 largest sigma_fp4 - eps; every true top-k entry passes.  On the index keys of
-the c4a decode workload (N(0,1) keys and queries, 64 heads of 128 dims, weights
+the c4a decode workload (N(0,1) keys and queries, 16 heads of 128 dims, weights
 U(0,1)), eps is about ten times the spread of the scores, so no entry is ever
 pruned: the stage would read the fp4 and the bf16 row of every entry.  This
 test checks both facts on a seeded sample of the workload (one query, 4096
