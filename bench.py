@@ -744,6 +744,8 @@ def main():
     ap.add_argument("--workload", default="c4a", choices=["c4a", "c4a_fp4", "c128a", "1m", "prefill", "qside_decode", "qside_prefill"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying HIP graphs")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="decode steps per HIP graph (the largest divisor of --steps not above this)")
     ap.add_argument("--timing-steps", type=int, default=200,
                     help="eager steps after the graph replays that time the dominant kernel")
     ap.add_argument("--side-stream", action="store_true",
@@ -809,15 +811,17 @@ def main():
     graphs = None
     per_graph = 1
     if not args.no_graph:
-        graphs = []
-        # one graph holds the R steps (one per cache replica, i.e. R successive layers)
-        per_graph = R if args.steps % R == 0 else 1
-        for r0 in range(0, R, per_graph):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for r in range(r0, r0 + per_graph):
-                    setup.step(r)
-            graphs.append(g)
+        # One graph holds G successive steps, step i on cache replica i % R (the replicas stand
+        # for successive layers, whose caches are distinct).  A serving engine replays one graph
+        # per decode iteration over every layer of the model; replaying a graph costs about 8 us
+        # of its own on this GPU, which G steps share.  G is the largest divisor of the timed
+        # step count not above --graph-steps, so that exactly K steps are timed.
+        per_graph = max(g for g in range(1, max(1, min(args.graph_steps, args.steps)) + 1) if args.steps % g == 0)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                setup.step(i % R)
+        graphs = [g]
         torch.cuda.synchronize()
         for g in graphs:
             g.replay()
