@@ -257,11 +257,12 @@ int decode_splits(int num_q, int comp_ratio, int k, int swa_window, int64_t max_
 
 // Decode attention on 512-dim bf16 or fp8 keys (decode_attn_kernel): G head groups of
 // 16; the key list (rounded up to 32-key tiles) split so that the launch holds
-// about 256 workgroups but no split has fewer than about three tiles (the last
-// arriving split reads every other split's partial, so short splits cost more
-// there than they save in the tile loop: the 8-query c128a step took 24.7 us with
-// six two-tile splits, 20.6 with four three-tile ones, 21.1 with two of six), with
-// 32..256 keys per split; at most 8 splits are merged inside the launch by the
+// about 256 workgroups but no split has fewer than about four tiles, two passes
+// of the loop's tile pairs (the last arriving split reads every other split's
+// partial, so short splits cost more there than they save in the tile loop: the
+// 8-query c128a step took 18.6 us with six two-tile splits, 15.4 with four
+// three-tile ones, 14.5 with three of four, 15.3 with two of six), with 32..256
+// keys per split; at most 8 splits are merged inside the launch by the
 // last arriving split (more, or more than kDecodeCounters (query, head group)
 // pairs: partials for the combine kernel).
 // (Fewer, longer splits measured slower: eight fp8 splits of 1040 keys for the
@@ -275,7 +276,7 @@ DecodePlan decode_plan(int num_q, int n_heads, int comp_ratio, int k, int swa_wi
     const int64_t keys = decode_tiles(comp_ratio, k, swa_window, max_q_pos) * 32;
     const int64_t groups = (int64_t)(num_q > 0 ? num_q : 1) * pl.G;
     int64_t want = 256 / groups > 1 ? 256 / groups : 1;
-    const int64_t by_tiles = (keys / 32 + 2) / 3;
+    const int64_t by_tiles = (keys / 32 + 3) / 4;
     if (by_tiles >= 1 && by_tiles < want) want = by_tiles;
     auto round32 = [](int64_t x) { return (x + 31) / 32 * 32; };
     int64_t per = round32((keys + want - 1) / want);

@@ -46,7 +46,7 @@ def test_workspace_sizes(csl):
     # heads * (dim + 2) floats, sized for the larger split count of the paths the key
     # type could take (fp8 keys: 2 tiles per split, one while the launch would hold
     # fewer than 32 workgroups; bf16 keys: 16-head groups with about 256 workgroups but
-    # about three tiles or more per split, 32..256 keys per split, at most 8 splits
+    # about four tiles or more per split, 32..256 keys per split, at most 8 splits
     # while the keys fit 8 x 256)
     part = 64 * 514 * 4
     cnt = 16384
