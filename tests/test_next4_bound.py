@@ -53,3 +53,27 @@ def test_certified_fp4_prefilter_prunes_nothing_on_the_workload(orc):
     # ... and it keeps every entry: the bound dwarfs the scores' spread
     assert np.median(eps) > 5 * np.std(sig)
     assert kept == n
+
+
+def test_certified_page_bound_prunes_nothing_on_the_workload():
+    """The other exact first stage a two-stage indexer could use: skip a 64-entry page
+    when an upper bound of its scores is below the k-th score.  Per head, q.k over a
+    page is bounded by sum_d max(q_d kmax_d, q_d kmin_d) with the page's per-dim
+    extremes, and w_h ReLU(.) is monotone, so the bound holds for every entry.  Even
+    against the exact k-th score (the most a first stage could know) it prunes no
+    page of the decode workload's index keys: the bound is about 25 times the k-th
+    score."""
+    w = W.c4a_decode()
+    n, k = 4096, 64
+    qd = W.queries(w)
+    q = qd["q_idx"][0].float().numpy().astype(np.float64)
+    wh = qd["w_idx"][0].numpy().astype(np.float64)
+    keys = W.index_keys(w, 0, 0, n).float().numpy().astype(np.float64)
+    sig = (np.maximum(keys @ q.T, 0.0) * wh).sum(1)
+    tau = np.sort(sig)[-k]
+    pages = keys.reshape(n // 64, 64, -1)
+    kmax, kmin = pages.max(1), pages.min(1)
+    bound = (np.maximum(np.clip(q, 0, None) @ kmax.T + np.clip(q, None, 0) @ kmin.T, 0.0) * wh[:, None]).sum(0)
+    assert np.all(bound >= sig.reshape(n // 64, 64).max(1) - 1e-9)  # a certificate
+    assert int(np.count_nonzero(bound < tau)) == 0
+    assert bound.min() > 10 * tau
